@@ -1,0 +1,199 @@
+/*
+ * tpmlp.h - C ABI of libtpmlp: one GPU's share of the tensor-parallel MLP
+ * block (and of the head-sharded attention projections) on AMD MI355X
+ * (gfx950).
+ *
+ * Pages cited (address, title, section):
+ *   [csdn]   damodev.csdn.net/6a43867610ee7a33f284fb9e.html, 1 张量并行
+ *            (1.1 矩阵分块乘法: 列切分 / 外积和切分; 1.2.1 MLP 模块的张量并行)
+ *   [zouht]  io.zouht.com/197.html, 2 张量并行 (2.1 概念, the two block
+ *            equations; 2.2.1 在 LLM 中的应用方式; 2.3 代价, f and f*)
+ *   [wangyu] wangyu.me/posts/llm/tensor-parallelism/, 大语言模型并行策略（三）：
+ *            张量并行 (两种切分方式: 按列切分, 按行切分; 通信模式;
+ *            注意力机制中的张量并行; 多层感知机（MLP）中的张量并行)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - A linear layer is Y = X W with X of shape T x K (T tokens) and W of shape
+ *   K x N [wangyu 两种切分方式].  A column shard of W is K x N/tp (contiguous
+ *   columns i*N/tp .. (i+1)*N/tp-1); a row shard is K/tp x N (contiguous rows)
+ *   [wangyu 按列切分, 按行切分; zouht 2.1].
+ * - Every matrix is row-major.  A matrix argument M comes with a leading
+ *   dimension ldm (elements between consecutive rows), so a shard may be a
+ *   view into the full matrix (ldw = N for a column shard of W) or a packed
+ *   copy (ldw = N/tp).  The buffer must hold rows x ldm elements.
+ * - dtype is the storage type of inputs, weights and typed outputs:
+ *   TPMLP_BF16 (bfloat16 bits, uint16) or TPMLP_F32.  Products accumulate in
+ *   fp32.  Partial sums and all gradients of weights and inputs that get
+ *   summed are fp32.  Conversion to bf16 rounds to nearest even.
+ * - All matrix pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or retains them.  stream is a hipStream_t passed
+ *   as void* (NULL = the null stream).  Work is enqueued asynchronously on
+ *   it; the library never synchronises the stream.  Calls on one stream run
+ *   in order; calls on different streams that share an output race.
+ * - Every call validates its arguments on the host before it enqueues
+ *   anything.  On any error nothing is launched and no output is touched.
+ *   A kernel that fails at run time surfaces at the caller's next
+ *   synchronisation; a failed launch returns TPMLP_E_HIP.
+ * - Validation rules (status returned):
+ *     NULL required pointer                                -> TPMLP_E_NULL
+ *     tp_size < 1, or a split width not divisible by tp_size
+ *       (the pages' rule that heads or columns must divide evenly
+ *       [zouht 2.2.1])                                     -> TPMLP_E_DIVISIBILITY
+ *     T < 0, any other size < 1, ld < row width            -> TPMLP_E_SHAPE
+ *     a row width or ld not a multiple of 8 (bf16) or 4
+ *       (fp32), or a pointer not 16-byte aligned           -> TPMLP_E_ALIGNMENT
+ *     unknown dtype / activation                           -> TPMLP_E_DTYPE / TPMLP_E_ACT
+ *     workspace too small                                  -> TPMLP_E_WORKSPACE
+ *     sizes beyond 2^31-1 elements per dimension           -> TPMLP_E_SHAPE
+ *   T == 0 (an empty batch) is valid and enqueues nothing; outputs whose
+ *   size does not depend on T (weight gradients) are then written as zeros.
+ * - Status detail: tpmlp_last_error() returns a thread-local message about
+ *   the last non-OK status of the calling thread.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TPMLP_OK = 0,
+  TPMLP_E_NULL = 1,
+  TPMLP_E_SHAPE = 2,
+  TPMLP_E_DIVISIBILITY = 3,
+  TPMLP_E_ALIGNMENT = 4,
+  TPMLP_E_DTYPE = 5,
+  TPMLP_E_ACT = 6,
+  TPMLP_E_WORKSPACE = 7,
+  TPMLP_E_HIP = 8
+} tpmlp_status;
+
+typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
+
+/* The elementwise activation between the two layers: the pages name ReLU or
+ * GeLU [csdn 1.2.1]; GeLU is used in its tanh form,
+ * gelu(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+typedef enum { TPMLP_ACT_NONE = 0, TPMLP_ACT_GELU_TANH = 1 } tpmlp_act;
+
+/* Column-parallel layer, shard i:  H_i = X W_i + b_i,  Y_i = Act(H_i).
+ * [zouht 2.1 first equation; wangyu 按列切分; csdn 1.1 列切分]
+ *   X          [T, K], ldx >= K           full input (every shard sees all of X)
+ *   W_shard    [K, N/tp], ldw >= N/tp     column shard i of W [K, N]
+ *   bias_shard [N/tp] or NULL             slice i of the bias, added before Act
+ *   Y_shard    [T, N/tp], ldy >= N/tp     output, storage dtype
+ *   H_save     [T, N/tp] or NULL, ldh     pre-activation H_i, storage dtype
+ *                                         (kept for the backward pass)
+ * N is the full (unsharded) width; N % tp_size must be 0. */
+int column_parallel_fwd(void* stream, int dtype, int act, int64_t T, int64_t K, int64_t N,
+                        int tp_size, const void* X, int64_t ldx, const void* W_shard, int64_t ldw,
+                        const void* bias_shard, void* Y_shard, int64_t ldy, void* H_save,
+                        int64_t ldh);
+
+/* Row-parallel layer, shard i:  Z_i = X_i W_i, an fp32 partial of full size.
+ * [zouht 2.1 second equation; wangyu 按行切分; csdn 1.1 外积和切分]
+ *   X_shard    [T, K/tp], ldx >= K/tp     column block i of the layer input
+ *   W_shard    [K/tp, N], ldw >= N        row shard i of W [K, N]
+ *   Z_partial  [T, N] fp32, ldz >= N      this shard's partial; the layer
+ *                                         output is the sum over shards
+ * K is the full reduction width; K % tp_size must be 0. */
+int row_parallel_fwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size,
+                     const void* X_shard, int64_t ldx, const void* W_shard, int64_t ldw,
+                     float* Z_partial, int64_t ldz);
+
+/* out = sum over i < tp_size of partials[i], added in ascending i in fp32.
+ * This is the local arithmetic of the All-Reduce that ends a row-parallel
+ * layer (f* in the forward pass, f in the backward) [zouht 2.3; wangyu
+ * 通信模式]; here all partials sit in this GPU's memory, no collective runs.
+ *   partials   element (i, r, c) at partials[i*shard_stride + r*ldp + c]
+ *   out        [T, N] fp32, ldo >= N; may alias partial 0 exactly
+ *              (partials == out and ldp == ldo), not any other partial.
+ * T rows may be a sub-range of a larger partial (pass offset pointers), which
+ * is one GPU's share of a reduce-scatter. */
+int shard_partial_sum(void* stream, int tp_size, int64_t T, int64_t N, const float* partials,
+                      int64_t shard_stride, int64_t ldp, float* out, int64_t ldo);
+
+/* One shard of the MLP block Z = GeLU(X W1 + b1) W2, with W1 split by
+ * columns and W2 by rows so the activation output is already the row-split
+ * input of the second layer [csdn 1.2.1; zouht 2.2.1 前馈网络; wangyu 多层感知机
+ * （MLP）中的张量并行].  Fs = F / tp_size.
+ *   X          [T, h] (ld h)
+ *   W1_shard   [h, Fs], ldw1 >= Fs (ldw1 = F for a view into W1)
+ *   b1_shard   [Fs] or NULL
+ *   W2_shard   [Fs, h] (ld h): rows i*Fs.. of W2 [F, h]
+ *   H_save     [T, Fs] or NULL (ld Fs): pre-activation, storage dtype
+ *   A_save     [T, Fs] (ld Fs): activation output, storage dtype
+ *   Z_partial  [T, h] fp32 (ld h): this shard's partial of Z */
+int tp_mlp_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size,
+               const void* X, const void* W1_shard, int64_t ldw1, const void* b1_shard,
+               const void* W2_shard, void* H_save, void* A_save, float* Z_partial);
+
+/* Bytes of device workspace tp_mlp_bwd needs for these sizes (0 on bad args). */
+size_t tpmlp_bwd_workspace_bytes(int dtype, int64_t T, int64_t h, int64_t F, int tp_size);
+
+/* One shard's backward of the MLP block for the upstream gradient dZ of the
+ * block output.  Every row shard receives the same dZ because Z is the sum of
+ * the partials [wangyu 按行切分, backward]; the input gradient of the
+ * column-split layer is a sum over shards [wangyu 按列切分, backward; zouht
+ * 2.3, f in the backward pass].  With dA_i = dZ W2_i^T and
+ * dH_i = dA_i * GeLU'(H_i):
+ *   dX_partial [T, h] fp32     dH_i W1_i^T (sum over shards = dX)
+ *   dW1_shard  [h, Fs] fp32    X^T dH_i   (W1's orientation, ld Fs)
+ *   db1_shard  [Fs] fp32 / NULL column sums of dH_i (before bf16 rounding)
+ *   dW2_shard  [Fs, h] fp32    A_i^T dZ   (W2's orientation, ld h)
+ * Inputs: X, W1_shard (ldw1), W2_shard, H_save and A_save from tp_mlp_fwd, and
+ * dZ [T, h] in the storage dtype.  workspace: device memory of at least
+ * tpmlp_bwd_workspace_bytes() bytes, 256-byte aligned, owned by the caller. */
+int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size,
+               const void* X, const void* W1_shard, int64_t ldw1, const void* W2_shard,
+               const void* H_save, const void* A_save, const void* dZ, float* dX_partial,
+               float* dW1_shard, float* db1_shard, float* dW2_shard, void* workspace,
+               size_t workspace_bytes);
+
+/* Backward of one column shard Y_i = X W_i (+ b_i) with no activation (the
+ * QKV projection), dY_i the gradient of Y_i [wangyu 按列切分, backward]:
+ *   dX_partial [T, K] fp32, lddx >= K   dY_i W_i^T (sum over shards = dX)
+ *   dW_shard   [K, N/tp] fp32, lddw     X^T dY_i
+ *   db_shard   [N/tp] fp32 or NULL      column sums of dY_i
+ * X [T, K] (ldx), W_shard [K, N/tp] (ldw), dY [T, N/tp] (lddy), storage dtype. */
+int column_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size,
+                        const void* X, int64_t ldx, const void* W_shard, int64_t ldw,
+                        const void* dY, int64_t lddy, float* dX_partial, int64_t lddx,
+                        float* dW_shard, int64_t lddw, float* db_shard);
+
+/* Backward of one row shard Z_i = X_i W_i (the output projection) for the
+ * full upstream gradient dY [T, N], which every shard receives unchanged
+ * [wangyu 按行切分, backward]:
+ *   dX_shard   [T, K/tp] fp32, lddx     dY W_i^T: column block i of dX
+ *   dW_shard   [K/tp, N] fp32, lddw     X_i^T dY
+ * X_shard [T, K/tp] (ldx), W_shard [K/tp, N] (ldw), dY (lddy), storage dtype. */
+int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size,
+                     const void* X_shard, int64_t ldx, const void* W_shard, int64_t ldw,
+                     const void* dY, int64_t lddy, float* dX_shard, int64_t lddx,
+                     float* dW_shard, int64_t lddw);
+
+/* Status name, and the calling thread's message for its last non-OK status. */
+const char* tpmlp_status_string(int status);
+const char* tpmlp_last_error(void);
+
+/* Library version string. */
+const char* tpmlp_version(void);
+
+/* Per-kernel timing on the launch stream (a profiling aid for benchmarks).
+ * tpmlp_profile_enable(filter): while enabled, every kernel the library
+ * launches whose role name contains `filter` ("" = all, NULL = disable) is
+ * bracketed by two hipEvents recorded on the launch stream.
+ * tpmlp_profile_collect(buf, len): waits for the recorded events, writes a
+ * JSON object {"role": [launches, total_ms, kernel_symbol], ...} to buf
+ * (truncated to len) and clears the record.  Returns TPMLP_OK or an error. */
+int tpmlp_profile_enable(const char* filter);
+int tpmlp_profile_collect(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPMLP_H */

@@ -1,0 +1,222 @@
+"""Python binding of libtpmlp, the gfx950 tensor-parallel MLP library.
+
+Argument marshalling only: every function turns torch tensors into device
+pointers, leading dimensions and the current HIP stream, and calls the C
+entry point of the same name (declared in include/tpmlp.h).  All arithmetic
+runs in the library's HIP kernels; there is no fallback.  If libtpmlp.so is
+not built this module refuses to import.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (one runtime per process; its soname is
+the same as the system runtime's).
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "TpmlpError", "lib", "LIB_PATH", "F32", "BF16", "ACT_NONE", "ACT_GELU_TANH",
+    "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
+    "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "profile_enable",
+    "profile_collect", "status_string", "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+
+F32, BF16 = 0, 1
+ACT_NONE, ACT_GELU_TANH = 0, 1
+_ACTS = {"none": ACT_NONE, "gelu_tanh": ACT_GELU_TANH, ACT_NONE: ACT_NONE, ACT_GELU_TANH: ACT_GELU_TANH}
+
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+_SIGNATURES = {
+    "column_parallel_fwd": [_vp, _int, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64],
+    "row_parallel_fwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64],
+    "shard_partial_sum": [_vp, _int, _i64, _i64, _vp, _i64, _i64, _vp, _i64],
+    "tp_mlp_fwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
+    "tp_mlp_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                   _vp, _sz],
+    "column_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                            _i64, _vp],
+    "row_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64],
+    "tpmlp_bwd_workspace_bytes": [_int, _i64, _i64, _i64, _int],
+    "tpmlp_status_string": [_int],
+    "tpmlp_last_error": [],
+    "tpmlp_version": [],
+    "tpmlp_profile_enable": [ctypes.c_char_p],
+    "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
+}
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
+             "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
+
+
+class TpmlpError(RuntimeError):
+    """A non-OK status from libtpmlp."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+        self.message = message
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m linear_layers_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, ctypes.c_int)
+    return handle
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.tpmlp_status_string(status).decode()
+
+
+def version() -> str:
+    return lib.tpmlp_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TpmlpError(status, f"{status_string(status)}: {lib.tpmlp_last_error().decode()}")
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; libtpmlp takes bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _ld(t: Optional[torch.Tensor], width: int) -> int:
+    """Leading dimension of a row-major 2-D tensor (or view)."""
+    if t is None:
+        return width
+    if t.dim() != 2:
+        raise ValueError(f"expected a 2-D tensor, got shape {tuple(t.shape)}")
+    if t.shape[0] > 1 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    return t.stride(0) if t.shape[0] > 1 else width
+
+
+def _stream(stream, like: torch.Tensor):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return torch.cuda.current_stream(like.device).cuda_stream
+
+
+def _require_contiguous(name: str, t: Optional[torch.Tensor]) -> None:
+    if t is not None and t.numel() > 0 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def column_parallel_fwd(X, W_shard, tp_size: int, Y_shard, bias_shard=None, H_save=None,
+                        act="gelu_tanh", stream=None) -> None:
+    """Y_shard = Act(X @ W_shard + bias_shard); optionally H_save = X @ W_shard + bias_shard."""
+    T, K = X.shape
+    Ns = W_shard.shape[1]
+    _check(lib.column_parallel_fwd(_stream(stream, X), _dtype(X), _ACTS[act], T, K, Ns * tp_size, tp_size,
+                                   _ptr(X), _ld(X, K), _ptr(W_shard), _ld(W_shard, Ns), _ptr(bias_shard),
+                                   _ptr(Y_shard), _ld(Y_shard, Ns), _ptr(H_save), _ld(H_save, Ns)))
+
+
+def row_parallel_fwd(X_shard, W_shard, tp_size: int, Z_partial, stream=None) -> None:
+    """Z_partial (fp32) = X_shard @ W_shard."""
+    T, Ks = X_shard.shape
+    N = W_shard.shape[1]
+    _check(lib.row_parallel_fwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
+                                _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N),
+                                _ptr(Z_partial), _ld(Z_partial, N)))
+
+
+def shard_partial_sum(partials, out, tp_size: Optional[int] = None, stream=None) -> None:
+    """out = partials[0] + ... + partials[tp-1] (fp32, ascending).
+
+    ``partials`` is a [tp, T, N] tensor (or a view with any shard stride and
+    row stride); ``out`` is [T, N].
+    """
+    tp = partials.shape[0] if tp_size is None else tp_size
+    T, N = partials.shape[1], partials.shape[2]
+    if partials.dim() != 3 or (T > 1 and N > 1 and partials.stride(2) != 1):
+        raise ValueError("partials must be [tp, T, N] with contiguous rows")
+    _check(lib.shard_partial_sum(_stream(stream, out), tp, T, N, _ptr(partials), partials.stride(0),
+                                 partials.stride(1) if T > 1 else N, _ptr(out), _ld(out, N)))
+
+
+def tp_mlp_fwd(X, W1_shard, b1_shard, W2_shard, tp_size: int, A_save, Z_partial, H_save=None,
+               stream=None) -> None:
+    """One shard of Z = GeLU(X W1 + b1) W2: writes A_save, H_save (optional) and Z_partial."""
+    T, h = X.shape
+    Fs = W1_shard.shape[1]
+    for n, t in (("X", X), ("W2_shard", W2_shard), ("A_save", A_save), ("Z_partial", Z_partial), ("H_save", H_save)):
+        _require_contiguous(n, t)
+    _check(lib.tp_mlp_fwd(_stream(stream, X), _dtype(X), T, h, Fs * tp_size, tp_size, _ptr(X), _ptr(W1_shard),
+                          _ld(W1_shard, Fs), _ptr(b1_shard), _ptr(W2_shard), _ptr(H_save), _ptr(A_save),
+                          _ptr(Z_partial)))
+
+
+def tpmlp_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: int) -> int:
+    return int(lib.tpmlp_bwd_workspace_bytes(dtype, T, h, F, tp_size))
+
+
+def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_partial, dW1_shard, dW2_shard,
+               db1_shard=None, workspace=None, stream=None) -> None:
+    """One shard's backward; workspace is a device uint8 tensor (allocated here if None)."""
+    T, h = X.shape
+    Fs = W1_shard.shape[1]
+    F = Fs * tp_size
+    for n, t in (("X", X), ("W2_shard", W2_shard), ("H_save", H_save), ("A_save", A_save), ("dZ", dZ),
+                 ("dX_partial", dX_partial), ("dW1_shard", dW1_shard), ("dW2_shard", dW2_shard)):
+        _require_contiguous(n, t)
+    dt = _dtype(X)
+    if workspace is None:
+        workspace = torch.empty(max(1, tpmlp_bwd_workspace_bytes(dt, T, h, F, tp_size)), dtype=torch.uint8,
+                                device=X.device)
+    _check(lib.tp_mlp_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W1_shard), _ld(W1_shard, Fs),
+                          _ptr(W2_shard), _ptr(H_save), _ptr(A_save), _ptr(dZ), _ptr(dX_partial), _ptr(dW1_shard),
+                          _ptr(db1_shard), _ptr(dW2_shard), _ptr(workspace), workspace.numel()))
+
+
+def column_parallel_bwd(X, W_shard, dY, tp_size: int, dX_partial, dW_shard, db_shard=None, stream=None) -> None:
+    """dX_partial = dY W_shard^T, dW_shard = X^T dY, db_shard = column sums of dY (fp32 outputs)."""
+    T, K = X.shape
+    Ns = W_shard.shape[1]
+    _check(lib.column_parallel_bwd(_stream(stream, X), _dtype(X), T, K, Ns * tp_size, tp_size, _ptr(X), _ld(X, K),
+                                   _ptr(W_shard), _ld(W_shard, Ns), _ptr(dY), _ld(dY, Ns), _ptr(dX_partial),
+                                   _ld(dX_partial, K), _ptr(dW_shard), _ld(dW_shard, Ns), _ptr(db_shard)))
+
+
+def row_parallel_bwd(X_shard, W_shard, dY, tp_size: int, dX_shard, dW_shard, stream=None) -> None:
+    """dX_shard = dY W_shard^T, dW_shard = X_shard^T dY (fp32 outputs)."""
+    T, Ks = X_shard.shape
+    N = W_shard.shape[1]
+    _check(lib.row_parallel_bwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
+                                _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N), _ptr(dY),
+                                _ld(dY, N), _ptr(dX_shard), _ld(dX_shard, Ks), _ptr(dW_shard), _ld(dW_shard, N)))
+
+
+def profile_enable(filter: Optional[str] = "") -> None:
+    """Bracket matching kernel launches with HIP events (None disables)."""
+    _check(lib.tpmlp_profile_enable(None if filter is None else filter.encode()))
+
+
+def profile_collect() -> dict:
+    """{role|symbol: (launches, total_ms, symbol)} of the launches recorded so far."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(lib.tpmlp_profile_collect(buf, len(buf)))
+    return {k: tuple(v) for k, v in json.loads(buf.value.decode() or "{}").items()}

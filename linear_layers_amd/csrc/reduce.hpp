@@ -1,0 +1,74 @@
+// Bandwidth-bound kernels of libtpmlp: the sum of shard partials, the final
+// reduction of per-tile column sums, and a zero fill.
+#pragma once
+
+#include "common.hpp"
+
+namespace tpmlp {
+
+// out[r, c] = sum_{i < tp} P[i*shard_stride + r*ldp + c], added in ascending i.
+// Each thread owns 16-byte column groups of a row and keeps all tp loads of a
+// group in flight together; rows are spread over the grid.  `UNROLL` groups
+// per thread per row pass raise the bytes in flight per wave.
+template <int UNROLL>
+__global__ void __launch_bounds__(256)
+partial_sum_kernel(const float* __restrict__ P, int64_t shard_stride, int64_t ldp,
+                   float* out, int64_t ldo, int tp, int T, int nvec) {
+  const int per_row_blocks = (nvec + 256 * UNROLL - 1) / (256 * UNROLL);
+  const int64_t total_blocks = (int64_t)T * per_row_blocks;
+  for (int64_t b = blockIdx.x; b < total_blocks; b += gridDim.x) {
+    const int r = (int)(b / per_row_blocks);
+    const int cb = (int)(b - (int64_t)r * per_row_blocks);
+    const float* src = P + (int64_t)r * ldp;
+    float* dst = out + (int64_t)r * ldo;
+    f32x4_t s[UNROLL];
+    int cv[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      cv[u] = (cb * UNROLL + u) * 256 + threadIdx.x;
+      s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (cv[u] < nvec) s[u] = *reinterpret_cast<const f32x4_t*>(src + 4 * (int64_t)cv[u]);
+    }
+    for (int i = 1; i < tp; ++i) {
+      const float* si = src + (int64_t)i * shard_stride;
+      f32x4_t x[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (cv[u] < nvec) x[u] = *reinterpret_cast<const f32x4_t*>(si + 4 * (int64_t)cv[u]);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        if (cv[u] < nvec) {
+          s[u][0] += x[u][0];
+          s[u][1] += x[u][1];
+          s[u][2] += x[u][2];
+          s[u][3] += x[u][3];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if (cv[u] < nvec) *reinterpret_cast<f32x4_t*>(dst + 4 * (int64_t)cv[u]) = s[u];
+  }
+}
+
+// out[n] = sum_{t < rows} part[t*N + n] in ascending t.
+__global__ void __launch_bounds__(256)
+colsum_reduce_kernel(const float* __restrict__ part, int rows, int N, float* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.0f;
+  for (int t = 0; t < rows; ++t) s += part[(int64_t)t * N + n];
+  out[n] = s;
+}
+
+// Zero rows x cols floats with row stride ld (a kernel, so it is safe inside
+// captured graphs, unlike a memset node).
+__global__ void __launch_bounds__(256)
+fill_zero_kernel(float* __restrict__ p, int rows, int cols, int64_t ld) {
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols;
+    p[r * ld + (i - r * cols)] = 0.0f;
+  }
+}
+
+}  // namespace tpmlp

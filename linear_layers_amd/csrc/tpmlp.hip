@@ -1,0 +1,636 @@
+// libtpmlp: C ABI, argument validation, launch planning and the per-kernel
+// timing hook.  The operations and their conventions are documented in
+// include/tpmlp.h; the kernels live in gemm.hpp and reduce.hpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/tpmlp.h"
+#include "gemm.hpp"
+#include "reduce.hpp"
+
+using namespace tpmlp;
+
+namespace {
+
+// ------------------------------------------------------------------ status --
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TPMLP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TPMLP_TRY(expr)               \
+  do {                                \
+    int _st = (expr);                 \
+    if (_st != TPMLP_OK) return _st;  \
+  } while (0)
+
+// -------------------------------------------------------------- profiling --
+struct ProfRecord {
+  std::string role, symbol;
+  hipEvent_t start, stop;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  std::string filter;
+  std::vector<ProfRecord> records;
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+// Launches `kernel` on `stream`; when profiling matches `role`, brackets the
+// launch with two events on the same stream.
+template <typename Kernel, typename... Args>
+int launch(const char* role, const char* symbol, Kernel kernel, dim3 grid, dim3 block,
+           hipStream_t stream, Args... args) {
+  Profiler& P = prof();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (P.enabled && std::strstr(role, P.filter.c_str()) != nullptr) {
+      e0 = P.take();
+      e1 = P.take();
+    }
+  }
+  if (e0 && e1) {
+    hipError_t e = hipEventRecord(e0, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return hip_fail(err, role);
+  if (e0 && e1) {
+    hipError_t e = hipEventRecord(e1, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    std::lock_guard<std::mutex> lk(P.mu);
+    P.records.push_back({role, symbol, e0, e1});
+  }
+  return TPMLP_OK;
+}
+
+// ------------------------------------------------------------ device info --
+int device_cus(int* cus) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(TPMLP_E_HIP, "device index %d out of range", dev);
+  if (cache[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    cache[dev] = n > 0 ? n : 256;
+  }
+  *cus = cache[dev];
+  return TPMLP_OK;
+}
+
+// ------------------------------------------------------------- validation --
+int elem_size(int dtype) { return dtype == TPMLP_BF16 ? 2 : 4; }
+int chunk_elems(int dtype) { return 16 / elem_size(dtype); }
+
+int check_dtype(int dtype) {
+  if (dtype != TPMLP_BF16 && dtype != TPMLP_F32) return fail(TPMLP_E_DTYPE, "unknown dtype %d", dtype);
+  return TPMLP_OK;
+}
+
+int check_act(int act) {
+  if (act != TPMLP_ACT_NONE && act != TPMLP_ACT_GELU_TANH) return fail(TPMLP_E_ACT, "unknown activation %d", act);
+  return TPMLP_OK;
+}
+
+int check_split(const char* what, int64_t n, int tp) {
+  if (tp < 1) return fail(TPMLP_E_DIVISIBILITY, "tp_size %d < 1", tp);
+  if (n >= 1 && n % tp != 0)
+    return fail(TPMLP_E_DIVISIBILITY, "%s = %lld is not divisible by tp_size %d", what, (long long)n, tp);
+  return TPMLP_OK;
+}
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+int check_rows(const char* what, int64_t t) {
+  if (t < 0 || t > kMaxDim) return fail(TPMLP_E_SHAPE, "%s = %lld out of range [0, 2^31-1]", what, (long long)t);
+  return TPMLP_OK;
+}
+
+int check_dim(const char* what, int64_t n) {
+  if (n < 1 || n > kMaxDim) return fail(TPMLP_E_SHAPE, "%s = %lld out of range [1, 2^31-1]", what, (long long)n);
+  return TPMLP_OK;
+}
+
+// A matrix operand: rows x width with leading dimension ld, element count
+// multiple `vec` for width and ld, pointer 16-byte aligned.
+int check_mat(const char* what, const void* p, int64_t rows, int64_t width, int64_t ld, int vec,
+              bool required = true) {
+  const bool empty = rows == 0 || width == 0;
+  if (p == nullptr) {
+    if (required && !empty) return fail(TPMLP_E_NULL, "%s is NULL", what);
+    return TPMLP_OK;
+  }
+  if (ld < width) return fail(TPMLP_E_SHAPE, "%s: ld %lld < width %lld", what, (long long)ld, (long long)width);
+  if (width % vec != 0 || ld % vec != 0)
+    return fail(TPMLP_E_ALIGNMENT, "%s: width %lld and ld %lld must be multiples of %d elements", what,
+                (long long)width, (long long)ld, vec);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(TPMLP_E_ALIGNMENT, "%s is not 16-byte aligned", what);
+  return TPMLP_OK;
+}
+
+int check_vec(const char* what, const void* p, int64_t n, bool required) {
+  if (p == nullptr) {
+    if (required && n > 0) return fail(TPMLP_E_NULL, "%s is NULL", what);
+    return TPMLP_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(TPMLP_E_ALIGNMENT, "%s is not 16-byte aligned", what);
+  return TPMLP_OK;
+}
+
+// --------------------------------------------------------------- planning --
+struct TileCfg {
+  int bm, bn;
+  float eff;  // relative per-CU throughput of the tile shape
+};
+constexpr TileCfg kCfgBf16[] = {{256, 256, 1.00f}, {256, 128, 0.90f}, {128, 128, 0.75f}};
+constexpr TileCfg kCfgF32[] = {{128, 128, 1.00f}, {64, 64, 0.60f}};
+constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
+
+int plan_cfg(int dtype, int M, int N, int cus) {
+  const TileCfg* cfgs = dtype == TPMLP_BF16 ? kCfgBf16 : kCfgF32;
+  const int n = dtype == TPMLP_BF16 ? 3 : 2;
+  int best = 0;
+  double best_score = -1.0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t tiles = (int64_t)((M + cfgs[i].bm - 1) / cfgs[i].bm) * ((N + cfgs[i].bn - 1) / cfgs[i].bn);
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    // useful fraction of the CU-rounds, times the tile's own efficiency, times
+    // the fraction of the padded tile area that is real output
+    const double fill = (double)tiles / (double)(rounds * cus);
+    const double pad = ((double)M * N) / ((double)tiles * cfgs[i].bm * cfgs[i].bn);
+    const double score = fill * cfgs[i].eff * pad;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = i;
+    }
+  }
+  return best;
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
+int run_gemm_cfg(const char* role, GemmArgs a, hipStream_t s) {
+  constexpr int BK = 8 * Elem<T>::kPerChunk;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  if (a.splits < 1) a.splits = 1;
+  if (a.splits == 1) {
+    a.k_per_split = ((a.K + BK - 1) / BK) * BK;
+  } else {
+    const int per = (a.K + a.splits - 1) / a.splits;
+    a.k_per_split = ((per + BK - 1) / BK) * BK;
+  }
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+  if (grid <= 0) return TPMLP_OK;
+  if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
+  char sym[128];
+  snprintf(sym, sizeof(sym), "gemm_kernel<%s,%d,%d,%d,%d,%d,%d,%d>", sizeof(T) == 2 ? "bf16" : "f32", BM, BN,
+           WGM, WGN, (int)AK, (int)BKM, EPI);
+  return launch(role, sym, gemm_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI>, dim3((unsigned)grid),
+                dim3(WGM * WGN * 64), s, a);
+}
+
+template <bool AK, bool BKM, int EPI>
+int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return TPMLP_OK;
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  const int cfg = plan_cfg(dtype, a.M, a.N, cus);
+  if (dtype == TPMLP_BF16) {
+    switch (cfg) {
+      case 0: return run_gemm_cfg<bf16_t, 256, 256, 2, 2, AK, BKM, EPI>(role, a, s);
+      case 1: return run_gemm_cfg<bf16_t, 256, 128, 2, 2, AK, BKM, EPI>(role, a, s);
+      default: return run_gemm_cfg<bf16_t, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
+    }
+  }
+  switch (cfg) {
+    case 0: return run_gemm_cfg<float, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
+    default: return run_gemm_cfg<float, 64, 64, 2, 2, AK, BKM, EPI>(role, a, s);
+  }
+}
+
+GemmArgs gemm_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K) {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = A;
+  a.lda = lda;
+  a.B = B;
+  a.ldb = ldb;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.splits = 1;
+  a.act = kActNone;
+  return a;
+}
+
+int fill_zero(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || p == nullptr) return TPMLP_OK;
+  const int64_t total = rows * cols;
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+  return launch("fill_zero", "fill_zero_kernel", fill_zero_kernel, dim3(grid), dim3(256), s, p, (int)rows,
+                (int)cols, ld);
+}
+
+int partial_sum(int tp, int64_t T, int64_t N, const float* P, int64_t stride, int64_t ldp, float* out,
+                int64_t ldo, hipStream_t s, const char* role = "partial_sum") {
+  if (T == 0) return TPMLP_OK;
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  const int nvec = (int)(N / 4);
+  constexpr int U = 2;
+  const int64_t per_row = (nvec + 256 * U - 1) / (256 * U);
+  const int64_t blocks = T * per_row;
+  const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * 16);
+  return launch(role, "partial_sum_kernel<2>", partial_sum_kernel<U>, dim3(grid), dim3(256), s, P, stride, ldp,
+                out, ldo, tp, (int)T, nvec);
+}
+
+// Column-parallel forward body (arguments already validated).
+int col_fwd(hipStream_t s, int dtype, int act, int64_t T, int64_t K, int64_t Ns, const void* X, int64_t ldx,
+            const void* W, int64_t ldw, const void* bias, void* Y, int64_t ldy, void* H, int64_t ldh,
+            const char* role) {
+  if (T == 0) return TPMLP_OK;
+  GemmArgs a = gemm_args(X, ldx, W, ldw, T, Ns, K);
+  a.Y = Y;
+  a.ldy = ldy;
+  a.H = H;
+  a.ldh = ldh;
+  a.bias = bias;
+  a.act = act;
+  return run_gemm<true, false, kEpiBiasAct>(role, dtype, a, s);
+}
+
+int row_fwd(hipStream_t s, int dtype, int64_t T, int64_t Ks, int64_t N, const void* X, int64_t ldx,
+            const void* W, int64_t ldw, float* Z, int64_t ldz, const char* role) {
+  if (T == 0) return TPMLP_OK;
+  GemmArgs a = gemm_args(X, ldx, W, ldw, T, N, Ks);
+  a.C = Z;
+  a.ldc = ldz;
+  return run_gemm<true, false, kEpiF32>(role, dtype, a, s);
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t dh_off, cs_off, total;
+};
+
+BwdLayout bwd_layout(int dtype, int64_t T, int64_t Fs) {
+  BwdLayout L;
+  L.dh_off = 0;
+  const size_t dh = align256((size_t)T * Fs * elem_size(dtype));
+  L.cs_off = dh;
+  const size_t cs = align256((size_t)((T + kMinBM - 1) / kMinBM) * Fs * sizeof(float));
+  L.total = dh + cs;
+  return L;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* tpmlp_version(void) { return "libtpmlp 0.1 (gfx950)"; }
+
+const char* tpmlp_status_string(int status) {
+  switch (status) {
+    case TPMLP_OK: return "TPMLP_OK";
+    case TPMLP_E_NULL: return "TPMLP_E_NULL";
+    case TPMLP_E_SHAPE: return "TPMLP_E_SHAPE";
+    case TPMLP_E_DIVISIBILITY: return "TPMLP_E_DIVISIBILITY";
+    case TPMLP_E_ALIGNMENT: return "TPMLP_E_ALIGNMENT";
+    case TPMLP_E_DTYPE: return "TPMLP_E_DTYPE";
+    case TPMLP_E_ACT: return "TPMLP_E_ACT";
+    case TPMLP_E_WORKSPACE: return "TPMLP_E_WORKSPACE";
+    case TPMLP_E_HIP: return "TPMLP_E_HIP";
+    default: return "TPMLP_E_UNKNOWN";
+  }
+}
+
+const char* tpmlp_last_error(void) { return g_last_error.c_str(); }
+
+int column_parallel_fwd(void* stream, int dtype, int act, int64_t T, int64_t K, int64_t N, int tp_size,
+                        const void* X, int64_t ldx, const void* W_shard, int64_t ldw, const void* bias_shard,
+                        void* Y_shard, int64_t ldy, void* H_save, int64_t ldh) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_act(act));
+  TPMLP_TRY(check_split("N", N, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("K", K));
+  TPMLP_TRY(check_dim("N", N));
+  const int64_t Ns = N / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X", X, T, K, ldx, v));
+  TPMLP_TRY(check_mat("W_shard", W_shard, K, Ns, ldw, v));
+  TPMLP_TRY(check_vec("bias_shard", bias_shard, Ns, false));
+  TPMLP_TRY(check_mat("Y_shard", Y_shard, T, Ns, ldy, v));
+  TPMLP_TRY(check_mat("H_save", H_save, T, Ns, ldh, v, false));
+  return col_fwd((hipStream_t)stream, dtype, act, T, K, Ns, X, ldx, W_shard, ldw, bias_shard, Y_shard, ldy, H_save,
+                 ldh, "gemm.col_fwd");
+}
+
+int row_parallel_fwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size, const void* X_shard,
+                     int64_t ldx, const void* W_shard, int64_t ldw, float* Z_partial, int64_t ldz) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("K", K, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("K", K));
+  TPMLP_TRY(check_dim("N", N));
+  const int64_t Ks = K / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X_shard", X_shard, T, Ks, ldx, v));
+  TPMLP_TRY(check_mat("W_shard", W_shard, Ks, N, ldw, v));
+  TPMLP_TRY(check_mat("Z_partial", Z_partial, T, N, ldz, 4));
+  return row_fwd((hipStream_t)stream, dtype, T, Ks, N, X_shard, ldx, W_shard, ldw, Z_partial, ldz,
+                 "gemm.row_fwd");
+}
+
+int shard_partial_sum(void* stream, int tp_size, int64_t T, int64_t N, const float* partials, int64_t shard_stride,
+                      int64_t ldp, float* out, int64_t ldo) {
+  if (tp_size < 1) return fail(TPMLP_E_DIVISIBILITY, "tp_size %d < 1", tp_size);
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("N", N));
+  if (shard_stride < 0) return fail(TPMLP_E_SHAPE, "shard_stride %lld < 0", (long long)shard_stride);
+  if (shard_stride % 4 != 0) return fail(TPMLP_E_ALIGNMENT, "shard_stride must be a multiple of 4 floats");
+  TPMLP_TRY(check_mat("partials", partials, T, N, ldp, 4));
+  TPMLP_TRY(check_mat("out", out, T, N, ldo, 4));
+  if (out != partials && T > 0) {
+    // out may alias partial 0 exactly; any other overlap with a partial is refused.
+    const char* o0 = reinterpret_cast<const char*>(out);
+    const char* o1 = o0 + ((T - 1) * ldo + N) * sizeof(float);
+    for (int i = 0; i < tp_size; ++i) {
+      const char* p0 = reinterpret_cast<const char*>(partials + (int64_t)i * shard_stride);
+      const char* p1 = p0 + ((T - 1) * ldp + N) * sizeof(float);
+      if (o0 < p1 && p0 < o1) return fail(TPMLP_E_SHAPE, "out overlaps partial %d", i);
+    }
+  } else if (out == partials && ldo != ldp) {
+    return fail(TPMLP_E_SHAPE, "in-place sum into partial 0 needs ldo == ldp");
+  }
+  return partial_sum(tp_size, T, N, partials, shard_stride, ldp, out, ldo, (hipStream_t)stream);
+}
+
+int tp_mlp_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
+               const void* W1_shard, int64_t ldw1, const void* b1_shard, const void* W2_shard, void* H_save,
+               void* A_save, float* Z_partial) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X", X, T, h, h, v));
+  TPMLP_TRY(check_mat("W1_shard", W1_shard, h, Fs, ldw1, v));
+  TPMLP_TRY(check_vec("b1_shard", b1_shard, Fs, false));
+  TPMLP_TRY(check_mat("W2_shard", W2_shard, Fs, h, h, v));
+  TPMLP_TRY(check_mat("H_save", H_save, T, Fs, Fs, v, false));
+  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, v));
+  TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
+  hipStream_t s = (hipStream_t)stream;
+  TPMLP_TRY(col_fwd(s, dtype, TPMLP_ACT_GELU_TANH, T, h, Fs, X, h, W1_shard, ldw1, b1_shard, A_save, Fs, H_save, Fs,
+                    "gemm.mlp_fwd1"));
+  return row_fwd(s, dtype, T, Fs, h, A_save, Fs, W2_shard, h, Z_partial, h, "gemm.mlp_fwd2");
+}
+
+size_t tpmlp_bwd_workspace_bytes(int dtype, int64_t T, int64_t h, int64_t F, int tp_size) {
+  if ((dtype != TPMLP_BF16 && dtype != TPMLP_F32) || tp_size < 1 || T < 0 || T > kMaxDim || h < 1 || F < 1 ||
+      F % tp_size != 0)
+    return 0;
+  (void)h;
+  return bwd_layout(dtype, T, F / tp_size).total;
+}
+
+int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
+               const void* W1_shard, int64_t ldw1, const void* W2_shard, const void* H_save, const void* A_save,
+               const void* dZ, float* dX_partial, float* dW1_shard, float* db1_shard, float* dW2_shard,
+               void* workspace, size_t workspace_bytes) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X", X, T, h, h, v));
+  TPMLP_TRY(check_mat("W1_shard", W1_shard, h, Fs, ldw1, v));
+  TPMLP_TRY(check_mat("W2_shard", W2_shard, Fs, h, h, v));
+  TPMLP_TRY(check_mat("H_save", H_save, T, Fs, Fs, v));
+  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, v));
+  TPMLP_TRY(check_mat("dZ", dZ, T, h, h, v));
+  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
+  TPMLP_TRY(check_mat("dW1_shard", dW1_shard, h, Fs, Fs, 4));
+  TPMLP_TRY(check_vec("db1_shard", db1_shard, Fs, false));
+  TPMLP_TRY(check_mat("dW2_shard", dW2_shard, Fs, h, h, 4));
+  const BwdLayout L = bwd_layout(dtype, T, Fs);
+  if (T > 0) {
+    if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+    if (workspace_bytes < L.total)
+      return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    TPMLP_TRY(fill_zero(dW1_shard, h, Fs, Fs, s));
+    TPMLP_TRY(fill_zero(dW2_shard, Fs, h, h, s));
+    return fill_zero(db1_shard, 1, Fs, Fs, s);
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* dH = ws + L.dh_off;
+  float* cs = reinterpret_cast<float*>(ws + L.cs_off);
+
+  // dH = (dZ W2_i^T) * GeLU'(H_i), with per-tile column sums of dH.
+  GemmArgs a = gemm_args(dZ, h, W2_shard, h, T, Fs, h);
+  a.Y = dH;
+  a.ldy = Fs;
+  a.H = const_cast<void*>(H_save);
+  a.ldh = Fs;
+  a.colsum = db1_shard ? cs : nullptr;
+  a.act = kActGeluTanh;
+  // The tile rows used by the plan decide how many column-sum rows exist.
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.mlp_dgrad_act", dtype, a, s)));
+  if (db1_shard) {
+    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, cus);
+    const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
+    const int rows = (int)((T + bm - 1) / bm);
+    TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 255) / 256)),
+                     dim3(256), s, (const float*)cs, rows, (int)Fs, db1_shard));
+  }
+  // dW2_i = A_i^T dZ
+  a = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
+  a.C = dW2_shard;
+  a.ldc = h;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad2", dtype, a, s)));
+  // dW1_i = X^T dH_i
+  a = gemm_args(X, h, dH, Fs, h, Fs, T);
+  a.C = dW1_shard;
+  a.ldc = Fs;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad1", dtype, a, s)));
+  // dX_i = dH_i W1_i^T
+  a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
+  a.C = dX_partial;
+  a.ldc = h;
+  return run_gemm<true, true, kEpiF32>("gemm.mlp_dgrad1", dtype, a, s);
+}
+
+int column_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size, const void* X,
+                        int64_t ldx, const void* W_shard, int64_t ldw, const void* dY, int64_t lddy,
+                        float* dX_partial, int64_t lddx, float* dW_shard, int64_t lddw, float* db_shard) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("N", N, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("K", K));
+  TPMLP_TRY(check_dim("N", N));
+  const int64_t Ns = N / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X", X, T, K, ldx, v));
+  TPMLP_TRY(check_mat("W_shard", W_shard, K, Ns, ldw, v));
+  TPMLP_TRY(check_mat("dY", dY, T, Ns, lddy, v));
+  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, K, lddx, 4));
+  TPMLP_TRY(check_mat("dW_shard", dW_shard, K, Ns, lddw, 4));
+  TPMLP_TRY(check_vec("db_shard", db_shard, Ns, false));
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    TPMLP_TRY(fill_zero(dW_shard, K, Ns, lddw, s));
+    return fill_zero(db_shard, 1, Ns, Ns, s);
+  }
+  // dX_partial = dY W_i^T
+  GemmArgs a = gemm_args(dY, lddy, W_shard, ldw, T, K, Ns);
+  a.C = dX_partial;
+  a.ldc = lddx;
+  TPMLP_TRY((run_gemm<true, true, kEpiF32>("gemm.col_dgrad", dtype, a, s)));
+  // dW_i = X^T dY (and db_i = column sums of dY, taken from the same tiles)
+  a = gemm_args(X, ldx, dY, lddy, K, Ns, T);
+  a.C = dW_shard;
+  a.ldc = lddw;
+  a.colsum = db_shard;
+  return run_gemm<false, false, kEpiF32>("gemm.col_wgrad", dtype, a, s);
+}
+
+int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size, const void* X_shard,
+                     int64_t ldx, const void* W_shard, int64_t ldw, const void* dY, int64_t lddy, float* dX_shard,
+                     int64_t lddx, float* dW_shard, int64_t lddw) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("K", K, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("K", K));
+  TPMLP_TRY(check_dim("N", N));
+  const int64_t Ks = K / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X_shard", X_shard, T, Ks, ldx, v));
+  TPMLP_TRY(check_mat("W_shard", W_shard, Ks, N, ldw, v));
+  TPMLP_TRY(check_mat("dY", dY, T, N, lddy, v));
+  TPMLP_TRY(check_mat("dX_shard", dX_shard, T, Ks, lddx, 4));
+  TPMLP_TRY(check_mat("dW_shard", dW_shard, Ks, N, lddw, 4));
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) return fill_zero(dW_shard, Ks, N, lddw, s);
+  // dX_i = dY W_i^T
+  GemmArgs a = gemm_args(dY, lddy, W_shard, ldw, T, Ks, N);
+  a.C = dX_shard;
+  a.ldc = lddx;
+  TPMLP_TRY((run_gemm<true, true, kEpiF32>("gemm.row_dgrad", dtype, a, s)));
+  // dW_i = X_i^T dY
+  a = gemm_args(X_shard, ldx, dY, lddy, Ks, N, T);
+  a.C = dW_shard;
+  a.ldc = lddw;
+  return run_gemm<false, false, kEpiF32>("gemm.row_wgrad", dtype, a, s);
+}
+
+int tpmlp_profile_enable(const char* filter) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.enabled = filter != nullptr;
+  P.filter = filter ? filter : "";
+  return TPMLP_OK;
+}
+
+int tpmlp_profile_collect(char* buf, size_t len) {
+  Profiler& P = prof();
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    recs.swap(P.records);
+  }
+  struct Agg {
+    std::string role, symbol;
+    long n;
+    double ms;
+  };
+  std::vector<Agg> aggs;
+  int status = TPMLP_OK;
+  for (auto& r : recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && status == TPMLP_OK) status = hip_fail(e, "profile event");
+    auto it = std::find_if(aggs.begin(), aggs.end(),
+                           [&](const Agg& a) { return a.role == r.role && a.symbol == r.symbol; });
+    if (it == aggs.end()) aggs.push_back({r.role, r.symbol, 1, (double)ms});
+    else { it->n += 1; it->ms += ms; }
+  }
+  {
+    std::lock_guard<std::mutex> lk(P.mu);
+    for (auto& r : recs) {
+      P.pool.push_back(r.start);
+      P.pool.push_back(r.stop);
+    }
+  }
+  std::string out = "{";
+  for (size_t i = 0; i < aggs.size(); ++i) {
+    char item[512];
+    snprintf(item, sizeof(item), "%s\"%s|%s\": [%ld, %.6f, \"%s\"]", i ? ", " : "", aggs[i].role.c_str(),
+             aggs[i].symbol.c_str(), aggs[i].n, aggs[i].ms, aggs[i].symbol.c_str());
+    out += item;
+  }
+  out += "}";
+  if (buf && len > 0) {
+    std::strncpy(buf, out.c_str(), len - 1);
+    buf[len - 1] = '\0';
+  }
+  return status;
+}
+
+}  // extern "C"

@@ -9,3 +9,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload cases")
+    # The binding refuses to import without the library; build it once if absent.
+    lib = os.path.join(ROOT, "linear_layers_amd", "libtpmlp.so")
+    if not os.path.exists(lib):
+        from linear_layers_amd.build import build
+        build()

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function include/tpmlp.h declares, and
+refuses bad arguments on the host before any HIP call, with the documented
+status codes.  Only invalid calls are made here, so no kernel is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_layers_amd as tl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_DIV, E_ALIGN, E_DTYPE, E_ACT, E_WS = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x100000  # a 16-byte aligned stand-in address; never dereferenced (validation fails first)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tpmlp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
+            "column_parallel_bwd", "row_parallel_bwd"} <= set(names)
+    handle = ctypes.CDLL(tl.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), f"{n} declared but not exported"
+
+
+def test_status_strings():
+    for code, name in [(OK, "TPMLP_OK"), (E_DIV, "TPMLP_E_DIVISIBILITY"), (8, "TPMLP_E_HIP")]:
+        assert tl.status_string(code) == name
+
+
+def call_fwd(dtype=1, T=64, h=64, F=128, tp=2, X=P, W1=P, ldw1=64, b1=None, W2=P, H=None, A=P, Z=P):
+    return tl.lib.tp_mlp_fwd(None, dtype, T, h, F, tp, X, W1, ldw1, b1, W2, H, A, Z)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tp=3), E_DIV), (dict(tp=0), E_DIV), (dict(tp=-1), E_DIV),
+    (dict(T=-1), E_SHAPE), (dict(h=0), E_SHAPE), (dict(F=0), E_SHAPE),
+    (dict(ldw1=32), E_SHAPE), (dict(T=1 << 31), E_SHAPE),
+    (dict(X=None), E_NULL), (dict(W1=None), E_NULL), (dict(A=None), E_NULL), (dict(Z=None), E_NULL),
+    (dict(X=P + 2), E_ALIGN), (dict(Z=P + 4), E_ALIGN), (dict(h=60), E_ALIGN), (dict(ldw1=68), E_ALIGN),
+    (dict(F=2 * 60), E_ALIGN), (dict(dtype=2), E_DTYPE), (dict(dtype=0, h=62), E_ALIGN),
+])
+def test_tp_mlp_fwd_validation(kw, status):
+    assert call_fwd(**kw) == status
+    assert tl.lib.tpmlp_last_error().decode() != ""
+
+
+def test_divisibility_message():
+    assert call_fwd(F=96, tp=5) == E_DIV
+    assert b"not divisible by tp_size 5" in tl.lib.tpmlp_last_error()
+
+
+def test_column_parallel_fwd_validation():
+    f = tl.lib.column_parallel_fwd
+    assert f(None, 1, 9, 8, 16, 32, 2, P, 16, P, 16, None, P, 16, None, 16) == E_ACT
+    assert f(None, 1, 1, 8, 16, 30, 4, P, 16, P, 8, None, P, 8, None, 8) == E_DIV
+    assert f(None, 1, 1, 8, 16, 32, 2, P, 8, P, 16, None, P, 16, None, 16) == E_SHAPE     # ldx < K
+    assert f(None, 1, 1, 8, 16, 32, 2, P, 16, P, 16, P + 8, P, 16, None, 16) == E_ALIGN  # bias misaligned
+    assert f(None, 1, 1, 8, 16, 32, 2, P, 16, P, 16, None, P, 16, P, 8) == E_SHAPE       # ldh < width
+
+
+def test_row_parallel_and_partial_sum_validation():
+    assert tl.lib.row_parallel_fwd(None, 1, 8, 30, 16, 4, P, 8, P, 16, P, 16) == E_DIV
+    assert tl.lib.row_parallel_fwd(None, 1, 8, 32, 16, 2, P, 16, P, 16, P, 12) == E_SHAPE
+    s = tl.lib.shard_partial_sum
+    assert s(None, 0, 8, 16, P, 128, 16, P + 4096, 16) == E_DIV
+    assert s(None, 2, 8, 18, P, 144, 18, P + 4096, 18) == E_ALIGN
+    assert s(None, 2, 8, 16, P, 130, 16, P + 4096, 16) == E_ALIGN
+    assert s(None, 2, 8, 16, P, 128, 16, P + 256, 16) == E_SHAPE     # out overlaps partial 0 (not exactly)
+    assert s(None, 2, 8, 16, P, 128, 16, P, 20) == E_SHAPE           # in place needs ldo == ldp
+    assert s(None, 2, 8, 16, None, 128, 16, P, 16) == E_NULL
+
+
+def test_bwd_validation_and_workspace_size():
+    ws = tl.tpmlp_bwd_workspace_bytes(1, 4096, 1024, 4096, 2)
+    assert ws >= 4096 * 2048 * 2 and ws % 256 == 0
+    assert tl.tpmlp_bwd_workspace_bytes(1, 8, 8, 30, 4) == 0
+    f = tl.lib.tp_mlp_bwd
+    args = [None, 1, 64, 64, 128, 2, P, P, 64, P, P, P, P, P, P, None, P]
+    assert f(*args, P, 16) == E_WS
+    assert f(*args, None, ws) == E_NULL
+    assert f(*args, P + 16, 1 << 30) == E_ALIGN
+    assert tl.lib.column_parallel_bwd(None, 1, 8, 16, 30, 4, P, 16, P, 8, P, 8, P, 16, P, 8, None) == E_DIV
+    assert tl.lib.row_parallel_bwd(None, 1, 8, 32, 16, 2, P, 16, P, 16, P, 16, P, 16, P, 8) == E_SHAPE
