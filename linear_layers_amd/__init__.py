@@ -75,20 +75,35 @@ def _load() -> ctypes.CDLL:
     return handle
 
 
-lib = _load()
+_lib = None
+
+
+def __getattr__(name):
+    # The library is loaded on first use, so the package (and its build
+    # module) import without it; any call then fails loudly if it is absent.
+    if name == "lib":
+        return _get_lib()
+    raise AttributeError(name)
+
+
+def _get_lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
 
 
 def status_string(status: int) -> str:
-    return lib.tpmlp_status_string(status).decode()
+    return _get_lib().tpmlp_status_string(status).decode()
 
 
 def version() -> str:
-    return lib.tpmlp_version().decode()
+    return _get_lib().tpmlp_version().decode()
 
 
 def _check(status: int) -> None:
     if status != 0:
-        raise TpmlpError(status, f"{status_string(status)}: {lib.tpmlp_last_error().decode()}")
+        raise TpmlpError(status, f"{status_string(status)}: {_get_lib().tpmlp_last_error().decode()}")
 
 
 def _dtype(t: torch.Tensor) -> int:
@@ -130,7 +145,7 @@ def column_parallel_fwd(X, W_shard, tp_size: int, Y_shard, bias_shard=None, H_sa
     """Y_shard = Act(X @ W_shard + bias_shard); optionally H_save = X @ W_shard + bias_shard."""
     T, K = X.shape
     Ns = W_shard.shape[1]
-    _check(lib.column_parallel_fwd(_stream(stream, X), _dtype(X), _ACTS[act], T, K, Ns * tp_size, tp_size,
+    _check(_get_lib().column_parallel_fwd(_stream(stream, X), _dtype(X), _ACTS[act], T, K, Ns * tp_size, tp_size,
                                    _ptr(X), _ld(X, K), _ptr(W_shard), _ld(W_shard, Ns), _ptr(bias_shard),
                                    _ptr(Y_shard), _ld(Y_shard, Ns), _ptr(H_save), _ld(H_save, Ns)))
 
@@ -139,7 +154,7 @@ def row_parallel_fwd(X_shard, W_shard, tp_size: int, Z_partial, stream=None) -> 
     """Z_partial (fp32) = X_shard @ W_shard."""
     T, Ks = X_shard.shape
     N = W_shard.shape[1]
-    _check(lib.row_parallel_fwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
+    _check(_get_lib().row_parallel_fwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
                                 _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N),
                                 _ptr(Z_partial), _ld(Z_partial, N)))
 
@@ -154,7 +169,7 @@ def shard_partial_sum(partials, out, tp_size: Optional[int] = None, stream=None)
     T, N = partials.shape[1], partials.shape[2]
     if partials.dim() != 3 or (T > 1 and N > 1 and partials.stride(2) != 1):
         raise ValueError("partials must be [tp, T, N] with contiguous rows")
-    _check(lib.shard_partial_sum(_stream(stream, out), tp, T, N, _ptr(partials), partials.stride(0),
+    _check(_get_lib().shard_partial_sum(_stream(stream, out), tp, T, N, _ptr(partials), partials.stride(0),
                                  partials.stride(1) if T > 1 else N, _ptr(out), _ld(out, N)))
 
 
@@ -165,13 +180,13 @@ def tp_mlp_fwd(X, W1_shard, b1_shard, W2_shard, tp_size: int, A_save, Z_partial,
     Fs = W1_shard.shape[1]
     for n, t in (("X", X), ("W2_shard", W2_shard), ("A_save", A_save), ("Z_partial", Z_partial), ("H_save", H_save)):
         _require_contiguous(n, t)
-    _check(lib.tp_mlp_fwd(_stream(stream, X), _dtype(X), T, h, Fs * tp_size, tp_size, _ptr(X), _ptr(W1_shard),
+    _check(_get_lib().tp_mlp_fwd(_stream(stream, X), _dtype(X), T, h, Fs * tp_size, tp_size, _ptr(X), _ptr(W1_shard),
                           _ld(W1_shard, Fs), _ptr(b1_shard), _ptr(W2_shard), _ptr(H_save), _ptr(A_save),
                           _ptr(Z_partial)))
 
 
 def tpmlp_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: int) -> int:
-    return int(lib.tpmlp_bwd_workspace_bytes(dtype, T, h, F, tp_size))
+    return int(_get_lib().tpmlp_bwd_workspace_bytes(dtype, T, h, F, tp_size))
 
 
 def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_partial, dW1_shard, dW2_shard,
@@ -187,7 +202,7 @@ def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_parti
     if workspace is None:
         workspace = torch.empty(max(1, tpmlp_bwd_workspace_bytes(dt, T, h, F, tp_size)), dtype=torch.uint8,
                                 device=X.device)
-    _check(lib.tp_mlp_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W1_shard), _ld(W1_shard, Fs),
+    _check(_get_lib().tp_mlp_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W1_shard), _ld(W1_shard, Fs),
                           _ptr(W2_shard), _ptr(H_save), _ptr(A_save), _ptr(dZ), _ptr(dX_partial), _ptr(dW1_shard),
                           _ptr(db1_shard), _ptr(dW2_shard), _ptr(workspace), workspace.numel()))
 
@@ -196,7 +211,7 @@ def column_parallel_bwd(X, W_shard, dY, tp_size: int, dX_partial, dW_shard, db_s
     """dX_partial = dY W_shard^T, dW_shard = X^T dY, db_shard = column sums of dY (fp32 outputs)."""
     T, K = X.shape
     Ns = W_shard.shape[1]
-    _check(lib.column_parallel_bwd(_stream(stream, X), _dtype(X), T, K, Ns * tp_size, tp_size, _ptr(X), _ld(X, K),
+    _check(_get_lib().column_parallel_bwd(_stream(stream, X), _dtype(X), T, K, Ns * tp_size, tp_size, _ptr(X), _ld(X, K),
                                    _ptr(W_shard), _ld(W_shard, Ns), _ptr(dY), _ld(dY, Ns), _ptr(dX_partial),
                                    _ld(dX_partial, K), _ptr(dW_shard), _ld(dW_shard, Ns), _ptr(db_shard)))
 
@@ -205,18 +220,18 @@ def row_parallel_bwd(X_shard, W_shard, dY, tp_size: int, dX_shard, dW_shard, str
     """dX_shard = dY W_shard^T, dW_shard = X_shard^T dY (fp32 outputs)."""
     T, Ks = X_shard.shape
     N = W_shard.shape[1]
-    _check(lib.row_parallel_bwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
+    _check(_get_lib().row_parallel_bwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
                                 _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N), _ptr(dY),
                                 _ld(dY, N), _ptr(dX_shard), _ld(dX_shard, Ks), _ptr(dW_shard), _ld(dW_shard, N)))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:
     """Bracket matching kernel launches with HIP events (None disables)."""
-    _check(lib.tpmlp_profile_enable(None if filter is None else filter.encode()))
+    _check(_get_lib().tpmlp_profile_enable(None if filter is None else filter.encode()))
 
 
 def profile_collect() -> dict:
     """{role|symbol: (launches, total_ms, symbol)} of the launches recorded so far."""
     buf = ctypes.create_string_buffer(1 << 16)
-    _check(lib.tpmlp_profile_collect(buf, len(buf)))
+    _check(_get_lib().tpmlp_profile_collect(buf, len(buf)))
     return {k: tuple(v) for k, v in json.loads(buf.value.decode() or "{}").items()}

@@ -34,7 +34,6 @@ struct GemmArgs {
   void* H; int64_t ldh;          // typed pre-activation: written (kEpiBiasAct, if non-null) / read (kEpiActBwd)
   const void* bias;              // typed [N] or null (kEpiBiasAct)
   float* colsum;                 // kEpiActBwd: fp32 [tiles_m][N] per-tile column sums of dH (or null)
-                                 // kEpiF32 with B MN-major: fp32 [N] column sums of B over K (or null)
   int act;
 };
 
@@ -95,24 +94,6 @@ struct TileLoader {
         }
       }
     }
-  }
-
-  // Column sums over this tile's K rows, for MN-major tiles: adds into
-  // cs[u*EPC + e] the EPC values of MN group gi held by unit u.
-  __device__ __forceinline__ void accumulate_colsum(float* cs) const {
-    static_assert(!KMAJ, "column sums are taken from MN-major tiles");
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-#pragma unroll
-      for (int j = 0; j < EPC; ++j)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const u32x4_t v = r[u * EPC + j];
-          float x;
-          if constexpr (EPC == 8) x = __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16));
-          else x = __uint_as_float(v[e]);
-          cs[u * EPC + e] += x;
-        }
   }
 
   __device__ __forceinline__ void store(u32x4_t* __restrict__ s, int tid) const {
@@ -201,15 +182,6 @@ gemm_kernel(const GemmArgs p) {
   TileLoader<T, BM, A_KMAJ, NT> la;
   TileLoader<T, BN, B_KMAJ, NT> lb;
 
-  // Column sums of B over K (bias gradient of a linear layer), taken by the
-  // workgroups of the first tile row only.
-  constexpr bool kBColsum = (EPI == kEpiF32) && !B_KMAJ;
-  constexpr int CSN = kBColsum ? TileLoader<T, BN, B_KMAJ, NT>::REGS : 1;
-  float bcs[CSN];
-  const bool do_bcs = kBColsum && p.colsum != nullptr && tmi == 0 && ks == 0 && p.splits == 1;
-#pragma unroll
-  for (int i = 0; i < CSN; ++i) bcs[i] = 0.0f;
-
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -221,7 +193,6 @@ gemm_kernel(const GemmArgs p) {
   if (nk > 0) {
     la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
     lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
-    if constexpr (kBColsum) if (do_bcs) lb.accumulate_colsum(bcs);
     la.store(lds, tid);
     lb.store(lds + BM * 8, tid);
     __syncthreads();
@@ -259,7 +230,6 @@ gemm_kernel(const GemmArgs p) {
         for (int j = 0; j < FN; ++j) Mfma<T>::step(acc[i][j], af[i], bfr[j]);
     }
     if (more) {
-      if constexpr (kBColsum) if (do_bcs) lb.accumulate_colsum(bcs);
       u32x4_t* nA = lds + (cur ^ 1) * STAGE;
       la.store(nA, tid);
       lb.store(nA + BM * 8, tid);
@@ -282,28 +252,6 @@ gemm_kernel(const GemmArgs p) {
           const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lchunk + (v & 3);
           if (row < M) C[(int64_t)row * p.ldc + col] = acc[i][j][v];
         }
-    }
-    if constexpr (kBColsum) {
-      if (do_bcs) {
-        // Reduce the per-thread sums over the K-chunk index c in fixed order.
-        using LB = TileLoader<T, BN, B_KMAJ, NT>;
-        float* red = reinterpret_cast<float*>(lds);  // [8][BN]; LDS is free after the last barrier
-#pragma unroll
-        for (int u = 0; u < LB::PER; ++u) {
-          const int idx = u * NT + tid;
-          if (!(LB::EXACT || idx < LB::UNITS)) continue;
-          const int gi = idx % LB::G, c = idx / LB::G;
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) red[c * BN + gi * EPC + e] = bcs[u * EPC + e];
-        }
-        __syncthreads();
-        for (int cidx = tid; cidx < BN; cidx += NT) {
-          float s = 0.0f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) s += red[c * BN + cidx];
-          if (n0 + cidx < N) p.colsum[n0 + cidx] = s;
-        }
-      }
     }
   } else if constexpr (EPI == kEpiBiasAct) {
     T* __restrict__ Y = static_cast<T*>(p.Y);

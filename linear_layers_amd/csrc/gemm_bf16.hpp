@@ -1,0 +1,465 @@
+// bf16 MFMA GEMM of libtpmlp for gfx950 (CDNA4): C[M,N] = sum_k A(m,k) B(k,n),
+// fp32 accumulate on v_mfma_f32_32x32x16_bf16, with fused epilogues.
+//
+// Operand orientation (template flags), as in the products of the block:
+//   A_KMAJ: A(m,k) = A[m*lda + k]   else A(m,k) = A[k*lda + m]
+//   B_KMAJ: B(k,n) = B[n*ldb + k]   else B(k,n) = B[k*ldb + n]
+//
+// Data path, per K step of 32:
+//   * Both tiles go from global memory straight into LDS with
+//     buffer_load_dwordx4 ... lds (no VGPR staging, no ds_write).  The buffer
+//     descriptor is re-based per tile so rows past the end of an operand read
+//     as zero; a K-contiguous tile whose last K step is partial gets its
+//     out-of-range chunks zeroed in LDS.
+//   * A K-contiguous tile is stored as rows of 4 x 16-byte chunks along K
+//     (chunk c of row r at position c ^ ((r >> 2) & 3)) and read with
+//     ds_read_b128: one read gives a lane 8 consecutive K values.
+//   * An M/N-contiguous tile is stored as 32 K-rows of BM (or BN) elements
+//     (16-byte chunk q of K-row k at position q ^ 4*(k&3)) and read with
+//     ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values across
+//     groups of 16 lanes, so two reads give a lane its 8 K values.
+//   * The MFMA takes the B fragment as its first operand and the A fragment
+//     as its second, so each lane's accumulators hold 4 consecutive output
+//     columns of one row, which the epilogue stores as 8- or 16-byte vectors.
+//   * NS LDS stages form a ring: the loads of step k+NS-1 are issued at the
+//     start of step k, so NS-1 steps of data are in flight behind the MFMAs
+//     (one wave per SIMD cannot hide memory latency any other way).  Each
+//     step has one barrier, in its middle: after it the first fragments of
+//     step k+1 are read while the second half of step k's MFMAs runs.
+//   * The stages are separate LDS objects indexed at compile time (the loop
+//     is unrolled NS times), so the compiler can tell in-flight loads into
+//     one stage from reads of another.  Trailing steps up to a multiple of NS
+//     are zero-filled stages, so the loop body carries no MFMA under a branch.
+#pragma once
+
+#include "common.hpp"
+#include <type_traits>
+
+#include "gemm.hpp"  // GemmArgs, EpiKind, map_tile
+
+namespace tpmlp {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kBK = 32;                   // K per step
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 0xf) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xc07f;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // v_cvt_pk_bf16_f32 rounds to nearest even.
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Position of 16-byte chunk q of K-row k in an M/N-contiguous tile.
+__device__ __forceinline__ int swz_t(int k, int q) { return q ^ ((k & 3) << 2); }
+
+template <int ROWS, bool KMAJ>
+struct Bf16Tile {
+  // One operand tile of ROWS (M or N) x 32 (K) bf16 = ROWS * 64 bytes.
+  static constexpr int BYTES = ROWS * 64;
+  static constexpr int SLOTS = ROWS * 4;        // 16-byte slots
+  static constexpr int INSTR = SLOTS / 256;     // buffer loads per wave (4 waves x 64 lanes)
+  static constexpr int QPR = ROWS / 8;          // chunks per K-row (M/N-contiguous layout)
+  static_assert(SLOTS % 256 == 0, "tile rows must be a multiple of 64");
+  static_assert(KMAJ || ROWS >= 128, "the K-row swizzle needs at least 16 chunks per K-row");
+
+  uint32_t voff[INSTR];   // per-lane byte offsets in the re-based buffer
+  uint32_t fbase[4];      // per-lane LDS offsets of the MFMA fragments
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int w0) {
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j) {
+      const int s = (wave * INSTR + j) * 64 + lane;
+      if constexpr (KMAJ) {
+        const int row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+        voff[j] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+      } else {
+        const int k = s / QPR, q = swz_t(k, s % QPR);
+        voff[j] = (uint32_t)(((int64_t)k * ld + q * 8) * 2);
+      }
+    }
+    // Fragment rows are w0 + 32 f + (lane & 31) with w0 a multiple of 32.
+    if constexpr (KMAJ) {
+      // chunk 2S + lane/32 sits at position (2S + lane/32) ^ (((lane & 31) >> 2) & 3)
+      const uint32_t lb = (uint32_t)(w0 + (lane & 31)) * 64u;
+      const int x = ((lane & 31) >> 2) & 3;
+#pragma unroll
+      for (int S = 0; S < 2; ++S) fbase[S] = lb + (uint32_t)(((2 * S + (lane >> 5)) ^ x) << 4);
+      fbase[2] = fbase[3] = 0;
+    } else {
+      // 16-lane group g reads K-rows kb + j/4 (j = lane & 15) at column
+      // w0 + 32 f + 16 (g&1) + 4 (j&3); the transpose hands lane j the 4 K
+      // values of column w0 + 32 f + 16 (g&1) + j.  (k & 3) = j >> 2.
+      const int g = lane >> 4, j = lane & 15;
+      const int qlow = 2 * (g & 1) + ((j & 3) >> 1);
+      const int kl = 8 * (g >> 1) + (j >> 2);
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        fbase[f] = (uint32_t)((kl * QPR + ((((w0 >> 3) + 4 * f) ^ (j & 12)) | qlow)) * 16 + (j & 1) * 8);
+    }
+  }
+
+  // Issue this wave's loads of one K step into `dst`; base/nbytes describe the
+  // re-based buffer (bytes past nbytes read as zero).  The loads are written
+  // as inline asm so that the compiler does not track them: it would
+  // otherwise add a full vmcnt(0) drain before reads of other LDS stages at
+  // the loop head.  The kernel waits for them itself (vmcnt before each
+  // barrier, and a full drain after the loop); the compiler's own waits stay
+  // correct because loads it does not count can only make them wait longer.
+  __device__ __forceinline__ void load(const bf16_t* base, uint32_t nbytes, lds_char* dst, int wave) const {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base);
+    const i32x4_t rsrc = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffffu), (int)nbytes, kBufferWord3};
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(dst + (wave * INSTR + j) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(lds), "v"(voff[j]), "s"(rsrc)
+                   : "memory", "m0");
+    }
+  }
+
+  // Zero this wave's slots of the tile (a step past the end of K).
+  __device__ __forceinline__ void zero(lds_char* dst, int wave, int lane) const {
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(dst + ((wave * INSTR + j) * 64 + lane) * 16) =
+          u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // K-contiguous tiles: zero the chunks at K offset >= kvalid (last, partial step).
+  __device__ __forceinline__ void zero_tail(lds_char* dst, int wave, int lane, int kvalid) const {
+    static_assert(KMAJ, "only K-contiguous tiles need the fix-up");
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j) {
+      const int s = (wave * INSTR + j) * 64 + lane;
+      const int row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+      if (c * 8 >= kvalid)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(dst + s * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // 8 K values (k = 16 S + 8 (lane/32) + t, t = 0..7) of fragment block F.
+  template <int F, int S>
+  __device__ __forceinline__ u32x4_t frag(const lds_char* src) const {
+    if constexpr (KMAJ) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src + fbase[S] + F * 32 * 64);
+    } else {
+      static_assert(F < 4, "too many fragment blocks");
+      const lds_char* p0 = src + fbase[F] + 16 * S * QPR * 16;
+      const lds_char* p1 = p0 + 4 * QPR * 16;
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p0);
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p1);
+      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0);
+      const u32x2_t w1 = __builtin_bit_cast(u32x2_t, v1);
+      return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+    }
+  }
+};
+
+// Reads fragments F..NF-1 of one tile for K-substep S (compile-time indices,
+// so every LDS offset is an immediate).
+template <int F, int NF, int S>
+struct FragLoop {
+  template <class Tile>
+  __device__ __forceinline__ static void run(const Tile& t, const lds_char* src, u32x4_t* out) {
+    out[F] = t.template frag<F, S>(src);
+    FragLoop<F + 1, NF, S>::run(t, src, out);
+  }
+};
+template <int NF, int S>
+struct FragLoop<NF, NF, S> {
+  template <class Tile>
+  __device__ __forceinline__ static void run(const Tile&, const lds_char*, u32x4_t*) {}
+};
+
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS>
+__global__ void __launch_bounds__(256)
+gemm_bf16_kernel(const GemmArgs p) {
+  constexpr int WTM = BM / 2, WTN = BN / 2;  // 2 x 2 waves
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  using TA = Bf16Tile<BM, A_KMAJ>;
+  using TB = Bf16Tile<BN, B_KMAJ>;
+  constexpr int STAGE = TA::BYTES + TB::BYTES;
+  constexpr int LPS = TA::INSTR + TB::INSTR;  // buffer loads per wave per step
+  static_assert(NS >= 2 && NS <= 6, "2..6 stages");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[NS > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st5[NS > 5 ? STAGE : 16];
+  auto stage = [&](auto I) -> lds_char* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return (lds_char*)st0;
+    else if constexpr (i == 1) return (lds_char*)st1;
+    else if constexpr (i == 2) return (lds_char*)st2;
+    else if constexpr (i == 3) return (lds_char*)st3;
+    else if constexpr (i == 4) return (lds_char*)st4;
+    else return (lds_char*)st5;
+  };
+  (void)stage;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tmi, tni, ks;
+  map_tile(p, tmi, tni, ks);
+  const int m0 = tmi * BM, n0 = tni * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int kbeg = ks * p.k_per_split;
+  const int kend = min(K, kbeg + p.k_per_split);
+  const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
+  const int nkp = ((nk + NS - 1) / NS) * NS;  // padded with zero-filled steps
+  const int ktail = (kend - kbeg) & (kBK - 1);  // valid K in the last real step (0 = full)
+
+  const bf16_t* A = static_cast<const bf16_t*>(p.A);
+  const bf16_t* B = static_cast<const bf16_t*>(p.B);
+  TA ta;
+  TB tb;
+  ta.init(wave, lane, p.lda, wm * WTM);
+  tb.init(wave, lane, p.ldb, wn * WTN);
+
+  // Step kt's tiles into stage `dst`: loads for real steps, zeros past the end.
+  auto issue = [&](int kt, lds_char* dst) {
+    if (kt < nk) {
+      const int k0 = kbeg + kt * kBK;
+      uint32_t na, nb;
+      const bf16_t* pa;
+      const bf16_t* pb;
+      if constexpr (A_KMAJ) {
+        const int rows = min(BM, M - m0);
+        na = (uint32_t)(((int64_t)(rows - 1) * p.lda + (kend - k0)) * 2);
+        pa = A + (int64_t)m0 * p.lda + k0;
+      } else {
+        const int kv = min(kBK, kend - k0);
+        na = (uint32_t)(((int64_t)(kv - 1) * p.lda + (M - m0)) * 2);
+        pa = A + (int64_t)k0 * p.lda + m0;
+      }
+      if constexpr (B_KMAJ) {
+        const int rows = min(BN, N - n0);
+        nb = (uint32_t)(((int64_t)(rows - 1) * p.ldb + (kend - k0)) * 2);
+        pb = B + (int64_t)n0 * p.ldb + k0;
+      } else {
+        const int kv = min(kBK, kend - k0);
+        nb = (uint32_t)(((int64_t)(kv - 1) * p.ldb + (N - n0)) * 2);
+        pb = B + (int64_t)k0 * p.ldb + n0;
+      }
+      ta.load(pa, na, dst, wave);
+      tb.load(pb, nb, dst + TA::BYTES, wave);
+    } else if (kt < nkp) {
+      ta.zero(dst, wave, lane);
+      tb.zero(dst + TA::BYTES, wave, lane);
+    }
+  };
+
+  // Wait until this wave's loads of step `next` have landed: the loads of the
+  // real steps after it (at most NS-2) may stay in flight.
+  auto wait_landed = [&](int next) {
+    const int later = min(NS - 2, max(0, nk - 1 - next));
+    switch (later) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(1 * LPS)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPS)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPS)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPS)); break;
+    }
+  };
+  auto fix_tail = [&](int kt, lds_char* dst) {
+    if (kt == nk - 1 && ktail != 0) {
+      if constexpr (A_KMAJ) ta.zero_tail(dst, wave, lane, ktail);
+      if constexpr (B_KMAJ) tb.zero_tail(dst + TA::BYTES, wave, lane, ktail);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto mfmas = [&](const u32x4_t (&af)[FM], const u32x4_t (&bfr)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                            __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
+  };
+
+  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];  // fragments of K-substeps 0 and 1
+
+  // One step in stage ST (compile time) with its substep-0 fragments in
+  // a0/b0.  Order (kept by the scheduling barriers): loads of step kt+NS-1;
+  // substep-1 reads; substep-0 MFMAs; wait for step kt+1 and barrier; its
+  // substep-0 reads; substep-1 MFMAs.
+  auto step = [&](auto STc, int kt) {
+    constexpr int ST = decltype(STc)::value;
+    lds_char* cur = stage(STc);
+    lds_char* nxt = stage(std::integral_constant<int, (ST + 1) % NS>{});
+    if (kt + NS - 1 < nkp) issue(kt + NS - 1, stage(std::integral_constant<int, (ST + NS - 1) % NS>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    FragLoop<0, FM, 1>::run(ta, cur, a1);
+    FragLoop<0, FN, 1>::run(tb, cur + TA::BYTES, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nkp) {
+      wait_landed(kt + 1);
+      fix_tail(kt + 1, nxt);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
+      FragLoop<0, FM, 0>::run(ta, nxt, a0);
+      FragLoop<0, FN, 0>::run(tb, nxt + TA::BYTES, b0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nk > 0) {
+    // Prologue: steps 0..NS-2 in flight, step 0 landed, its first fragments read.
+    issue(0, stage(std::integral_constant<int, 0>{}));
+    issue(1, stage(std::integral_constant<int, 1>{}));
+    if constexpr (NS > 2) issue(2, stage(std::integral_constant<int, 2>{}));
+    if constexpr (NS > 3) issue(3, stage(std::integral_constant<int, 3>{}));
+    if constexpr (NS > 4) issue(4, stage(std::integral_constant<int, 4>{}));
+    wait_landed(0);
+    fix_tail(0, stage(std::integral_constant<int, 0>{}));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    FragLoop<0, FM, 0>::run(ta, stage(std::integral_constant<int, 0>{}), a0);
+    FragLoop<0, FN, 0>::run(tb, stage(std::integral_constant<int, 0>{}) + TA::BYTES, b0);
+    for (int kt = 0; kt < nkp; kt += NS) {
+      step(std::integral_constant<int, 0>{}, kt);
+      step(std::integral_constant<int, 1>{}, kt + 1);
+      if constexpr (NS > 2) step(std::integral_constant<int, 2>{}, kt + 2);
+      if constexpr (NS > 3) step(std::integral_constant<int, 3>{}, kt + 3);
+      if constexpr (NS > 4) step(std::integral_constant<int, 4>{}, kt + 4);
+      if constexpr (NS > 5) step(std::integral_constant<int, 5>{}, kt + 5);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the loads the compiler does not see
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(st0);  // epilogue scratch (LDS is free now)
+  (void)red;
+
+  // ------------------------------------------------------------ epilogue --
+  // Lane l, block (i, j), register v: row m0 + wm*WTM + 32 i + (l & 31),
+  // column n0 + wn*WTN + 32 j + 8 (v/4) + 4 (l/32) + v%4.
+  const int mrow = m0 + wm * WTM + (lane & 31);
+  const int ncol = n0 + wn * WTN + 4 * (lane >> 5);
+  if constexpr (EPI == kEpiF32) {
+    float* __restrict__ C = p.C + (int64_t)ks * p.split_stride;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = mrow + 32 * i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = ncol + 32 * j + 8 * g;
+          if (col < N)
+            *reinterpret_cast<f32x4_t*>(C + (int64_t)row * p.ldc + col) =
+                f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        }
+    }
+  } else if constexpr (EPI == kEpiBiasAct) {
+    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
+    bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
+    const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = ncol + 32 * j + 8 * g;
+        if (col >= N) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+          const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + col);
+          bv[0] = bf16lo(w[0]); bv[1] = bf16hi(w[0]); bv[2] = bf16lo(w[1]); bv[3] = bf16hi(w[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = mrow + 32 * i;
+          if (row >= M) continue;
+          float h[4], a[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = acc[i][j][4 * g + e] + bv[e];
+            a[e] = act_apply(p.act, h[e]);
+          }
+          const int64_t o = (int64_t)row * p.ldy + col;
+          *reinterpret_cast<u32x2_t*>(Y + o) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          if (Hs)
+            *reinterpret_cast<u32x2_t*>(Hs + (int64_t)row * p.ldh + col) =
+                u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        }
+      }
+  } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
+    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
+    const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
+    // red: [2 (wm)][BN] floats in stage 0
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = ncol + 32 * j + 8 * g;
+        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+        if (col < N) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = mrow + 32 * i;
+            if (row >= M) continue;
+            const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + col);
+            const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              d[e] = acc[i][j][4 * g + e] * (p.act == kActGeluTanh ? gelu_tanh_grad(hv[e]) : 1.0f);
+              cs[e] += d[e];
+            }
+            *reinterpret_cast<u32x2_t*>(Y + (int64_t)row * p.ldy + col) =
+                u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+          }
+        }
+        // Sum over the 32 rows held by lanes with the same lane/32.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int x = 1; x < 32; x <<= 1) cs[e] += __shfl_xor(cs[e], x);
+        }
+        if ((lane & 31) == 0) {
+          const int c = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[wm * BN + c + e] = cs[e];
+        }
+      }
+    if (p.colsum) {
+      __syncthreads();
+      for (int c = tid; c < BN; c += 256) {
+        if (n0 + c < N) p.colsum[(int64_t)tmi * N + n0 + c] = red[c] + red[BN + c];
+      }
+    }
+  }
+}
+
+}  // namespace tpmlp

@@ -60,6 +60,42 @@ colsum_reduce_kernel(const float* __restrict__ part, int rows, int N, float* __r
   out[n] = s;
 }
 
+// out[n] = sum_{t < rows} Y[t*ld + n] in fp32: the bias gradient of a linear
+// layer from its output gradient.  A block owns 8 chunks of 16 bytes along N
+// and 32 row lanes; lane r adds rows r, r+32, ... in order, then the 32 lane
+// sums are added in order, so the result does not depend on the launch.
+template <typename T>
+__global__ void __launch_bounds__(256)
+colsum_rows_kernel(const T* __restrict__ Y, int64_t ld, int rows, int N, float* __restrict__ out) {
+  constexpr int EPC = Elem<T>::kPerChunk;
+  constexpr int COLS = 8 * EPC;
+  __shared__ float part[32][COLS];
+  const int cl = threadIdx.x & 7, rl = threadIdx.x >> 3;
+  const int c0 = blockIdx.x * COLS + cl * EPC;
+  float s[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) s[e] = 0.0f;
+  if (c0 < N) {
+    for (int r = rl; r < rows; r += 32) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Y + (int64_t)r * ld + c0);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (EPC == 8) s[e] += __uint_as_float((e & 1) ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16));
+        else s[e] += __uint_as_float(v[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[rl][cl * EPC + e] = s[e];
+  __syncthreads();
+  if (threadIdx.x < COLS) {
+    const int n = blockIdx.x * COLS + threadIdx.x;
+    float t = 0.0f;
+    for (int r = 0; r < 32; ++r) t += part[r][threadIdx.x];
+    if (n < N) out[n] = t;
+  }
+}
+
 // Zero rows x cols floats with row stride ld (a kernel, so it is safe inside
 // captured graphs, unlike a memset node).
 __global__ void __launch_bounds__(256)

@@ -13,6 +13,7 @@
 
 #include "../../include/tpmlp.h"
 #include "gemm.hpp"
+#include "gemm_bf16.hpp"
 #include "reduce.hpp"
 
 using namespace tpmlp;
@@ -230,17 +231,39 @@ int run_gemm_cfg(const char* role, GemmArgs a, hipStream_t s) {
                 dim3(WGM * WGN * 64), s, a);
 }
 
+template <int BM, int BN, bool AK, bool BKM, int EPI>
+int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s) {
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  if (a.splits < 1) a.splits = 1;
+  const int per = (a.K + a.splits - 1) / a.splits;
+  a.k_per_split = ((per + kBK - 1) / kBK) * kBK;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+  if (grid <= 0) return TPMLP_OK;
+  if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
+  char sym[128];
+  constexpr int NS = BM + BN >= 512 ? 4 : (BM + BN >= 384 ? 5 : 6);
+  snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS);
+  return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS>, dim3((unsigned)grid), dim3(256), s, a);
+}
+
+// Buffer offsets inside a tile are 32-bit: a tile spans at most 256 rows of
+// a K-contiguous operand (or 64 K-rows of an M/N-contiguous one).
+constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
 template <bool AK, bool BKM, int EPI>
 int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return TPMLP_OK;
+  if (a.lda >= kMaxLd || a.ldb >= kMaxLd)
+    return fail(TPMLP_E_SHAPE, "%s: leading dimension above 2^22 elements", role);
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
   const int cfg = plan_cfg(dtype, a.M, a.N, cus);
   if (dtype == TPMLP_BF16) {
     switch (cfg) {
-      case 0: return run_gemm_cfg<bf16_t, 256, 256, 2, 2, AK, BKM, EPI>(role, a, s);
-      case 1: return run_gemm_cfg<bf16_t, 256, 128, 2, 2, AK, BKM, EPI>(role, a, s);
-      default: return run_gemm_cfg<bf16_t, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
+      case 0: return run_gemm_bf16<256, 256, AK, BKM, EPI>(role, a, s);
+      case 1: return run_gemm_bf16<256, 128, AK, BKM, EPI>(role, a, s);
+      default: return run_gemm_bf16<128, 128, AK, BKM, EPI>(role, a, s);
     }
   }
   switch (cfg) {
@@ -542,12 +565,20 @@ int column_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N
   a.C = dX_partial;
   a.ldc = lddx;
   TPMLP_TRY((run_gemm<true, true, kEpiF32>("gemm.col_dgrad", dtype, a, s)));
-  // dW_i = X^T dY (and db_i = column sums of dY, taken from the same tiles)
+  // dW_i = X^T dY
   a = gemm_args(X, ldx, dY, lddy, K, Ns, T);
   a.C = dW_shard;
   a.ldc = lddw;
-  a.colsum = db_shard;
-  return run_gemm<false, false, kEpiF32>("gemm.col_wgrad", dtype, a, s);
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.col_wgrad", dtype, a, s)));
+  if (db_shard == nullptr) return TPMLP_OK;
+  // db_i = column sums of dY
+  const int cols = 8 * chunk_elems(dtype);
+  const dim3 grid((unsigned)((Ns + cols - 1) / cols));
+  if (dtype == TPMLP_BF16)
+    return launch("colsum_rows", "colsum_rows_kernel<bf16>", colsum_rows_kernel<bf16_t>, grid, dim3(256), s,
+                  static_cast<const bf16_t*>(dY), lddy, (int)T, (int)Ns, db_shard);
+  return launch("colsum_rows", "colsum_rows_kernel<f32>", colsum_rows_kernel<float>, grid, dim3(256), s,
+                static_cast<const float*>(dY), lddy, (int)T, (int)Ns, db_shard);
 }
 
 int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size, const void* X_shard,
