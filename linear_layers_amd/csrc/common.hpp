@@ -37,13 +37,17 @@ template <> struct Elem<float> {
 };
 
 // GeLU, tanh form: gelu(x) = x/2 * (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// tanh(u) is evaluated from the identity tanh(u) = 1 - 2 / (exp(2u) + 1), which
-// saturates to +-1 correctly when exp overflows to inf or underflows to 0.
+// tanh(u) is evaluated from the identity tanh(u) = 1 - 2 / (exp(2u) + 1) with
+// the hardware base-2 exponential and reciprocal (each about 1 ulp); it
+// saturates to +-1 correctly when the exponential overflows to inf or
+// underflows to 0.
 constexpr float kSqrt2OverPi = 0.79788456080286535588f;
 constexpr float kGeluCubic = 0.044715f;
+constexpr float kTwoLog2e = 2.88539008177792681472f;  // 2 / ln 2
 
 __device__ __forceinline__ float tanh_from_exp(float u) {
-  return 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  const float e = __builtin_amdgcn_exp2f(u * kTwoLog2e);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
 __device__ __forceinline__ float gelu_tanh(float x) {

@@ -35,6 +35,7 @@ struct GemmArgs {
   const void* bias;              // typed [N] or null (kEpiBiasAct)
   float* colsum;                 // kEpiActBwd: fp32 [tiles_m][N] per-tile column sums of dH (or null)
   int act;
+  int group_m;                   // tile rows per raster group (0: 8)
 };
 
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id.  Renumber
@@ -47,7 +48,7 @@ __device__ __forceinline__ void map_tile(const GemmArgs& p, int& tm, int& tn, in
   const int per = p.tiles_m * p.tiles_n;
   ks = pid / per;
   const int t = pid - ks * per;
-  constexpr int G = 8;
+  const int G = p.group_m > 0 ? p.group_m : 8;
   const int width = G * p.tiles_n;
   const int gid = t / width;
   const int first = gid * G;

@@ -46,7 +46,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kBK = 32;                   // K per step
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 0xf) | ((n >> 4) << 14); }
@@ -64,39 +63,57 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 // Position of 16-byte chunk q of K-row k in an M/N-contiguous tile.
 __device__ __forceinline__ int swz_t(int k, int q) { return q ^ ((k & 3) << 2); }
 
-template <int ROWS, bool KMAJ>
+template <int ROWS, bool KMAJ, int BKT>
 struct Bf16Tile {
-  // One operand tile of ROWS (M or N) x 32 (K) bf16 = ROWS * 64 bytes.
-  static constexpr int BYTES = ROWS * 64;
-  static constexpr int SLOTS = ROWS * 4;        // 16-byte slots
+  // One operand tile of ROWS (M or N) x BKT (K) bf16 = ROWS * BKT * 2 bytes.
+  static constexpr int CPR = BKT / 8;           // 16-byte chunks per K-contiguous row
+  static constexpr int BYTES = ROWS * BKT * 2;
+  static constexpr int SLOTS = ROWS * CPR;      // 16-byte slots
   static constexpr int INSTR = SLOTS / 256;     // buffer loads per wave (4 waves x 64 lanes)
   static constexpr int QPR = ROWS / 8;          // chunks per K-row (M/N-contiguous layout)
-  static_assert(SLOTS % 256 == 0, "tile rows must be a multiple of 64");
+  static_assert(BKT == 32 || BKT == 64, "K step of 32 or 64");
+  static_assert(SLOTS % 256 == 0, "tile too small for 4 waves");
   static_assert(KMAJ || ROWS >= 128, "the K-row swizzle needs at least 16 chunks per K-row");
 
   uint32_t voff[INSTR];   // per-lane byte offsets in the re-based buffer
   uint32_t fbase[4];      // per-lane LDS offsets of the MFMA fragments
+
+  // Position of chunk c of row r in a K-contiguous tile: conflict-free for
+  // one row written as CPR chunks and for 16 consecutive rows read at one chunk.
+  static __device__ __forceinline__ int pos_k(int r, int c) {
+    if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
+    else return c ^ (r & 7) ^ ((r >> 3) & 7);
+  }
 
   __device__ __forceinline__ void init(int wave, int lane, int64_t ld, int w0) {
 #pragma unroll
     for (int j = 0; j < INSTR; ++j) {
       const int s = (wave * INSTR + j) * 64 + lane;
       if constexpr (KMAJ) {
-        const int row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+        const int row = s / CPR, c = pos_k(row, s % CPR);   // pos_k is an involution in c
         voff[j] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
       } else {
         const int k = s / QPR, q = swz_t(k, s % QPR);
         voff[j] = (uint32_t)(((int64_t)k * ld + q * 8) * 2);
       }
     }
-    // Fragment rows are w0 + 32 f + (lane & 31) with w0 a multiple of 32.
+    // Fragment rows are w0 + 32 f + (lane & 31) with w0 a multiple of 64.
     if constexpr (KMAJ) {
-      // chunk 2S + lane/32 sits at position (2S + lane/32) ^ (((lane & 31) >> 2) & 3)
-      const uint32_t lb = (uint32_t)(w0 + (lane & 31)) * 64u;
-      const int x = ((lane & 31) >> 2) & 3;
+      const uint32_t lb = (uint32_t)(w0 + (lane & 31)) * (uint32_t)(CPR * 16);
+      if constexpr (CPR == 4) {
+        // chunk 2S + lane/32 at (2S + lane/32) ^ (((lane & 31) >> 2) & 3): one base per S
+        const int x = ((lane & 31) >> 2) & 3;
 #pragma unroll
-      for (int S = 0; S < 2; ++S) fbase[S] = lb + (uint32_t)(((2 * S + (lane >> 5)) ^ x) << 4);
-      fbase[2] = fbase[3] = 0;
+        for (int S = 0; S < 2; ++S) fbase[S] = lb + (uint32_t)(((2 * S + (lane >> 5)) ^ x) << 4);
+        fbase[2] = fbase[3] = 0;
+      } else {
+        // chunk 2S + lane/32 of row r at (2S + lane/32) ^ (r & 7) ^ ((r >> 3) & 7); with
+        // r = w0 + 32 f + (lane & 31) the XOR term is L ^ 4 (f & 1), so the bases are
+        // indexed by X = (2S ^ 4(f&1)) / 2.
+        const int L = (lane >> 5) ^ (lane & 7) ^ ((lane & 31) >> 3);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) fbase[x] = lb + (uint32_t)((L ^ (2 * x)) << 4);
+      }
     } else {
       // 16-lane group g reads K-rows kb + j/4 (j = lane & 15) at column
       // w0 + 32 f + 16 (g&1) + 4 (j&3); the transpose hands lane j the 4 K
@@ -144,7 +161,7 @@ struct Bf16Tile {
 #pragma unroll
     for (int j = 0; j < INSTR; ++j) {
       const int s = (wave * INSTR + j) * 64 + lane;
-      const int row = s >> 2, c = (s & 3) ^ ((row >> 2) & 3);
+      const int row = s / CPR, c = pos_k(row, s % CPR);
       if (c * 8 >= kvalid)
         *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(dst + s * 16) = u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -154,7 +171,8 @@ struct Bf16Tile {
   template <int F, int S>
   __device__ __forceinline__ u32x4_t frag(const lds_char* src) const {
     if constexpr (KMAJ) {
-      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src + fbase[S] + F * 32 * 64);
+      constexpr int X = CPR == 4 ? S : (((2 * S) ^ (4 * (F & 1))) >> 1);
+      return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src + fbase[X] + F * 32 * CPR * 16);
     } else {
       static_assert(F < 4, "too many fragment blocks");
       const lds_char* p0 = src + fbase[F] + 16 * S * QPR * 16;
@@ -184,17 +202,18 @@ struct FragLoop<NF, NF, S> {
   __device__ __forceinline__ static void run(const Tile&, const lds_char*, u32x4_t*) {}
 };
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS>
-__global__ void __launch_bounds__(256)
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32>
+__global__ void __launch_bounds__(256, OCC)
 gemm_bf16_kernel(const GemmArgs p) {
   constexpr int WTM = BM / 2, WTN = BN / 2;  // 2 x 2 waves
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  using TA = Bf16Tile<BM, A_KMAJ>;
-  using TB = Bf16Tile<BN, B_KMAJ>;
+  constexpr int NSUB = BKT / 16;             // MFMA K-substeps per step
+  using TA = Bf16Tile<BM, A_KMAJ, BKT>;
+  using TB = Bf16Tile<BN, B_KMAJ, BKT>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LPS = TA::INSTR + TB::INSTR;  // buffer loads per wave per step
   static_assert(NS >= 2 && NS <= 6, "2..6 stages");
-  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  static_assert(NS * STAGE * OCC <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
@@ -224,9 +243,9 @@ gemm_bf16_kernel(const GemmArgs p) {
   const int M = p.M, N = p.N, K = p.K;
   const int kbeg = ks * p.k_per_split;
   const int kend = min(K, kbeg + p.k_per_split);
-  const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
+  const int nk = kend > kbeg ? (kend - kbeg + BKT - 1) / BKT : 0;
   const int nkp = ((nk + NS - 1) / NS) * NS;  // padded with zero-filled steps
-  const int ktail = (kend - kbeg) & (kBK - 1);  // valid K in the last real step (0 = full)
+  const int ktail = (kend - kbeg) & (BKT - 1);  // valid K in the last real step (0 = full)
 
   const bf16_t* A = static_cast<const bf16_t*>(p.A);
   const bf16_t* B = static_cast<const bf16_t*>(p.B);
@@ -238,7 +257,7 @@ gemm_bf16_kernel(const GemmArgs p) {
   // Step kt's tiles into stage `dst`: loads for real steps, zeros past the end.
   auto issue = [&](int kt, lds_char* dst) {
     if (kt < nk) {
-      const int k0 = kbeg + kt * kBK;
+      const int k0 = kbeg + kt * BKT;
       uint32_t na, nb;
       const bf16_t* pa;
       const bf16_t* pb;
@@ -247,7 +266,7 @@ gemm_bf16_kernel(const GemmArgs p) {
         na = (uint32_t)(((int64_t)(rows - 1) * p.lda + (kend - k0)) * 2);
         pa = A + (int64_t)m0 * p.lda + k0;
       } else {
-        const int kv = min(kBK, kend - k0);
+        const int kv = min(BKT, kend - k0);
         na = (uint32_t)(((int64_t)(kv - 1) * p.lda + (M - m0)) * 2);
         pa = A + (int64_t)k0 * p.lda + m0;
       }
@@ -256,7 +275,7 @@ gemm_bf16_kernel(const GemmArgs p) {
         nb = (uint32_t)(((int64_t)(rows - 1) * p.ldb + (kend - k0)) * 2);
         pb = B + (int64_t)n0 * p.ldb + k0;
       } else {
-        const int kv = min(kBK, kend - k0);
+        const int kv = min(BKT, kend - k0);
         nb = (uint32_t)(((int64_t)(kv - 1) * p.ldb + (N - n0)) * 2);
         pb = B + (int64_t)k0 * p.ldb + n0;
       }
@@ -304,12 +323,13 @@ gemm_bf16_kernel(const GemmArgs p) {
                                                             __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
   };
 
-  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];  // fragments of K-substeps 0 and 1
+  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];  // fragments of even / odd K-substeps
 
   // One step in stage ST (compile time) with its substep-0 fragments in
   // a0/b0.  Order (kept by the scheduling barriers): loads of step kt+NS-1;
-  // substep-1 reads; substep-0 MFMAs; wait for step kt+1 and barrier; its
-  // substep-0 reads; substep-1 MFMAs.
+  // then for each substep s the reads of substep s+1 go out before the MFMAs
+  // of substep s; before the last substep's MFMAs the kernel waits for step
+  // kt+1, passes the barrier and reads that step's substep-0 fragments.
   auto step = [&](auto STc, int kt) {
     constexpr int ST = decltype(STc)::value;
     lds_char* cur = stage(STc);
@@ -321,6 +341,18 @@ gemm_bf16_kernel(const GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     mfmas(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NSUB == 4) {
+      FragLoop<0, FM, 2>::run(ta, cur, a0);
+      FragLoop<0, FN, 2>::run(tb, cur + TA::BYTES, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      FragLoop<0, FM, 3>::run(ta, cur, a1);
+      FragLoop<0, FN, 3>::run(tb, cur + TA::BYTES, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (kt + 1 < nkp) {
       wait_landed(kt + 1);
       fix_tail(kt + 1, nxt);

@@ -7,9 +7,11 @@
 namespace tpmlp {
 
 // out[r, c] = sum_{i < tp} P[i*shard_stride + r*ldp + c], added in ascending i.
-// Each thread owns 16-byte column groups of a row and keeps all tp loads of a
-// group in flight together; rows are spread over the grid.  `UNROLL` groups
-// per thread per row pass raise the bytes in flight per wave.
+// Each thread owns UNROLL 16-byte column groups of a row.  Shards are taken
+// in groups of 8 whose loads are all issued before any of their adds, so up
+// to 8 * UNROLL loads per thread are in flight; the partials are read once,
+// so loads and stores bypass cache residency (non-temporal).  Rows are spread
+// over the grid.
 template <int UNROLL>
 __global__ void __launch_bounds__(256)
 partial_sum_kernel(const float* __restrict__ P, int64_t shard_stride, int64_t ldp,
@@ -21,32 +23,40 @@ partial_sum_kernel(const float* __restrict__ P, int64_t shard_stride, int64_t ld
     const int cb = (int)(b - (int64_t)r * per_row_blocks);
     const float* src = P + (int64_t)r * ldp;
     float* dst = out + (int64_t)r * ldo;
-    f32x4_t s[UNROLL];
     int cv[UNROLL];
+    f32x4_t s[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       cv[u] = (cb * UNROLL + u) * 256 + threadIdx.x;
       s[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (cv[u] < nvec) s[u] = *reinterpret_cast<const f32x4_t*>(src + 4 * (int64_t)cv[u]);
     }
-    for (int i = 1; i < tp; ++i) {
-      const float* si = src + (int64_t)i * shard_stride;
-      f32x4_t x[UNROLL];
+    for (int i0 = 0; i0 < tp; i0 += 8) {
+      f32x4_t x[8][UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        if (cv[u] < nvec) x[u] = *reinterpret_cast<const f32x4_t*>(si + 4 * (int64_t)cv[u]);
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        if (cv[u] < nvec) {
-          s[u][0] += x[u][0];
-          s[u][1] += x[u][1];
-          s[u][2] += x[u][2];
-          s[u][3] += x[u][3];
-        }
+        for (int u = 0; u < UNROLL; ++u)
+          if (i0 + j < tp && cv[u] < nvec)
+            x[j][u] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4_t*>(src + (int64_t)(i0 + j) * shard_stride + 4 * (int64_t)cv[u]));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+          if (i0 + j < tp && cv[u] < nvec) {
+            if (i0 + j == 0) {
+              s[u] = x[j][u];
+            } else {
+              s[u][0] += x[j][u][0];
+              s[u][1] += x[j][u][1];
+              s[u][2] += x[j][u][2];
+              s[u][3] += x[j][u][3];
+            }
+          }
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
-      if (cv[u] < nvec) *reinterpret_cast<f32x4_t*>(dst + 4 * (int64_t)cv[u]) = s[u];
+      if (cv[u] < nvec) __builtin_nontemporal_store(s[u], reinterpret_cast<f32x4_t*>(dst + 4 * (int64_t)cv[u]));
   }
 }
 

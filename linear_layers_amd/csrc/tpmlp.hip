@@ -181,26 +181,31 @@ int check_vec(const char* what, const void* p, int64_t n, bool required) {
 
 // --------------------------------------------------------------- planning --
 struct TileCfg {
-  int bm, bn;
-  float eff;  // relative per-CU throughput of the tile shape
+  int bm, bn, occ;   // tile, workgroups per CU
+  float eff, eff_act; // measured relative throughput: plain fp32 epilogue / activation epilogues
 };
-constexpr TileCfg kCfgBf16[] = {{256, 256, 1.00f}, {256, 128, 0.90f}, {128, 128, 0.75f}};
-constexpr TileCfg kCfgF32[] = {{128, 128, 1.00f}, {64, 64, 0.60f}};
+// bf16: 256x256 with one workgroup per CU is fastest when it fills the chip;
+// 128x128 with two per CU wins for under-filled grids and for the GeLU
+// epilogues (the second workgroup computes while one runs its epilogue).
+constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 0.85f}, {128, 128, 2, 0.96f, 1.00f}};
+constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f}, {64, 64, 1, 0.60f, 0.60f}};
 constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
 
-int plan_cfg(int dtype, int M, int N, int cus) {
+int plan_cfg(int dtype, int M, int N, int epi, int cus) {
   const TileCfg* cfgs = dtype == TPMLP_BF16 ? kCfgBf16 : kCfgF32;
-  const int n = dtype == TPMLP_BF16 ? 3 : 2;
+  const int n = 2;
   int best = 0;
   double best_score = -1.0;
   for (int i = 0; i < n; ++i) {
     const int64_t tiles = (int64_t)((M + cfgs[i].bm - 1) / cfgs[i].bm) * ((N + cfgs[i].bn - 1) / cfgs[i].bn);
-    const int64_t rounds = (tiles + cus - 1) / cus;
-    // useful fraction of the CU-rounds, times the tile's own efficiency, times
-    // the fraction of the padded tile area that is real output
-    const double fill = (double)tiles / (double)(rounds * cus);
+    const int64_t slots = (int64_t)cus * cfgs[i].occ;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    // useful fraction of the workgroup slots over all rounds, times the
+    // fraction of the padded tile area that is real output, times the
+    // configuration's measured relative throughput
+    const double fill = (double)tiles / (double)(rounds * slots);
     const double pad = ((double)M * N) / ((double)tiles * cfgs[i].bm * cfgs[i].bn);
-    const double score = fill * cfgs[i].eff * pad;
+    const double score = fill * pad * (epi == kEpiF32 ? cfgs[i].eff : cfgs[i].eff_act);
     if (score > best_score + 1e-9) {
       best_score = score;
       best = i;
@@ -231,20 +236,22 @@ int run_gemm_cfg(const char* role, GemmArgs a, hipStream_t s) {
                 dim3(WGM * WGN * 64), s, a);
 }
 
-template <int BM, int BN, bool AK, bool BKM, int EPI>
-int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s) {
+template <int BM, int BN, bool AK, bool BKM, int EPI, int NS, int OCC, int BKT>
+int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
+  a.group_m = group;
   if (a.splits < 1) a.splits = 1;
   const int per = (a.K + a.splits - 1) / a.splits;
-  a.k_per_split = ((per + kBK - 1) / kBK) * kBK;
+  a.k_per_split = ((per + BKT - 1) / BKT) * BKT;
   const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
   if (grid <= 0) return TPMLP_OK;
   if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
   char sym[128];
-  constexpr int NS = BM + BN >= 512 ? 4 : (BM + BN >= 384 ? 5 : 6);
-  snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS);
-  return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS>, dim3((unsigned)grid), dim3(256), s, a);
+  snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS, OCC,
+           BKT);
+  return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS, OCC, BKT>, dim3((unsigned)grid), dim3(256), s,
+                a);
 }
 
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 256 rows of
@@ -258,13 +265,10 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     return fail(TPMLP_E_SHAPE, "%s: leading dimension above 2^22 elements", role);
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
-  const int cfg = plan_cfg(dtype, a.M, a.N, cus);
+  const int cfg = plan_cfg(dtype, a.M, a.N, EPI, cus);
   if (dtype == TPMLP_BF16) {
-    switch (cfg) {
-      case 0: return run_gemm_bf16<256, 256, AK, BKM, EPI>(role, a, s);
-      case 1: return run_gemm_bf16<256, 128, AK, BKM, EPI>(role, a, s);
-      default: return run_gemm_bf16<128, 128, AK, BKM, EPI>(role, a, s);
-    }
+    if (cfg == 0) return run_gemm_bf16<256, 256, AK, BKM, EPI, 2, 1, 64>(role, a, s, 4);
+    return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, 8);
   }
   switch (cfg) {
     case 0: return run_gemm_cfg<float, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
@@ -516,7 +520,7 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
   TPMLP_TRY(device_cus(&cus));
   TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.mlp_dgrad_act", dtype, a, s)));
   if (db1_shard) {
-    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, cus);
+    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, cus);
     const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
     const int rows = (int)((T + bm - 1) / bm);
     TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 255) / 256)),
