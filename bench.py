@@ -3,23 +3,33 @@
 
 One step = the whole per-GPU hot path for shard 0 of the Llama-7B-scale MLP
 (T=8192 tokens, h=4096, F=16384, tp=8, bf16 storage, fp32 accumulate):
-  tp_mlp_fwd       GEMM1 + bias/GeLU epilogue, GEMM2 -> fp32 partial Z_0
+  tp_mlp_fwd        GEMM1 + bias/GeLU epilogue, GEMM2 -> fp32 partial Z_0
   shard_partial_sum this GPU's 1/tp share of the Z all-reduce arithmetic
                     (rows [0, T/tp) of all tp partials; the other shards'
                     partials were computed once during set-up)
-  tp_mlp_bwd       dH (GEMM + GeLU'), dW2, dW1, dX_0 partial
+  tp_mlp_bwd        dH (GEMM + GeLU'), dW2, dW1, dX_0 partial
   shard_partial_sum the same share of the dX all-reduce
 Inputs sit in HBM before the timed region starts.  `value` is the GEMM work
 (6 products of 2*T*h*F/tp flops) per second over the timed steps.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on
 one GPU.
+
+Profiling helpers (used with rocprofv3, see the profiles/ summaries):
+  --profile-pass OUT.json   a plain copy of known size, then one step; writes
+                            the step's kernel roles and symbols in launch order
+  --summarize-profile DIR   turn rocprofv3 output under DIR into the text
+                            summaries and traffic table under profiles/
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,8 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 2.4 GHz)
-PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
+CALIB_BYTES = 256 << 20     # the plain copy used to scale the HBM byte counters
 
 
 def parse():
@@ -42,7 +54,25 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time for the baseline")
     ap.add_argument("--breakdown", action="store_true", help="also print per-kernel timings to stderr")
+    ap.add_argument("--profile-pass", metavar="OUT_JSON", default=None)
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None)
     return ap.parse_args()
+
+
+def kernel_fingerprint() -> str:
+    """Hash of the kernel sources: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_layers_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def canon(name: str) -> str:
+    """Kernel name as the library reports it, from a demangled rocprofv3 name."""
+    n = name.replace("void tpmlp::", "").replace("tpmlp::", "")
+    n = re.sub(r"\(.*\)$", "", n).replace(" ", "").replace("true", "1").replace("false", "0")
+    return n
 
 
 def gemm_flops(wl):
@@ -58,7 +88,7 @@ def cpu_baseline(wl, raw, target_s: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
-    tp, Fs = wl.tp, wl.Fs
+    Fs = wl.Fs
     W1 = synth.to_f64(raw["W1"][:, :Fs], wl.dtype)
     W2 = synth.to_f64(raw["W2"][:Fs], wl.dtype)
     b1 = synth.to_f64(raw["b1"][:Fs], wl.dtype) if "b1" in raw else None
@@ -87,16 +117,83 @@ def cpu_baseline(wl, raw, target_s: float):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle, shard 0 fwd+bwd on the first {rows} of {wl.T} token rows "
                       f"(h={wl.h}, F/tp={Fs}); {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs on one GPU only; "
-                                   "the multi-GPU path is a design, not code"}))
-        sys.exit(2)
+class Step:
+    """Device buffers of the workload and the step's library calls."""
 
+    def __init__(self, wl, raw, tl, torch):
+        self.wl, self.tl = wl, tl
+        T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
+        dev = torch.device("cuda:0")
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.X, self.dZ = up(raw["X"]), up(raw["dZ"])
+        # Each shard's weights packed as its own rank would hold them.
+        self.W1s = [up(np.ascontiguousarray(raw["W1"][:, i * Fs:(i + 1) * Fs])) for i in range(tp)]
+        self.W2s = [up(raw["W2"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        self.b1s = [None if "b1" not in raw else up(raw["b1"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        bf = torch.bfloat16
+        self.A = torch.empty((T, Fs), dtype=bf, device=dev)
+        self.H = torch.empty((T, Fs), dtype=bf, device=dev)
+        self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.dXp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.rows = T // tp
+        self.Zsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dXsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dW1 = torch.empty((h, Fs), dtype=torch.float32, device=dev)
+        self.dW2 = torch.empty((Fs, h), dtype=torch.float32, device=dev)
+        self.db1 = torch.empty((Fs,), dtype=torch.float32, device=dev) if "b1" in raw else None
+        self.ws = torch.empty(tl.tpmlp_bwd_workspace_bytes(tl.BF16, T, h, F, tp), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        for i in range(1, tp):  # the other shards' partials, computed once
+            self.shard(i)
+
+    def shard(self, i):
+        tl, s = self.tl, self
+        tl.tp_mlp_fwd(s.X, s.W1s[i], s.b1s[i], s.W2s[i], s.wl.tp, s.A, s.Zp[i], H_save=s.H, stream=s.stream)
+        tl.tp_mlp_bwd(s.X, s.W1s[i], s.W2s[i], s.H, s.A, s.dZ, s.wl.tp, s.dXp[i], s.dW1, s.dW2, db1_shard=s.db1,
+                      workspace=s.ws, stream=s.stream)
+
+    def __call__(self):
+        tl, s = self.tl, self
+        tl.tp_mlp_fwd(s.X, s.W1s[0], s.b1s[0], s.W2s[0], s.wl.tp, s.A, s.Zp[0], H_save=s.H, stream=s.stream)
+        tl.shard_partial_sum(s.Zp[:, :s.rows], s.Zsum, stream=s.stream)
+        tl.tp_mlp_bwd(s.X, s.W1s[0], s.W2s[0], s.H, s.A, s.dZ, s.wl.tp, s.dXp[0], s.dW1, s.dW2, db1_shard=s.db1,
+                      workspace=s.ws, stream=s.stream)
+        tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
+
+
+def step_roles(tl, step, torch):
+    """Kernel roles and symbols of one step, in launch order."""
+    tl.profile_enable("")
+    step()
+    torch.cuda.synchronize()
+    order = tl.profile_collect(ordered=True)
+    tl.profile_enable(None)
+    return order
+
+
+def load_traffic(symbol: str, role: str):
+    """Calibrated HBM bytes per launch of (role, symbol), if measured on these sources."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, "no traffic table"
+    if t.get("fingerprint") != kernel_fingerprint():
+        return None, "kernel sources changed since the counters were taken"
+    e = t.get("launches", {}).get(role)
+    if not e or e.get("kernel") != symbol:
+        return None, "no counters for this kernel"
+    return e["fetch_bytes"] + e["write_bytes"], "FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
+
+
+def run_bench(args):
     import torch
     import synth
     import linear_layers_amd as tl
@@ -107,50 +204,10 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     assert wl.kind == "mlp" and wl.dtype == "bf16"
     T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
-    dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
     raw = synth.mlp_inputs(wl)
-
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    X, dZ = up(raw["X"]), up(raw["dZ"])
-    W1_full, W2_full = up(raw["W1"]), up(raw["W2"])
-    b1_full = up(raw["b1"]) if "b1" in raw else None
-    # Each shard's weights packed as its own rank would hold them.
-    W1s = [W1_full[:, i * Fs:(i + 1) * Fs].contiguous() for i in range(tp)]
-    W2s = [W2_full[i * Fs:(i + 1) * Fs].contiguous() for i in range(tp)]
-    b1s = [None if b1_full is None else b1_full[i * Fs:(i + 1) * Fs].contiguous() for i in range(tp)]
-    del W1_full, W2_full
-    bf = torch.bfloat16
-    A = torch.empty((T, Fs), dtype=bf, device=dev)
-    H = torch.empty((T, Fs), dtype=bf, device=dev)
-    Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
-    dXp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
-    rows = T // tp
-    Zsum = torch.empty((rows, h), dtype=torch.float32, device=dev)
-    dXsum = torch.empty((rows, h), dtype=torch.float32, device=dev)
-    dW1 = torch.empty((h, Fs), dtype=torch.float32, device=dev)
-    dW2 = torch.empty((Fs, h), dtype=torch.float32, device=dev)
-    db1 = torch.empty((Fs,), dtype=torch.float32, device=dev) if b1_full is not None else None
-    ws = torch.empty(tl.tpmlp_bwd_workspace_bytes(tl.BF16, T, h, F, tp), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def shard(i):
-        tl.tp_mlp_fwd(X, W1s[i], b1s[i], W2s[i], tp, A, Zp[i], H_save=H, stream=stream)
-        tl.tp_mlp_bwd(X, W1s[i], W2s[i], H, A, dZ, tp, dXp[i], dW1, dW2, db1_shard=db1, workspace=ws,
-                      stream=stream)
-
-    for i in range(1, tp):       # the other shards' partials, computed once
-        shard(i)
-
-    def step():
-        tl.tp_mlp_fwd(X, W1s[0], b1s[0], W2s[0], tp, A, Zp[0], H_save=H, stream=stream)
-        tl.shard_partial_sum(Zp[:, :rows], Zsum, stream=stream)
-        tl.tp_mlp_bwd(X, W1s[0], W2s[0], H, A, dZ, tp, dXp[0], dW1, dW2, db1_shard=db1, workspace=ws,
-                      stream=stream)
-        tl.shard_partial_sum(dXp[:, :rows], dXsum, stream=stream)
-
+    step = Step(wl, raw, tl, torch)
+    stream = step.stream
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -161,8 +218,13 @@ def main():
     torch.cuda.synchronize()
     warm = tl.profile_collect()
     tl.profile_enable(None)
-    by_time = sorted(warm.items(), key=lambda kv: -kv[1][1])
-    dominant = by_time[0][0].split("|")[0]
+    by_role = {}
+    for k, (n, ms, sym) in warm.items():
+        role = k.split("|")[0]
+        r = by_role.setdefault(role, [0, 0.0, sym])
+        r[0] += n
+        r[1] += ms
+    dominant = max(by_role, key=lambda r: by_role[r][1])
 
     # Timed region: K steps between two synchronisations; the dominant
     # kernel's launches are bracketed by events on the launch stream.
@@ -178,8 +240,7 @@ def main():
     wall = time.perf_counter() - w0
     timed = tl.profile_collect()
     tl.profile_enable(None)
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
+    ms_step = e0.elapsed_time(e1) / args.steps
 
     flops_step = 6 * gemm_flops(wl)
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -189,21 +250,29 @@ def main():
     n_launch, dom_ms, dom_sym = timed[dom_key]
     per_launch_ms = dom_ms / n_launch
     achieved = gemm_flops(wl) / (per_launch_ms * 1e-3) / 1e12
+    traffic, traffic_note = load_traffic(dom_sym, dominant)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": dom_sym, "role": dominant, "launches": n_launch,
-                "mean_launch_us": round(per_launch_ms * 1e3, 2),
-                "flop_per_launch": gemm_flops(wl)}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_note": traffic_note,
+                "algorithmic_bytes": None, "kernel": dom_sym, "role": dominant, "launches": n_launch,
+                "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": gemm_flops(wl)}
+    # the dominant GEMM's operands and outputs, once each (algorithmic bytes)
+    alg = {"gemm.mlp_fwd1": T * h * 2 + h * Fs * 2 + 2 * T * Fs * 2,
+           "gemm.mlp_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
+           "gemm.mlp_dgrad_act": T * h * 2 + Fs * h * 2 + T * Fs * 2 + T * Fs * 2,
+           "gemm.mlp_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
+           "gemm.mlp_wgrad1": T * h * 2 + T * Fs * 2 + h * Fs * 4,
+           "gemm.mlp_dgrad1": T * Fs * 2 + h * Fs * 2 + T * h * 4}
+    roofline["algorithmic_bytes"] = alg.get(dominant)
 
     kernels = {}
-    for k, (n, ms, sym) in sorted(warm.items(), key=lambda kv: -kv[1][1]):
-        role = k.split("|")[0]
+    for role, (n, ms, sym) in sorted(by_role.items(), key=lambda kv: -kv[1][1]):
         us = ms / n * 1e3
         entry = {"kernel": sym, "mean_us": round(us, 2)}
         if role.startswith("gemm"):
             entry["tflops"] = round(gemm_flops(wl) / (us * 1e-6) / 1e12, 1)
         elif role == "partial_sum":
-            entry["gbs"] = round((tp + 1) * rows * h * 4 / (us * 1e-6) / 1e9, 1)
+            entry["gbs"] = round((tp + 1) * step.rows * h * 4 / (us * 1e-6) / 1e9, 1)
         kernels[role] = entry
 
     out = {
@@ -235,6 +304,115 @@ def main():
     if args.breakdown:
         print(json.dumps(timed), file=sys.stderr)
     print(json.dumps(out), flush=True)
+
+
+def run_profile_pass(args):
+    """A plain copy of CALIB_BYTES, then set-up and one step (for rocprofv3 --pmc)."""
+    import torch
+    import synth
+    import linear_layers_amd as tl
+
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)            # the first kernel of the process: the calibration copy
+    torch.cuda.synchronize()
+    wl = synth.WORKLOADS[args.workload]
+    raw = synth.mlp_inputs(wl)
+    step = Step(wl, raw, tl, torch)
+    step()                    # warm
+    torch.cuda.synchronize()
+    order = step_roles(tl, step, torch)   # the last step: its launches in order
+    with open(args.profile_pass, "w") as f:
+        json.dump({"workload": wl.name, "order": order, "fingerprint": kernel_fingerprint()}, f)
+    print(json.dumps({"profile_pass": args.profile_pass, "launches": len(order)}), flush=True)
+
+
+def _read_pmc(csv_path, counter):
+    """(dispatch id, kernel name, value) of one counter, in dispatch order."""
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_profile(d):
+    """Write profiles/*.txt and profiles/traffic.json from rocprofv3 output under d."""
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(d, "roles.json")) as f:
+        roles = json.load(f)
+    cmds = {}
+    if os.path.exists(os.path.join(d, "commands.json")):
+        with open(os.path.join(d, "commands.json")) as f:
+            cmds = json.load(f)
+    scaled = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        csvs = glob.glob(os.path.join(d, counter.lower(), "**", "*counter_collection.csv"), recursive=True)
+        rows = _read_pmc(csvs[0], counter)
+        calib = next(r for r in rows if "copy" in r[1].lower())
+        factor = CALIB_BYTES / (calib[2] * 1024.0)
+        lib = [r for r in rows if "tpmlp::" in r[1]]
+        last = lib[-len(roles["order"]):]
+        for (role, sym), (_, name, kib) in zip(roles["order"], last):
+            assert canon(name) == sym, f"launch order mismatch: {canon(name)} != {sym}"
+            scaled.setdefault(role, {"kernel": sym})[counter] = (kib, kib * 1024.0 * factor)
+        scaled.setdefault("_calibration", {})[counter] = {"counter_kib": calib[2], "factor": factor}
+    launches = {}
+    lines = [f"# HBM traffic per launch, {roles['workload']} step (one launch of each kernel role)",
+             "", f"fetch: {cmds.get('fetch', 'rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --profile-pass OUT')}",
+             f"write: {cmds.get('write', 'rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --profile-pass OUT')}",
+             "", "Counters are KiB per dispatch, scaled by the factor that maps a plain "
+             f"{CALIB_BYTES >> 20} MiB copy (torch copy_, first kernel of the process) to its known bytes:",
+             f"  FETCH_SIZE factor {scaled['_calibration']['FETCH_SIZE']['factor']:.4f} "
+             f"(copy read {scaled['_calibration']['FETCH_SIZE']['counter_kib']:.0f} KiB)",
+             f"  WRITE_SIZE factor {scaled['_calibration']['WRITE_SIZE']['factor']:.4f} "
+             f"(copy wrote {scaled['_calibration']['WRITE_SIZE']['counter_kib']:.0f} KiB)", "",
+             f"{'role':22s} {'kernel':44s} {'fetch MB':>9s} {'write MB':>9s}"]
+    for role, e in scaled.items():
+        if role.startswith("_"):
+            continue
+        fb, wb = e["FETCH_SIZE"][1], e["WRITE_SIZE"][1]
+        launches[role] = {"kernel": e["kernel"], "fetch_bytes": fb, "write_bytes": wb}
+        lines.append(f"{role:22s} {e['kernel']:44s} {fb / 1e6:9.1f} {wb / 1e6:9.1f}")
+    with open(os.path.join(PROFILES, f"{roles['workload']}_step_hbm_traffic.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump({"fingerprint": roles["fingerprint"], "workload": roles["workload"], "launches": launches,
+                   "calibration": scaled["_calibration"]}, f, indent=1)
+    # kernel-trace statistics
+    stats = glob.glob(os.path.join(d, "stats", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        with open(stats[0]) as f:
+            st = list(csv.DictReader(f))
+        out = [f"# Kernel durations, {roles['workload']} bench run",
+               "", f"command: {cmds.get('stats', 'rocprofv3 --kernel-trace --stats -- python3 bench.py')}", "",
+               f"{'kernel':60s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'%':>6s}"]
+        for r in st:
+            name = canon(r["Name"])
+            if len(name) > 60:
+                name = name[:57] + "..."
+            out.append(f"{name:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                       f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+        with open(os.path.join(PROFILES, f"{roles['workload']}_kernel_stats.txt"), "w") as f:
+            f.write("\n".join(out) + "\n")
+    print(f"wrote profiles for {roles['workload']}")
+
+
+def main():
+    args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs on one GPU only; "
+                                   "the multi-GPU path is a design, not code"}))
+        sys.exit(2)
+    if args.profile_pass:
+        run_profile_pass(args)
+        return
+    run_bench(args)
 
 
 if __name__ == "__main__":

@@ -46,8 +46,8 @@
  *     unknown dtype / activation                           -> TPMLP_E_DTYPE / TPMLP_E_ACT
  *     workspace too small                                  -> TPMLP_E_WORKSPACE
  *     sizes beyond 2^31-1 elements per dimension           -> TPMLP_E_SHAPE
- *   T == 0 (an empty batch) is valid and enqueues nothing; outputs whose
- *   size does not depend on T (weight gradients) are then written as zeros.
+ *   T == 0 (an empty batch) is valid: forward calls enqueue nothing; backward
+ *   calls write zeros to the weight and bias gradients (sums over no rows).
  * - Status detail: tpmlp_last_error() returns a thread-local message about
  *   the last non-OK status of the calling thread.
  */
@@ -187,9 +187,10 @@ const char* tpmlp_version(void);
  * tpmlp_profile_enable(filter): while enabled, every kernel the library
  * launches whose role name contains `filter` ("" = all, NULL = disable) is
  * bracketed by two hipEvents recorded on the launch stream.
- * tpmlp_profile_collect(buf, len): waits for the recorded events, writes a
- * JSON object {"role": [launches, total_ms, kernel_symbol], ...} to buf
- * (truncated to len) and clears the record.  Returns TPMLP_OK or an error. */
+ * tpmlp_profile_collect(buf, len): waits for the recorded events, writes the
+ * launches in order as a JSON list [["role", "kernel_symbol", ms], ...] to buf
+ * and clears the record.  Returns TPMLP_OK, TPMLP_E_SHAPE if the text did not
+ * fit in len bytes (it is truncated), or TPMLP_E_HIP. */
 int tpmlp_profile_enable(const char* filter);
 int tpmlp_profile_collect(char* buf, size_t len);
 

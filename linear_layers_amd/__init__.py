@@ -230,8 +230,19 @@ def profile_enable(filter: Optional[str] = "") -> None:
     _check(_get_lib().tpmlp_profile_enable(None if filter is None else filter.encode()))
 
 
-def profile_collect() -> dict:
-    """{role|symbol: (launches, total_ms, symbol)} of the launches recorded so far."""
-    buf = ctypes.create_string_buffer(1 << 16)
+def profile_collect(ordered: bool = False):
+    """Launches recorded since the last collect.
+
+    ordered=True: [(role, symbol), ...] in launch order.  Otherwise
+    {role|symbol: (launches, total_ms, symbol)}.
+    """
+    buf = ctypes.create_string_buffer(1 << 20)
     _check(_get_lib().tpmlp_profile_collect(buf, len(buf)))
-    return {k: tuple(v) for k, v in json.loads(buf.value.decode() or "{}").items()}
+    recs = json.loads(buf.value.decode() or "[]")
+    if ordered:
+        return [(r, s) for r, s, _ in recs]
+    agg = {}
+    for role, sym, ms in recs:
+        n, tot, _ = agg.get(f"{role}|{sym}", (0, 0.0, sym))
+        agg[f"{role}|{sym}"] = (n + 1, tot + ms, sym)
+    return agg

@@ -418,71 +418,114 @@ gemm_bf16_kernel(const GemmArgs p) {
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
     bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
     const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
+    const int h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = ncol + 32 * j + 8 * g;
-        if (col >= N) continue;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int pr = 0; pr < 2; ++pr) {
+        // Register groups g = 2pr (columns c + 4h..) and 2pr+1 (c + 8 + 4h..);
+        // after the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
+        const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+        float bv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         if (bias) {
-          const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + col);
-          bv[0] = bf16lo(w[0]); bv[1] = bf16hi(w[0]); bv[2] = bf16lo(w[1]); bv[3] = bf16hi(w[1]);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int cq = c + 8 * q + 4 * h;
+            if (cq < N) {
+              const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
+              bv[q][0] = bf16lo(w[0]); bv[q][1] = bf16hi(w[0]); bv[q][2] = bf16lo(w[1]); bv[q][3] = bf16hi(w[1]);
+            }
+          }
         }
+        const int cs = c + 8 * h;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int row = mrow + 32 * i;
-          if (row >= M) continue;
-          float h[4], a[4];
+          uint32_t aw[2][2], hw[2][2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            h[e] = acc[i][j][4 * g + e] + bv[e];
-            a[e] = act_apply(p.act, h[e]);
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * pr + q;
+            float hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[q][e];
+            aw[q][0] = pack_bf16x2(act_apply(p.act, hv[0]), act_apply(p.act, hv[1]));
+            aw[q][1] = pack_bf16x2(act_apply(p.act, hv[2]), act_apply(p.act, hv[3]));
+            hw[q][0] = pack_bf16x2(hv[0], hv[1]);
+            hw[q][1] = pack_bf16x2(hv[2], hv[3]);
           }
-          const int64_t o = (int64_t)row * p.ldy + col;
-          *reinterpret_cast<u32x2_t*>(Y + o) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          if (Hs)
-            *reinterpret_cast<u32x2_t*>(Hs + (int64_t)row * p.ldh + col) =
-                u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
+            aw[0][w] = ra[0];
+            aw[1][w] = ra[1];
+            const auto rh = __builtin_amdgcn_permlane32_swap(hw[0][w], hw[1][w], false, false);
+            hw[0][w] = rh[0];
+            hw[1][w] = rh[1];
+          }
+          if (row < M && cs < N) {
+            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
+            if (Hs)
+              *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) =
+                  u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+          }
         }
       }
   } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
     const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
-    // red: [2 (wm)][BN] floats in stage 0
+    const int h = lane >> 5;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = ncol + 32 * j + 8 * g;
-        float cs[4] = {0.f, 0.f, 0.f, 0.f};
-        if (col < N) {
+      for (int pr = 0; pr < 2; ++pr) {
+        const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+        float csum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int cs = c + 8 * h;
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = mrow + 32 * i;
-            if (row >= M) continue;
-            const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + col);
-            const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
-            float d[4];
+        for (int i = 0; i < FM; ++i) {
+          const int row = mrow + 32 * i;
+          uint32_t dw[2][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              d[e] = acc[i][j][4 * g + e] * (p.act == kActGeluTanh ? gelu_tanh_grad(hv[e]) : 1.0f);
-              cs[e] += d[e];
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * pr + q;
+            const int cq = c + 8 * q + 4 * h;
+            float d[4] = {0.f, 0.f, 0.f, 0.f};
+            if (row < M && cq < N) {
+              const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
+              const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                d[e] = acc[i][j][4 * g + e] * (p.act == kActGeluTanh ? gelu_tanh_grad(hv[e]) : 1.0f);
+                csum[q][e] += d[e];
+              }
             }
-            *reinterpret_cast<u32x2_t*>(Y + (int64_t)row * p.ldy + col) =
-                u32x2_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+            dw[q][0] = pack_bf16x2(d[0], d[1]);
+            dw[q][1] = pack_bf16x2(d[2], d[3]);
           }
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(dw[0][w], dw[1][w], false, false);
+            dw[0][w] = r[0];
+            dw[1][w] = r[1];
+          }
+          if (row < M && cs < N)
+            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
         }
         // Sum over the 32 rows held by lanes with the same lane/32.
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int x = 1; x < 32; x <<= 1) cs[e] += __shfl_xor(cs[e], x);
-        }
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int x = 1; x < 32; x <<= 1) csum[q][e] += __shfl_xor(csum[q][e], x);
+          }
         if ((lane & 31) == 0) {
-          const int c = wn * WTN + 32 * j + 8 * g + 4 * (lane >> 5);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) red[wm * BN + c + e] = cs[e];
+          for (int q = 0; q < 2; ++q) {
+            const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[q][e];
+          }
         }
       }
     if (p.colsum) {

@@ -629,23 +629,19 @@ int tpmlp_profile_collect(char* buf, size_t len) {
     std::lock_guard<std::mutex> lk(P.mu);
     recs.swap(P.records);
   }
-  struct Agg {
-    std::string role, symbol;
-    long n;
-    double ms;
-  };
-  std::vector<Agg> aggs;
   int status = TPMLP_OK;
-  for (auto& r : recs) {
+  std::string out = "[";
+  for (size_t i = 0; i < recs.size(); ++i) {
     float ms = 0.0f;
-    hipError_t e = hipEventSynchronize(r.stop);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    hipError_t e = hipEventSynchronize(recs[i].stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, recs[i].start, recs[i].stop);
     if (e != hipSuccess && status == TPMLP_OK) status = hip_fail(e, "profile event");
-    auto it = std::find_if(aggs.begin(), aggs.end(),
-                           [&](const Agg& a) { return a.role == r.role && a.symbol == r.symbol; });
-    if (it == aggs.end()) aggs.push_back({r.role, r.symbol, 1, (double)ms});
-    else { it->n += 1; it->ms += ms; }
+    char item[512];
+    snprintf(item, sizeof(item), "%s[\"%s\", \"%s\", %.6f]", i ? ", " : "", recs[i].role.c_str(),
+             recs[i].symbol.c_str(), ms);
+    out += item;
   }
+  out += "]";
   {
     std::lock_guard<std::mutex> lk(P.mu);
     for (auto& r : recs) {
@@ -653,18 +649,11 @@ int tpmlp_profile_collect(char* buf, size_t len) {
       P.pool.push_back(r.stop);
     }
   }
-  std::string out = "{";
-  for (size_t i = 0; i < aggs.size(); ++i) {
-    char item[512];
-    snprintf(item, sizeof(item), "%s\"%s|%s\": [%ld, %.6f, \"%s\"]", i ? ", " : "", aggs[i].role.c_str(),
-             aggs[i].symbol.c_str(), aggs[i].n, aggs[i].ms, aggs[i].symbol.c_str());
-    out += item;
-  }
-  out += "}";
   if (buf && len > 0) {
     std::strncpy(buf, out.c_str(), len - 1);
     buf[len - 1] = '\0';
   }
+  if (status == TPMLP_OK && out.size() >= len) return fail(TPMLP_E_SHAPE, "profile buffer too small");
   return status;
 }
 
