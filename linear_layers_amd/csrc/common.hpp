@@ -37,31 +37,37 @@ template <> struct Elem<float> {
 };
 
 // GeLU, tanh form: gelu(x) = x/2 * (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
-// tanh(u) is evaluated from the identity tanh(u) = 1 - 2 / (exp(2u) + 1) with
-// the hardware base-2 exponential and reciprocal (each about 1 ulp); it
-// saturates to +-1 correctly when the exponential overflows to inf or
-// underflows to 0.
-constexpr float kSqrt2OverPi = 0.79788456080286535588f;
-constexpr float kGeluCubic = 0.044715f;
-constexpr float kTwoLog2e = 2.88539008177792681472f;  // 2 / ln 2
+// Since (1 + tanh(u)) / 2 is the logistic function of 2u, gelu(x) = x * s with
+// s = 1 / (1 + exp(-2u)), evaluated with the hardware base-2 exponential and
+// reciprocal (each about 1 ulp).  This form has no cancellation for negative
+// x, and saturates correctly: exp overflowing to inf gives s = 0, underflow
+// to 0 gives s = 1.
+constexpr float kGeluZ1 = 2.302208198144325f;     // 2 sqrt(2/pi) / ln 2
+constexpr float kGeluZ3 = 0.1029432395800235f;    // the same times 0.044715
+constexpr float kGeluD0 = 1.5957691216057308f;    // 2 sqrt(2/pi)
+constexpr float kGeluD2 = 0.21406444881780076f;   // the same times 3 * 0.044715
 
-__device__ __forceinline__ float tanh_from_exp(float u) {
-  const float e = __builtin_amdgcn_exp2f(u * kTwoLog2e);
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// s = logistic(2u) of the GeLU argument x, and x^2.
+__device__ __forceinline__ float gelu_gate(float x, float& x2) {
+  x2 = x * x;
+  const float z = x * __builtin_fmaf(x2, kGeluZ3, kGeluZ1);  // 2u / ln 2
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z));
 }
 
 __device__ __forceinline__ float gelu_tanh(float x) {
-  float u = kSqrt2OverPi * (x + kGeluCubic * x * x * x);
-  return 0.5f * x * (1.0f + tanh_from_exp(u));
+  float x2;
+  return x * gelu_gate(x, x2);
 }
 
-// d/dx gelu(x) = (1 + t)/2 + x/2 (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 x^2).
+// d/dx gelu(x) = s + x s (1 - s) 2u'(x), u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2).
+// x is clamped to +-64 first (the derivative is exactly 0 or 1 in fp32 there),
+// so that x^2 stays finite.
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
-  float x2 = x * x;
-  float u = kSqrt2OverPi * (x + kGeluCubic * x2 * x);
-  float t = tanh_from_exp(u);
-  float du = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * x2);
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * du;
+  const float xc = __builtin_amdgcn_fmed3f(x, -64.0f, 64.0f);
+  float x2;
+  const float s = gelu_gate(xc, x2);
+  const float t = xc * __builtin_fmaf(x2, kGeluD2, kGeluD0);  // 2 x u'(x)
+  return s * __builtin_fmaf(t, 1.0f - s, 1.0f);
 }
 
 enum ActKind { kActNone = 0, kActGeluTanh = 1 };

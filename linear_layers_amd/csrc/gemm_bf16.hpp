@@ -63,16 +63,16 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 // Position of 16-byte chunk q of K-row k in an M/N-contiguous tile.
 __device__ __forceinline__ int swz_t(int k, int q) { return q ^ ((k & 3) << 2); }
 
-template <int ROWS, bool KMAJ, int BKT>
+template <int ROWS, bool KMAJ, int BKT, int NW = 4>
 struct Bf16Tile {
   // One operand tile of ROWS (M or N) x BKT (K) bf16 = ROWS * BKT * 2 bytes.
   static constexpr int CPR = BKT / 8;           // 16-byte chunks per K-contiguous row
   static constexpr int BYTES = ROWS * BKT * 2;
   static constexpr int SLOTS = ROWS * CPR;      // 16-byte slots
-  static constexpr int INSTR = SLOTS / 256;     // buffer loads per wave (4 waves x 64 lanes)
+  static constexpr int INSTR = SLOTS / (64 * NW);  // buffer loads per wave
   static constexpr int QPR = ROWS / 8;          // chunks per K-row (M/N-contiguous layout)
   static_assert(BKT == 32 || BKT == 64, "K step of 32 or 64");
-  static_assert(SLOTS % 256 == 0, "tile too small for 4 waves");
+  static_assert(SLOTS % (64 * NW) == 0, "tile too small for the waves");
   static_assert(KMAJ || ROWS >= 128, "the K-row swizzle needs at least 16 chunks per K-row");
 
   uint32_t voff[INSTR];   // per-lane byte offsets in the re-based buffer
@@ -202,14 +202,16 @@ struct FragLoop<NF, NF, S> {
   __device__ __forceinline__ static void run(const Tile&, const lds_char*, u32x4_t*) {}
 };
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32>
-__global__ void __launch_bounds__(256, OCC)
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
+__global__ void __launch_bounds__(128 * WGN, OCC)
 gemm_bf16_kernel(const GemmArgs p) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;  // 2 x 2 waves
+  constexpr int WGM = 2;                     // waves along M
+  constexpr int NW = WGM * WGN, NT = 64 * NW;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int NSUB = BKT / 16;             // MFMA K-substeps per step
-  using TA = Bf16Tile<BM, A_KMAJ, BKT>;
-  using TB = Bf16Tile<BN, B_KMAJ, BKT>;
+  using TA = Bf16Tile<BM, A_KMAJ, BKT, NW>;
+  using TB = Bf16Tile<BN, B_KMAJ, BKT, NW>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LPS = TA::INSTR + TB::INSTR;  // buffer loads per wave per step
   static_assert(NS >= 2 && NS <= 6, "2..6 stages");
@@ -235,7 +237,7 @@ gemm_bf16_kernel(const GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   int tmi, tni, ks;
   map_tile(p, tmi, tni, ks);
@@ -254,31 +256,35 @@ gemm_bf16_kernel(const GemmArgs p) {
   ta.init(wave, lane, p.lda, wm * WTM);
   tb.init(wave, lane, p.ldb, wn * WTN);
 
+  // Re-based buffers of step kt (bytes past nbytes read as zero).
+  auto bases = [&](int kt, const bf16_t*& pa, uint32_t& na, const bf16_t*& pb, uint32_t& nb) {
+    const int k0 = kbeg + kt * BKT;
+    if constexpr (A_KMAJ) {
+      const int rows = min(BM, M - m0);
+      na = (uint32_t)(((int64_t)(rows - 1) * p.lda + (kend - k0)) * 2);
+      pa = A + (int64_t)m0 * p.lda + k0;
+    } else {
+      const int kv = min(BKT, kend - k0);
+      na = (uint32_t)(((int64_t)(kv - 1) * p.lda + (M - m0)) * 2);
+      pa = A + (int64_t)k0 * p.lda + m0;
+    }
+    if constexpr (B_KMAJ) {
+      const int rows = min(BN, N - n0);
+      nb = (uint32_t)(((int64_t)(rows - 1) * p.ldb + (kend - k0)) * 2);
+      pb = B + (int64_t)n0 * p.ldb + k0;
+    } else {
+      const int kv = min(BKT, kend - k0);
+      nb = (uint32_t)(((int64_t)(kv - 1) * p.ldb + (N - n0)) * 2);
+      pb = B + (int64_t)k0 * p.ldb + n0;
+    }
+  };
   // Step kt's tiles into stage `dst`: loads for real steps, zeros past the end.
   auto issue = [&](int kt, lds_char* dst) {
     if (kt < nk) {
-      const int k0 = kbeg + kt * BKT;
-      uint32_t na, nb;
       const bf16_t* pa;
       const bf16_t* pb;
-      if constexpr (A_KMAJ) {
-        const int rows = min(BM, M - m0);
-        na = (uint32_t)(((int64_t)(rows - 1) * p.lda + (kend - k0)) * 2);
-        pa = A + (int64_t)m0 * p.lda + k0;
-      } else {
-        const int kv = min(BKT, kend - k0);
-        na = (uint32_t)(((int64_t)(kv - 1) * p.lda + (M - m0)) * 2);
-        pa = A + (int64_t)k0 * p.lda + m0;
-      }
-      if constexpr (B_KMAJ) {
-        const int rows = min(BN, N - n0);
-        nb = (uint32_t)(((int64_t)(rows - 1) * p.ldb + (kend - k0)) * 2);
-        pb = B + (int64_t)n0 * p.ldb + k0;
-      } else {
-        const int kv = min(BKT, kend - k0);
-        nb = (uint32_t)(((int64_t)(kv - 1) * p.ldb + (N - n0)) * 2);
-        pb = B + (int64_t)k0 * p.ldb + n0;
-      }
+      uint32_t na, nb;
+      bases(kt, pa, na, pb, nb);
       ta.load(pa, na, dst, wave);
       tb.load(pb, nb, dst + TA::BYTES, wave);
     } else if (kt < nkp) {
@@ -287,8 +293,9 @@ gemm_bf16_kernel(const GemmArgs p) {
     }
   };
 
-  // Wait until this wave's loads of step `next` have landed: the loads of the
-  // real steps after it (at most NS-2) may stay in flight.
+  // Wait until this wave's loads of step `next` have landed: the loads of
+  // the real steps after it that are already issued (at most NS-2) may stay
+  // in flight.
   auto wait_landed = [&](int next) {
     const int later = min(NS - 2, max(0, nk - 1 - next));
     switch (later) {
@@ -369,10 +376,10 @@ gemm_bf16_kernel(const GemmArgs p) {
   if (nk > 0) {
     // Prologue: steps 0..NS-2 in flight, step 0 landed, its first fragments read.
     issue(0, stage(std::integral_constant<int, 0>{}));
-    issue(1, stage(std::integral_constant<int, 1>{}));
-    if constexpr (NS > 2) issue(2, stage(std::integral_constant<int, 2>{}));
-    if constexpr (NS > 3) issue(3, stage(std::integral_constant<int, 3>{}));
-    if constexpr (NS > 4) issue(4, stage(std::integral_constant<int, 4>{}));
+    if constexpr (NS > 2) issue(1, stage(std::integral_constant<int, 1>{}));
+    if constexpr (NS > 3) issue(2, stage(std::integral_constant<int, 2>{}));
+    if constexpr (NS > 4) issue(3, stage(std::integral_constant<int, 3>{}));
+    if constexpr (NS > 5) issue(4, stage(std::integral_constant<int, 4>{}));
     wait_landed(0);
     fix_tail(0, stage(std::integral_constant<int, 0>{}));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -415,122 +422,138 @@ gemm_bf16_kernel(const GemmArgs p) {
         }
     }
   } else if constexpr (EPI == kEpiBiasAct) {
-    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
-    bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
-    const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
-    const int h = lane >> 5;
+    // The activation is a compile-time choice inside, taken by one uniform branch.
+    auto epilogue = [&](auto GeluC) {
+      constexpr bool kGelu = decltype(GeluC)::value;
+      bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
+      bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
+      const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
+      const int h = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        // Register groups g = 2pr (columns c + 4h..) and 2pr+1 (c + 8 + 4h..);
-        // after the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
-        const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-        float bv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        if (bias) {
+        for (int pr = 0; pr < 2; ++pr) {
+          // Register groups g = 2pr (columns c + 4h..) and 2pr+1 (c + 8 + 4h..);
+          // after the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
+          const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+          float bv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+          if (bias) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int cq = c + 8 * q + 4 * h;
-            if (cq < N) {
-              const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
-              bv[q][0] = bf16lo(w[0]); bv[q][1] = bf16hi(w[0]); bv[q][2] = bf16lo(w[1]); bv[q][3] = bf16hi(w[1]);
-            }
-          }
-        }
-        const int cs = c + 8 * h;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = mrow + 32 * i;
-          uint32_t aw[2][2], hw[2][2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * pr + q;
-            float hv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[q][e];
-            aw[q][0] = pack_bf16x2(act_apply(p.act, hv[0]), act_apply(p.act, hv[1]));
-            aw[q][1] = pack_bf16x2(act_apply(p.act, hv[2]), act_apply(p.act, hv[3]));
-            hw[q][0] = pack_bf16x2(hv[0], hv[1]);
-            hw[q][1] = pack_bf16x2(hv[2], hv[3]);
-          }
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
-            aw[0][w] = ra[0];
-            aw[1][w] = ra[1];
-            const auto rh = __builtin_amdgcn_permlane32_swap(hw[0][w], hw[1][w], false, false);
-            hw[0][w] = rh[0];
-            hw[1][w] = rh[1];
-          }
-          if (row < M && cs < N) {
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
-            if (Hs)
-              *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) =
-                  u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
-          }
-        }
-      }
-  } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
-    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
-    const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
-    const int h = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-        float csum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        const int cs = c + 8 * h;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = mrow + 32 * i;
-          uint32_t dw[2][2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * pr + q;
-            const int cq = c + 8 * q + 4 * h;
-            float d[4] = {0.f, 0.f, 0.f, 0.f};
-            if (row < M && cq < N) {
-              const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
-              const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                d[e] = acc[i][j][4 * g + e] * (p.act == kActGeluTanh ? gelu_tanh_grad(hv[e]) : 1.0f);
-                csum[q][e] += d[e];
+            for (int q = 0; q < 2; ++q) {
+              const int cq = c + 8 * q + 4 * h;
+              if (cq < N) {
+                const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
+                bv[q][0] = bf16lo(w[0]); bv[q][1] = bf16hi(w[0]); bv[q][2] = bf16lo(w[1]); bv[q][3] = bf16hi(w[1]);
               }
             }
-            dw[q][0] = pack_bf16x2(d[0], d[1]);
-            dw[q][1] = pack_bf16x2(d[2], d[3]);
           }
+          const int cs = c + 8 * h;
 #pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto r = __builtin_amdgcn_permlane32_swap(dw[0][w], dw[1][w], false, false);
-            dw[0][w] = r[0];
-            dw[1][w] = r[1];
+          for (int i = 0; i < FM; ++i) {
+            const int row = mrow + 32 * i;
+            uint32_t aw[2][2], hw[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int g = 2 * pr + q;
+              float hv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[q][e];
+              if constexpr (kGelu) {
+                aw[q][0] = pack_bf16x2(gelu_tanh(hv[0]), gelu_tanh(hv[1]));
+                aw[q][1] = pack_bf16x2(gelu_tanh(hv[2]), gelu_tanh(hv[3]));
+              } else {
+                aw[q][0] = pack_bf16x2(hv[0], hv[1]);
+                aw[q][1] = pack_bf16x2(hv[2], hv[3]);
+              }
+              hw[q][0] = pack_bf16x2(hv[0], hv[1]);
+              hw[q][1] = pack_bf16x2(hv[2], hv[3]);
+            }
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
+              aw[0][w] = ra[0];
+              aw[1][w] = ra[1];
+              const auto rh = __builtin_amdgcn_permlane32_swap(hw[0][w], hw[1][w], false, false);
+              hw[0][w] = rh[0];
+              hw[1][w] = rh[1];
+            }
+            if (row < M && cs < N) {
+              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
+              if (Hs)
+                *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) =
+                    u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+            }
           }
-          if (row < M && cs < N)
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
         }
-        // Sum over the 32 rows held by lanes with the same lane/32.
+    };
+    if (p.act == kActGeluTanh) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
+  } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
+    auto epilogue = [&](auto GeluC) {
+      constexpr bool kGelu = decltype(GeluC)::value;
+      bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
+      const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
+      const int h = lane >> 5;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+        for (int pr = 0; pr < 2; ++pr) {
+          const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+          float csum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+          const int cs = c + 8 * h;
 #pragma unroll
-            for (int x = 1; x < 32; x <<= 1) csum[q][e] += __shfl_xor(csum[q][e], x);
+          for (int i = 0; i < FM; ++i) {
+            const int row = mrow + 32 * i;
+            uint32_t dw[2][2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int g = 2 * pr + q;
+              const int cq = c + 8 * q + 4 * h;
+              float d[4] = {0.f, 0.f, 0.f, 0.f};
+              if (row < M && cq < N) {
+                const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
+                const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  d[e] = kGelu ? acc[i][j][4 * g + e] * gelu_tanh_grad(hv[e]) : acc[i][j][4 * g + e];
+                  csum[q][e] += d[e];
+                }
+              }
+              dw[q][0] = pack_bf16x2(d[0], d[1]);
+              dw[q][1] = pack_bf16x2(d[2], d[3]);
+            }
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto r = __builtin_amdgcn_permlane32_swap(dw[0][w], dw[1][w], false, false);
+              dw[0][w] = r[0];
+              dw[1][w] = r[1];
+            }
+            if (row < M && cs < N)
+              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
           }
-        if ((lane & 31) == 0) {
+          // Sum over the 32 rows held by lanes with the same lane/32.
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+          for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[q][e];
+            for (int e = 0; e < 4; ++e) {
+#pragma unroll
+              for (int x = 1; x < 32; x <<= 1) csum[q][e] += __shfl_xor(csum[q][e], x);
+            }
+          if ((lane & 31) == 0) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[q][e];
+            }
           }
         }
-      }
+    };
+    if (p.act == kActGeluTanh) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
     if (p.colsum) {
       __syncthreads();
-      for (int c = tid; c < BN; c += 256) {
+      for (int c = tid; c < BN; c += NT) {
         if (n0 + c < N) p.colsum[(int64_t)tmi * N + n0 + c] = red[c] + red[BN + c];
       }
     }

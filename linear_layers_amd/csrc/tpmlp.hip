@@ -184,10 +184,10 @@ struct TileCfg {
   int bm, bn, occ;   // tile, workgroups per CU
   float eff, eff_act; // measured relative throughput: plain fp32 epilogue / activation epilogues
 };
-// bf16: 256x256 with one workgroup per CU is fastest when it fills the chip;
-// 128x128 with two per CU wins for under-filled grids and for the GeLU
-// epilogues (the second workgroup computes while one runs its epilogue).
-constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 0.85f}, {128, 128, 2, 0.96f, 1.00f}};
+// bf16: 256x256 with 8 waves (two per SIMD, so one issues MFMAs while the
+// other waits) is fastest when it fills the chip; 128x128 with 4 waves and two
+// workgroups per CU wins for grids that would leave CUs idle.
+constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f}, {128, 128, 2, 0.98f, 0.90f}};
 constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f}, {64, 64, 1, 0.60f, 0.60f}};
 constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
 
@@ -236,7 +236,7 @@ int run_gemm_cfg(const char* role, GemmArgs a, hipStream_t s) {
                 dim3(WGM * WGN * 64), s, a);
 }
 
-template <int BM, int BN, bool AK, bool BKM, int EPI, int NS, int OCC, int BKT>
+template <int BM, int BN, bool AK, bool BKM, int EPI, int NS, int OCC, int BKT, int WGN = 2>
 int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
@@ -248,10 +248,10 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
   if (grid <= 0) return TPMLP_OK;
   if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
   char sym[128];
-  snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS, OCC,
-           BKT);
-  return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS, OCC, BKT>, dim3((unsigned)grid), dim3(256), s,
-                a);
+  snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS,
+           OCC, BKT, WGN);
+  return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS, OCC, BKT, WGN>, dim3((unsigned)grid),
+                dim3(128 * WGN), s, a);
 }
 
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 256 rows of
@@ -267,8 +267,18 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   TPMLP_TRY(device_cus(&cus));
   const int cfg = plan_cfg(dtype, a.M, a.N, EPI, cus);
   if (dtype == TPMLP_BF16) {
-    if (cfg == 0) return run_gemm_bf16<256, 256, AK, BKM, EPI, 2, 1, 64>(role, a, s, 4);
-    return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, 8);
+    // Raster group: the tiles one XCD runs at once (CUs/8 x occupancy) span
+    // whole rows of tiles, so each round of an XCD shares its A rows.
+    const int bm = kCfgBf16[cfg].bm, bn = kCfgBf16[cfg].bn;
+    const int tiles_m = (a.M + bm - 1) / bm, tiles_n = (a.N + bn - 1) / bn;
+    const int group = std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
+    if (cfg == 0) {
+      // K step 32 with a 4-stage ring when B is read through the transposing
+      // LDS reads (more loads in flight hide their latency); 64 x 2 otherwise.
+      if constexpr (AK && !BKM) return run_gemm_bf16<256, 256, AK, BKM, EPI, 4, 1, 32, 4>(role, a, s, group);
+      else return run_gemm_bf16<256, 256, AK, BKM, EPI, 2, 1, 64, 4>(role, a, s, group);
+    }
+    return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, group);
   }
   switch (cfg) {
     case 0: return run_gemm_cfg<float, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
