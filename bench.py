@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 2.4 GHz)
+PEAK_SCLK_GHZ = 2.4         # the engine clock that peak assumes
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
@@ -219,11 +220,12 @@ def run_bench(args):
     warm = tl.profile_collect()
     tl.profile_enable(None)
     by_role = {}
-    for k, (n, ms, sym) in warm.items():
+    for k, (n, ms, sym, clocks) in warm.items():
         role = k.split("|")[0]
-        r = by_role.setdefault(role, [0, 0.0, sym])
+        r = by_role.setdefault(role, [0, 0.0, sym, []])
         r[0] += n
         r[1] += ms
+        r[3] += clocks
     dominant = max(by_role, key=lambda r: by_role[r][1])
 
     # Timed region: K steps between two synchronisations; the dominant
@@ -247,15 +249,22 @@ def run_bench(args):
 
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
-    n_launch, dom_ms, dom_sym = timed[dom_key]
+    n_launch, dom_ms, dom_sym, dom_clocks = timed[dom_key]
     per_launch_ms = dom_ms / n_launch
     achieved = gemm_flops(wl) / (per_launch_ms * 1e-3) / 1e12
+    # The peak assumes the 2.4 GHz peak engine clock; the clock the GEMM
+    # actually ran at (sampled in-kernel over workgroup 0's main loop) is
+    # reported beside it, with the peak scaled to that clock.
+    sclk = sum(dom_clocks) / len(dom_clocks) if dom_clocks else None
     traffic, traffic_note = load_traffic(dom_sym, dominant)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "traffic_note": traffic_note,
                 "algorithmic_bytes": None, "kernel": dom_sym, "role": dominant, "launches": n_launch,
-                "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": gemm_flops(wl)}
+                "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": gemm_flops(wl),
+                "sclk_ghz": round(sclk, 3) if sclk else None,
+                "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ, 1) if sclk else None,
+                "frac_at_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ), 4) if sclk else None}
     # the dominant GEMM's operands and outputs, once each (algorithmic bytes)
     alg = {"gemm.mlp_fwd1": T * h * 2 + h * Fs * 2 + 2 * T * Fs * 2,
            "gemm.mlp_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
@@ -266,9 +275,11 @@ def run_bench(args):
     roofline["algorithmic_bytes"] = alg.get(dominant)
 
     kernels = {}
-    for role, (n, ms, sym) in sorted(by_role.items(), key=lambda kv: -kv[1][1]):
+    for role, (n, ms, sym, clocks) in sorted(by_role.items(), key=lambda kv: -kv[1][1]):
         us = ms / n * 1e3
         entry = {"kernel": sym, "mean_us": round(us, 2)}
+        if clocks:
+            entry["sclk_ghz"] = round(sum(clocks) / len(clocks), 3)
         if role.startswith("gemm"):
             entry["tflops"] = round(gemm_flops(wl) / (us * 1e-6) / 1e12, 1)
         elif role == "partial_sum":

@@ -234,15 +234,17 @@ def profile_collect(ordered: bool = False):
     """Launches recorded since the last collect.
 
     ordered=True: [(role, symbol), ...] in launch order.  Otherwise
-    {role|symbol: (launches, total_ms, symbol)}.
+    {role|symbol: (launches, total_ms, symbol, clocks_ghz)}, where clocks_ghz
+    lists the shader clock sampled over workgroup 0's main loop of each
+    bf16 GEMM launch (empty for other kernels).
     """
     buf = ctypes.create_string_buffer(1 << 20)
     _check(_get_lib().tpmlp_profile_collect(buf, len(buf)))
     recs = json.loads(buf.value.decode() or "[]")
     if ordered:
-        return [(r, s) for r, s, _ in recs]
+        return [(r[0], r[1]) for r in recs]
     agg = {}
-    for role, sym, ms in recs:
-        n, tot, _ = agg.get(f"{role}|{sym}", (0, 0.0, sym))
-        agg[f"{role}|{sym}"] = (n + 1, tot + ms, sym)
+    for role, sym, ms, ghz in recs:
+        n, tot, _, clocks = agg.get(f"{role}|{sym}", (0, 0.0, sym, []))
+        agg[f"{role}|{sym}"] = (n + 1, tot + ms, sym, clocks + ([ghz] if ghz > 0 else []))
     return agg

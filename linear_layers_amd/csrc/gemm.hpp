@@ -36,6 +36,8 @@ struct GemmArgs {
   float* colsum;                 // kEpiActBwd: fp32 [tiles_m][N] per-tile column sums of dH (or null)
   int act;
   int group_m;                   // tile rows per raster group (0: 8)
+  unsigned long long* clk;       // profiling: workgroup 0 writes its main loop's shader-clock
+                                 // ticks and 100 MHz reference ticks here (or null)
 };
 
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id.  Renumber

@@ -239,6 +239,13 @@ gemm_bf16_kernel(const GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
+  // Profiling only: the shader clock over workgroup 0's main loop.
+  unsigned long long clk0 = 0, ref0 = 0;
+  if (p.clk != nullptr && blockIdx.x == 0) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    ref0 = __builtin_amdgcn_s_memrealtime();
+  }
+
   int tmi, tni, ks;
   map_tile(p, tmi, tni, ks);
   const int m0 = tmi * BM, n0 = tni * BN;
@@ -397,6 +404,10 @@ gemm_bf16_kernel(const GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the loads the compiler does not see
   __syncthreads();
+  if (p.clk != nullptr && blockIdx.x == 0 && tid == 0) {
+    p.clk[0] = __builtin_amdgcn_s_memtime() - clk0;
+    p.clk[1] = __builtin_amdgcn_s_memrealtime() - ref0;
+  }
   float* red = reinterpret_cast<float*>(st0);  // epilogue scratch (LDS is free now)
   (void)red;
 

@@ -47,6 +47,7 @@ int hip_fail(hipError_t e, const char* what) {
 struct ProfRecord {
   std::string role, symbol;
   hipEvent_t start, stop;
+  int clk_slot;  // slot of the clock buffer this launch wrote, or -1
 };
 
 struct Profiler {
@@ -55,6 +56,14 @@ struct Profiler {
   std::string filter;
   std::vector<ProfRecord> records;
   std::vector<hipEvent_t> pool;
+  // Clock samples of profiled GEMM launches: kClkSlots pairs of (shader
+  // clock ticks, 100 MHz ticks), device memory allocated by
+  // tpmlp_profile_enable on the device current then.
+  static constexpr int kClkSlots = 4096;
+  unsigned long long* clk = nullptr;
+  int clk_device = -1;
+  int clk_next = 0;
+  int pending_slot = -1;  // slot handed to the launch being prepared
 
   hipEvent_t take() {
     if (!pool.empty()) {
@@ -80,8 +89,11 @@ int launch(const char* role, const char* symbol, Kernel kernel, dim3 grid, dim3 
            hipStream_t stream, Args... args) {
   Profiler& P = prof();
   hipEvent_t e0 = nullptr, e1 = nullptr;
+  int slot = -1;
   {
     std::lock_guard<std::mutex> lk(P.mu);
+    slot = P.pending_slot;
+    P.pending_slot = -1;
     if (P.enabled && std::strstr(role, P.filter.c_str()) != nullptr) {
       e0 = P.take();
       e1 = P.take();
@@ -98,9 +110,23 @@ int launch(const char* role, const char* symbol, Kernel kernel, dim3 grid, dim3 
     hipError_t e = hipEventRecord(e1, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     std::lock_guard<std::mutex> lk(P.mu);
-    P.records.push_back({role, symbol, e0, e1});
+    P.records.push_back({role, symbol, e0, e1, slot});
   }
   return TPMLP_OK;
+}
+
+// Clock-buffer slot for a GEMM launch of `role` when profiling covers it on
+// the current device; null otherwise.
+unsigned long long* prof_clock_slot(const char* role) {
+  Profiler& P = prof();
+  std::lock_guard<std::mutex> lk(P.mu);
+  P.pending_slot = -1;
+  if (!P.enabled || P.clk == nullptr || std::strstr(role, P.filter.c_str()) == nullptr) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != P.clk_device) return nullptr;
+  P.pending_slot = P.clk_next;
+  P.clk_next = (P.clk_next + 1) % Profiler::kClkSlots;
+  return P.clk + 2 * P.pending_slot;
 }
 
 // ------------------------------------------------------------ device info --
@@ -250,6 +276,7 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
   char sym[128];
   snprintf(sym, sizeof(sym), "gemm_bf16_kernel<%d,%d,%d,%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI, NS,
            OCC, BKT, WGN);
+  a.clk = prof_clock_slot(role);
   return launch(role, sym, gemm_bf16_kernel<BM, BN, AK, BKM, EPI, NS, OCC, BKT, WGN>, dim3((unsigned)grid),
                 dim3(128 * WGN), s, a);
 }
@@ -629,6 +656,16 @@ int tpmlp_profile_enable(const char* filter) {
   std::lock_guard<std::mutex> lk(P.mu);
   P.enabled = filter != nullptr;
   P.filter = filter ? filter : "";
+  if (P.enabled && P.clk == nullptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&P.clk), sizeof(unsigned long long) * 2 * Profiler::kClkSlots);
+    if (e != hipSuccess) {
+      P.clk = nullptr;
+      return hip_fail(e, "profile clock buffer");
+    }
+    P.clk_device = dev;
+  }
   return TPMLP_OK;
 }
 
@@ -640,15 +677,31 @@ int tpmlp_profile_collect(char* buf, size_t len) {
     recs.swap(P.records);
   }
   int status = TPMLP_OK;
+  std::vector<float> ms(recs.size(), 0.0f);
+  for (size_t i = 0; i < recs.size(); ++i) {
+    hipError_t e = hipEventSynchronize(recs[i].stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], recs[i].start, recs[i].stop);
+    if (e != hipSuccess && status == TPMLP_OK) status = hip_fail(e, "profile event");
+  }
+  // All recorded launches have finished: their clock samples are final.
+  std::vector<unsigned long long> clk;
+  if (P.clk != nullptr && !recs.empty()) {
+    clk.resize(2 * Profiler::kClkSlots);
+    hipError_t e = hipMemcpy(clk.data(), P.clk, clk.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      clk.clear();
+      if (status == TPMLP_OK) status = hip_fail(e, "profile clock copy");
+    }
+  }
   std::string out = "[";
   for (size_t i = 0; i < recs.size(); ++i) {
-    float ms = 0.0f;
-    hipError_t e = hipEventSynchronize(recs[i].stop);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, recs[i].start, recs[i].stop);
-    if (e != hipSuccess && status == TPMLP_OK) status = hip_fail(e, "profile event");
+    // shader clock in GHz over workgroup 0's main loop, -1 when not sampled
+    double ghz = -1.0;
+    const int sl = recs[i].clk_slot;
+    if (sl >= 0 && !clk.empty() && clk[2 * sl + 1] > 0) ghz = (double)clk[2 * sl] / ((double)clk[2 * sl + 1] * 10.0);
     char item[512];
-    snprintf(item, sizeof(item), "%s[\"%s\", \"%s\", %.6f]", i ? ", " : "", recs[i].role.c_str(),
-             recs[i].symbol.c_str(), ms);
+    snprintf(item, sizeof(item), "%s[\"%s\", \"%s\", %.6f, %.4f]", i ? ", " : "", recs[i].role.c_str(),
+             recs[i].symbol.c_str(), ms[i], ghz);
     out += item;
   }
   out += "]";

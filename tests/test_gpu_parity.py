@@ -269,3 +269,35 @@ def test_bitwise_deterministic():
         outs.append([t.clone() for t in (A, H, Z, dX, dW1, db1, dW2)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_profiler_times_and_clocks():
+    """Profiling brackets each launch with events; bf16 GEMMs also report the
+    shader clock of workgroup 0's main loop.  Results stay bitwise equal to
+    an unprofiled run."""
+    need_gpu()
+    dtype, T, h, F, tp = "bf16", 515, 256, 1024, 2
+    raw, _ = _inputs(dtype, T, h, F, seed=4, bias=True)
+    Fs = F // tp
+    X, W1, W2, b1 = (to_dev(raw[k], dtype) for k in ("X", "W1", "W2", "b1"))
+
+    def run():
+        A, Z = empty((T, Fs), dtype), empty_f32((T, h))
+        tl.tp_mlp_fwd(X, W1[:, :Fs], b1[:Fs], W2[:Fs], tp, A, Z)
+        sync()
+        return A, Z
+
+    A0, Z0 = run()
+    tl.profile_enable("gemm")
+    try:
+        A1, Z1 = run()
+        recs = tl.profile_collect()
+    finally:
+        tl.profile_enable(None)
+    assert torch.equal(A0, A1) and torch.equal(Z0, Z1)
+    roles = {k.split("|")[0] for k in recs}
+    assert roles == {"gemm.mlp_fwd1", "gemm.mlp_fwd2"}
+    for n, ms, sym, clocks in recs.values():
+        assert n == 1 and ms > 0.0 and sym.startswith("gemm_bf16_kernel<")
+        assert len(clocks) == 1 and 0.05 < clocks[0] < 5.0
+    assert tl.profile_collect() == {}
