@@ -84,3 +84,47 @@ def mlp_bwd_by_differences(X, W1, b1, W2, dZ, step: float = 1e-5):
         bm = [b]
         out["db1"] = grad_matrix(bm, lambda: loss(X, W1, bm[0], W2))[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Gated MLP (wangyu.me 大语言模型并行策略（三）：张量并行, 多层感知机（MLP）中的
+# 张量并行): gate = X W_gate, up = X W_up, x = silu(gate) * up, down = x W_down.
+# ---------------------------------------------------------------------------
+def silu(x: float) -> float:
+    if x >= 0.0:
+        return x / (1.0 + math.exp(-x))
+    e = math.exp(x)
+    return x * e / (1.0 + e)
+
+
+def swiglu_fwd(X, W_gate, W_up, W_down):
+    X, Wg, Wu, Wd = to_lists(X), to_lists(W_gate), to_lists(W_up), to_lists(W_down)
+    G = matmul(X, Wg)
+    U = matmul(X, Wu)
+    A = [[silu(g) * u for g, u in zip(gr, ur)] for gr, ur in zip(G, U)]
+    return G, U, A, matmul(A, Wd)
+
+
+def swiglu_bwd_by_differences(X, W_gate, W_up, W_down, dZ, step: float = 1e-5):
+    """Gradients of L = sum(dZ * down) by central differences (tiny shapes only)."""
+    X, Wg, Wu, Wd, dZ = (to_lists(m) for m in (X, W_gate, W_up, W_down, dZ))
+
+    def loss():
+        Z = swiglu_fwd(X, Wg, Wu, Wd)[3]
+        return sum(dZ[r][c] * Z[r][c] for r in range(len(Z)) for c in range(len(Z[0])))
+
+    def grad_matrix(M):
+        g = [[0.0] * len(M[0]) for _ in M]
+        for r in range(len(M)):
+            for c in range(len(M[0])):
+                old = M[r][c]
+                e = step * max(1.0, abs(old))
+                M[r][c] = old + e
+                lp = loss()
+                M[r][c] = old - e
+                lm = loss()
+                M[r][c] = old
+                g[r][c] = (lp - lm) / (2.0 * e)
+        return g
+
+    return {"dX": grad_matrix(X), "dW_gate": grad_matrix(Wg), "dW_up": grad_matrix(Wu), "dW_down": grad_matrix(Wd)}
