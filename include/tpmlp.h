@@ -176,6 +176,60 @@ int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, i
                      const void* dY, int64_t lddy, float* dX_shard, int64_t lddx,
                      float* dW_shard, int64_t lddw);
 
+/* ---- Gated MLP (SwiGLU) -------------------------------------------------
+ * The Qwen3 MLP on [wangyu 多层感知机（MLP）中的张量并行]: gate = X W_gate,
+ * up = X W_up, x = silu(gate) * up, down = x W_down, with W_gate and W_up
+ * joined along their columns so one product yields both, the joined layer
+ * split by columns and W_down by rows; silu(g) = g / (1 + exp(-g)); no
+ * biases.  Shard i owns columns [i*Fs, (i+1)*Fs) of both W_gate and W_up,
+ * Fs = F / tp_size, which must be a multiple of 8.
+ *
+ * Packed order: shard i's joined weight W_gu_shard [h, 2 Fs] holds in packed
+ * column 16q + r the gate column 8q + r (r < 8) or the up column 8q + r - 8
+ * (r >= 8) of the shard.  The saved pre-activations GU_save [T, 2 Fs] and the
+ * gradient dW_gu_shard [h, 2 Fs] use the same order.  The bf16 GEMMs are the
+ * only implementation (TPMLP_E_DTYPE for fp32).  */
+
+/* Builds W_gu_shard [h, 2 Fs] (contiguous, storage dtype) from columns
+ * [shard*Fs, (shard+1)*Fs) of W_gate [h, F] (ldg) and W_up [h, F] (ldu). */
+int swiglu_pack_shard(void* stream, int dtype, int64_t h, int64_t F, int tp_size, int shard,
+                      const void* W_gate, int64_t ldg, const void* W_up, int64_t ldu, void* W_gu_shard);
+
+/* Writes the packed fp32 gradient dW_gu_shard [h, 2 Fs] into columns
+ * [shard*Fs, (shard+1)*Fs) of dW_gate [h, F] (ldg) and dW_up [h, F] (ldu). */
+int swiglu_unpack_grad(void* stream, int64_t h, int64_t F, int tp_size, int shard,
+                       const float* dW_gu_shard, float* dW_gate, int64_t ldg, float* dW_up, int64_t ldu);
+
+/* One shard's forward: GU = X W_gu_shard (packed), A = silu(gate) * up,
+ * Z_partial = A W_down_shard.
+ *   X             [T, h] bf16 (ld h)
+ *   W_gu_shard    [h, 2 Fs] bf16, packed order
+ *   W_down_shard  [Fs, h] bf16: rows i*Fs.. of W_down [F, h]
+ *   GU_save       [T, 2 Fs] bf16 packed pre-activations, or NULL
+ *   A_save        [T, Fs] bf16 (ld Fs)
+ *   Z_partial     [T, h] fp32: this shard's partial of down */
+int tp_swiglu_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size,
+                  const void* X, const void* W_gu_shard, const void* W_down_shard,
+                  void* GU_save, void* A_save, float* Z_partial);
+
+/* Bytes of device workspace tp_swiglu_bwd needs (0 on bad args). */
+size_t tp_swiglu_bwd_workspace_bytes(int dtype, int64_t T, int64_t h, int64_t F, int tp_size);
+
+/* One shard's backward for the upstream gradient dZ [T, h] (bf16) of down.
+ * With dA = dZ W_down_shard^T and, per column, dgate = dA * up * silu'(gate),
+ * dup = dA * silu(gate) (packed as dGU, bf16, kept in the workspace):
+ *   dX_partial     [T, h] fp32      dGU W_gu_shard^T (sum over shards = dX)
+ *   dW_gu_shard    [h, 2 Fs] fp32   X^T dGU, packed order
+ *   dW_down_shard  [Fs, h] fp32     A^T dZ
+ * GU_save and A_save come from tp_swiglu_fwd.  workspace: device memory of at
+ * least tp_swiglu_bwd_workspace_bytes() bytes, 256-byte aligned, owned by the
+ * caller.  T = 0 writes zero weight gradients. */
+int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size,
+                  const void* X, const void* W_gu_shard, const void* W_down_shard,
+                  const void* GU_save, const void* A_save, const void* dZ,
+                  float* dX_partial, float* dW_gu_shard, float* dW_down_shard,
+                  void* workspace, size_t workspace_bytes);
+
 /* Status name, and the calling thread's message for its last non-OK status. */
 const char* tpmlp_status_string(int status);
 const char* tpmlp_last_error(void);
@@ -188,8 +242,12 @@ const char* tpmlp_version(void);
  * launches whose role name contains `filter` ("" = all, NULL = disable) is
  * bracketed by two hipEvents recorded on the launch stream.
  * tpmlp_profile_collect(buf, len): waits for the recorded events, writes the
- * launches in order as a JSON list [["role", "kernel_symbol", ms], ...] to buf
- * and clears the record.  Returns TPMLP_OK, TPMLP_E_SHAPE if the text did not
+ * launches in order as a JSON list [["role", "kernel_symbol", ms, ghz], ...]
+ * to buf and clears the record.  ghz is the shader clock over workgroup 0's
+ * main loop for bf16 GEMM launches (sampled with the s_memtime and
+ * s_memrealtime counters; the first tpmlp_profile_enable allocates a small
+ * device buffer for these samples, kept until the process ends), -1 for
+ * other kernels.  Returns TPMLP_OK, TPMLP_E_SHAPE if the text did not
  * fit in len bytes (it is truncated), or TPMLP_E_HIP. */
 int tpmlp_profile_enable(const char* filter);
 int tpmlp_profile_collect(char* buf, size_t len);

@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "TpmlpError", "lib", "LIB_PATH", "F32", "BF16", "ACT_NONE", "ACT_GELU_TANH",
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
-    "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "profile_enable",
+    "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
+    "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -45,13 +46,18 @@ _SIGNATURES = {
                             _i64, _vp],
     "row_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64],
     "tpmlp_bwd_workspace_bytes": [_int, _i64, _i64, _i64, _int],
+    "swiglu_pack_shard": [_vp, _int, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _vp],
+    "swiglu_unpack_grad": [_vp, _i64, _i64, _int, _int, _vp, _vp, _i64, _vp, _i64],
+    "tp_swiglu_fwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_swiglu_bwd_workspace_bytes": [_int, _i64, _i64, _i64, _int],
+    "tp_swiglu_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz],
     "tpmlp_status_string": [_int],
     "tpmlp_last_error": [],
     "tpmlp_version": [],
     "tpmlp_profile_enable": [ctypes.c_char_p],
     "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
 }
-_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
              "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
 
 
@@ -223,6 +229,57 @@ def row_parallel_bwd(X_shard, W_shard, dY, tp_size: int, dX_shard, dW_shard, str
     _check(_get_lib().row_parallel_bwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
                                 _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N), _ptr(dY),
                                 _ld(dY, N), _ptr(dX_shard), _ld(dX_shard, Ks), _ptr(dW_shard), _ld(dW_shard, N)))
+
+
+def swiglu_pack_shard(W_gate, W_up, tp_size: int, shard: int, W_gu_shard, stream=None) -> None:
+    """W_gu_shard [h, 2F/tp] = shard `shard` of [W_gate | W_up], interleaved in groups of 8 columns."""
+    h, F = W_gate.shape
+    _require_contiguous("W_gu_shard", W_gu_shard)
+    _check(_get_lib().swiglu_pack_shard(_stream(stream, W_gate), _dtype(W_gate), h, F, tp_size, shard,
+                                        _ptr(W_gate), _ld(W_gate, F), _ptr(W_up), _ld(W_up, F), _ptr(W_gu_shard)))
+
+
+def swiglu_unpack_grad(dW_gu_shard, tp_size: int, shard: int, dW_gate, dW_up, stream=None) -> None:
+    """Columns of shard `shard` of dW_gate and dW_up [h, F] (fp32) from the packed dW_gu_shard."""
+    h, F = dW_gate.shape
+    _require_contiguous("dW_gu_shard", dW_gu_shard)
+    _check(_get_lib().swiglu_unpack_grad(_stream(stream, dW_gu_shard), h, F, tp_size, shard, _ptr(dW_gu_shard),
+                                         _ptr(dW_gate), _ld(dW_gate, F), _ptr(dW_up), _ld(dW_up, F)))
+
+
+def tp_swiglu_fwd(X, W_gu_shard, W_down_shard, tp_size: int, A_save, Z_partial, GU_save=None, stream=None) -> None:
+    """One shard of down = (silu(X W_gate) * (X W_up)) W_down: writes A_save, GU_save (optional), Z_partial."""
+    T, h = X.shape
+    Fs = W_down_shard.shape[0]
+    for n, t in (("X", X), ("W_gu_shard", W_gu_shard), ("W_down_shard", W_down_shard), ("A_save", A_save),
+                 ("Z_partial", Z_partial), ("GU_save", GU_save)):
+        _require_contiguous(n, t)
+    _check(_get_lib().tp_swiglu_fwd(_stream(stream, X), _dtype(X), T, h, Fs * tp_size, tp_size, _ptr(X),
+                                    _ptr(W_gu_shard), _ptr(W_down_shard), _ptr(GU_save), _ptr(A_save),
+                                    _ptr(Z_partial)))
+
+
+def tp_swiglu_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: int) -> int:
+    return int(_get_lib().tp_swiglu_bwd_workspace_bytes(dtype, T, h, F, tp_size))
+
+
+def tp_swiglu_bwd(X, W_gu_shard, W_down_shard, GU_save, A_save, dZ, tp_size: int, dX_partial, dW_gu_shard,
+                  dW_down_shard, workspace=None, stream=None) -> None:
+    """One shard's backward of the gated MLP; workspace is a device uint8 tensor (allocated here if None)."""
+    T, h = X.shape
+    Fs = W_down_shard.shape[0]
+    F = Fs * tp_size
+    for n, t in (("X", X), ("W_gu_shard", W_gu_shard), ("W_down_shard", W_down_shard), ("GU_save", GU_save),
+                 ("A_save", A_save), ("dZ", dZ), ("dX_partial", dX_partial), ("dW_gu_shard", dW_gu_shard),
+                 ("dW_down_shard", dW_down_shard)):
+        _require_contiguous(n, t)
+    dt = _dtype(X)
+    if workspace is None:
+        workspace = torch.empty(max(1, tp_swiglu_bwd_workspace_bytes(dt, T, h, F, tp_size)), dtype=torch.uint8,
+                                device=X.device)
+    _check(_get_lib().tp_swiglu_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W_gu_shard),
+                                    _ptr(W_down_shard), _ptr(GU_save), _ptr(A_save), _ptr(dZ), _ptr(dX_partial),
+                                    _ptr(dW_gu_shard), _ptr(dW_down_shard), _ptr(workspace), workspace.numel()))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:

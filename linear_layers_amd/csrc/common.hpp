@@ -70,6 +70,21 @@ __device__ __forceinline__ float gelu_tanh_grad(float x) {
   return s * __builtin_fmaf(t, 1.0f - s, 1.0f);
 }
 
+// SiLU: silu(g) = g * s, s = 1 / (1 + exp(-g)), with the hardware base-2
+// exponential and reciprocal; exp overflowing to inf gives s = 0.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float sigmoidf_fast(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
+}
+
+// d silu / dg = s (1 + g (1 - s)); finite for every finite g.
+__device__ __forceinline__ void silu_and_grad(float g, float& silu, float& grad) {
+  const float s = sigmoidf_fast(g);
+  silu = g * s;
+  grad = s * __builtin_fmaf(g, 1.0f - s, 1.0f);
+}
+
 enum ActKind { kActNone = 0, kActGeluTanh = 1 };
 
 __device__ __forceinline__ float act_apply(int act, float x) {

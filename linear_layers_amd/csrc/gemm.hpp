@@ -20,7 +20,13 @@
 
 namespace tpmlp {
 
-enum EpiKind { kEpiF32 = 0, kEpiBiasAct = 1, kEpiActBwd = 2 };
+enum EpiKind {
+  kEpiF32 = 0,        // fp32 C
+  kEpiBiasAct = 1,    // Y = Act(acc + bias), H = acc + bias
+  kEpiActBwd = 2,     // Y = acc * Act'(H), per-tile column sums
+  kEpiSwiGLU = 3,     // packed gate/up columns: Y = silu(gate) * up (N/2 columns), H = acc (packed)
+  kEpiSwiGLUBwd = 4,  // acc = dA (N columns): Y = packed [dA * up * silu'(gate) | dA * silu(gate)], H = packed gate/up
+};
 
 struct GemmArgs {
   const void* A; int64_t lda;
@@ -30,8 +36,10 @@ struct GemmArgs {
   int k_per_split;               // multiple of BK; split s covers [s*k_per_split, min(K, ...))
   float* C; int64_t ldc;         // kEpiF32 output; split s writes C + s*split_stride
   int64_t split_stride;
-  void* Y; int64_t ldy;          // typed output: activation (kEpiBiasAct) or dH (kEpiActBwd)
-  void* H; int64_t ldh;          // typed pre-activation: written (kEpiBiasAct, if non-null) / read (kEpiActBwd)
+  void* Y; int64_t ldy;          // typed output: activation (kEpiBiasAct, kEpiSwiGLU) or gradient
+                                 // (kEpiActBwd, kEpiSwiGLUBwd)
+  void* H; int64_t ldh;          // typed pre-activation: written (kEpiBiasAct, kEpiSwiGLU; if non-null)
+                                 // or read (kEpiActBwd, kEpiSwiGLUBwd)
   const void* bias;              // typed [N] or null (kEpiBiasAct)
   float* colsum;                 // kEpiActBwd: fp32 [tiles_m][N] per-tile column sums of dH (or null)
   int act;

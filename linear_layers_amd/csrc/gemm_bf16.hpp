@@ -499,6 +499,111 @@ gemm_bf16_kernel(const GemmArgs p) {
     };
     if (p.act == kActGeluTanh) epilogue(std::true_type{});
     else epilogue(std::false_type{});
+  } else if constexpr (EPI == kEpiSwiGLU) {
+    // Packed column 16q + r holds gate (r < 8) or up (r >= 8) of output
+    // column 8q + r % 8.  In a 32-column block, register groups g = 2p (gate)
+    // and 2p + 1 (up) of a lane hold the same 4 output columns, so
+    // silu(gate) * up needs no data from other lanes; lane-pair swaps then
+    // give every lane 8 consecutive columns for one 16-byte store.
+    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);   // [M, N/2]
+    bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);  // [M, N] packed, or null
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int c0 = n0 + wn * WTN + 32 * j;  // packed column, a multiple of 32
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = mrow + 32 * i;
+        uint32_t aw[2][2], hw[2][2][2];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          float av[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = acc[i][j][8 * pr + e], u = acc[i][j][8 * pr + 4 + e];
+            av[e] = g * sigmoidf_fast(g) * u;
+          }
+          aw[pr][0] = pack_bf16x2(av[0], av[1]);
+          aw[pr][1] = pack_bf16x2(av[2], av[3]);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            hw[pr][q][0] = pack_bf16x2(acc[i][j][8 * pr + 4 * q], acc[i][j][8 * pr + 4 * q + 1]);
+            hw[pr][q][1] = pack_bf16x2(acc[i][j][8 * pr + 4 * q + 2], acc[i][j][8 * pr + 4 * q + 3]);
+          }
+        }
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
+          aw[0][w] = ra[0];
+          aw[1][w] = ra[1];
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const auto rh = __builtin_amdgcn_permlane32_swap(hw[pr][0][w], hw[pr][1][w], false, false);
+            hw[pr][0][w] = rh[0];
+            hw[pr][1][w] = rh[1];
+          }
+        }
+        if (row < M) {
+          // lane h: output columns c0/2 + 8h .. +7 (from block half p = h)
+          if (c0 + 16 * h < N)
+            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + c0 / 2 + 8 * h) =
+                u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
+          if (Hs) {
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+              if (c0 + 16 * pr < N)
+                *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + c0 + 16 * pr + 8 * h) =
+                    u32x4_t{hw[pr][0][0], hw[pr][0][1], hw[pr][1][0], hw[pr][1][1]};
+          }
+        }
+      }
+    }
+  } else if constexpr (EPI == kEpiSwiGLUBwd) {
+    // acc = dA for output columns c (N of them).  Column c = 8q + r reads
+    // gate and up at packed columns 16q + r and 16q + 8 + r of H and writes
+    // dgate = dA * up * silu'(gate) and dup = dA * silu(gate) to the same
+    // packed columns of Y.  A lane holds r = 4h .. 4h+3 of one q per register
+    // group; the lane-pair swap gives lane h = 0 the 8 dgate values and lane
+    // h = 1 the 8 dup values of that q.
+    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);        // [M, 2N] packed
+    const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);  // [M, 2N] packed
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c8 = n0 + wn * WTN + 32 * j + 8 * g;  // output column 8q
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = mrow + 32 * i;
+          float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
+          if (row < M && c8 < N) {
+            const bf16_t* src = Hs + (int64_t)row * p.ldh + 2 * c8 + 4 * h;
+            const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(src);
+            const u32x2_t uw = *reinterpret_cast<const u32x2_t*>(src + 8);
+            const float gv[4] = {bf16lo(gw[0]), bf16hi(gw[0]), bf16lo(gw[1]), bf16hi(gw[1])};
+            const float uv[4] = {bf16lo(uw[0]), bf16hi(uw[0]), bf16lo(uw[1]), bf16hi(uw[1])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float sl, sg;
+              silu_and_grad(gv[e], sl, sg);
+              const float da = acc[i][j][4 * g + e];
+              dg[e] = da * uv[e] * sg;
+              du[e] = da * sl;
+            }
+          }
+          uint32_t x[2] = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          uint32_t y[2] = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane32_swap(x[w], y[w], false, false);
+            x[w] = r[0];
+            y[w] = r[1];
+          }
+          if (row < M && c8 < N)
+            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + 2 * c8 + 8 * h) = u32x4_t{x[0], x[1], y[0], y[1]};
+        }
+      }
   } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
     auto epilogue = [&](auto GeluC) {
       constexpr bool kGelu = decltype(GeluC)::value;

@@ -15,6 +15,7 @@
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "reduce.hpp"
+#include "swiglu.hpp"
 
 using namespace tpmlp;
 
@@ -307,9 +308,13 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     }
     return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, group);
   }
-  switch (cfg) {
-    case 0: return run_gemm_cfg<float, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
-    default: return run_gemm_cfg<float, 64, 64, 2, 2, AK, BKM, EPI>(role, a, s);
+  if constexpr (EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd) {
+    return fail(TPMLP_E_DTYPE, "%s: the gated MLP epilogues are bf16 only", role);
+  } else {
+    switch (cfg) {
+      case 0: return run_gemm_cfg<float, 128, 128, 2, 2, AK, BKM, EPI>(role, a, s);
+      default: return run_gemm_cfg<float, 64, 64, 2, 2, AK, BKM, EPI>(role, a, s);
+    }
   }
 }
 
@@ -649,6 +654,150 @@ int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, i
   a.C = dW_shard;
   a.ldc = lddw;
   return run_gemm<false, false, kEpiF32>("gemm.row_wgrad", dtype, a, s);
+}
+
+// ------------------------------------------------- gated MLP (SwiGLU) --
+int swiglu_pack_shard(void* stream, int dtype, int64_t h, int64_t F, int tp_size, int shard, const void* W_gate,
+                      int64_t ldg, const void* W_up, int64_t ldu, void* W_gu_shard) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  if (Fs % 8 != 0) return fail(TPMLP_E_DIVISIBILITY, "F/tp_size = %lld is not a multiple of 8", (long long)Fs);
+  if (shard < 0 || shard >= tp_size) return fail(TPMLP_E_SHAPE, "shard %d outside [0, %d)", shard, tp_size);
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("W_gate", W_gate, h, F, ldg, v));
+  TPMLP_TRY(check_mat("W_up", W_up, h, F, ldu, v));
+  TPMLP_TRY(check_mat("W_gu_shard", W_gu_shard, h, 2 * Fs, 2 * Fs, v));
+  if (h == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t total = h * (Fs / 4);
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  const int64_t c0 = (int64_t)shard * Fs;
+  if (dtype == TPMLP_BF16)
+    return launch("swiglu_pack", "swiglu_pack_kernel<bf16>", swiglu_pack_kernel<bf16_t>, dim3(grid), dim3(256), s,
+                  static_cast<const bf16_t*>(W_gate), ldg, static_cast<const bf16_t*>(W_up), ldu, c0, (int)h,
+                  (int)Fs, static_cast<bf16_t*>(W_gu_shard));
+  return launch("swiglu_pack", "swiglu_pack_kernel<f32>", swiglu_pack_kernel<float>, dim3(grid), dim3(256), s,
+                static_cast<const float*>(W_gate), ldg, static_cast<const float*>(W_up), ldu, c0, (int)h, (int)Fs,
+                static_cast<float*>(W_gu_shard));
+}
+
+int swiglu_unpack_grad(void* stream, int64_t h, int64_t F, int tp_size, int shard, const float* dW_gu_shard,
+                       float* dW_gate, int64_t ldg, float* dW_up, int64_t ldu) {
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  if (Fs % 8 != 0) return fail(TPMLP_E_DIVISIBILITY, "F/tp_size = %lld is not a multiple of 8", (long long)Fs);
+  if (shard < 0 || shard >= tp_size) return fail(TPMLP_E_SHAPE, "shard %d outside [0, %d)", shard, tp_size);
+  TPMLP_TRY(check_mat("dW_gu_shard", dW_gu_shard, h, 2 * Fs, 2 * Fs, 4));
+  TPMLP_TRY(check_mat("dW_gate", dW_gate, h, F, ldg, 4));
+  TPMLP_TRY(check_mat("dW_up", dW_up, h, F, ldu, 4));
+  if (h == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t total = h * (Fs / 4);
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  return launch("swiglu_unpack", "swiglu_unpack_kernel", swiglu_unpack_kernel, dim3(grid), dim3(256), s,
+                dW_gu_shard, (int)h, (int)Fs, (int64_t)shard * Fs, dW_gate, ldg, dW_up, ldu);
+}
+
+int tp_swiglu_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
+                  const void* W_gu_shard, const void* W_down_shard, void* GU_save, void* A_save, float* Z_partial) {
+  TPMLP_TRY(check_dtype(dtype));
+  if (dtype != TPMLP_BF16) return fail(TPMLP_E_DTYPE, "the gated MLP is bf16 only");
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  if (Fs % 8 != 0) return fail(TPMLP_E_DIVISIBILITY, "F/tp_size = %lld is not a multiple of 8", (long long)Fs);
+  TPMLP_TRY(check_mat("X", X, T, h, h, 8));
+  TPMLP_TRY(check_mat("W_gu_shard", W_gu_shard, h, 2 * Fs, 2 * Fs, 8));
+  TPMLP_TRY(check_mat("W_down_shard", W_down_shard, Fs, h, h, 8));
+  TPMLP_TRY(check_mat("GU_save", GU_save, T, 2 * Fs, 2 * Fs, 8, false));
+  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, 8));
+  TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
+  if (T == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  // [gate | up] = X W_gu (packed), A = silu(gate) * up
+  GemmArgs a = gemm_args(X, h, W_gu_shard, 2 * Fs, T, 2 * Fs, h);
+  a.Y = A_save;
+  a.ldy = Fs;
+  a.H = GU_save;
+  a.ldh = 2 * Fs;
+  TPMLP_TRY((run_gemm<true, false, kEpiSwiGLU>("gemm.swiglu_fwd1", dtype, a, s)));
+  // Z_i = A W_down_i
+  a = gemm_args(A_save, Fs, W_down_shard, h, T, h, Fs);
+  a.C = Z_partial;
+  a.ldc = h;
+  return run_gemm<true, false, kEpiF32>("gemm.swiglu_fwd2", dtype, a, s);
+}
+
+size_t tp_swiglu_bwd_workspace_bytes(int dtype, int64_t T, int64_t h, int64_t F, int tp_size) {
+  if (dtype != TPMLP_BF16 || tp_size < 1 || T < 0 || T > kMaxDim || h < 1 || F < 1 || F % tp_size != 0 ||
+      (F / tp_size) % 8 != 0)
+    return 0;
+  return align256((size_t)T * 2 * (F / tp_size) * sizeof(bf16_t));
+}
+
+int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
+                  const void* W_gu_shard, const void* W_down_shard, const void* GU_save, const void* A_save,
+                  const void* dZ, float* dX_partial, float* dW_gu_shard, float* dW_down_shard, void* workspace,
+                  size_t workspace_bytes) {
+  TPMLP_TRY(check_dtype(dtype));
+  if (dtype != TPMLP_BF16) return fail(TPMLP_E_DTYPE, "the gated MLP is bf16 only");
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  if (Fs % 8 != 0) return fail(TPMLP_E_DIVISIBILITY, "F/tp_size = %lld is not a multiple of 8", (long long)Fs);
+  TPMLP_TRY(check_mat("X", X, T, h, h, 8));
+  TPMLP_TRY(check_mat("W_gu_shard", W_gu_shard, h, 2 * Fs, 2 * Fs, 8));
+  TPMLP_TRY(check_mat("W_down_shard", W_down_shard, Fs, h, h, 8));
+  TPMLP_TRY(check_mat("GU_save", GU_save, T, 2 * Fs, 2 * Fs, 8));
+  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, 8));
+  TPMLP_TRY(check_mat("dZ", dZ, T, h, h, 8));
+  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
+  TPMLP_TRY(check_mat("dW_gu_shard", dW_gu_shard, h, 2 * Fs, 2 * Fs, 4));
+  TPMLP_TRY(check_mat("dW_down_shard", dW_down_shard, Fs, h, h, 4));
+  const size_t need = align256((size_t)T * 2 * Fs * sizeof(bf16_t));
+  if (T > 0) {
+    if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+    if (workspace_bytes < need) return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    TPMLP_TRY(fill_zero(dW_gu_shard, h, 2 * Fs, 2 * Fs, s));
+    return fill_zero(dW_down_shard, Fs, h, h, s);
+  }
+  void* dGU = workspace;
+  // dA = dZ W_down_i^T; packed [dgate | dup] from dA and the saved gate/up
+  GemmArgs a = gemm_args(dZ, h, W_down_shard, h, T, Fs, h);
+  a.Y = dGU;
+  a.ldy = 2 * Fs;
+  a.H = const_cast<void*>(GU_save);
+  a.ldh = 2 * Fs;
+  TPMLP_TRY((run_gemm<true, true, kEpiSwiGLUBwd>("gemm.swiglu_dgrad_act", dtype, a, s)));
+  // dW_down_i = A^T dZ
+  a = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
+  a.C = dW_down_shard;
+  a.ldc = h;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.swiglu_wgrad2", dtype, a, s)));
+  // dW_gu = X^T dGU (packed)
+  a = gemm_args(X, h, dGU, 2 * Fs, h, 2 * Fs, T);
+  a.C = dW_gu_shard;
+  a.ldc = 2 * Fs;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.swiglu_wgrad1", dtype, a, s)));
+  // dX_i = dGU W_gu^T
+  a = gemm_args(dGU, 2 * Fs, W_gu_shard, 2 * Fs, T, h, 2 * Fs);
+  a.C = dX_partial;
+  a.ldc = h;
+  return run_gemm<true, true, kEpiF32>("gemm.swiglu_dgrad1", dtype, a, s);
 }
 
 int tpmlp_profile_enable(const char* filter) {

@@ -165,3 +165,45 @@ def unpack_grad_shard(dW_gu: np.ndarray, F: int, tp: int, i: int):
     out_g[:, i * Fs:(i + 1) * Fs] = dg
     out_u[:, i * Fs:(i + 1) * Fs] = du
     return out_g, out_u
+
+
+# --------------------------------------------------------------------------
+# Sampled views for sizes where the whole shard is too large for the CPU.
+# Rows of the forward and of dX depend only on the same rows of X (and dZ);
+# a column of a weight gradient needs that column over every row.  These
+# take the shard's packed weight W_gu and its W_down block directly.
+# --------------------------------------------------------------------------
+def shard_fwd_rows(X, W_gu, Wd_i, rows) -> Dict[str, np.ndarray]:
+    Xr = np.asarray(X, dtype=np.float64)[np.asarray(rows)]
+    GU = matmul(Xr, W_gu)
+    G, U = deinterleave(GU)
+    A = silu(G) * U
+    return {"GU": GU, "A": A, "Z": matmul(A, Wd_i)}
+
+
+def shard_bwd_rows(X, W_gu, Wd_i, dZ, rows) -> Dict[str, np.ndarray]:
+    """dGU and dX of the given rows."""
+    rows = np.asarray(rows)
+    Xr = np.asarray(X, dtype=np.float64)[rows]
+    G, U = deinterleave(matmul(Xr, W_gu))
+    dA = matmul(np.asarray(dZ, dtype=np.float64)[rows], np.asarray(Wd_i, dtype=np.float64).T)
+    dGU = interleave(dA * U * silu_grad(G), dA * silu(G))
+    return {"dGU": dGU, "dX": matmul(dGU, np.asarray(W_gu, dtype=np.float64).T)}
+
+
+def shard_bwd_cols(X, W_gu, Wd_i, dZ, cols) -> Dict[str, np.ndarray]:
+    """For shard columns c (of the F/tp): dW_gu's packed gate and up columns
+    16(c//8) + c%8 and 16(c//8) + 8 + c%8, and rows c of dW_down."""
+    cols = np.asarray(cols)
+    X = np.asarray(X, dtype=np.float64)
+    W_gu = np.asarray(W_gu, dtype=np.float64)
+    gcol = 16 * (cols // GROUP) + cols % GROUP
+    ucol = gcol + GROUP
+    G = matmul(X, W_gu[:, gcol])
+    U = matmul(X, W_gu[:, ucol])
+    A = silu(G) * U
+    dZ = np.asarray(dZ, dtype=np.float64)
+    dA = matmul(dZ, np.asarray(Wd_i, dtype=np.float64)[cols].T)
+    return {"gate_cols": gcol, "up_cols": ucol,
+            "dW_gate_cols": matmul(X.T, dA * U * silu_grad(G)), "dW_up_cols": matmul(X.T, dA * silu(G)),
+            "dW_down_rows": matmul(A.T, dZ)}

@@ -30,6 +30,7 @@ __all__ = [
     "draw",
     "mlp_inputs",
     "proj_inputs",
+    "swiglu_inputs",
 ]
 
 
@@ -48,7 +49,7 @@ class Workload:
     w_std: float = 0.02
     b_std: Optional[float] = None   # None: no bias; 0.0: a zero bias buffer
     dz_std: Optional[float] = None  # None: forward only
-    kind: str = "mlp"           # "mlp" or "proj" (head-sharded QKV / O projections)
+    kind: str = "mlp"           # "mlp", "proj" (head-sharded QKV / O projections) or "swiglu" (gated MLP)
     heads: int = 0
     head_dim: int = 0
 
@@ -70,6 +71,10 @@ WORKLOADS: Dict[str, Workload] = {
                                kind="proj", heads=40, head_dim=128),
     "gpt3_bf16": Workload("gpt3_bf16", 5, "bf16", T=2048, h=12288, F=49152, tp=8,
                           x_std=1.0, w_std=0.02, b_std=None, dz_std=1.0),
+    # The gated MLP of the pages' Qwen3 example at Qwen3-8B's sizes (hidden
+    # 4096, gate/up width 12288), 8 shards of F/tp = 1536 columns each.
+    "qwen3_swiglu_bf16": Workload("qwen3_swiglu_bf16", 6, "bf16", T=8192, h=4096, F=12288, tp=8,
+                                  x_std=1.0, w_std=0.02, b_std=None, dz_std=1.0, kind="swiglu"),
 }
 
 
@@ -118,7 +123,8 @@ def draw(seed: int, index: int, shape: Tuple[int, ...], std: float, dtype: str,
 
 # Tensor indices inside a workload's stream family.
 _IDX = {"X": 0, "W1": 1, "b1": 2, "W2": 3, "dZ": 4,
-        "Wq": 10, "Wk": 11, "Wv": 12, "O_in": 13, "Wo": 14, "dQKV": 15, "dOut": 16}
+        "Wq": 10, "Wk": 11, "Wv": 12, "O_in": 13, "Wo": 14, "dQKV": 15, "dOut": 16,
+        "W_gate": 20, "W_up": 21, "W_down": 22}
 
 
 def mlp_inputs(wl: Workload, which=("X", "W1", "b1", "W2", "dZ"), T: Optional[int] = None,
@@ -164,6 +170,17 @@ def proj_inputs(wl: Workload, which=("X", "Wq", "Wk", "Wv", "O_in", "Wo", "dQKV"
     stds = {"X": wl.x_std, "Wq": wl.w_std, "Wk": wl.w_std, "Wv": wl.w_std, "O_in": wl.x_std,
             "Wo": wl.w_std, "dQKV": wl.dz_std, "dOut": wl.dz_std}
     return {n: draw(wl.seed, _IDX[n], shapes[n], stds[n], wl.dtype) for n in which}
+
+
+def swiglu_inputs(wl: Workload, which=("X", "W_gate", "W_up", "W_down", "dZ"), T: Optional[int] = None,
+                  h: Optional[int] = None, F: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Full (unsharded) gated-MLP inputs: X [T,h], W_gate and W_up [h,F], W_down [F,h], dZ [T,h]."""
+    T = wl.T if T is None else T
+    h = wl.h if h is None else h
+    F = wl.F if F is None else F
+    shapes = {"X": (T, h), "W_gate": (h, F), "W_up": (h, F), "W_down": (F, h), "dZ": (T, h)}
+    stds = {"X": wl.x_std, "W_gate": wl.w_std, "W_up": wl.w_std, "W_down": wl.w_std, "dZ": wl.dz_std}
+    return {n: draw(wl.seed, _IDX[n], shapes[n], stds[n], wl.dtype) for n in which if stds[n] is not None}
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -154,5 +154,27 @@ def pin_finite_differences(sw):
         _close(g[k], fd[k], 1e-7, f"{k} by differences")
 
 
+def pin_sampled_views(sw):
+    """The sampled row and column views agree with the whole shard."""
+    X, Wg, Wu, Wd, dZ = _block(8, 11, 16, 64)
+    tp, i = 2, 1
+    W_gu = sw.pack_shard(Wg, Wu, tp, i)
+    Wd_i = Wd[32:64]
+    f = sw.tp_swiglu_fwd_shard(X, Wg, Wu, Wd, tp, i)
+    b = sw.tp_swiglu_bwd_shard(X, Wg, Wu, Wd, dZ, tp, i)
+    rows = [0, 3, 10]
+    fr = sw.shard_fwd_rows(X, W_gu, Wd_i, rows)
+    for k in ("GU", "A", "Z"):
+        _close(fr[k], f[k][rows], 1e-13, f"rows {k}")
+    br = sw.shard_bwd_rows(X, W_gu, Wd_i, dZ, rows)
+    _close(br["dGU"], b["dGU"][rows], 1e-13, "rows dGU")
+    _close(br["dX"], b["dX"][rows], 1e-13, "rows dX")
+    cols = [0, 7, 8, 19, 31]
+    bc = sw.shard_bwd_cols(X, W_gu, Wd_i, dZ, cols)
+    _close(bc["dW_gate_cols"], b["dW_gu"][:, bc["gate_cols"]], 1e-13, "cols dW_gate")
+    _close(bc["dW_up_cols"], b["dW_gu"][:, bc["up_cols"]], 1e-13, "cols dW_up")
+    _close(bc["dW_down_rows"], b["dW_down"][cols], 1e-13, "cols dW_down")
+
+
 ALL_PINS = [pin_silu_closed_forms, pin_silu_vs_torch, pin_silu_grad_differences, pin_storage_order,
-            pin_brute_force, pin_tp_invariance, pin_autograd, pin_finite_differences]
+            pin_brute_force, pin_tp_invariance, pin_autograd, pin_finite_differences, pin_sampled_views]

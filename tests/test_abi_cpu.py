@@ -93,3 +93,30 @@ def test_bwd_validation_and_workspace_size():
     assert f(*args, P + 16, 1 << 30) == E_ALIGN
     assert tl.lib.column_parallel_bwd(None, 1, 8, 16, 30, 4, P, 16, P, 8, P, 8, P, 16, P, 8, None) == E_DIV
     assert tl.lib.row_parallel_bwd(None, 1, 8, 32, 16, 2, P, 16, P, 16, P, 16, P, 16, P, 8) == E_SHAPE
+
+
+def test_swiglu_validation():
+    fwd = tl.lib.tp_swiglu_fwd
+    # (stream, dtype, T, h, F, tp, X, W_gu, W_down, GU, A, Z); every call here is refused on the host
+    assert fwd(None, 0, 64, 64, 256, 2, P, P, P, None, P, P) == E_DTYPE   # fp32 is not implemented
+    assert fwd(None, 1, 64, 64, 40, 2, P, P, P, None, P, P) == E_DIV     # F/tp = 20, not a multiple of 8
+    assert fwd(None, 1, 64, 64, 256, 3, P, P, P, None, P, P) == E_DIV    # 256 % 3
+    assert fwd(None, 1, 64, 64, 256, 2, None, P, P, None, P, P) == E_NULL
+    assert fwd(None, 1, 64, 64, 256, 2, P, P, P, P + 8, P, P) == E_ALIGN
+    bwd = tl.lib.tp_swiglu_bwd
+    ws = tl.tp_swiglu_bwd_workspace_bytes(1, 64, 64, 256, 2)
+    assert ws >= 64 * 256 * 2 and ws % 256 == 0
+    assert tl.tp_swiglu_bwd_workspace_bytes(0, 64, 64, 256, 2) == 0
+    assert tl.tp_swiglu_bwd_workspace_bytes(1, 64, 64, 40, 2) == 0
+    args = [None, 1, 64, 64, 256, 2, P, P, P, P, P, P, P, P, P]
+    assert bwd(*args, P, 16) == E_WS
+    assert bwd(*args, None, ws) == E_NULL
+    assert bwd(*args, P + 16, ws) == E_ALIGN
+    pack = tl.lib.swiglu_pack_shard
+    assert pack(None, 1, 64, 256, 2, 2, P, 256, P, 256, P) == E_SHAPE    # shard out of range
+    assert pack(None, 1, 64, 256, 2, -1, P, 256, P, 256, P) == E_SHAPE
+    assert pack(None, 1, 64, 40, 2, 0, P, 40, P, 40, P) == E_DIV
+    assert pack(None, 1, 64, 256, 2, 0, P, 128, P, 256, P) == E_SHAPE    # ldg < F
+    unpack = tl.lib.swiglu_unpack_grad
+    assert unpack(None, 64, 256, 2, 0, P, P, 256, P, 250) == E_SHAPE     # ldu < F
+    assert unpack(None, 64, 256, 2, 0, P, P, 258, P, 256) == E_ALIGN
