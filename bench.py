@@ -42,7 +42,11 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 
 PEAK_SCLK_GHZ = 2.4         # the engine clock that peak assumes
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_JSON = os.path.join(PROFILES, "traffic.json")
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_traffic.json")
+
 CALIB_BYTES = 256 << 20     # the plain copy used to scale the HBM byte counters
 
 
@@ -76,37 +80,81 @@ def canon(name: str) -> str:
     return n
 
 
-def gemm_flops(wl):
-    return 2.0 * wl.T * wl.h * wl.Fs
+# GEMMs of one shard's step, in units of 2*T*h*(F/tp) flops: the plain MLP
+# has six equal ones; in the gated MLP the joined gate/up layer is twice as
+# wide, so its forward product, its weight gradient and the input gradient
+# through it count twice.
+ROLE_UNITS = {
+    "mlp": {"gemm.mlp_fwd1": 1, "gemm.mlp_fwd2": 1, "gemm.mlp_dgrad_act": 1, "gemm.mlp_wgrad2": 1,
+            "gemm.mlp_wgrad1": 1, "gemm.mlp_dgrad1": 1},
+    "swiglu": {"gemm.swiglu_fwd1": 2, "gemm.swiglu_fwd2": 1, "gemm.swiglu_dgrad_act": 1, "gemm.swiglu_wgrad2": 1,
+               "gemm.swiglu_wgrad1": 2, "gemm.swiglu_dgrad1": 2},
+}
+
+
+def role_flops(wl, role):
+    return ROLE_UNITS[wl.kind][role] * 2.0 * wl.T * wl.h * wl.Fs
+
+
+def step_flops(wl):
+    return sum(ROLE_UNITS[wl.kind].values()) * 2.0 * wl.T * wl.h * wl.Fs
+
+
+def algorithmic_bytes(wl, role):
+    """The GEMM's operands and outputs, each read or written once."""
+    T, h, Fs = wl.T, wl.h, wl.Fs
+    return {"gemm.mlp_fwd1": T * h * 2 + h * Fs * 2 + 2 * T * Fs * 2,
+            "gemm.mlp_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
+            "gemm.mlp_dgrad_act": T * h * 2 + Fs * h * 2 + T * Fs * 2 + T * Fs * 2,
+            "gemm.mlp_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
+            "gemm.mlp_wgrad1": T * h * 2 + T * Fs * 2 + h * Fs * 4,
+            "gemm.mlp_dgrad1": T * Fs * 2 + h * Fs * 2 + T * h * 4,
+            "gemm.swiglu_fwd1": T * h * 2 + h * 2 * Fs * 2 + T * Fs * 2 + T * 2 * Fs * 2,
+            "gemm.swiglu_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
+            "gemm.swiglu_dgrad_act": T * h * 2 + Fs * h * 2 + T * 2 * Fs * 2 + T * 2 * Fs * 2,
+            "gemm.swiglu_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
+            "gemm.swiglu_wgrad1": T * h * 2 + T * 2 * Fs * 2 + h * 2 * Fs * 4,
+            "gemm.swiglu_dgrad1": T * 2 * Fs * 2 + h * 2 * Fs * 2 + T * h * 4}.get(role)
 
 
 def cpu_baseline(wl, raw, target_s: float):
     """Time the float64 oracle (fwd + bwd of shard 0) on a sample of rows."""
     import synth
     from oracle import ref
+    from oracle import swiglu as sw
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
     Fs = wl.Fs
-    W1 = synth.to_f64(raw["W1"][:, :Fs], wl.dtype)
-    W2 = synth.to_f64(raw["W2"][:Fs], wl.dtype)
-    b1 = synth.to_f64(raw["b1"][:Fs], wl.dtype) if "b1" in raw else None
+    if wl.kind == "swiglu":
+        W_gu = sw.pack_shard(synth.to_f64(raw["W_gate"], wl.dtype), synth.to_f64(raw["W_up"], wl.dtype), wl.tp, 0)
+        Wd = synth.to_f64(raw["W_down"][:Fs], wl.dtype)
+    else:
+        W1 = synth.to_f64(raw["W1"][:, :Fs], wl.dtype)
+        W2 = synth.to_f64(raw["W2"][:Fs], wl.dtype)
+        b1 = synth.to_f64(raw["b1"][:Fs], wl.dtype) if "b1" in raw else None
 
     def run(rows):
         X = synth.to_f64(raw["X"][:rows], wl.dtype)
         dZ = synth.to_f64(raw["dZ"][:rows], wl.dtype)
         t0 = time.perf_counter()
-        H = ref.matmul(X, W1) + (b1[None, :] if b1 is not None else 0.0)
-        A = ref.gelu_tanh(H)
-        Z = ref.matmul(A, W2)
-        dA = ref.matmul(dZ, W2.T)
-        dW2 = ref.matmul(A.T, dZ)
-        dH = dA * ref.gelu_tanh_grad(H)
-        dW1 = ref.matmul(X.T, dH)
-        dX = ref.matmul(dH, W1.T)
-        del Z, dW2, dW1, dX
+        if wl.kind == "swiglu":
+            G, U = sw.deinterleave(ref.matmul(X, W_gu))
+            A = sw.silu(G) * U
+            out = [ref.matmul(A, Wd)]
+            dA = ref.matmul(dZ, Wd.T)
+            dGU = sw.interleave(dA * U * sw.silu_grad(G), dA * sw.silu(G))
+            out += [ref.matmul(A.T, dZ), ref.matmul(X.T, dGU), ref.matmul(dGU, W_gu.T)]
+        else:
+            H = ref.matmul(X, W1) + (b1[None, :] if b1 is not None else 0.0)
+            A = ref.gelu_tanh(H)
+            out = [ref.matmul(A, W2)]
+            dA = ref.matmul(dZ, W2.T)
+            dH = dA * ref.gelu_tanh_grad(H)
+            out += [ref.matmul(A.T, dZ), ref.matmul(X.T, dH), ref.matmul(dH, W1.T)]
+        del out
         return time.perf_counter() - t0
 
     probe = min(wl.T, 256)
@@ -114,7 +162,7 @@ def cpu_baseline(wl, raw, target_s: float):
     rows = int(min(wl.T, max(probe, probe * target_s / max(dt, 1e-3))))
     rows = max(probe, rows - rows % 8)
     dt = run(rows)
-    flops = 6 * 2.0 * rows * wl.h * Fs
+    flops = step_flops(wl) * rows / wl.T
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle, shard 0 fwd+bwd on the first {rows} of {wl.T} token rows "
                       f"(h={wl.h}, F/tp={Fs}); {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
@@ -169,6 +217,71 @@ class Step:
         tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
 
 
+class SwiGLUStep:
+    """The gated MLP's device buffers and step: shard 0 fwd, its share of the
+    partial sum of down, shard 0 bwd, its share of the partial sum of dX."""
+
+    def __init__(self, wl, raw, tl, torch):
+        self.wl, self.tl = wl, tl
+        T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(bf).to(dev)
+
+        self.stream = torch.cuda.current_stream(dev)
+        self.X, self.dZ = up(raw["X"]), up(raw["dZ"])
+        Wg, Wu = up(raw["W_gate"]), up(raw["W_up"])
+        self.Wgus = []
+        for i in range(tp):  # each shard's joined weight as its own rank would hold it
+            w = torch.empty((h, 2 * Fs), dtype=bf, device=dev)
+            tl.swiglu_pack_shard(Wg, Wu, tp, i, w, stream=self.stream)
+            self.Wgus.append(w)
+        del Wg, Wu
+        self.Wds = [up(raw["W_down"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        self.A = torch.empty((T, Fs), dtype=bf, device=dev)
+        self.GU = torch.empty((T, 2 * Fs), dtype=bf, device=dev)
+        self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.dXp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.rows = T // tp
+        self.Zsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dXsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dWgu = torch.empty((h, 2 * Fs), dtype=torch.float32, device=dev)
+        self.dWd = torch.empty((Fs, h), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(tl.tp_swiglu_bwd_workspace_bytes(tl.BF16, T, h, F, tp), dtype=torch.uint8, device=dev)
+        for i in range(1, tp):
+            self.fwd(i)
+            self.bwd(i)
+
+    def fwd(self, i):
+        s = self
+        s.tl.tp_swiglu_fwd(s.X, s.Wgus[i], s.Wds[i], s.wl.tp, s.A, s.Zp[i], GU_save=s.GU, stream=s.stream)
+
+    def bwd(self, i):
+        s = self
+        s.tl.tp_swiglu_bwd(s.X, s.Wgus[i], s.Wds[i], s.GU, s.A, s.dZ, s.wl.tp, s.dXp[i], s.dWgu, s.dWd,
+                           workspace=s.ws, stream=s.stream)
+
+    def __call__(self):
+        s = self
+        s.fwd(0)
+        s.tl.shard_partial_sum(s.Zp[:, :s.rows], s.Zsum, stream=s.stream)
+        s.bwd(0)
+        s.tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
+
+
+def make_step(wl, tl, torch):
+    import synth
+    if wl.kind == "swiglu":
+        raw = synth.swiglu_inputs(wl)
+        return raw, SwiGLUStep(wl, raw, tl, torch)
+    if wl.kind == "mlp" and wl.dtype == "bf16":
+        raw = synth.mlp_inputs(wl)
+        return raw, Step(wl, raw, tl, torch)
+    raise SystemExit(f"workload {wl.name}: the benchmark step covers the bf16 MLP and gated-MLP workloads")
+
+
 def step_roles(tl, step, torch):
     """Kernel roles and symbols of one step, in launch order."""
     tl.profile_enable("")
@@ -179,10 +292,10 @@ def step_roles(tl, step, torch):
     return order
 
 
-def load_traffic(symbol: str, role: str):
+def load_traffic(workload: str, symbol: str, role: str):
     """Calibrated HBM bytes per launch of (role, symbol), if measured on these sources."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_path(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None, "no traffic table"
@@ -194,6 +307,15 @@ def load_traffic(symbol: str, role: str):
     return e["fetch_bytes"] + e["write_bytes"], "FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
 
 
+def workload_text(wl):
+    T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
+    what = {"llama7b_bf16": "the Llama-7B-scale MLP", "gpt2m_bf16": "the GPT-2-medium-scale MLP",
+            "gpt3_bf16": "the GPT-3-175B-scale MLP",
+            "qwen3_swiglu_bf16": "the Qwen3-8B-scale gated MLP (SwiGLU)"}.get(wl.name, "the MLP")
+    return (f"{wl.name}: one shard of {what}, T={T} tokens, h={h}, F={F}, tp={tp} (F/tp={Fs}), bf16 storage, "
+            f"fp32 accumulate; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums")
+
+
 def run_bench(args):
     import torch
     import synth
@@ -203,11 +325,9 @@ def run_bench(args):
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     wl = synth.WORKLOADS[args.workload]
-    assert wl.kind == "mlp" and wl.dtype == "bf16"
     T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
     t_setup = time.perf_counter()
-    raw = synth.mlp_inputs(wl)
-    step = Step(wl, raw, tl, torch)
+    raw, step = make_step(wl, tl, torch)
     stream = step.stream
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -244,35 +364,28 @@ def run_bench(args):
     tl.profile_enable(None)
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    flops_step = 6 * gemm_flops(wl)
+    flops_step = step_flops(wl)
     value = flops_step / (ms_step * 1e-3) / 1e12
 
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
     n_launch, dom_ms, dom_sym, dom_clocks = timed[dom_key]
     per_launch_ms = dom_ms / n_launch
-    achieved = gemm_flops(wl) / (per_launch_ms * 1e-3) / 1e12
+    achieved = role_flops(wl, dominant) / (per_launch_ms * 1e-3) / 1e12
     # The peak assumes the 2.4 GHz peak engine clock; the clock the GEMM
     # actually ran at (sampled in-kernel over workgroup 0's main loop) is
     # reported beside it, with the peak scaled to that clock.
     sclk = sum(dom_clocks) / len(dom_clocks) if dom_clocks else None
-    traffic, traffic_note = load_traffic(dom_sym, dominant)
+    traffic, traffic_note = load_traffic(wl.name, dom_sym, dominant)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "traffic_note": traffic_note,
                 "algorithmic_bytes": None, "kernel": dom_sym, "role": dominant, "launches": n_launch,
-                "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": gemm_flops(wl),
+                "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": role_flops(wl, dominant),
                 "sclk_ghz": round(sclk, 3) if sclk else None,
                 "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ, 1) if sclk else None,
                 "frac_at_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ), 4) if sclk else None}
-    # the dominant GEMM's operands and outputs, once each (algorithmic bytes)
-    alg = {"gemm.mlp_fwd1": T * h * 2 + h * Fs * 2 + 2 * T * Fs * 2,
-           "gemm.mlp_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
-           "gemm.mlp_dgrad_act": T * h * 2 + Fs * h * 2 + T * Fs * 2 + T * Fs * 2,
-           "gemm.mlp_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
-           "gemm.mlp_wgrad1": T * h * 2 + T * Fs * 2 + h * Fs * 4,
-           "gemm.mlp_dgrad1": T * Fs * 2 + h * Fs * 2 + T * h * 4}
-    roofline["algorithmic_bytes"] = alg.get(dominant)
+    roofline["algorithmic_bytes"] = algorithmic_bytes(wl, dominant)
 
     kernels = {}
     for role, (n, ms, sym, clocks) in sorted(by_role.items(), key=lambda kv: -kv[1][1]):
@@ -281,13 +394,14 @@ def run_bench(args):
         if clocks:
             entry["sclk_ghz"] = round(sum(clocks) / len(clocks), 3)
         if role.startswith("gemm"):
-            entry["tflops"] = round(gemm_flops(wl) / (us * 1e-6) / 1e12, 1)
+            entry["tflops"] = round(role_flops(wl, role) / (us * 1e-6) / 1e12, 1)
         elif role == "partial_sum":
             entry["gbs"] = round((tp + 1) * step.rows * h * 4 / (us * 1e-6) / 1e9, 1)
         kernels[role] = entry
 
     out = {
-        "metric": "TFLOP/s and % of bf16 MFMA peak for TP-sharded MLP fwd+bwd",
+        "metric": ("TFLOP/s and % of bf16 MFMA peak for TP-sharded MLP fwd+bwd" if wl.kind == "mlp" else
+                   "TFLOP/s and % of bf16 MFMA peak for TP-sharded gated MLP (SwiGLU) fwd+bwd"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -299,9 +413,7 @@ def run_bench(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded normal inputs and random-init weights of the workload's shapes)",
-        "config": {"workload": f"{wl.name}: one shard of the Llama-7B-scale MLP, T={T} tokens, h={h}, "
-                               f"F={F}, tp={tp} (F/tp={Fs}), bf16 storage, fp32 accumulate; "
-                               f"fwd+bwd plus this GPU's 1/tp share of the Z and dX partial sums",
+        "config": {"workload": workload_text(wl),
                    "global_batch": T, "seq_len": None, "parallelism": f"tp{tp} shard simulated on 1 GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
@@ -328,8 +440,7 @@ def run_profile_pass(args):
     dst.copy_(src)            # the first kernel of the process: the calibration copy
     torch.cuda.synchronize()
     wl = synth.WORKLOADS[args.workload]
-    raw = synth.mlp_inputs(wl)
-    step = Step(wl, raw, tl, torch)
+    raw, step = make_step(wl, tl, torch)
     step()                    # warm
     torch.cuda.synchronize()
     order = step_roles(tl, step, torch)   # the last step: its launches in order
@@ -389,7 +500,7 @@ def summarize_profile(d):
         lines.append(f"{role:22s} {e['kernel']:44s} {fb / 1e6:9.1f} {wb / 1e6:9.1f}")
     with open(os.path.join(PROFILES, f"{roles['workload']}_step_hbm_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(TRAFFIC_JSON, "w") as f:
+    with open(traffic_path(roles["workload"]), "w") as f:
         json.dump({"fingerprint": roles["fingerprint"], "workload": roles["workload"], "launches": launches,
                    "calibration": scaled["_calibration"]}, f, indent=1)
     # kernel-trace statistics
