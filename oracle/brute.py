@@ -128,3 +128,18 @@ def swiglu_bwd_by_differences(X, W_gate, W_up, W_down, dZ, step: float = 1e-5):
         return g
 
     return {"dX": grad_matrix(X), "dW_gate": grad_matrix(Wg), "dW_up": grad_matrix(Wu), "dW_down": grad_matrix(Wd)}
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm of one hidden state (io.zouht.com/197, 2.2.2, LayerNorm): mean,
+# biased variance, normalise with eps under the square root, scale and shift.
+# ---------------------------------------------------------------------------
+def layernorm_rows(X, gamma, beta, eps: float = 1e-5):
+    out = []
+    for row in to_lists(X):
+        n = len(row)
+        mu = sum(row) / n
+        var = sum((v - mu) ** 2 for v in row) / n
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([float(gamma[c]) * (v - mu) * inv + float(beta[c]) for c, v in enumerate(row)])
+    return out
