@@ -70,7 +70,8 @@ typedef enum {
   TPMLP_E_DTYPE = 5,
   TPMLP_E_ACT = 6,
   TPMLP_E_WORKSPACE = 7,
-  TPMLP_E_HIP = 8
+  TPMLP_E_HIP = 8,
+  TPMLP_E_VALUE = 9   /* a scalar argument outside its range (dropout probability, eps) */
 } tpmlp_status;
 
 typedef enum { TPMLP_F32 = 0, TPMLP_BF16 = 1 } tpmlp_dtype;
@@ -229,6 +230,60 @@ int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
                   const void* GU_save, const void* A_save, const void* dZ,
                   float* dX_partial, float* dW_gu_shard, float* dW_down_shard,
                   void* workspace, size_t workspace_bytes);
+
+/* ---- Sequence-parallel region (SP) ---------------------------------------
+ * With SP the activations outside the tensor-parallel block — LayerNorm,
+ * Dropout, the residual add — are split along the sequence: each GPU holds
+ * rows [row0, row0 + rows) of the [T, h] residual stream; the block's input
+ * is all-gathered and its output reduce-scattered [zouht 2.2.2 与序列并行结合,
+ * 2.3 代价 (g / g*); sunjinbo SP · 序列并行].  On one GPU the gather is this
+ * GPU's LayerNorm writing its rows of the gathered [T, h] buffer (pass Y =
+ * gathered + row0*ldy) and the scatter is the sum of the shard partials over
+ * its rows, fused below with the dropout and the residual.  Widths h must be
+ * multiples of 8 and at most 16384; activations are bf16, LayerNorm
+ * parameters, statistics and gradients fp32.
+ *
+ * Dropout keeps element (r, c) of the [T, h] tensor (r the global row) iff
+ * word e % 4 (e = r*h + c) of Philox4x32-10 (Salmon et al., SC 2011) at
+ * counter (n mod 2^32, n >> 32, 0, 0), n = e / 4, key (seed mod 2^32,
+ * seed >> 32), is >= floor(p * 2^32); kept values are scaled by 1/(1-p).
+ * The mask depends on the global row only, not on how rows are split.
+ * 0 <= p < 1, else TPMLP_E_VALUE. */
+
+/* Y = gamma * (X - mean) / sqrt(var + eps) + beta per row (biased variance).
+ *   X [rows, h] bf16 (ldx); gamma, beta [h] fp32; Y [rows, h] bf16 (ldy);
+ *   mean, rstd [rows] fp32: the row statistics the backward needs.
+ * eps > 0, else TPMLP_E_VALUE. */
+int layernorm_fwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t ldx, const float* gamma,
+                  const float* beta, float eps, void* Y, int64_t ldy, float* mean, float* rstd);
+
+/* LayerNorm backward for upstream dY [rows, h] fp32 (lddy):
+ *   dX [rows, h] fp32 (lddx) = rstd (g - mean(g) - xhat mean(g xhat)), g = dY gamma,
+ *                              plus dRes [rows, h] bf16 (ldr) if not NULL
+ *                              (the residual path's gradient);
+ *   dgamma, dbeta [h] fp32 or NULL: sums over these rows of dY xhat and dY
+ *   (this GPU's share; the full gradients sum over all GPUs' rows).
+ * X, gamma, mean and rstd as given to / returned by layernorm_fwd. */
+int layernorm_bwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t ldx, const float* gamma,
+                  const float* mean, const float* rstd, const float* dY, int64_t lddy, const void* dRes,
+                  int64_t ldr, float* dX, int64_t lddx, float* dgamma, float* dbeta);
+
+/* out = residual + Dropout(sum over s < tp_size of partials[s]) on this GPU's
+ * rows: the reduce-scatter end of the block (shards added in ascending order
+ * in fp32), then the sequence-split dropout and residual add, rounded once.
+ *   partials   element (s, r, c) at partials[s*shard_stride + r*ldp + c], fp32
+ *              (pass the pointer to this GPU's first row)
+ *   residual   [rows, h] bf16 (ldr); out [rows, h] bf16 (ldo)
+ *   row0       global row of the first row (selects the dropout bits) */
+int sp_partial_sum_dropout_residual(void* stream, int tp_size, int64_t rows, int64_t h, const float* partials,
+                                    int64_t shard_stride, int64_t ldp, const void* residual, int64_t ldr,
+                                    float p, uint64_t seed, int64_t row0, void* out, int64_t ldo);
+
+/* Backward of the dropout for this GPU's rows: dZ = kept ? dOut/(1-p) : 0,
+ * dOut, dZ [rows, h] bf16.  Point dZ at this GPU's rows of the gathered
+ * [T, h] upstream gradient of the tensor-parallel block (the all-gather). */
+int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int64_t ldi, float p, uint64_t seed,
+                   int64_t row0, void* dZ, int64_t ldz);
 
 /* Status name, and the calling thread's message for its last non-OK status. */
 const char* tpmlp_status_string(int status);

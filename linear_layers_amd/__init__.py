@@ -23,7 +23,8 @@ __all__ = [
     "TpmlpError", "lib", "LIB_PATH", "F32", "BF16", "ACT_NONE", "ACT_GELU_TANH",
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
     "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
-    "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "profile_enable",
+    "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
+    "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -34,6 +35,7 @@ ACT_NONE, ACT_GELU_TANH = 0, 1
 _ACTS = {"none": ACT_NONE, "gelu_tanh": ACT_GELU_TANH, ACT_NONE: ACT_NONE, ACT_GELU_TANH: ACT_GELU_TANH}
 
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_f32, _u64 = ctypes.c_float, ctypes.c_uint64
 
 _SIGNATURES = {
     "column_parallel_fwd": [_vp, _int, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64],
@@ -51,6 +53,11 @@ _SIGNATURES = {
     "tp_swiglu_fwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_swiglu_bwd_workspace_bytes": [_int, _i64, _i64, _i64, _int],
     "tp_swiglu_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz],
+    "layernorm_fwd": [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _f32, _vp, _i64, _vp, _vp],
+    "layernorm_bwd": [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp],
+    "sp_partial_sum_dropout_residual": [_vp, _int, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp,
+                                        _i64],
+    "sp_dropout_bwd": [_vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp, _i64],
     "tpmlp_status_string": [_int],
     "tpmlp_last_error": [],
     "tpmlp_version": [],
@@ -280,6 +287,41 @@ def tp_swiglu_bwd(X, W_gu_shard, W_down_shard, GU_save, A_save, dZ, tp_size: int
     _check(_get_lib().tp_swiglu_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W_gu_shard),
                                     _ptr(W_down_shard), _ptr(GU_save), _ptr(A_save), _ptr(dZ), _ptr(dX_partial),
                                     _ptr(dW_gu_shard), _ptr(dW_down_shard), _ptr(workspace), workspace.numel()))
+
+
+def layernorm_fwd(X, gamma, beta, Y, mean, rstd, eps: float = 1e-5, stream=None) -> None:
+    """Y = LayerNorm(X) per row (bf16 in/out, fp32 gamma/beta/statistics).  Y may be a row block of a larger buffer."""
+    rows, h = X.shape
+    _check(_get_lib().layernorm_fwd(_stream(stream, X), rows, h, _ptr(X), _ld(X, h), _ptr(gamma), _ptr(beta), eps,
+                                    _ptr(Y), _ld(Y, h), _ptr(mean), _ptr(rstd)))
+
+
+def layernorm_bwd(X, gamma, mean, rstd, dY, dX, dgamma=None, dbeta=None, dRes=None, stream=None) -> None:
+    """dX (fp32) from dY (fp32), plus dRes (bf16) if given; dgamma/dbeta = this block's sums (fp32)."""
+    rows, h = X.shape
+    _check(_get_lib().layernorm_bwd(_stream(stream, X), rows, h, _ptr(X), _ld(X, h), _ptr(gamma), _ptr(mean),
+                                    _ptr(rstd), _ptr(dY), _ld(dY, h), _ptr(dRes), _ld(dRes, h), _ptr(dX), _ld(dX, h),
+                                    _ptr(dgamma), _ptr(dbeta)))
+
+
+def sp_partial_sum_dropout_residual(partials, residual, out, p: float, seed: int, row0: int,
+                                    tp_size: Optional[int] = None, stream=None) -> None:
+    """out = residual + Dropout(sum of partials[s]) over this GPU's rows (partials: [tp, rows, h] view, fp32)."""
+    tp = partials.shape[0] if tp_size is None else tp_size
+    rows, h = partials.shape[1], partials.shape[2]
+    if partials.dim() != 3 or (rows > 1 and h > 1 and partials.stride(2) != 1):
+        raise ValueError("partials must be [tp, rows, h] with contiguous rows")
+    _check(_get_lib().sp_partial_sum_dropout_residual(_stream(stream, out), tp, rows, h, _ptr(partials),
+                                                      partials.stride(0), partials.stride(1) if rows > 1 else h,
+                                                      _ptr(residual), _ld(residual, h), p, seed, row0, _ptr(out),
+                                                      _ld(out, h)))
+
+
+def sp_dropout_bwd(dOut, dZ, p: float, seed: int, row0: int, stream=None) -> None:
+    """dZ = Dropout'(dOut) for this GPU's rows (bf16); dZ may be a row block of the gathered gradient."""
+    rows, h = dOut.shape
+    _check(_get_lib().sp_dropout_bwd(_stream(stream, dOut), rows, h, _ptr(dOut), _ld(dOut, h), p, seed, row0,
+                                     _ptr(dZ), _ld(dZ, h)))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -15,6 +16,7 @@
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "reduce.hpp"
+#include "sp.hpp"
 #include "swiglu.hpp"
 
 using namespace tpmlp;
@@ -413,6 +415,7 @@ const char* tpmlp_status_string(int status) {
     case TPMLP_E_ACT: return "TPMLP_E_ACT";
     case TPMLP_E_WORKSPACE: return "TPMLP_E_WORKSPACE";
     case TPMLP_E_HIP: return "TPMLP_E_HIP";
+    case TPMLP_E_VALUE: return "TPMLP_E_VALUE";
     default: return "TPMLP_E_UNKNOWN";
   }
 }
@@ -798,6 +801,111 @@ int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
   a.C = dX_partial;
   a.ldc = h;
   return run_gemm<true, true, kEpiF32>("gemm.swiglu_dgrad1", dtype, a, s);
+}
+
+// ------------------------------------------------ sequence-parallel region --
+namespace {
+constexpr int64_t kLnMaxWidth = 256 * 8 * kLnMaxChunks;
+
+int check_sp_width(int64_t h) {
+  TPMLP_TRY(check_dim("h", h));
+  if (h % 8 != 0) return fail(TPMLP_E_ALIGNMENT, "h = %lld is not a multiple of 8", (long long)h);
+  return TPMLP_OK;
+}
+
+int dropout_params(float p, uint32_t* thr, float* scale) {
+  if (!(p >= 0.0f && p < 1.0f)) return fail(TPMLP_E_VALUE, "dropout probability %g outside [0, 1)", (double)p);
+  *thr = (uint32_t)std::floor((double)p * 4294967296.0);
+  *scale = (float)(1.0 / (1.0 - (double)p));
+  return TPMLP_OK;
+}
+
+unsigned grid_for(int64_t items) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, 16384)); }
+}  // namespace
+
+int layernorm_fwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t ldx, const float* gamma,
+                  const float* beta, float eps, void* Y, int64_t ldy, float* mean, float* rstd) {
+  TPMLP_TRY(check_rows("rows", rows));
+  TPMLP_TRY(check_sp_width(h));
+  if (h > kLnMaxWidth) return fail(TPMLP_E_SHAPE, "h = %lld above %lld", (long long)h, (long long)kLnMaxWidth);
+  if (!(eps > 0.0f)) return fail(TPMLP_E_VALUE, "eps = %g must be positive", (double)eps);
+  TPMLP_TRY(check_mat("X", X, rows, h, ldx, 8));
+  TPMLP_TRY(check_mat("Y", Y, rows, h, ldy, 8));
+  TPMLP_TRY(check_vec("gamma", gamma, h, true));
+  TPMLP_TRY(check_vec("beta", beta, h, true));
+  TPMLP_TRY(check_vec("mean", mean, rows, true));
+  TPMLP_TRY(check_vec("rstd", rstd, rows, true));
+  if (rows == 0) return TPMLP_OK;
+  return launch("layernorm_fwd", "layernorm_fwd_kernel", layernorm_fwd_kernel, dim3((unsigned)rows), dim3(256),
+                (hipStream_t)stream, static_cast<const bf16_t*>(X), ldx, (int)h, gamma, beta, eps,
+                static_cast<bf16_t*>(Y), ldy, mean, rstd);
+}
+
+int layernorm_bwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t ldx, const float* gamma,
+                  const float* mean, const float* rstd, const float* dY, int64_t lddy, const void* dRes,
+                  int64_t ldr, float* dX, int64_t lddx, float* dgamma, float* dbeta) {
+  TPMLP_TRY(check_rows("rows", rows));
+  TPMLP_TRY(check_sp_width(h));
+  if (h > kLnMaxWidth) return fail(TPMLP_E_SHAPE, "h = %lld above %lld", (long long)h, (long long)kLnMaxWidth);
+  TPMLP_TRY(check_mat("X", X, rows, h, ldx, 8));
+  TPMLP_TRY(check_mat("dY", dY, rows, h, lddy, 4));
+  TPMLP_TRY(check_mat("dRes", dRes, rows, h, ldr, 8, false));
+  TPMLP_TRY(check_mat("dX", dX, rows, h, lddx, 4));
+  TPMLP_TRY(check_vec("gamma", gamma, h, true));
+  TPMLP_TRY(check_vec("mean", mean, rows, true));
+  TPMLP_TRY(check_vec("rstd", rstd, rows, true));
+  TPMLP_TRY(check_vec("dgamma", dgamma, h, false));
+  TPMLP_TRY(check_vec("dbeta", dbeta, h, false));
+  hipStream_t s = (hipStream_t)stream;
+  if (rows == 0) {
+    TPMLP_TRY(fill_zero(dgamma, 1, h, h, s));
+    return fill_zero(dbeta, 1, h, h, s);
+  }
+  TPMLP_TRY(launch("layernorm_bwd", "layernorm_bwd_kernel", layernorm_bwd_kernel, dim3((unsigned)rows), dim3(256),
+                   s, static_cast<const bf16_t*>(X), ldx, (int)h, gamma, mean, rstd, dY, lddy,
+                   static_cast<const bf16_t*>(dRes), ldr, dX, lddx));
+  if (dgamma == nullptr && dbeta == nullptr) return TPMLP_OK;
+  return launch("layernorm_param_grad", "layernorm_param_grad_kernel", layernorm_param_grad_kernel,
+                dim3((unsigned)((h + 15) / 16)), dim3(256), s, static_cast<const bf16_t*>(X), ldx, (int)rows, (int)h,
+                mean, rstd, dY, lddy, dgamma, dbeta);
+}
+
+int sp_partial_sum_dropout_residual(void* stream, int tp_size, int64_t rows, int64_t h, const float* partials,
+                                    int64_t shard_stride, int64_t ldp, const void* residual, int64_t ldr,
+                                    float p, uint64_t seed, int64_t row0, void* out, int64_t ldo) {
+  if (tp_size < 1) return fail(TPMLP_E_DIVISIBILITY, "tp_size %d < 1", tp_size);
+  TPMLP_TRY(check_rows("rows", rows));
+  TPMLP_TRY(check_sp_width(h));
+  if (row0 < 0 || row0 > kMaxDim) return fail(TPMLP_E_SHAPE, "row0 = %lld out of range", (long long)row0);
+  uint32_t thr;
+  float scale;
+  TPMLP_TRY(dropout_params(p, &thr, &scale));
+  TPMLP_TRY(check_mat("partials", partials, rows, h, ldp, 4));
+  if (tp_size > 1 && (shard_stride % 4 != 0 || shard_stride < 0))
+    return fail(TPMLP_E_ALIGNMENT, "shard_stride %lld must be a non-negative multiple of 4", (long long)shard_stride);
+  TPMLP_TRY(check_mat("residual", residual, rows, h, ldr, 8));
+  TPMLP_TRY(check_mat("out", out, rows, h, ldo, 8));
+  if (rows == 0) return TPMLP_OK;
+  return launch("sp_partial_sum_dropout_residual", "sp_sum_dropout_residual_kernel", sp_sum_dropout_residual_kernel,
+                dim3(grid_for(rows * (h / 8))), dim3(256), (hipStream_t)stream, partials, shard_stride, ldp,
+                tp_size, (int)rows, (int)h, static_cast<const bf16_t*>(residual), ldr, thr, scale, seed, row0,
+                static_cast<bf16_t*>(out), ldo);
+}
+
+int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int64_t ldi, float p, uint64_t seed,
+                   int64_t row0, void* dZ, int64_t ldz) {
+  TPMLP_TRY(check_rows("rows", rows));
+  TPMLP_TRY(check_sp_width(h));
+  if (row0 < 0 || row0 > kMaxDim) return fail(TPMLP_E_SHAPE, "row0 = %lld out of range", (long long)row0);
+  uint32_t thr;
+  float scale;
+  TPMLP_TRY(dropout_params(p, &thr, &scale));
+  TPMLP_TRY(check_mat("dOut", dOut, rows, h, ldi, 8));
+  TPMLP_TRY(check_mat("dZ", dZ, rows, h, ldz, 8));
+  if (rows == 0) return TPMLP_OK;
+  return launch("sp_dropout_bwd", "sp_dropout_bwd_kernel", sp_dropout_bwd_kernel, dim3(grid_for(rows * (h / 8))),
+                dim3(256), (hipStream_t)stream, static_cast<const bf16_t*>(dOut), ldi, (int)rows, (int)h, thr, scale,
+                seed, row0, static_cast<bf16_t*>(dZ), ldz);
 }
 
 int tpmlp_profile_enable(const char* filter) {

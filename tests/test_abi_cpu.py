@@ -120,3 +120,30 @@ def test_swiglu_validation():
     unpack = tl.lib.swiglu_unpack_grad
     assert unpack(None, 64, 256, 2, 0, P, P, 256, P, 250) == E_SHAPE     # ldu < F
     assert unpack(None, 64, 256, 2, 0, P, P, 258, P, 256) == E_ALIGN
+
+
+E_VALUE = 9
+
+
+def test_sp_validation():
+    lib = tl.lib
+    assert tl.status_string(E_VALUE) == "TPMLP_E_VALUE"
+    # layernorm_fwd(stream, rows, h, X, ldx, gamma, beta, eps, Y, ldy, mean, rstd): refused on the host
+    assert lib.layernorm_fwd(None, 8, 64, P, 64, P, P, 0.0, P, 64, P, P) == E_VALUE
+    assert lib.layernorm_fwd(None, 8, 60, P, 64, P, P, 1e-5, P, 64, P, P) == E_ALIGN
+    assert lib.layernorm_fwd(None, 8, 16392, P, 16392, P, P, 1e-5, P, 16392, P, P) == E_SHAPE
+    assert lib.layernorm_fwd(None, 8, 64, P, 64, None, P, 1e-5, P, 64, P, P) == E_NULL
+    assert lib.layernorm_fwd(None, 8, 64, P, 32, P, P, 1e-5, P, 64, P, P) == E_SHAPE
+    assert lib.layernorm_bwd(None, 8, 64, P, 64, P, P, P, P, 64, P + 8, 64, P, 64, None, None) == E_ALIGN
+    assert lib.layernorm_bwd(None, 8, 64, P, 64, P, P, P, None, 64, None, 64, P, 64, None, None) == E_NULL
+    s = lib.sp_partial_sum_dropout_residual
+    assert s(None, 2, 8, 64, P, 512, 64, P, 64, 1.0, 1, 0, P, 64) == E_VALUE
+    assert s(None, 2, 8, 64, P, 512, 64, P, 64, -0.1, 1, 0, P, 64) == E_VALUE
+    assert s(None, 2, 8, 64, P, 512, 64, P, 64, float("nan"), 1, 0, P, 64) == E_VALUE
+    assert s(None, 0, 8, 64, P, 512, 64, P, 64, 0.1, 1, 0, P, 64) == E_DIV
+    assert s(None, 2, 8, 64, P, 514, 64, P, 64, 0.1, 1, 0, P, 64) == E_ALIGN
+    assert s(None, 2, 8, 64, P, 512, 64, P, 64, 0.1, 1, -1, P, 64) == E_SHAPE
+    d = lib.sp_dropout_bwd
+    assert d(None, 8, 64, P, 64, 1.5, 1, 0, P, 64) == E_VALUE
+    assert d(None, 8, 64, P, 64, 0.1, 1, 0, None, 64) == E_NULL
+    assert d(None, 8, 64, P, 60, 0.1, 1, 0, P, 64) == E_SHAPE
