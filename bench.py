@@ -85,6 +85,8 @@ def canon(name: str) -> str:
 # wide, so its forward product, its weight gradient and the input gradient
 # through it count twice.
 ROLE_UNITS = {
+    "sp_mlp": {"gemm.mlp_fwd1": 1, "gemm.mlp_fwd2": 1, "gemm.mlp_dgrad_act": 1, "gemm.mlp_wgrad2": 1,
+               "gemm.mlp_wgrad1": 1, "gemm.mlp_dgrad1": 1},
     "mlp": {"gemm.mlp_fwd1": 1, "gemm.mlp_fwd2": 1, "gemm.mlp_dgrad_act": 1, "gemm.mlp_wgrad2": 1,
             "gemm.mlp_wgrad1": 1, "gemm.mlp_dgrad1": 1},
     "swiglu": {"gemm.swiglu_fwd1": 2, "gemm.swiglu_fwd2": 1, "gemm.swiglu_dgrad_act": 1, "gemm.swiglu_wgrad2": 1,
@@ -122,6 +124,7 @@ def cpu_baseline(wl, raw, target_s: float):
     import synth
     from oracle import ref
     from oracle import swiglu as sw
+    from oracle import sp as osp
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
@@ -140,6 +143,9 @@ def cpu_baseline(wl, raw, target_s: float):
         X = synth.to_f64(raw["X"][:rows], wl.dtype)
         dZ = synth.to_f64(raw["dZ"][:rows], wl.dtype)
         t0 = time.perf_counter()
+        if wl.kind == "sp_mlp":
+            ln = osp.layernorm_fwd(X, raw["ln_gamma"], raw["ln_beta"])
+            X = ln["Y"]
         if wl.kind == "swiglu":
             G, U = sw.deinterleave(ref.matmul(X, W_gu))
             A = sw.silu(G) * U
@@ -154,6 +160,11 @@ def cpu_baseline(wl, raw, target_s: float):
             dA = ref.matmul(dZ, W2.T)
             dH = dA * ref.gelu_tanh_grad(H)
             out += [ref.matmul(A.T, dZ), ref.matmul(X.T, dH), ref.matmul(dH, W1.T)]
+        if wl.kind == "sp_mlp":
+            Xr = synth.to_f64(raw["X"][:rows], wl.dtype)
+            out.append(osp.partial_sum_dropout_residual([out[0]], Xr, synth.SP_DROPOUT_P, wl.seed, 0))
+            out.append(osp.dropout_bwd(dZ, synth.SP_DROPOUT_P, wl.seed, 0))
+            out.append(osp.layernorm_bwd(Xr, raw["ln_gamma"], out[3])["dX"])
         del out
         return time.perf_counter() - t0
 
@@ -271,8 +282,89 @@ class SwiGLUStep:
         s.tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
 
 
+class SPStep:
+    """The MLP inside the sequence-parallel region, rank 0's step: LayerNorm of
+    its T/tp rows into its block of the gathered input (the other ranks' blocks
+    are filled once in set-up), the shard's MLP forward, its reduce-scatter
+    rows fused with dropout and the residual; backward: dropout' of its rows
+    into its block of the gathered gradient, the shard's MLP backward, the
+    reduce-scatter rows of dX, LayerNorm backward plus the residual path."""
+
+    def __init__(self, wl, raw, tl, torch):
+        import synth
+        self.wl, self.tl = wl, tl
+        T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(bf).to(dev)
+
+        self.stream = torch.cuda.current_stream(dev)
+        self.p, self.seed = synth.SP_DROPOUT_P, wl.seed
+        self.rows = T // tp
+        self.X, self.dOut = up(raw["X"]), up(raw["dZ"])
+        self.gamma = torch.from_numpy(raw["ln_gamma"]).to(dev)
+        self.beta = torch.from_numpy(raw["ln_beta"]).to(dev)
+        self.W1s = [up(np.ascontiguousarray(raw["W1"][:, i * Fs:(i + 1) * Fs])) for i in range(tp)]
+        self.W2s = [up(raw["W2"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        self.Y = torch.empty((T, h), dtype=bf, device=dev)          # gathered LayerNorm output
+        self.dZ = torch.empty((T, h), dtype=bf, device=dev)         # gathered upstream gradient
+        self.mean = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.rstd = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.A = torch.empty((T, Fs), dtype=bf, device=dev)
+        self.H = torch.empty((T, Fs), dtype=bf, device=dev)
+        self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.dXp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.out = torch.empty((self.rows, h), dtype=bf, device=dev)
+        self.dYln = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dXseq = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dgamma = torch.empty((h,), dtype=torch.float32, device=dev)
+        self.dbeta = torch.empty((h,), dtype=torch.float32, device=dev)
+        self.dW1 = torch.empty((h, Fs), dtype=torch.float32, device=dev)
+        self.dW2 = torch.empty((Fs, h), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(tl.tpmlp_bwd_workspace_bytes(tl.BF16, T, h, F, tp), dtype=torch.uint8, device=dev)
+        for i in range(1, tp):  # the other ranks' gathered blocks
+            self.ln(i)
+            self.drop_bwd(i)
+        for j in range(1, tp):  # and the other shards' partials
+            self.mlp(j)
+
+    def blk(self, i):
+        return slice(i * self.rows, (i + 1) * self.rows)
+
+    def ln(self, i):
+        s, b = self, self.blk(i)
+        s.tl.layernorm_fwd(s.X[b], s.gamma, s.beta, s.Y[b], s.mean[b], s.rstd[b], stream=s.stream)
+
+    def drop_bwd(self, i):
+        s, b = self, self.blk(i)
+        s.tl.sp_dropout_bwd(s.dOut[b], s.dZ[b], s.p, s.seed, i * s.rows, stream=s.stream)
+
+    def mlp(self, j):
+        s, tl = self, self.tl
+        tl.tp_mlp_fwd(s.Y, s.W1s[j], None, s.W2s[j], s.wl.tp, s.A, s.Zp[j], H_save=s.H, stream=s.stream)
+        tl.tp_mlp_bwd(s.Y, s.W1s[j], s.W2s[j], s.H, s.A, s.dZ, s.wl.tp, s.dXp[j], s.dW1, s.dW2, workspace=s.ws,
+                      stream=s.stream)
+
+    def __call__(self):
+        s, tl, b = self, self.tl, self.blk(0)
+        s.ln(0)
+        tl.tp_mlp_fwd(s.Y, s.W1s[0], None, s.W2s[0], s.wl.tp, s.A, s.Zp[0], H_save=s.H, stream=s.stream)
+        tl.sp_partial_sum_dropout_residual(s.Zp[:, b], s.X[b], s.out, s.p, s.seed, 0, stream=s.stream)
+        s.drop_bwd(0)
+        tl.tp_mlp_bwd(s.Y, s.W1s[0], s.W2s[0], s.H, s.A, s.dZ, s.wl.tp, s.dXp[0], s.dW1, s.dW2, workspace=s.ws,
+                      stream=s.stream)
+        tl.shard_partial_sum(s.dXp[:, b], s.dYln, stream=s.stream)
+        tl.layernorm_bwd(s.X[b], s.gamma, s.mean[b], s.rstd[b], s.dYln, s.dXseq, dgamma=s.dgamma, dbeta=s.dbeta,
+                         dRes=s.dOut[b], stream=s.stream)
+
+
 def make_step(wl, tl, torch):
     import synth
+    if wl.kind == "sp_mlp":
+        raw = synth.sp_inputs(wl)
+        return raw, SPStep(wl, raw, tl, torch)
     if wl.kind == "swiglu":
         raw = synth.swiglu_inputs(wl)
         return raw, SwiGLUStep(wl, raw, tl, torch)
@@ -311,7 +403,10 @@ def workload_text(wl):
     T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
     what = {"llama7b_bf16": "the Llama-7B-scale MLP", "gpt2m_bf16": "the GPT-2-medium-scale MLP",
             "gpt3_bf16": "the GPT-3-175B-scale MLP",
-            "qwen3_swiglu_bf16": "the Qwen3-8B-scale gated MLP (SwiGLU)"}.get(wl.name, "the MLP")
+            "qwen3_swiglu_bf16": "the Qwen3-8B-scale gated MLP (SwiGLU)",
+            "llama7b_sp_bf16": "the Llama-7B-scale MLP inside the sequence-parallel region (LayerNorm before it, "
+                               "dropout p=0.1 and the residual after it, T/tp rows of the residual stream per GPU)",
+            }.get(wl.name, "the MLP")
     return (f"{wl.name}: one shard of {what}, T={T} tokens, h={h}, F={F}, tp={tp} (F/tp={Fs}), bf16 storage, "
             f"fp32 accumulate; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums")
 
@@ -400,8 +495,9 @@ def run_bench(args):
         kernels[role] = entry
 
     out = {
-        "metric": ("TFLOP/s and % of bf16 MFMA peak for TP-sharded MLP fwd+bwd" if wl.kind == "mlp" else
-                   "TFLOP/s and % of bf16 MFMA peak for TP-sharded gated MLP (SwiGLU) fwd+bwd"),
+        "metric": {"mlp": "TFLOP/s and % of bf16 MFMA peak for TP-sharded MLP fwd+bwd",
+                   "swiglu": "TFLOP/s and % of bf16 MFMA peak for TP-sharded gated MLP (SwiGLU) fwd+bwd",
+                   "sp_mlp": "TFLOP/s and % of bf16 MFMA peak for the TP+SP MLP block fwd+bwd"}[wl.kind],
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -88,21 +88,27 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 constexpr int kLnMaxChunks = 8;  // 8-element chunks per thread: rows up to 256 * 8 * 8 = 16384 wide
 
 // ------------------------------------------------------------- LayerNorm --
-// One workgroup of 256 threads per row; the row stays in registers: mean,
-// then the biased variance around it, then Y = gamma * (x - mean) * rstd + beta.
-__global__ void __launch_bounds__(256) layernorm_fwd_kernel(const bf16_t* __restrict__ X, int64_t ldx, int h,
+// One workgroup of 256 threads per row (measured faster than one wave per
+// row, which leaves too few waves per CU to hide the load latency).  The row
+// stays in registers: mean, then the biased variance around it, then
+// Y = gamma * (x - mean) * rstd + beta.
+constexpr int kLnThreads = 256;  // threads per row
+
+__global__ void __launch_bounds__(256) layernorm_fwd_kernel(const bf16_t* __restrict__ X, int64_t ldx, int rows, int h,
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ beta, float eps,
                                                             bf16_t* __restrict__ Y, int64_t ldy,
                                                             float* __restrict__ mean, float* __restrict__ rstd) {
   __shared__ float red[4];
+  const int tr = threadIdx.x;
   const int64_t r = blockIdx.x;
+  (void)rows;
   const int chunks = h >> 3;
   float x[kLnMaxChunks][8];
   float s = 0.0f;
 #pragma unroll
   for (int k = 0; k < kLnMaxChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+    const int c = tr + kLnThreads * k;
     if (c < chunks) {
       unpack8(*reinterpret_cast<const u32x4_t*>(X + r * ldx + 8 * c), x[k]);
 #pragma unroll
@@ -113,7 +119,7 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(const bf16_t* __rest
   float q = 0.0f;
 #pragma unroll
   for (int k = 0; k < kLnMaxChunks; ++k) {
-    if (threadIdx.x + 256 * k < chunks) {
+    if (tr + kLnThreads * k < chunks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float d = x[k][e] - mu;
@@ -125,7 +131,7 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(const bf16_t* __rest
   const float rs = rsqrtf(var + eps);
 #pragma unroll
   for (int k = 0; k < kLnMaxChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+    const int c = tr + kLnThreads * k;
     if (c < chunks) {
       const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gamma + 8 * c);
       const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gamma + 8 * c + 4);
@@ -140,15 +146,15 @@ __global__ void __launch_bounds__(256) layernorm_fwd_kernel(const bf16_t* __rest
       *reinterpret_cast<u32x4_t*>(Y + r * ldy + 8 * c) = pack8(y);
     }
   }
-  if (threadIdx.x == 0) {
+  if (tr == 0) {
     mean[r] = mu;
     rstd[r] = rs;
   }
 }
 
 // dX = rstd * (g - mean(g) - xhat * mean(g * xhat)) (+ dRes), g = dY * gamma,
-// xhat = (x - mean) * rstd; one workgroup per row.
-__global__ void __launch_bounds__(256) layernorm_bwd_kernel(const bf16_t* __restrict__ X, int64_t ldx, int h,
+// xhat = (x - mean) * rstd; one workgroup per row as in the forward.
+__global__ void __launch_bounds__(256) layernorm_bwd_kernel(const bf16_t* __restrict__ X, int64_t ldx, int rows, int h,
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ mean,
                                                             const float* __restrict__ rstd,
@@ -156,14 +162,16 @@ __global__ void __launch_bounds__(256) layernorm_bwd_kernel(const bf16_t* __rest
                                                             const bf16_t* __restrict__ dRes, int64_t ldr,
                                                             float* __restrict__ dX, int64_t lddx) {
   __shared__ float red[4];
+  const int tr = threadIdx.x;
   const int64_t r = blockIdx.x;
+  (void)rows;
   const int chunks = h >> 3;
   const float mu = mean[r], rs = rstd[r];
   float xh[kLnMaxChunks][8], g[kLnMaxChunks][8];
   float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
   for (int k = 0; k < kLnMaxChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+    const int c = tr + kLnThreads * k;
     if (c < chunks) {
       unpack8(*reinterpret_cast<const u32x4_t*>(X + r * ldx + 8 * c), xh[k]);
       const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(dY + r * lddy + 8 * c);
@@ -187,7 +195,7 @@ __global__ void __launch_bounds__(256) layernorm_bwd_kernel(const bf16_t* __rest
   const float m2 = block_sum256(s2, red) / (float)h;
 #pragma unroll
   for (int k = 0; k < kLnMaxChunks; ++k) {
-    const int c = threadIdx.x + 256 * k;
+    const int c = tr + kLnThreads * k;
     if (c < chunks) {
       float o[8];
 #pragma unroll
@@ -218,6 +226,7 @@ __global__ void __launch_bounds__(256) layernorm_param_grad_kernel(const bf16_t*
   const int c0 = blockIdx.x * 16 + 4 * cl;
   float sg[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
   if (c0 < h) {
+#pragma unroll 4
     for (int r = rl; r < rows; r += 64) {
       const f32x4_t d = *reinterpret_cast<const f32x4_t*>(dY + (int64_t)r * lddy + c0);
       const u32x2_t xw = *reinterpret_cast<const u32x2_t*>(X + (int64_t)r * ldx + c0);
@@ -261,10 +270,10 @@ __global__ void __launch_bounds__(256) sp_sum_dropout_residual_kernel(
     const float* __restrict__ P, int64_t shard_stride, int64_t ldp, int tp, int rows, int h,
     const bf16_t* __restrict__ res, int64_t ldr, uint32_t thr, float scale, uint64_t seed, int64_t row0,
     bf16_t* __restrict__ out, int64_t ldo) {
-  const int cpr = h >> 3;
-  const int64_t total = (int64_t)rows * cpr;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
-    const int r = (int)(t / cpr), c = 8 * (int)(t % cpr);
+  const uint32_t cpr = (uint32_t)h >> 3;
+  const uint32_t total = (uint32_t)rows * cpr;  // < 2^31, checked on the host
+  for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < total; t += gridDim.x * 256) {
+    const uint32_t r = t / cpr, c = 8 * (t - r * cpr);
     float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float* base = P + (int64_t)r * ldp + c;
     for (int s0 = 0; s0 < tp; s0 += 8) {
@@ -303,10 +312,10 @@ __global__ void __launch_bounds__(256) sp_sum_dropout_residual_kernel(
 __global__ void __launch_bounds__(256) sp_dropout_bwd_kernel(const bf16_t* __restrict__ dOut, int64_t ldi, int rows,
                                                              int h, uint32_t thr, float scale, uint64_t seed,
                                                              int64_t row0, bf16_t* __restrict__ dZ, int64_t ldz) {
-  const int cpr = h >> 3;
-  const int64_t total = (int64_t)rows * cpr;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
-    const int r = (int)(t / cpr), c = 8 * (int)(t % cpr);
+  const uint32_t cpr = (uint32_t)h >> 3;
+  const uint32_t total = (uint32_t)rows * cpr;  // < 2^31, checked on the host
+  for (uint32_t t = blockIdx.x * 256 + threadIdx.x; t < total; t += gridDim.x * 256) {
+    const uint32_t r = t / cpr, c = 8 * (t - r * cpr);
     const uint32_t keep = keep8((uint64_t)(row0 + r) * (uint64_t)h + (uint64_t)c, seed, thr);
     float d[8];
     unpack8(*reinterpret_cast<const u32x4_t*>(dOut + (int64_t)r * ldi + c), d);

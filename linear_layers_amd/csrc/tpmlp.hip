@@ -805,7 +805,7 @@ int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
 
 // ------------------------------------------------ sequence-parallel region --
 namespace {
-constexpr int64_t kLnMaxWidth = 256 * 8 * kLnMaxChunks;
+constexpr int64_t kLnMaxWidth = 256 * 8 * kLnMaxChunks;  // one workgroup per row, held in registers
 
 int check_sp_width(int64_t h) {
   TPMLP_TRY(check_dim("h", h));
@@ -836,9 +836,9 @@ int layernorm_fwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t 
   TPMLP_TRY(check_vec("mean", mean, rows, true));
   TPMLP_TRY(check_vec("rstd", rstd, rows, true));
   if (rows == 0) return TPMLP_OK;
-  return launch("layernorm_fwd", "layernorm_fwd_kernel", layernorm_fwd_kernel, dim3((unsigned)rows), dim3(256),
-                (hipStream_t)stream, static_cast<const bf16_t*>(X), ldx, (int)h, gamma, beta, eps,
-                static_cast<bf16_t*>(Y), ldy, mean, rstd);
+  return launch("layernorm_fwd", "layernorm_fwd_kernel", layernorm_fwd_kernel, dim3((unsigned)rows),
+                dim3(256), (hipStream_t)stream, static_cast<const bf16_t*>(X), ldx, (int)rows, (int)h, gamma, beta,
+                eps, static_cast<bf16_t*>(Y), ldy, mean, rstd);
 }
 
 int layernorm_bwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t ldx, const float* gamma,
@@ -861,8 +861,8 @@ int layernorm_bwd(void* stream, int64_t rows, int64_t h, const void* X, int64_t 
     TPMLP_TRY(fill_zero(dgamma, 1, h, h, s));
     return fill_zero(dbeta, 1, h, h, s);
   }
-  TPMLP_TRY(launch("layernorm_bwd", "layernorm_bwd_kernel", layernorm_bwd_kernel, dim3((unsigned)rows), dim3(256),
-                   s, static_cast<const bf16_t*>(X), ldx, (int)h, gamma, mean, rstd, dY, lddy,
+  TPMLP_TRY(launch("layernorm_bwd", "layernorm_bwd_kernel", layernorm_bwd_kernel, dim3((unsigned)rows), dim3(256), s,
+                   static_cast<const bf16_t*>(X), ldx, (int)rows, (int)h, gamma, mean, rstd, dY, lddy,
                    static_cast<const bf16_t*>(dRes), ldr, dX, lddx));
   if (dgamma == nullptr && dbeta == nullptr) return TPMLP_OK;
   return launch("layernorm_param_grad", "layernorm_param_grad_kernel", layernorm_param_grad_kernel,
@@ -885,6 +885,7 @@ int sp_partial_sum_dropout_residual(void* stream, int tp_size, int64_t rows, int
     return fail(TPMLP_E_ALIGNMENT, "shard_stride %lld must be a non-negative multiple of 4", (long long)shard_stride);
   TPMLP_TRY(check_mat("residual", residual, rows, h, ldr, 8));
   TPMLP_TRY(check_mat("out", out, rows, h, ldo, 8));
+  if (rows * (h / 8) > kMaxDim) return fail(TPMLP_E_SHAPE, "rows * h / 8 above 2^31 - 1");
   if (rows == 0) return TPMLP_OK;
   return launch("sp_partial_sum_dropout_residual", "sp_sum_dropout_residual_kernel", sp_sum_dropout_residual_kernel,
                 dim3(grid_for(rows * (h / 8))), dim3(256), (hipStream_t)stream, partials, shard_stride, ldp,
@@ -902,6 +903,7 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
   TPMLP_TRY(dropout_params(p, &thr, &scale));
   TPMLP_TRY(check_mat("dOut", dOut, rows, h, ldi, 8));
   TPMLP_TRY(check_mat("dZ", dZ, rows, h, ldz, 8));
+  if (rows * (h / 8) > kMaxDim) return fail(TPMLP_E_SHAPE, "rows * h / 8 above 2^31 - 1");
   if (rows == 0) return TPMLP_OK;
   return launch("sp_dropout_bwd", "sp_dropout_bwd_kernel", sp_dropout_bwd_kernel, dim3(grid_for(rows * (h / 8))),
                 dim3(256), (hipStream_t)stream, static_cast<const bf16_t*>(dOut), ldi, (int)rows, (int)h, thr, scale,

@@ -31,6 +31,7 @@ __all__ = [
     "mlp_inputs",
     "proj_inputs",
     "swiglu_inputs",
+    "sp_inputs",
 ]
 
 
@@ -49,7 +50,8 @@ class Workload:
     w_std: float = 0.02
     b_std: Optional[float] = None   # None: no bias; 0.0: a zero bias buffer
     dz_std: Optional[float] = None  # None: forward only
-    kind: str = "mlp"           # "mlp", "proj" (head-sharded QKV / O projections) or "swiglu" (gated MLP)
+    kind: str = "mlp"           # "mlp", "proj" (head-sharded QKV / O projections), "swiglu" (gated MLP)
+                                # or "sp_mlp" (the MLP inside the sequence-parallel region)
     heads: int = 0
     head_dim: int = 0
 
@@ -75,7 +77,14 @@ WORKLOADS: Dict[str, Workload] = {
     # 4096, gate/up width 12288), 8 shards of F/tp = 1536 columns each.
     "qwen3_swiglu_bf16": Workload("qwen3_swiglu_bf16", 6, "bf16", T=8192, h=4096, F=12288, tp=8,
                                   x_std=1.0, w_std=0.02, b_std=None, dz_std=1.0, kind="swiglu"),
+    # The Llama-7B-scale MLP inside the sequence-parallel region: LayerNorm
+    # before it, dropout (p = 0.1) and the residual after it, each GPU holding
+    # T/tp rows of the residual stream.
+    "llama7b_sp_bf16": Workload("llama7b_sp_bf16", 7, "bf16", T=8192, h=4096, F=16384, tp=8,
+                                x_std=1.0, w_std=0.02, b_std=None, dz_std=1.0, kind="sp_mlp"),
 }
+
+SP_DROPOUT_P = 0.1
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:
@@ -124,7 +133,7 @@ def draw(seed: int, index: int, shape: Tuple[int, ...], std: float, dtype: str,
 # Tensor indices inside a workload's stream family.
 _IDX = {"X": 0, "W1": 1, "b1": 2, "W2": 3, "dZ": 4,
         "Wq": 10, "Wk": 11, "Wv": 12, "O_in": 13, "Wo": 14, "dQKV": 15, "dOut": 16,
-        "W_gate": 20, "W_up": 21, "W_down": 22}
+        "W_gate": 20, "W_up": 21, "W_down": 22, "ln_gamma": 30, "ln_beta": 31}
 
 
 def mlp_inputs(wl: Workload, which=("X", "W1", "b1", "W2", "dZ"), T: Optional[int] = None,
@@ -181,6 +190,18 @@ def swiglu_inputs(wl: Workload, which=("X", "W_gate", "W_up", "W_down", "dZ"), T
     shapes = {"X": (T, h), "W_gate": (h, F), "W_up": (h, F), "W_down": (F, h), "dZ": (T, h)}
     stds = {"X": wl.x_std, "W_gate": wl.w_std, "W_up": wl.w_std, "W_down": wl.w_std, "dZ": wl.dz_std}
     return {n: draw(wl.seed, _IDX[n], shapes[n], stds[n], wl.dtype) for n in which if stds[n] is not None}
+
+
+def sp_inputs(wl: Workload, T: Optional[int] = None, h: Optional[int] = None,
+              F: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """MLP inputs plus the LayerNorm parameters: gamma = 1 + N(0, 0.1^2),
+    beta = N(0, 0.1^2), both float32 [h].  X is the residual stream; dZ is the
+    upstream gradient of the block output."""
+    out = mlp_inputs(wl, T=T, h=h, F=F)
+    h = wl.h if h is None else h
+    out["ln_gamma"] = np.float32(1.0) + draw(wl.seed, _IDX["ln_gamma"], (h,), 0.1, "f32")
+    out["ln_beta"] = draw(wl.seed, _IDX["ln_beta"], (h,), 0.1, "f32")
+    return out
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
