@@ -1,0 +1,106 @@
+"""float64 CPU oracle of the attention core between the head-sharded projections.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark, never by the GPU library.
+
+Pages cited:
+  [csdn]     damodev.csdn.net/6a43867610ee7a33f284fb9e.html, 1.2.2 Self-Attention
+             模块的张量并行: every head is computed on its own from its own Q, K, V
+             projections, so heads can be placed on different GPUs; the head
+             outputs are concatenated before the output projection.
+  [zouht]    io.zouht.com/197.html, 2.2.1 多头注意力机制: Q/K/V split by columns,
+             each GPU owns a group of heads (32 heads on 4 GPUs: 8 each).
+  [wangyu]   wangyu.me/posts/llm/tensor-parallelism/, 注意力机制中的张量并行:
+             Q, K, V from X, the per-head output O_i, then O W_O.
+  [sunjinbo] sunjinbo.space/document/parallelism.html, CP · 上下文并行: the
+             attention of a query block is softmax(Q K^T) V over all key
+             blocks, accumulated block by block with an online softmax.
+
+Readings where the pages leave a step open (their formulas were lost):
+  * O = softmax(Q K^T * scale) V per head and per sequence, scale =
+    1/sqrt(head_dim) (the standard scaled form; the CP text's shorthand
+    drops the scale).  An optional causal mask lets query position i see key
+    positions j <= i only.
+  * Layout: T = batch * seq token rows; head h of the shard reads columns
+    [h*d, (h+1)*d) of Q, K and V (each [T, heads*d] with its own row stride,
+    e.g. the three blocks of the fused QKV projection output); O and the
+    gradients use the same column layout.
+  * The log-sum-exp of each query row, LSE = log(sum_j exp(s_ij)), is kept
+    for the backward.
+  * Backward from the chain rule through the softmax: with P = softmax(S),
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - D), D_i = sum_j P_ij dP_ij =
+    sum_d dO_id O_id, dQ = dS K * scale, dK = dS^T Q * scale.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict
+
+import numpy as np
+
+
+def _heads(M: np.ndarray, batch: int, seq: int, heads: int, d: int) -> np.ndarray:
+    """[T, >= heads*d] -> [batch, heads, seq, d]."""
+    M = np.asarray(M, dtype=np.float64)[:, :heads * d]
+    return M.reshape(batch, seq, heads, d).transpose(0, 2, 1, 3)
+
+
+def _unheads(A: np.ndarray) -> np.ndarray:
+    b, h, s, d = A.shape
+    return A.transpose(0, 2, 1, 3).reshape(b * s, h * d)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def _mask(seq: int, causal: bool) -> np.ndarray:
+    if not causal:
+        return np.zeros((seq, seq), dtype=bool)
+    return np.triu(np.ones((seq, seq), dtype=bool), k=1)   # True where key j > query i
+
+
+def attn_fwd(Q, K, V, batch: int, seq: int, heads: int, d: int, causal: bool, scale: float) -> Dict[str, np.ndarray]:
+    """Plain definition: per (batch, head) S = Q K^T * scale (masked), P = softmax(S), O = P V."""
+    q, k, v = (_heads(M, batch, seq, heads, d) for M in (Q, K, V))
+    S = np.matmul(q, k.transpose(0, 1, 3, 2)) * scale
+    S = np.where(_mask(seq, causal)[None, None], -np.inf, S)
+    m = S.max(axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=-1, keepdims=True)
+    P = E / l
+    O = np.matmul(P, v)
+    lse = (m + np.log(l))[..., 0]                     # [batch, heads, seq]
+    return {"O": _unheads(O), "P": P, "lse": lse.transpose(1, 0, 2).reshape(heads, batch * seq)}
+
+
+def attn_bwd(Q, K, V, dO, batch: int, seq: int, heads: int, d: int, causal: bool,
+             scale: float) -> Dict[str, np.ndarray]:
+    f = attn_fwd(Q, K, V, batch, seq, heads, d, causal, scale)
+    q, k, v = (_heads(M, batch, seq, heads, d) for M in (Q, K, V))
+    do = _heads(dO, batch, seq, heads, d)
+    P = f["P"]
+    o = _heads(f["O"], batch, seq, heads, d)
+    dV = np.matmul(P.transpose(0, 1, 3, 2), do)
+    dP = np.matmul(do, v.transpose(0, 1, 3, 2))
+    D = (do * o).sum(axis=-1, keepdims=True)
+    dS = P * (dP - D)
+    dQ = np.matmul(dS, k) * scale
+    dK = np.matmul(dS.transpose(0, 1, 3, 2), q) * scale
+    return {"dQ": _unheads(dQ), "dK": _unheads(dK), "dV": _unheads(dV),
+            "D": D[..., 0].transpose(1, 0, 2).reshape(heads, batch * seq), "O": f["O"], "lse": f["lse"]}
+
+
+def attn_fwd_rows(Q, K, V, batch: int, seq: int, heads: int, d: int, causal: bool, scale: float,
+                  b: int, h: int, rows) -> Dict[str, np.ndarray]:
+    """Output rows (positions) of one (batch, head) at full sequence length: each
+    query row needs every key, but only its own query."""
+    rows = np.asarray(rows)
+    q, k, v = (_heads(M, batch, seq, heads, d)[b, h] for M in (Q, K, V))
+    S = np.matmul(q[rows], k.T) * scale
+    if causal:
+        S = np.where(np.arange(seq)[None, :] > rows[:, None], -np.inf, S)
+    m = S.max(axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=-1, keepdims=True)
+    return {"O": np.matmul(E / l, v), "lse": (m + np.log(l))[:, 0]}

@@ -143,3 +143,20 @@ def layernorm_rows(X, gamma, beta, eps: float = 1e-5):
         inv = 1.0 / math.sqrt(var + eps)
         out.append([float(gamma[c]) * (v - mu) * inv + float(beta[c]) for c, v in enumerate(row)])
     return out
+
+
+# ---------------------------------------------------------------------------
+# Attention of one head: o_i = sum_j softmax_j(q_i . k_j * scale) v_j, with
+# keys j > i left out when causal.
+# ---------------------------------------------------------------------------
+def attention_head(q, k, v, scale: float, causal: bool):
+    q, k, v = to_lists(q), to_lists(k), to_lists(v)
+    out = []
+    for i, qi in enumerate(q):
+        js = range(i + 1) if causal else range(len(k))
+        s = [scale * sum(a * b for a, b in zip(qi, k[j])) for j in js]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        out.append([sum(e[t] / z * v[j][c] for t, j in enumerate(js)) for c in range(len(v[0]))])
+    return out
