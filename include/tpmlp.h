@@ -285,6 +285,21 @@ int sp_partial_sum_dropout_residual(void* stream, int tp_size, int64_t rows, int
 int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int64_t ldi, float p, uint64_t seed,
                    int64_t row0, void* dZ, int64_t ldz);
 
+/* ---- Attention core -------------------------------------------------------
+ * Between the head-sharded QKV (column) and O (row) projections each shard
+ * computes its own heads independently [csdn 1.2.2; zouht 2.2.1 多头注意力机制;
+ * wangyu 注意力机制中的张量并行]: per head and sequence
+ * O = softmax(Q K^T * scale) V, with keys j > i masked for query i when
+ * causal = 1.  T = batch * seq token rows (sequence b is rows
+ * [b*seq, (b+1)*seq)); head h reads columns [h*head_dim, (h+1)*head_dim) of
+ * Q, K, V (bf16, row strides ldq, ldk, ldv — e.g. the three blocks of the
+ * fused QKV output, ld = 3*heads*head_dim) and writes the same columns of O
+ * (bf16, ldo).  head_dim must be 128.  lse [heads, T] fp32 (row h*T + t)
+ * receives log(sum_j exp(s_tj)) of each query row, or pass NULL. */
+int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
+             const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, void* O,
+             int64_t ldo, float* lse);
+
 /* Status name, and the calling thread's message for its last non-OK status. */
 const char* tpmlp_status_string(int status);
 const char* tpmlp_last_error(void);

@@ -24,7 +24,7 @@ __all__ = [
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
     "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
-    "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "profile_enable",
+    "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -58,6 +58,7 @@ _SIGNATURES = {
     "sp_partial_sum_dropout_residual": [_vp, _int, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp,
                                         _i64],
     "sp_dropout_bwd": [_vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp, _i64],
+    "attn_fwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
     "tpmlp_status_string": [_int],
     "tpmlp_last_error": [],
     "tpmlp_version": [],
@@ -322,6 +323,15 @@ def sp_dropout_bwd(dOut, dZ, p: float, seed: int, row0: int, stream=None) -> Non
     rows, h = dOut.shape
     _check(_get_lib().sp_dropout_bwd(_stream(stream, dOut), rows, h, _ptr(dOut), _ld(dOut, h), p, seed, row0,
                                      _ptr(dZ), _ld(dZ, h)))
+
+
+def attn_fwd(Q, K, V, O, batch: int, seq: int, heads: int, causal: bool = True, scale: Optional[float] = None,
+             lse=None, head_dim: int = 128, stream=None) -> None:
+    """O = softmax(Q K^T * scale) V per head (bf16; head h in columns [128h, 128h+128)); lse [heads, T] fp32."""
+    w = heads * head_dim
+    sc = head_dim ** -0.5 if scale is None else scale
+    _check(_get_lib().attn_fwd(_stream(stream, O), batch, seq, heads, head_dim, int(bool(causal)), sc, _ptr(Q),
+                               _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(lse)))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:

@@ -16,6 +16,7 @@
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "reduce.hpp"
+#include "attn.hpp"
 #include "sp.hpp"
 #include "swiglu.hpp"
 
@@ -908,6 +909,52 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
   return launch("sp_dropout_bwd", "sp_dropout_bwd_kernel", sp_dropout_bwd_kernel, dim3(grid_for(rows * (h / 8))),
                 dim3(256), (hipStream_t)stream, static_cast<const bf16_t*>(dOut), ldi, (int)rows, (int)h, thr, scale,
                 seed, row0, static_cast<bf16_t*>(dZ), ldz);
+}
+
+// ------------------------------------------------------ attention core --
+namespace {
+int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale) {
+  if (head_dim != kAttnD) return fail(TPMLP_E_SHAPE, "head_dim %d: this build takes head_dim 128", head_dim);
+  if (heads < 1 || heads > 65535) return fail(TPMLP_E_SHAPE, "heads = %d out of range [1, 65535]", heads);
+  if (batch < 0 || batch > 65535) return fail(TPMLP_E_SHAPE, "batch = %lld out of range", (long long)batch);
+  TPMLP_TRY(check_rows("seq", seq));
+  if (batch * seq > kMaxDim) return fail(TPMLP_E_SHAPE, "batch * seq above 2^31 - 1");
+  if (causal != 0 && causal != 1) return fail(TPMLP_E_VALUE, "causal = %d must be 0 or 1", causal);
+  if (!std::isfinite(scale)) return fail(TPMLP_E_VALUE, "scale must be finite");
+  return TPMLP_OK;
+}
+}  // namespace
+
+int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
+             const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, void* O,
+             int64_t ldo, float* lse) {
+  TPMLP_TRY(check_attn(batch, seq, heads, head_dim, causal, scale));
+  const int64_t T = batch * seq, w = (int64_t)heads * head_dim;
+  TPMLP_TRY(check_mat("Q", Q, T, w, ldq, 8));
+  TPMLP_TRY(check_mat("K", K, T, w, ldk, 8));
+  TPMLP_TRY(check_mat("V", V, T, w, ldv, 8));
+  TPMLP_TRY(check_mat("O", O, T, w, ldo, 8));
+  TPMLP_TRY(check_vec("lse", lse, T * heads, false));
+  if (T == 0) return TPMLP_OK;
+  if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd)
+    return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
+  AttnArgs a;
+  a.Q = static_cast<const bf16_t*>(Q);
+  a.K = static_cast<const bf16_t*>(K);
+  a.V = static_cast<const bf16_t*>(V);
+  a.ldq = ldq;
+  a.ldk = ldk;
+  a.ldv = ldv;
+  a.O = static_cast<bf16_t*>(O);
+  a.ldo = ldo;
+  a.lse = lse;
+  a.batch = (int)batch;
+  a.seq = (int)seq;
+  a.heads = heads;
+  a.causal = causal;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const dim3 grid((unsigned)((seq + kAttnBQ - 1) / kAttnBQ), (unsigned)heads, (unsigned)batch);
+  return launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), (hipStream_t)stream, a);
 }
 
 int tpmlp_profile_enable(const char* filter) {
