@@ -300,6 +300,22 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
              const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, void* O,
              int64_t ldo, float* lse);
 
+/* Bytes of device workspace attn_bwd needs (fp32 [heads, T]; 0 on bad args). */
+size_t attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads);
+
+/* Backward of attn_fwd for the upstream gradient dO (bf16, same layout as O).
+ * With P = softmax(Q K^T * scale) (recomputed from lse), D = rowsum(dO * O):
+ *   dV = P^T dO, dS = P * (dO V^T - D), dQ = dS K * scale, dK = dS^T Q * scale,
+ * written as bf16 into dQ, dK, dV (head h in columns [h*128, (h+1)*128), row
+ * strides lddq, lddk, lddv — e.g. the three blocks of a fused dQKV buffer).
+ * O and lse as written by attn_fwd.  Deterministic: no atomics.  workspace:
+ * device memory of at least attn_bwd_workspace_bytes() bytes, 256-byte
+ * aligned, owned by the caller. */
+int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
+             const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, const void* O,
+             int64_t ldo, const void* dO, int64_t lddo, const float* lse, void* dQ, int64_t lddq, void* dK,
+             int64_t lddk, void* dV, int64_t lddv, void* workspace, size_t workspace_bytes);
+
 /* Status name, and the calling thread's message for its last non-OK status. */
 const char* tpmlp_status_string(int status);
 const char* tpmlp_last_error(void);

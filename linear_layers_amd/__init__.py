@@ -24,7 +24,8 @@ __all__ = [
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
     "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
-    "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "profile_enable",
+    "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "attn_bwd",
+    "attn_bwd_workspace_bytes", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -59,13 +60,16 @@ _SIGNATURES = {
                                         _i64],
     "sp_dropout_bwd": [_vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp, _i64],
     "attn_fwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
+    "attn_bwd_workspace_bytes": [_i64, _i64, _int],
+    "attn_bwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                 _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz],
     "tpmlp_status_string": [_int],
     "tpmlp_last_error": [],
     "tpmlp_version": [],
     "tpmlp_profile_enable": [ctypes.c_char_p],
     "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
 }
-_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
              "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
 
 
@@ -332,6 +336,24 @@ def attn_fwd(Q, K, V, O, batch: int, seq: int, heads: int, causal: bool = True, 
     sc = head_dim ** -0.5 if scale is None else scale
     _check(_get_lib().attn_fwd(_stream(stream, O), batch, seq, heads, head_dim, int(bool(causal)), sc, _ptr(Q),
                                _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(lse)))
+
+
+def attn_bwd_workspace_bytes(batch: int, seq: int, heads: int) -> int:
+    return int(_get_lib().attn_bwd_workspace_bytes(batch, seq, heads))
+
+
+def attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, batch: int, seq: int, heads: int, causal: bool = True,
+             scale: Optional[float] = None, workspace=None, head_dim: int = 128, stream=None) -> None:
+    """dQ, dK, dV (bf16) of attn_fwd for upstream dO; workspace a device uint8 tensor (allocated here if None)."""
+    w = heads * head_dim
+    sc = head_dim ** -0.5 if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(max(1, attn_bwd_workspace_bytes(batch, seq, heads)), dtype=torch.uint8,
+                                device=Q.device)
+    _check(_get_lib().attn_bwd(_stream(stream, Q), batch, seq, heads, head_dim, int(bool(causal)), sc, _ptr(Q),
+                               _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(dO),
+                               _ld(dO, w), _ptr(lse), _ptr(dQ), _ld(dQ, w), _ptr(dK), _ld(dK, w), _ptr(dV),
+                               _ld(dV, w), _ptr(workspace), workspace.numel()))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:

@@ -215,4 +215,381 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   }
 }
 
+// ================================================================ backward --
+// With P = softmax(S) and D_q = sum_d dO[q,d] O[q,d]: dV = P^T dO, dP = dO V^T,
+// dS = P * (dP - D), dQ = dS K * scale, dK = dS^T Q * scale.  Two kernels,
+// no atomics: one owns a block of keys and loops over query blocks (dK, dV),
+// the other owns a block of queries and loops over key blocks (dQ); both
+// recompute P from the saved log-sum-exp.
+
+struct AttnBwdArgs {
+  const bf16_t* Q;
+  const bf16_t* K;
+  const bf16_t* V;
+  const bf16_t* O;
+  const bf16_t* dO;
+  int64_t ldq, ldk, ldv, ldo, lddo;
+  const float* lse;   // [heads, T] natural log
+  float* D;           // [heads, T] workspace: sum_d dO * O
+  bf16_t* dQ;
+  bf16_t* dK;
+  bf16_t* dV;
+  int64_t lddq, lddk, lddv;
+  int batch, seq, heads, causal;
+  float scale, scale_log2;
+};
+
+// D[head][t] = sum over the head's 128 columns of dO * O; 16 lanes per (row, head).
+__global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const AttnBwdArgs p) {
+  const int64_t T = (int64_t)p.batch * p.seq;
+  const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (row, head) = (item / heads, item % heads)
+  const int j = threadIdx.x & 15;
+  float acc = 0.0f;
+  const bool live = item < T * p.heads;
+  const int64_t t = live ? item / p.heads : 0;
+  const int head = live ? (int)(item % p.heads) : 0;
+  if (live) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p.dO + t * p.lddo + head * kAttnD + 8 * j);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p.O + t * p.ldo + head * kAttnD + 8 * j);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc += bf16lo(a[k]) * bf16lo(b[k]) + bf16hi(a[k]) * bf16hi(b[k]);
+  }
+#pragma unroll
+  for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
+  if (live && j == 0) p.D[(int64_t)head * T + t] = acc;
+}
+
+// A tile of ROWS token rows x 128 of d in LDS, read two ways: 8 consecutive d
+// of one row (ds_read_b128) and 4 consecutive rows of one d column through
+// the transposing read (ds_read_b64_tr_b16).  Chunk q (8 values of d) of row
+// r sits at position q ^ (4 (r & 3) | ((r >> 2) & 3)), which keeps both
+// patterns free of bank conflicts.
+template <int ROWS, int NW>
+struct AttnRowTile {
+  static constexpr int BYTES = ROWS * 256;
+  static constexpr int SLOTS = ROWS * 16;
+  static constexpr int INSTR = SLOTS / (64 * NW);
+  static_assert(SLOTS % (64 * NW) == 0, "tile too small for the waves");
+  uint32_t voff[INSTR];
+  uint32_t kb;          // row-read base: (lane & 31) * 256
+  uint32_t ksw;         // row-read swizzle of row lane & 31
+  uint32_t tb[4][2];    // transposing-read bases per 32-column block F (p0, p1)
+
+  static __device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j) {
+      const int s = (wave * INSTR + j) * 64 + lane;
+      const int r = s >> 4, q = (s & 15) ^ sw(r);
+      voff[j] = (uint32_t)(((int64_t)r * ld + q * 8) * 2);
+    }
+    kb = (uint32_t)(lane & 31) * 256u;
+    ksw = (uint32_t)sw(lane & 31);
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int F = 0; F < 4; ++F)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int kr = 8 * (g >> 1) + (j >> 2) + 4 * pp;     // row within a 16-row substep
+        const int q = 4 * F + 2 * (g & 1) + ((j & 3) >> 1);
+        tb[F][pp] = (uint32_t)(kr * 256 + ((q ^ sw(kr)) << 4) + 8 * (j & 1));
+      }
+  }
+
+  __device__ __forceinline__ void load(const bf16_t* base, uint32_t nbytes, lds_char* dst, int wave) const {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base);
+    const i32x4_t rsrc = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffffu), (int)nbytes, kBufferWord3};
+#pragma unroll
+    for (int j = 0; j < INSTR; ++j) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(dst + (wave * INSTR + j) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(lds), "v"(voff[j]), "s"(rsrc)
+                   : "memory", "m0");
+    }
+  }
+
+  // Row read (b fragment whose n index is the row): lane holds row 32F + (lane & 31),
+  // d = 16 S + 8 (lane >> 5) .. + 7.
+  template <int F, int S>
+  __device__ __forceinline__ u32x4_t row(const lds_char* src, int lane) const {
+    const uint32_t c = (uint32_t)(2 * S + (lane >> 5)) ^ ksw;
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src + F * 32 * 256 + kb + (c << 4));
+  }
+
+  // Transposing read (b fragment whose k index is the row): lane holds rows
+  // 16 S + 8 (lane >> 5) .. + 7 of column 32F + (lane & 31).
+  template <int F, int S>
+  __device__ __forceinline__ u32x4_t col(const lds_char* src) const {
+    const lds_char* p0 = src + S * 16 * 256 + tb[F][0];
+    const lds_char* p1 = src + S * 16 * 256 + tb[F][1];
+    const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p0);
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p1);
+    const u32x2_t w0 = __builtin_bit_cast(u32x2_t, v0);
+    const u32x2_t w1 = __builtin_bit_cast(u32x2_t, v1);
+    return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+  }
+};
+
+// acc[f] += B(tile rows as n) x A over the 8 d-substeps: C[m][n] with m from a, n = tile row.
+template <int S, int NF, class Tile>
+__device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int lane, const u32x4_t (&a)[8],
+                                        f32x16_t (&acc)[NF]) {
+  if constexpr (NF >= 1) acc[0] = mfma_bf16(t.template row<0, S>(src, lane), a[S], acc[0]);
+  if constexpr (NF >= 2) acc[1] = mfma_bf16(t.template row<1, S>(src, lane), a[S], acc[1]);
+  if constexpr (S + 1 < 8) mm_rows<S + 1, NF>(t, src, lane, a, acc);
+}
+
+// acc[F] += B(tile rows as k, d block F as n) x A over NT row-substeps of 16.
+template <int T, int NT, class Tile>
+__device__ __forceinline__ void mm_cols(const Tile& t, const lds_char* src, const u32x4_t (&a)[NT],
+                                        f32x16_t (&acc)[4]) {
+#pragma unroll
+  for (int F = 0; F < 4; ++F) {
+    u32x4_t b;
+    if (F == 0) b = t.template col<0, T>(src);
+    else if (F == 1) b = t.template col<1, T>(src);
+    else if (F == 2) b = t.template col<2, T>(src);
+    else b = t.template col<3, T>(src);
+    acc[F] = mfma_bf16(b, a[T], acc[F]);
+  }
+  if constexpr (T + 1 < NT) mm_cols<T + 1, NT>(t, src, a, acc);
+}
+
+// A fragments of a 32 x 32k block held in accumulator layout (row = lane & 31,
+// 4-column groups) for the k-substeps 16t .. 16t + 15, t < 2 * NF.
+template <int NF>
+__device__ __forceinline__ void acc_to_afrag(const float (&x)[NF][16], u32x4_t (&af)[2 * NF]) {
+#pragma unroll
+  for (int t = 0; t < 2 * NF; ++t) {
+    const int f = t >> 1, v0 = 8 * (t & 1);
+    af[t] = swap_pack(pack_bf16x2(x[f][v0], x[f][v0 + 1]), pack_bf16x2(x[f][v0 + 2], x[f][v0 + 3]),
+                      pack_bf16x2(x[f][v0 + 4], x[f][v0 + 5]), pack_bf16x2(x[f][v0 + 6], x[f][v0 + 7]));
+  }
+}
+
+// Stores a wave's 32 x 128 fp32 block (accumulator layout) as bf16 rows times `mul`.
+__device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[4], float mul, bf16_t* rowp, int h) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+      const int g0 = 8 * pr;
+      const u32x4_t w = swap_pack(pack_bf16x2(acc[f][g0] * mul, acc[f][g0 + 1] * mul),
+                                  pack_bf16x2(acc[f][g0 + 2] * mul, acc[f][g0 + 3] * mul),
+                                  pack_bf16x2(acc[f][g0 + 4] * mul, acc[f][g0 + 5] * mul),
+                                  pack_bf16x2(acc[f][g0 + 6] * mul, acc[f][g0 + 7] * mul));
+      *reinterpret_cast<u32x4_t*>(rowp + 32 * f + 16 * pr + 8 * h) = w;
+    }
+}
+
+constexpr int kAttnBwdBQ = 64;   // query rows per block in the key-stationary kernel
+using AttnQTile = AttnRowTile<kAttnBwdBQ, 2>;   // 64 rows, 2 waves load it
+constexpr int kAttnDkvStage = 2 * AttnQTile::BYTES;  // Q and dO: 32 KB
+
+// dK, dV for 64 keys of one head (2 waves x 32 keys), over all query blocks
+// that see them.  K and V rows stay in registers as A fragments.
+__global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) char st0[kAttnDkvStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kAttnDkvStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = p.seq;
+  const int nkb = (seq + 63) / 64;
+  const int kb = p.causal ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x;  // most query blocks first
+  const int head = blockIdx.y;
+  const int64_t T = (int64_t)p.batch * seq;
+  const int64_t row_base = (int64_t)blockIdx.z * seq;
+  const int k0 = kb * 64;
+  const int kw0 = k0 + 32 * wave;
+  const int krow = kw0 + (lane & 31);
+
+  u32x4_t kf[8], vf[8];
+  {
+    const bf16_t* kp = p.K + (row_base + krow) * p.ldk + head * kAttnD + 8 * h;
+    const bf16_t* vp = p.V + (row_base + krow) * p.ldv + head * kAttnD + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = krow < seq ? *reinterpret_cast<const u32x4_t*>(kp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+      vf[s] = krow < seq ? *reinterpret_cast<const u32x4_t*>(vp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  AttnQTile qt, ot;
+  qt.init(wave, lane, p.ldq);
+  ot.init(wave, lane, p.lddo);
+  const bf16_t* Qh = p.Q + row_base * p.ldq + head * kAttnD;
+  const bf16_t* dOh = p.dO + row_base * p.lddo + head * kAttnD;
+  auto issue = [&](int qb, lds_char* dst) {
+    const int q0 = qb * kAttnBwdBQ;
+    const int rows = min(kAttnBwdBQ, seq - q0);
+    qt.load(Qh + (int64_t)q0 * p.ldq, (uint32_t)(((int64_t)(rows - 1) * p.ldq + kAttnD) * 2), dst, wave);
+    ot.load(dOh + (int64_t)q0 * p.lddo, (uint32_t)(((int64_t)(rows - 1) * p.lddo + kAttnD) * 2),
+            dst + AttnQTile::BYTES, wave);
+  };
+  const float* lse_h = p.lse + (int64_t)head * T + row_base;
+  const float* D_h = p.D + (int64_t)head * T + row_base;
+  const float log2e = 1.4426950408889634f;
+
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[f][v] = dv[f][v] = 0.0f;
+
+  const int nqb = (seq + kAttnBwdBQ - 1) / kAttnBwdBQ;
+  const int qb0 = p.causal ? k0 / kAttnBwdBQ : 0;
+  if (qb0 < nqb) {
+    issue(qb0, (lds_char*)st0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+  }
+  for (int qb = qb0; qb < nqb; ++qb) {
+    lds_char* cur = ((qb - qb0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = ((qb - qb0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+    if (qb + 1 < nqb) issue(qb + 1, nxt);
+    const int q0 = qb * kAttnBwdBQ;
+    // S^T (keys x queries) and dP^T = V dO^T
+    f32x16_t st[2], dpt[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[f][v] = dpt[f][v] = 0.0f;
+    mm_rows<0, 2>(qt, cur, lane, kf, st);
+    mm_rows<0, 2>(ot, cur + AttnQTile::BYTES, lane, vf, dpt);
+    // P^T and dS^T; columns are queries q0 + 32 f + 8 g + 4 h + e
+    float pt[2][16], dst_[2][16];
+    const bool edge = q0 + kAttnBwdBQ > seq || (p.causal && q0 < kw0 + 31);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qc = q0 + 32 * f + 8 * g + 4 * h;
+        float l4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)   // scalar loads: head * T + row_base need not be a multiple of 4
+          if (qc + e < seq) {
+            l4[e] = lse_h[qc + e];
+            d4[e] = D_h[qc + e];
+          }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          float pv = __builtin_amdgcn_exp2f(st[f][v] * p.scale_log2 - l4[e] * log2e);
+          if (edge) {
+            const int q = qc + e;
+            if (q >= seq || krow >= seq || (p.causal && q < krow)) pv = 0.0f;
+          }
+          pt[f][v] = pv;
+          dst_[f][v] = pv * (dpt[f][v] - d4[e]);
+        }
+      }
+    u32x4_t pa[4], da[4];
+    acc_to_afrag<2>(pt, pa);
+    acc_to_afrag<2>(dst_, da);
+    mm_cols<0, 4>(ot, cur + AttnQTile::BYTES, pa, dv);   // dV += P^T dO
+    mm_cols<0, 4>(qt, cur, da, dk);                      // dK += dS^T Q
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+  }
+  if (krow < seq) {
+    store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
+    store_rows_bf16(dk, p.scale, p.dK + (row_base + krow) * p.lddk + head * kAttnD, h);
+  }
+}
+
+using AttnKVTile = AttnRowTile<kAttnBK, 4>;   // 64 key rows x 128, 4 waves load it
+constexpr int kAttnDqStage = 2 * AttnKVTile::BYTES;  // K and V: 32 KB
+
+// dQ for 128 query rows of one head (4 waves x 32), over the key blocks they see.
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) char st0[kAttnDqStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kAttnDqStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = p.seq;
+  const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const int qb = p.causal ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int head = blockIdx.y;
+  const int64_t T = (int64_t)p.batch * seq;
+  const int64_t row_base = (int64_t)blockIdx.z * seq;
+  const int q0 = qb * kAttnBQ;
+  const int wq0 = q0 + 32 * wave;
+  const int qrow = wq0 + (lane & 31);
+
+  u32x4_t qf[8], of[8];
+  {
+    const bf16_t* qp = p.Q + (row_base + qrow) * p.ldq + head * kAttnD + 8 * h;
+    const bf16_t* op = p.dO + (row_base + qrow) * p.lddo + head * kAttnD + 8 * h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qf[s] = qrow < seq ? *reinterpret_cast<const u32x4_t*>(qp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+      of[s] = qrow < seq ? *reinterpret_cast<const u32x4_t*>(op + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  const float log2e = 1.4426950408889634f;
+  const float lse2 = qrow < seq ? p.lse[(int64_t)head * T + row_base + qrow] * log2e : 0.0f;
+  const float Dq = qrow < seq ? p.D[(int64_t)head * T + row_base + qrow] : 0.0f;
+  AttnKVTile ktile, vtile;
+  ktile.init(wave, lane, p.ldk);
+  vtile.init(wave, lane, p.ldv);
+  const bf16_t* Kh = p.K + row_base * p.ldk + head * kAttnD;
+  const bf16_t* Vh = p.V + row_base * p.ldv + head * kAttnD;
+  auto issue = [&](int j, lds_char* dst) {
+    const int kv0 = j * kAttnBK;
+    const int rows = min(kAttnBK, seq - kv0);
+    ktile.load(Kh + (int64_t)kv0 * p.ldk, (uint32_t)(((int64_t)(rows - 1) * p.ldk + kAttnD) * 2), dst, wave);
+    vtile.load(Vh + (int64_t)kv0 * p.ldv, (uint32_t)(((int64_t)(rows - 1) * p.ldv + kAttnD) * 2),
+               dst + AttnKVTile::BYTES, wave);
+  };
+
+  f32x16_t dq[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dq[f][v] = 0.0f;
+  const int kv_end = p.causal ? min(seq, q0 + kAttnBQ) : seq;
+  const int nkb = (kv_end + kAttnBK - 1) / kAttnBK;
+  issue(0, (lds_char*)st0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  for (int j = 0; j < nkb; ++j) {
+    lds_char* cur = (j & 1) ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = (j & 1) ? (lds_char*)st0 : (lds_char*)st1;
+    if (j + 1 < nkb) issue(j + 1, nxt);
+    const int kv0 = j * kAttnBK;
+    if (!(p.causal && kv0 > wq0 + 31)) {
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[f][v] = dp[f][v] = 0.0f;
+      mm_rows<0, 2>(ktile, cur, lane, qf, s);                       // S = Q K^T
+      mm_rows<0, 2>(vtile, cur + AttnKVTile::BYTES, lane, of, dp);  // dP = dO V^T
+      const bool edge = kv0 + kAttnBK > seq || (p.causal && kv0 + kAttnBK - 1 > wq0);
+      float ds[2][16];
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float pv = __builtin_amdgcn_exp2f(s[f][v] * p.scale_log2 - lse2);
+          if (edge) {
+            const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (kv >= seq || (p.causal && kv > qrow)) pv = 0.0f;
+          }
+          ds[f][v] = pv * (dp[f][v] - Dq);
+        }
+      u32x4_t da[4];
+      acc_to_afrag<2>(ds, da);
+      mm_cols<0, 4>(ktile, cur, da, dq);   // dQ += dS K
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+  }
+  if (qrow < seq) store_rows_bf16(dq, p.scale, p.dQ + (row_base + qrow) * p.lddq + head * kAttnD, h);
+}
+
 }  // namespace tpmlp

@@ -957,6 +957,68 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   return launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), (hipStream_t)stream, a);
 }
 
+size_t attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads) {
+  if (batch < 0 || seq < 0 || heads < 1 || batch * seq > kMaxDim) return 0;
+  return align256((size_t)batch * seq * heads * sizeof(float));
+}
+
+int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
+             const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, const void* O,
+             int64_t ldo, const void* dO, int64_t lddo, const float* lse, void* dQ, int64_t lddq, void* dK,
+             int64_t lddk, void* dV, int64_t lddv, void* workspace, size_t workspace_bytes) {
+  TPMLP_TRY(check_attn(batch, seq, heads, head_dim, causal, scale));
+  const int64_t T = batch * seq, w = (int64_t)heads * head_dim;
+  TPMLP_TRY(check_mat("Q", Q, T, w, ldq, 8));
+  TPMLP_TRY(check_mat("K", K, T, w, ldk, 8));
+  TPMLP_TRY(check_mat("V", V, T, w, ldv, 8));
+  TPMLP_TRY(check_mat("O", O, T, w, ldo, 8));
+  TPMLP_TRY(check_mat("dO", dO, T, w, lddo, 8));
+  TPMLP_TRY(check_mat("dQ", dQ, T, w, lddq, 8));
+  TPMLP_TRY(check_mat("dK", dK, T, w, lddk, 8));
+  TPMLP_TRY(check_mat("dV", dV, T, w, lddv, 8));
+  TPMLP_TRY(check_vec("lse", lse, T * heads, true));
+  if (T == 0) return TPMLP_OK;
+  if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd || lddo >= kMaxLd)
+    return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
+  const size_t need = align256((size_t)T * heads * sizeof(float));
+  if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+  if (workspace_bytes < need) return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  AttnBwdArgs a;
+  a.Q = static_cast<const bf16_t*>(Q);
+  a.K = static_cast<const bf16_t*>(K);
+  a.V = static_cast<const bf16_t*>(V);
+  a.O = static_cast<const bf16_t*>(O);
+  a.dO = static_cast<const bf16_t*>(dO);
+  a.ldq = ldq;
+  a.ldk = ldk;
+  a.ldv = ldv;
+  a.ldo = ldo;
+  a.lddo = lddo;
+  a.lse = lse;
+  a.D = static_cast<float*>(workspace);
+  a.dQ = static_cast<bf16_t*>(dQ);
+  a.dK = static_cast<bf16_t*>(dK);
+  a.dV = static_cast<bf16_t*>(dV);
+  a.lddq = lddq;
+  a.lddk = lddk;
+  a.lddv = lddv;
+  a.batch = (int)batch;
+  a.seq = (int)seq;
+  a.heads = heads;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t items = T * heads;
+  TPMLP_TRY(launch("attn_bwd_dot", "attn_bwd_dot_kernel", attn_bwd_dot_kernel, dim3((unsigned)((items + 15) / 16)),
+                   dim3(256), s, a));
+  TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
+                   dim3((unsigned)((seq + 63) / 64), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
+  return launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
+                dim3((unsigned)((seq + kAttnBQ - 1) / kAttnBQ), (unsigned)heads, (unsigned)batch), dim3(256), s, a);
+}
+
 int tpmlp_profile_enable(const char* filter) {
   Profiler& P = prof();
   std::lock_guard<std::mutex> lk(P.mu);

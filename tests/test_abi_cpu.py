@@ -147,3 +147,22 @@ def test_sp_validation():
     assert d(None, 8, 64, P, 64, 1.5, 1, 0, P, 64) == E_VALUE
     assert d(None, 8, 64, P, 64, 0.1, 1, 0, None, 64) == E_NULL
     assert d(None, 8, 64, P, 60, 0.1, 1, 0, P, 64) == E_SHAPE
+
+
+def test_attn_validation():
+    f = tl.lib.attn_fwd
+    # (stream, batch, seq, heads, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, O, ldo, lse): refused on the host
+    assert f(None, 1, 8, 1, 64, 1, 0.1, P, 64, P, 64, P, 64, P, 64, None) == E_SHAPE
+    assert f(None, 1, 8, 1, 128, 2, 0.1, P, 128, P, 128, P, 128, P, 128, None) == E_VALUE
+    assert f(None, 1, 8, 1, 128, 1, float("inf"), P, 128, P, 128, P, 128, P, 128, None) == E_VALUE
+    assert f(None, 1, 8, 0, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None) == E_SHAPE
+    assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None) == E_SHAPE   # ldq < heads*128
+    assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None) == E_NULL
+    assert f(None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P + 8, 128, None) == E_ALIGN
+    b = tl.lib.attn_bwd
+    args = [None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, P, 128, P, P, 128, P, 128, P, 128]
+    assert b(*args, P, 16) == E_WS
+    assert b(*args, None, 1 << 20) == E_NULL
+    assert b(*args, P + 16, 1 << 20) == E_ALIGN
+    args[15] = None   # lse is required by the backward
+    assert b(*args, P, 1 << 20) == E_NULL

@@ -106,3 +106,69 @@ def test_attn_fwd_workload_sampled():
                                 rows)
         assert_close(Og[rows, hd * D:(hd + 1) * D], ref["O"], "bf16", f"O head {hd}")
         _lse_close(Lg[hd, rows], ref["lse"], f"lse head {hd}")
+
+
+def _bwd_case(batch, seq, heads, causal, seed, scale=None):
+    T, w = batch * seq, heads * D
+    qkv = _qkv(seed, T, heads)
+    r = np.random.default_rng(seed + 1)
+    dO = synth.bf16_round_bits(r.standard_normal((T, w)).astype(np.float32))
+    dev, dOd = to_dev(qkv, "bf16"), to_dev(dO, "bf16")
+    Q, K, V = dev[:, :w], dev[:, w:2 * w], dev[:, 2 * w:]
+    O, lse = empty((T, w), "bf16"), empty_f32((heads, T))
+    tl.attn_fwd(Q, K, V, O, batch, seq, heads, causal=causal, scale=scale, lse=lse)
+    dqkv = empty((T, 3 * w), "bf16")
+    tl.attn_bwd(Q, K, V, O, dOd, lse, dqkv[:, :w], dqkv[:, w:2 * w], dqkv[:, 2 * w:], batch, seq, heads,
+                causal=causal, scale=scale)
+    sync()
+    return qkv, dO, dqkv
+
+
+@pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
+                                                    (1, 300, 2, True), (1, 130, 1, False), (3, 128, 1, True),
+                                                    (1, 1000, 2, True), (1, 1000, 1, False)])
+def test_attn_bwd(batch, seq, heads, causal):
+    need_gpu()
+    _say(f"attn bwd batch={batch} seq={seq} heads={heads} causal={causal}")
+    qkv, dO, dqkv = _bwd_case(batch, seq, heads, causal, seed=batch * 100 + seq)
+    w = heads * D
+    f = synth.to_f64(qkv, "bf16")
+    ref = oat.attn_bwd(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], synth.to_f64(dO, "bf16"), batch, seq, heads, D, causal,
+                       D ** -0.5)
+    g = to_f64(dqkv)
+    assert_close(g[:, :w], ref["dQ"], "bf16", "dQ")
+    assert_close(g[:, w:2 * w], ref["dK"], "bf16", "dK")
+    assert_close(g[:, 2 * w:], ref["dV"], "bf16", "dV")
+
+
+def test_attn_bwd_deterministic_and_workspace():
+    need_gpu()
+    a = _bwd_case(1, 200, 2, True, seed=9)[2]
+    b = _bwd_case(1, 200, 2, True, seed=9)[2]
+    assert torch.equal(a, b)
+    assert tl.attn_bwd_workspace_bytes(2, 100, 3) >= 2 * 100 * 3 * 4
+    Z = torch.zeros((4, D), dtype=torch.bfloat16, device="cuda")
+    L = torch.zeros((1, 4), device="cuda")
+    small = torch.zeros(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tl.TpmlpError) as e:
+        tl.attn_bwd(Z, Z, Z, Z, Z, L, Z, Z, Z, 1, 4, 1, workspace=small)
+    assert e.value.status == 7
+
+
+@pytest.mark.slow
+def test_attn_bwd_workload_two_heads():
+    """4096 tokens, 10 heads, causal: full dQ, dK, dV of heads 0 and 7 against the oracle (heads are
+    independent, so each head's gradients come from the oracle run on that head's columns alone)."""
+    need_gpu()
+    seq, heads = 4096, 10
+    _say(f"attn bwd seq={seq} heads={heads}")
+    qkv, dO, dqkv = _bwd_case(1, seq, heads, True, seed=123)
+    w = heads * D
+    f, fd, g = synth.to_f64(qkv, "bf16"), synth.to_f64(dO, "bf16"), to_f64(dqkv)
+    for hd in (0, 7):
+        cs = slice(hd * D, (hd + 1) * D)
+        ref = oat.attn_bwd(f[:, cs], f[:, w:2 * w][:, cs], f[:, 2 * w:][:, cs], fd[:, cs], 1, seq, 1, D, True,
+                           D ** -0.5)
+        assert_close(g[:, :w][:, cs], ref["dQ"], "bf16", f"dQ head {hd}")
+        assert_close(g[:, w:2 * w][:, cs], ref["dK"], "bf16", f"dK head {hd}")
+        assert_close(g[:, 2 * w:][:, cs], ref["dV"], "bf16", f"dV head {hd}")
