@@ -30,6 +30,11 @@ Readings where the pages leave a step open (their formulas were lost):
   * Backward from the chain rule through the softmax: with P = softmax(S),
     dV = P^T dO, dP = dO V^T, dS = P * (dP - D), D_i = sum_j P_ij dP_ij =
     sum_d dO_id O_id, dQ = dS K * scale, dK = dS^T Q * scale.
+  * The head-sharded block around it: shard i of tp owns heads
+    [i*H/tp, (i+1)*H/tp), i.e. columns c = [i*w, (i+1)*w), w = H/tp * d, of
+    each of Wq, Wk, Wv (column split) and rows c of Wo (row split); its fused
+    QKV weight is [Wq[:, c] | Wk[:, c] | Wv[:, c]].  Z_i = O_i Wo[c, :] is an
+    fp32 partial and the block output is the sum over shards; no biases.
 """
 from __future__ import annotations
 
@@ -104,3 +109,59 @@ def attn_fwd_rows(Q, K, V, batch: int, seq: int, heads: int, d: int, causal: boo
     E = np.exp(S - m)
     l = E.sum(axis=-1, keepdims=True)
     return {"O": np.matmul(E / l, v), "lse": (m + np.log(l))[:, 0]}
+
+
+def _shard_cols(heads: int, d: int, tp: int, i: int) -> slice:
+    if heads % tp:
+        raise ValueError(f"heads={heads} is not divisible by tp={tp}")
+    w = heads // tp * d
+    return slice(i * w, (i + 1) * w)
+
+
+def qkv_shard_weight(Wq, Wk, Wv, heads: int, d: int, tp: int, i: int) -> np.ndarray:
+    """Shard i's fused QKV weight [h, 3w] = [Wq_i | Wk_i | Wv_i] (columns of its heads)."""
+    c = _shard_cols(heads, d, tp, i)
+    return np.concatenate([np.asarray(W, dtype=np.float64)[:, c] for W in (Wq, Wk, Wv)], axis=1)
+
+
+def tp_attn_block_fwd_shard(X, Wq, Wk, Wv, Wo, batch: int, seq: int, heads: int, d: int, tp: int, i: int,
+                            causal: bool, scale: float) -> Dict[str, np.ndarray]:
+    """Shard i's forward: QKV = X Wqkv_i, O = attention over its heads, Z = O Wo_i (a partial)."""
+    c = _shard_cols(heads, d, tp, i)
+    w = c.stop - c.start
+    X = np.asarray(X, dtype=np.float64)
+    QKV = X @ qkv_shard_weight(Wq, Wk, Wv, heads, d, tp, i)
+    f = attn_fwd(QKV[:, :w], QKV[:, w:2 * w], QKV[:, 2 * w:], batch, seq, heads // tp, d, causal, scale)
+    Z = f["O"] @ np.asarray(Wo, dtype=np.float64)[c, :]
+    return {"QKV": QKV, "O": f["O"], "lse": f["lse"], "Z": Z}
+
+
+def tp_attn_block_bwd_shard(X, Wq, Wk, Wv, Wo, dZ, batch: int, seq: int, heads: int, d: int, tp: int, i: int,
+                            causal: bool, scale: float) -> Dict[str, np.ndarray]:
+    """Shard i's backward for the gradient dZ of the block output, which every
+    shard receives whole (Z is a sum of partials): dO = dZ Wo_i^T, dWo_i =
+    O^T dZ, the attention backward gives dQKV, dWqkv_i = X^T dQKV and the
+    partial dX_i = dQKV Wqkv_i^T (the sum over shards is dX)."""
+    c = _shard_cols(heads, d, tp, i)
+    w = c.stop - c.start
+    X, dZ = np.asarray(X, dtype=np.float64), np.asarray(dZ, dtype=np.float64)
+    Wqkv = qkv_shard_weight(Wq, Wk, Wv, heads, d, tp, i)
+    Wo_i = np.asarray(Wo, dtype=np.float64)[c, :]
+    f = tp_attn_block_fwd_shard(X, Wq, Wk, Wv, Wo, batch, seq, heads, d, tp, i, causal, scale)
+    QKV = f["QKV"]
+    dO = dZ @ Wo_i.T
+    g = attn_bwd(QKV[:, :w], QKV[:, w:2 * w], QKV[:, 2 * w:], dO, batch, seq, heads // tp, d, causal, scale)
+    dQKV = np.concatenate([g["dQ"], g["dK"], g["dV"]], axis=1)
+    return {"dO": dO, "dWo": f["O"].T @ dZ, "dQKV": dQKV, "dWqkv": X.T @ dQKV, "dX": dQKV @ Wqkv.T,
+            "D": g["D"], **f}
+
+
+def tp_attn_block_fwd(X, Wq, Wk, Wv, Wo, batch: int, seq: int, heads: int, d: int, tp: int, causal: bool,
+                      scale: float) -> np.ndarray:
+    """The block output: the sum of all tp shards' partials."""
+    parts = [tp_attn_block_fwd_shard(X, Wq, Wk, Wv, Wo, batch, seq, heads, d, tp, i, causal, scale)["Z"]
+             for i in range(tp)]
+    out = np.zeros_like(parts[0])
+    for p in parts:
+        out += p
+    return out

@@ -151,5 +151,50 @@ def pin_online_softmax_and_rows(at):
     _close(fr["lse"], f["lse"][0][rows], 1e-13, "rows lse")
 
 
+def _block_case(seed, B, S, H, d):
+    r = np.random.default_rng(seed)
+    h = H * d
+    X = r.standard_normal((B * S, h))
+    Ws = [r.standard_normal((h, h)) / math.sqrt(h) for _ in range(4)]
+    dZ = r.standard_normal((B * S, h))
+    return X, Ws, dZ
+
+
+def pin_block_vs_torch_mha(at):
+    """The head-sharded block (sum over shards of the partials, and of the dX
+    partials; the shards' weight gradients as column / row slices of the whole
+    ones) against torch's float64 multi-head attention and its autograd, for
+    tp = 1, 2, 4."""
+    B, S, H, d = 2, 9, 4, 4
+    h = H * d
+    X, (Wq, Wk, Wv, Wo), dZ = _block_case(8, B, S, H, d)
+    for causal in (False, True):
+        tX = torch.tensor(X.reshape(B, S, h).transpose(1, 0, 2).copy(), requires_grad=True)   # (L, N, E)
+        tw = [torch.tensor(W.T.copy(), requires_grad=True) for W in (Wq, Wk, Wv, Wo)]         # x @ W^T form
+        mask = torch.ones(S, S, dtype=torch.bool).triu(1) if causal else None
+        out, _ = torch.nn.functional.multi_head_attention_forward(
+            tX, tX, tX, h, H, None, None, None, None, False, 0.0, tw[3], None, training=False,
+            need_weights=False, attn_mask=mask, use_separate_proj_weight=True, q_proj_weight=tw[0],
+            k_proj_weight=tw[1], v_proj_weight=tw[2])
+        tdZ = torch.tensor(dZ.reshape(B, S, h).transpose(1, 0, 2).copy())
+        grads = torch.autograd.grad((out * tdZ).sum(), [tX] + tw)
+        Zt = out.detach().numpy().transpose(1, 0, 2).reshape(B * S, h)
+        dXt = grads[0].numpy().transpose(1, 0, 2).reshape(B * S, h)
+        dWt = [g.numpy().T for g in grads[1:]]                                                  # back to X @ W form
+        for tp in (1, 2, 4):
+            Z = at.tp_attn_block_fwd(X, Wq, Wk, Wv, Wo, B, S, H, d, tp, causal, d ** -0.5)
+            _close(Z, Zt, 1e-12, f"block output tp={tp} causal={causal}")
+            dX = np.zeros_like(X)
+            w = H // tp * d
+            for i in range(tp):
+                g = at.tp_attn_block_bwd_shard(X, Wq, Wk, Wv, Wo, dZ, B, S, H, d, tp, i, causal, d ** -0.5)
+                dX += g["dX"]
+                c = slice(i * w, (i + 1) * w)
+                for k, Wt in enumerate(dWt[:3]):
+                    _close(g["dWqkv"][:, k * w:(k + 1) * w], Wt[:, c], 1e-11, f"dW{'qkv'[k]} shard {i}/{tp}")
+                _close(g["dWo"], dWt[3][c, :], 1e-11, f"dWo shard {i}/{tp}")
+            _close(dX, dXt, 1e-11, f"sum of dX partials tp={tp} causal={causal}")
+
+
 ALL_PINS = [pin_vs_torch_sdpa, pin_closed_forms, pin_brute_force, pin_finite_differences, pin_heads_independent,
-            pin_online_softmax_and_rows]
+            pin_online_softmax_and_rows, pin_block_vs_torch_mha]

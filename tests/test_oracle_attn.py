@@ -18,6 +18,10 @@ MUTATIONS = {
     "dS_missing_D": ("\n    dS = P * (dP - D)\n", "\n    dS = P * dP\n"),
     "heads_interleaved": ("return M.reshape(batch, seq, heads, d).transpose(0, 2, 1, 3)",
                           "return M.reshape(batch, seq, d, heads).transpose(0, 3, 1, 2)"),
+    "block_shard_by_heads_not_columns": ("return slice(i * w, (i + 1) * w)",
+                                         "return slice(i * (heads // tp), i * (heads // tp) + w)"),
+    "block_dO_from_Wo_columns": ("dO = dZ @ Wo_i.T", "dO = dZ @ np.asarray(Wo, dtype=np.float64)[:, c].T"),
+    "block_dX_from_queries_only": ('"dX": dQKV @ Wqkv.T', '"dX": dQKV[:, :w] @ Wqkv[:, :w].T'),
 }
 
 
