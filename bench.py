@@ -94,12 +94,40 @@ ROLE_UNITS = {
 }
 
 
+def attn_product_flops(wl, T=None):
+    """Flops of one score-sized product (Q K^T, P V, ...) over the shard's heads:
+    2 * d per unmasked (query, key) pair, causal, one sequence of T tokens."""
+    T = wl.T if T is None else T
+    return 2.0 * (T * (T + 1) / 2) * wl.head_dim * (wl.heads // wl.tp)
+
+
+def proj_role_flops(wl, T=None):
+    """The head-sharded attention block's kernels.  Each attention kernel counts
+    the products its own outputs need: the forward 2 (S, PV); the dK/dV kernel
+    4 (S and dP recomputed, dV, dK); the dQ kernel 3 (S, dP, dQ)."""
+    T = wl.T if T is None else T
+    w = wl.heads // wl.tp * wl.head_dim
+    pm = attn_product_flops(wl, T)
+    g = 2.0 * T * wl.h * w
+    return {"gemm.attn_qkv": 3 * g, "attn_fwd": 2 * pm, "gemm.attn_out": g, "gemm.attn_out_dgrad": g,
+            "gemm.attn_out_wgrad": g, "attn_bwd_dkdv": 4 * pm, "attn_bwd_dq": 3 * pm, "gemm.attn_qkv_wgrad": 3 * g,
+            "gemm.attn_qkv_dgrad": 3 * g}
+
+
 def role_flops(wl, role):
+    if wl.kind == "proj":
+        return proj_role_flops(wl).get(role, 0.0)
     return ROLE_UNITS[wl.kind][role] * 2.0 * wl.T * wl.h * wl.Fs
 
 
-def step_flops(wl):
-    return sum(ROLE_UNITS[wl.kind].values()) * 2.0 * wl.T * wl.h * wl.Fs
+def step_flops(wl, T=None):
+    """Algorithmic flops of one step.  The attention backward counts 5 products
+    (S, dP, dV, dK, dQ), whatever the kernels recompute."""
+    if wl.kind == "proj":
+        r = proj_role_flops(wl, T)
+        return sum(v for k, v in r.items() if k.startswith("gemm.")) + 7 * attn_product_flops(wl, T)
+    T = wl.T if T is None else T
+    return sum(ROLE_UNITS[wl.kind].values()) * 2.0 * T * wl.h * wl.Fs
 
 
 def algorithmic_bytes(wl, role):
@@ -116,7 +144,26 @@ def algorithmic_bytes(wl, role):
             "gemm.swiglu_dgrad_act": T * h * 2 + Fs * h * 2 + T * 2 * Fs * 2 + T * 2 * Fs * 2,
             "gemm.swiglu_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
             "gemm.swiglu_wgrad1": T * h * 2 + T * 2 * Fs * 2 + h * 2 * Fs * 4,
-            "gemm.swiglu_dgrad1": T * 2 * Fs * 2 + h * 2 * Fs * 2 + T * h * 4}.get(role)
+            "gemm.swiglu_dgrad1": T * 2 * Fs * 2 + h * 2 * Fs * 2 + T * h * 4}.get(role) if wl.kind != "proj" \
+        else _proj_bytes(wl, role)
+
+
+def _proj_bytes(wl, role):
+    T, h = wl.T, wl.h
+    hs = wl.heads // wl.tp
+    w = hs * wl.head_dim
+    return {"gemm.attn_qkv": T * h * 2 + h * 3 * w * 2 + T * 3 * w * 2,
+            "gemm.attn_out": T * w * 2 + w * h * 2 + T * h * 4,
+            "gemm.attn_out_dgrad": T * h * 2 + w * h * 2 + T * w * 2,
+            "gemm.attn_out_wgrad": T * w * 2 + T * h * 2 + w * h * 4,
+            "gemm.attn_qkv_wgrad": T * h * 2 + T * 3 * w * 2 + h * 3 * w * 4,
+            "gemm.attn_qkv_dgrad": T * 3 * w * 2 + h * 3 * w * 2 + T * h * 4,
+            # Q, K, V in, O out, lse out
+            "attn_fwd": T * 3 * w * 2 + T * w * 2 + T * hs * 4,
+            # Q, K, V, dO, lse, D in; dK, dV out
+            "attn_bwd_dkdv": T * 4 * w * 2 + 2 * T * hs * 4 + T * 2 * w * 2,
+            # Q, K, V, dO, lse, D in; dQ out
+            "attn_bwd_dq": T * 4 * w * 2 + 2 * T * hs * 4 + T * w * 2}.get(role)
 
 
 def cpu_baseline(wl, raw, target_s: float):
@@ -131,6 +178,8 @@ def cpu_baseline(wl, raw, target_s: float):
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
     Fs = wl.Fs
+    if wl.kind == "proj":
+        return _cpu_baseline_proj(wl, raw, target_s, threads)
     if wl.kind == "swiglu":
         W_gu = sw.pack_shard(synth.to_f64(raw["W_gate"], wl.dtype), synth.to_f64(raw["W_up"], wl.dtype), wl.tp, 0)
         Wd = synth.to_f64(raw["W_down"][:Fs], wl.dtype)
@@ -177,6 +226,35 @@ def cpu_baseline(wl, raw, target_s: float):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle, shard 0 fwd+bwd on the first {rows} of {wl.T} token rows "
                       f"(h={wl.h}, F/tp={Fs}); {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
+            "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def _cpu_baseline_proj(wl, raw, target_s, threads):
+    """The attention block oracle (shard 0 fwd+bwd) on a causal sequence made of
+    the first rows tokens; the flops use the same count at that length."""
+    import synth
+    from oracle import attn as oat
+    W = {n: synth.to_f64(raw[n], wl.dtype) for n in ("Wq", "Wk", "Wv", "Wo")}
+
+    def run(rows):
+        X = synth.to_f64(raw["X"][:rows], wl.dtype)
+        dZ = synth.to_f64(raw["dOut"][:rows], wl.dtype)
+        t0 = time.perf_counter()
+        oat.tp_attn_block_bwd_shard(X, W["Wq"], W["Wk"], W["Wv"], W["Wo"], dZ, 1, rows, wl.heads, wl.head_dim,
+                                    wl.tp, 0, True, wl.head_dim ** -0.5)
+        return time.perf_counter() - t0
+
+    probe = min(wl.T, 128)
+    dt = run(probe)
+    rows = int(min(wl.T, max(probe, probe * target_s / max(dt, 1e-3))))
+    rows = max(probe, rows - rows % 8)
+    dt = run(rows)
+    flops = step_flops(wl, rows)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle, shard 0 fwd+bwd of the attention block on a causal sequence of the "
+                      f"first {rows} of {wl.T} tokens (h={wl.h}, {wl.heads // wl.tp} heads); {dt:.2f} s for "
+                      f"{flops / 1e9:.1f} GFLOP",
             "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
@@ -360,8 +438,66 @@ class SPStep:
                          dRes=s.dOut[b], stream=s.stream)
 
 
+class AttnBlockStep:
+    """The head-sharded attention block, shard 0's step: tp_attn_fwd (QKV
+    projection, causal attention over its heads, O-projection partial), its
+    share of the partial sum of the output, tp_attn_bwd, its share of the
+    partial sum of dX.  The other shards' partials are computed once."""
+
+    def __init__(self, wl, raw, tl, torch):
+        self.wl, self.tl = wl, tl
+        T, h, tp = wl.T, wl.h, wl.tp
+        hs = wl.heads // tp
+        w = hs * wl.head_dim
+        dev = torch.device("cuda:0")
+        bf = torch.bfloat16
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(bf).to(dev)
+
+        self.stream = torch.cuda.current_stream(dev)
+        self.X, self.dZ = up(raw["X"]), up(raw["dOut"])
+        self.Wqkv = [up(np.concatenate([raw[n][:, i * w:(i + 1) * w] for n in ("Wq", "Wk", "Wv")], axis=1))
+                     for i in range(tp)]
+        self.Wo = [up(raw["Wo"][i * w:(i + 1) * w]) for i in range(tp)]
+        self.QKV = torch.empty((T, 3 * w), dtype=bf, device=dev)
+        self.O = torch.empty((T, w), dtype=bf, device=dev)
+        self.lse = torch.empty((hs, T), dtype=torch.float32, device=dev)
+        self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.dXp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.rows = T // tp
+        self.Zsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dXsum = torch.empty((self.rows, h), dtype=torch.float32, device=dev)
+        self.dWqkv = torch.empty((h, 3 * w), dtype=torch.float32, device=dev)
+        self.dWo = torch.empty((w, h), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(tl.tp_attn_bwd_workspace_bytes(1, T, wl.heads, tp), dtype=torch.uint8, device=dev)
+        for i in range(1, tp):
+            self.fwd(i)
+            self.bwd(i)
+
+    def fwd(self, i):
+        s = self
+        s.tl.tp_attn_fwd(s.X, s.Wqkv[i], s.Wo[i], s.QKV, s.O, s.lse, s.Zp[i], 1, s.wl.T, s.wl.heads, s.wl.tp,
+                         causal=True, stream=s.stream)
+
+    def bwd(self, i):
+        s = self
+        s.tl.tp_attn_bwd(s.X, s.Wqkv[i], s.Wo[i], s.QKV, s.O, s.lse, s.dZ, s.dXp[i], s.dWqkv, s.dWo, 1, s.wl.T,
+                         s.wl.heads, s.wl.tp, causal=True, workspace=s.ws, stream=s.stream)
+
+    def __call__(self):
+        s = self
+        s.fwd(0)
+        s.tl.shard_partial_sum(s.Zp[:, :s.rows], s.Zsum, stream=s.stream)
+        s.bwd(0)
+        s.tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
+
+
 def make_step(wl, tl, torch):
     import synth
+    if wl.kind == "proj":
+        raw = synth.proj_inputs(wl, which=("X", "Wq", "Wk", "Wv", "Wo", "dOut"))
+        return raw, AttnBlockStep(wl, raw, tl, torch)
     if wl.kind == "sp_mlp":
         raw = synth.sp_inputs(wl)
         return raw, SPStep(wl, raw, tl, torch)
@@ -407,6 +543,13 @@ def workload_text(wl):
             "llama7b_sp_bf16": "the Llama-7B-scale MLP inside the sequence-parallel region (LayerNorm before it, "
                                "dropout p=0.1 and the residual after it, T/tp rows of the residual stream per GPU)",
             }.get(wl.name, "the MLP")
+    if wl.kind == "proj":
+        hs = wl.heads // tp
+        return (f"{wl.name}: one shard of the head-sharded attention block, T={T} tokens (one causal sequence), "
+                f"h={h}, {wl.heads} heads of {wl.head_dim}, tp={tp} ({hs} heads per shard): fused QKV projection "
+                f"{h}x{3 * hs * wl.head_dim}, flash attention, O projection {hs * wl.head_dim}x{h} into an fp32 "
+                f"partial; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums; bf16 storage, "
+                f"fp32 accumulate")
     return (f"{wl.name}: one shard of {what}, T={T} tokens, h={h}, F={F}, tp={tp} (F/tp={Fs}), bf16 storage, "
             f"fp32 accumulate; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums")
 
@@ -488,7 +631,7 @@ def run_bench(args):
         entry = {"kernel": sym, "mean_us": round(us, 2)}
         if clocks:
             entry["sclk_ghz"] = round(sum(clocks) / len(clocks), 3)
-        if role.startswith("gemm"):
+        if role.startswith("gemm") or role_flops(wl, role):
             entry["tflops"] = round(role_flops(wl, role) / (us * 1e-6) / 1e12, 1)
         elif role == "partial_sum":
             entry["gbs"] = round((tp + 1) * step.rows * h * 4 / (us * 1e-6) / 1e9, 1)
@@ -497,7 +640,8 @@ def run_bench(args):
     out = {
         "metric": {"mlp": "TFLOP/s and % of bf16 MFMA peak for TP-sharded MLP fwd+bwd",
                    "swiglu": "TFLOP/s and % of bf16 MFMA peak for TP-sharded gated MLP (SwiGLU) fwd+bwd",
-                   "sp_mlp": "TFLOP/s and % of bf16 MFMA peak for the TP+SP MLP block fwd+bwd"}[wl.kind],
+                   "sp_mlp": "TFLOP/s and % of bf16 MFMA peak for the TP+SP MLP block fwd+bwd",
+                   "proj": "TFLOP/s and % of bf16 MFMA peak for the head-sharded attention block fwd+bwd"}[wl.kind],
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

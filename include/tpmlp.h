@@ -316,6 +316,46 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
              int64_t ldo, const void* dO, int64_t lddo, const float* lse, void* dQ, int64_t lddq, void* dK,
              int64_t lddk, void* dV, int64_t lddv, void* workspace, size_t workspace_bytes);
 
+/* ---- Head-sharded attention block ----------------------------------------
+ * One shard of the attention block whose heads are split over tp_size GPUs
+ * [csdn 1.2.2 Self-Attention 模块的张量并行; zouht 2.2.1 多头注意力机制;
+ * wangyu 注意力机制中的张量并行]: shard i owns heads [i*H/tp, (i+1)*H/tp),
+ * i.e. columns c = [i*w, (i+1)*w), w = H/tp * head_dim, of each of the
+ * projections Wq, Wk, Wv (a column split) and rows c of Wo (a row split); the
+ * block output is the sum over shards of Z_i = O_i Wo[c, :].  No biases, bf16
+ * storage, fp32 accumulation, head_dim 128, heads % tp_size == 0.
+ *   X            [T, h] (ld h), T = batch * seq token rows
+ *   Wqkv_shard   [h, 3w] (ld 3w) = [Wq[:, c] | Wk[:, c] | Wv[:, c]]
+ *   Wo_shard     [w, h] (ld h) = Wo[c, :]
+ *   QKV_save     [T, 3w] (ld 3w) bf16: X Wqkv_shard, kept for the backward
+ *   O_save       [T, w] (ld w) bf16: the attention output of the shard's heads
+ *   lse          [H/tp, T] fp32: log-sum-exp of each query row (as attn_fwd)
+ *   Z_partial    [T, h] fp32 (ld h): this shard's partial of the output
+ * causal and scale as in attn_fwd. */
+int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
+                int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
+                void* QKV_save, void* O_save, float* lse, float* Z_partial);
+
+/* Bytes of device workspace tp_attn_bwd needs (0 on bad args). */
+size_t tp_attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int head_dim, int tp_size);
+
+/* Backward of tp_attn_fwd for the gradient dZ [T, h] (bf16, ld h) of the
+ * block output, which every shard receives whole [wangyu 按行切分, backward]:
+ * dO = dZ Wo_shard^T, dWo_shard = O^T dZ, the attention backward gives dQKV,
+ * dWqkv_shard = X^T dQKV and dX_partial = dQKV Wqkv_shard^T (the sum over
+ * shards is dX [wangyu 按列切分, backward]).
+ *   dX_partial   [T, h] fp32 (ld h)
+ *   dWqkv_shard  [h, 3w] fp32 (ld 3w), the packed order of Wqkv_shard
+ *   dWo_shard    [w, h] fp32 (ld h)
+ * X, the weights, QKV_save, O_save and lse as passed to / written by
+ * tp_attn_fwd.  workspace: at least tp_attn_bwd_workspace_bytes() bytes,
+ * 256-byte aligned, owned by the caller (holds dO, dQKV in bf16 and the
+ * attention backward's row sums). */
+int tp_attn_bwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
+                int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
+                const void* QKV_save, const void* O_save, const float* lse, const void* dZ, float* dX_partial,
+                float* dWqkv_shard, float* dWo_shard, void* workspace, size_t workspace_bytes);
+
 /* Status name, and the calling thread's message for its last non-OK status. */
 const char* tpmlp_status_string(int status);
 const char* tpmlp_last_error(void);

@@ -25,7 +25,7 @@ __all__ = [
     "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
     "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "attn_bwd",
-    "attn_bwd_workspace_bytes", "profile_enable",
+    "attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace_bytes", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -63,13 +63,17 @@ _SIGNATURES = {
     "attn_bwd_workspace_bytes": [_i64, _i64, _int],
     "attn_bwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                  _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz],
+    "tp_attn_fwd": [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_attn_bwd_workspace_bytes": [_i64, _i64, _int, _int, _int],
+    "tp_attn_bwd": [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                    _vp, _vp, _sz],
     "tpmlp_status_string": [_int],
     "tpmlp_last_error": [],
     "tpmlp_version": [],
     "tpmlp_profile_enable": [ctypes.c_char_p],
     "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
 }
-_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_attn_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
              "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
 
 
@@ -354,6 +358,43 @@ def attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, batch: int, seq: int, heads: int, 
                                _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(dO),
                                _ld(dO, w), _ptr(lse), _ptr(dQ), _ld(dQ, w), _ptr(dK), _ld(dK, w), _ptr(dV),
                                _ld(dV, w), _ptr(workspace), workspace.numel()))
+
+
+def tp_attn_fwd(X, Wqkv_shard, Wo_shard, QKV_save, O_save, lse, Z_partial, batch: int, seq: int, heads: int,
+                tp_size: int, causal: bool = True, scale: Optional[float] = None, head_dim: int = 128,
+                stream=None) -> None:
+    """One shard of the head-sharded attention block (contiguous tensors; heads = all heads of the layer)."""
+    h = X.shape[1]
+    sc = head_dim ** -0.5 if scale is None else scale
+    for n, t in (("X", X), ("Wqkv_shard", Wqkv_shard), ("Wo_shard", Wo_shard), ("QKV_save", QKV_save),
+                 ("O_save", O_save), ("lse", lse), ("Z_partial", Z_partial)):
+        _require_contiguous(n, t)
+    _check(_get_lib().tp_attn_fwd(_stream(stream, X), batch, seq, h, heads, head_dim, tp_size, int(bool(causal)), sc,
+                                  _ptr(X), _ptr(Wqkv_shard), _ptr(Wo_shard), _ptr(QKV_save), _ptr(O_save), _ptr(lse),
+                                  _ptr(Z_partial)))
+
+
+def tp_attn_bwd_workspace_bytes(batch: int, seq: int, heads: int, tp_size: int, head_dim: int = 128) -> int:
+    return int(_get_lib().tp_attn_bwd_workspace_bytes(batch, seq, heads, head_dim, tp_size))
+
+
+def tp_attn_bwd(X, Wqkv_shard, Wo_shard, QKV_save, O_save, lse, dZ, dX_partial, dWqkv_shard, dWo_shard,
+                batch: int, seq: int, heads: int, tp_size: int, causal: bool = True, scale: Optional[float] = None,
+                workspace=None, head_dim: int = 128, stream=None) -> None:
+    """Backward of tp_attn_fwd for dZ; workspace a device uint8 tensor (allocated here if None)."""
+    h = X.shape[1]
+    sc = head_dim ** -0.5 if scale is None else scale
+    for n, t in (("X", X), ("Wqkv_shard", Wqkv_shard), ("Wo_shard", Wo_shard), ("QKV_save", QKV_save),
+                 ("O_save", O_save), ("lse", lse), ("dZ", dZ), ("dX_partial", dX_partial),
+                 ("dWqkv_shard", dWqkv_shard), ("dWo_shard", dWo_shard)):
+        _require_contiguous(n, t)
+    if workspace is None:
+        workspace = torch.empty(max(1, tp_attn_bwd_workspace_bytes(batch, seq, heads, tp_size, head_dim)),
+                                dtype=torch.uint8, device=X.device)
+    _check(_get_lib().tp_attn_bwd(_stream(stream, X), batch, seq, h, heads, head_dim, tp_size, int(bool(causal)), sc,
+                                  _ptr(X), _ptr(Wqkv_shard), _ptr(Wo_shard), _ptr(QKV_save), _ptr(O_save), _ptr(lse),
+                                  _ptr(dZ), _ptr(dX_partial), _ptr(dWqkv_shard), _ptr(dWo_shard), _ptr(workspace),
+                                  workspace.numel()))
 
 
 def profile_enable(filter: Optional[str] = "") -> None:

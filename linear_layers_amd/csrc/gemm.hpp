@@ -300,8 +300,10 @@ gemm_kernel(const GemmArgs p) {
           for (int v = 0; v < 16; ++v) {
             const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lchunk + (v & 3);
             if (row < M) {
-              const float hv = Elem<T>::load(Hs + (int64_t)row * p.ldh + col);
-              const float d = acc[i][j][v] * (p.act == kActGeluTanh ? gelu_tanh_grad(hv) : 1.0f);
+              // H is read only for the GeLU derivative: with no activation it may be NULL.
+              const float d = p.act == kActGeluTanh
+                                  ? acc[i][j][v] * gelu_tanh_grad(Elem<T>::load(Hs + (int64_t)row * p.ldh + col))
+                                  : acc[i][j][v];
               Elem<T>::store(Y + (int64_t)row * p.ldy + col, d);
               cs += d;
             }

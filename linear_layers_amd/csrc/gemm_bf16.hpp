@@ -625,13 +625,17 @@ gemm_bf16_kernel(const GemmArgs p) {
               const int cq = c + 8 * q + 4 * h;
               float d[4] = {0.f, 0.f, 0.f, 0.f};
               if (row < M && cq < N) {
-                const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
-                const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
+                if constexpr (kGelu) {   // with no activation H is not read (it may be NULL)
+                  const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
+                  const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  d[e] = kGelu ? acc[i][j][4 * g + e] * gelu_tanh_grad(hv[e]) : acc[i][j][4 * g + e];
-                  csum[q][e] += d[e];
+                  for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e] * gelu_tanh_grad(hv[e]);
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e];
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) csum[q][e] += d[e];
               }
               dw[q][0] = pack_bf16x2(d[0], d[1]);
               dw[q][1] = pack_bf16x2(d[2], d[3]);

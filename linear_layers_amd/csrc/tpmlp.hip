@@ -1019,6 +1019,125 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
                 dim3((unsigned)((seq + kAttnBQ - 1) / kAttnBQ), (unsigned)heads, (unsigned)batch), dim3(256), s, a);
 }
 
+// ------------------------------------------- head-sharded attention block --
+namespace {
+struct AttnBlockDims {
+  int64_t T, w, hs;
+};
+
+int check_attn_block(int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size, int causal,
+                     float scale, AttnBlockDims* d) {
+  TPMLP_TRY(check_attn(batch, seq, heads, head_dim, causal, scale));
+  TPMLP_TRY(check_split("heads", heads, tp_size));
+  TPMLP_TRY(check_dim("h", h));
+  d->T = batch * seq;
+  d->hs = heads / tp_size;
+  d->w = d->hs * head_dim;
+  return TPMLP_OK;
+}
+
+struct AttnBlockWs {
+  size_t do_off, dqkv_off, d_off, total;
+};
+
+AttnBlockWs attn_block_ws(int64_t T, int64_t w, int64_t hs) {
+  AttnBlockWs L;
+  L.do_off = 0;
+  L.dqkv_off = align256((size_t)T * w * 2);
+  L.d_off = L.dqkv_off + align256((size_t)T * 3 * w * 2);
+  L.total = L.d_off + align256((size_t)T * hs * sizeof(float));
+  return L;
+}
+}  // namespace
+
+int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
+                int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
+                void* QKV_save, void* O_save, float* lse, float* Z_partial) {
+  AttnBlockDims d;
+  TPMLP_TRY(check_attn_block(batch, seq, h, heads, head_dim, tp_size, causal, scale, &d));
+  const int64_t T = d.T, w = d.w;
+  TPMLP_TRY(check_mat("X", X, T, h, h, 8));
+  TPMLP_TRY(check_mat("Wqkv_shard", Wqkv_shard, h, 3 * w, 3 * w, 8));
+  TPMLP_TRY(check_mat("Wo_shard", Wo_shard, w, h, h, 8));
+  TPMLP_TRY(check_mat("QKV_save", QKV_save, T, 3 * w, 3 * w, 8));
+  TPMLP_TRY(check_mat("O_save", O_save, T, w, w, 8));
+  TPMLP_TRY(check_vec("lse", lse, T * d.hs, true));
+  TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
+  if (T == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  TPMLP_TRY(col_fwd(s, TPMLP_BF16, kActNone, T, h, 3 * w, X, h, Wqkv_shard, 3 * w, nullptr, QKV_save, 3 * w,
+                    nullptr, 0, "gemm.attn_qkv"));
+  const bf16_t* qkv = static_cast<const bf16_t*>(QKV_save);
+  TPMLP_TRY(attn_fwd(stream, batch, seq, (int)d.hs, head_dim, causal, scale, qkv, 3 * w, qkv + w, 3 * w,
+                     qkv + 2 * w, 3 * w, O_save, w, lse));
+  return row_fwd(s, TPMLP_BF16, T, w, h, O_save, w, Wo_shard, h, Z_partial, h, "gemm.attn_out");
+}
+
+size_t tp_attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int head_dim, int tp_size) {
+  if (batch < 0 || seq < 0 || heads < 1 || head_dim != kAttnD || tp_size < 1 || heads % tp_size != 0 ||
+      batch * seq > kMaxDim)
+    return 0;
+  const int64_t hs = heads / tp_size;
+  return attn_block_ws(batch * seq, hs * head_dim, hs).total;
+}
+
+int tp_attn_bwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
+                int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
+                const void* QKV_save, const void* O_save, const float* lse, const void* dZ, float* dX_partial,
+                float* dWqkv_shard, float* dWo_shard, void* workspace, size_t workspace_bytes) {
+  AttnBlockDims d;
+  TPMLP_TRY(check_attn_block(batch, seq, h, heads, head_dim, tp_size, causal, scale, &d));
+  const int64_t T = d.T, w = d.w;
+  TPMLP_TRY(check_mat("X", X, T, h, h, 8));
+  TPMLP_TRY(check_mat("Wqkv_shard", Wqkv_shard, h, 3 * w, 3 * w, 8));
+  TPMLP_TRY(check_mat("Wo_shard", Wo_shard, w, h, h, 8));
+  TPMLP_TRY(check_mat("QKV_save", QKV_save, T, 3 * w, 3 * w, 8));
+  TPMLP_TRY(check_mat("O_save", O_save, T, w, w, 8));
+  TPMLP_TRY(check_vec("lse", lse, T * d.hs, true));
+  TPMLP_TRY(check_mat("dZ", dZ, T, h, h, 8));
+  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
+  TPMLP_TRY(check_mat("dWqkv_shard", dWqkv_shard, h, 3 * w, 3 * w, 4));
+  TPMLP_TRY(check_mat("dWo_shard", dWo_shard, w, h, h, 4));
+  const AttnBlockWs L = attn_block_ws(T, w, d.hs);
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    TPMLP_TRY(fill_zero(dWqkv_shard, h, 3 * w, 3 * w, s));
+    return fill_zero(dWo_shard, w, h, h, s);
+  }
+  if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  bf16_t* dO = reinterpret_cast<bf16_t*>(ws + L.do_off);
+  bf16_t* dqkv = reinterpret_cast<bf16_t*>(ws + L.dqkv_off);
+  // dO = dZ Wo_i^T, straight to bf16 (no activation, so no pre-activation is read).
+  GemmArgs a = gemm_args(dZ, h, Wo_shard, h, T, w, h);
+  a.Y = dO;
+  a.ldy = w;
+  TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.attn_out_dgrad", TPMLP_BF16, a, s)));
+  // dWo_i = O^T dZ
+  a = gemm_args(O_save, w, dZ, h, w, h, T);
+  a.C = dWo_shard;
+  a.ldc = h;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.attn_out_wgrad", TPMLP_BF16, a, s)));
+  const bf16_t* qkv = static_cast<const bf16_t*>(QKV_save);
+  TPMLP_TRY(attn_bwd(stream, batch, seq, (int)d.hs, head_dim, causal, scale, qkv, 3 * w, qkv + w, 3 * w,
+                     qkv + 2 * w, 3 * w, O_save, w, dO, w, lse, dqkv, 3 * w, dqkv + w, 3 * w, dqkv + 2 * w, 3 * w,
+                     ws + L.d_off, L.total - L.d_off));
+  // dWqkv_i = X^T dQKV
+  a = gemm_args(X, h, dqkv, 3 * w, h, 3 * w, T);
+  a.C = dWqkv_shard;
+  a.ldc = 3 * w;
+  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.attn_qkv_wgrad", TPMLP_BF16, a, s)));
+  // dX_i = dQKV Wqkv_i^T
+  a = gemm_args(dqkv, 3 * w, Wqkv_shard, 3 * w, T, h, 3 * w);
+  a.C = dX_partial;
+  a.ldc = h;
+  return run_gemm<true, true, kEpiF32>("gemm.attn_qkv_dgrad", TPMLP_BF16, a, s);
+}
+
 int tpmlp_profile_enable(const char* filter) {
   Profiler& P = prof();
   std::lock_guard<std::mutex> lk(P.mu);

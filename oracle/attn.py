@@ -111,6 +111,29 @@ def attn_fwd_rows(Q, K, V, batch: int, seq: int, heads: int, d: int, causal: boo
     return {"O": np.matmul(E / l, v), "lse": (m + np.log(l))[:, 0]}
 
 
+def attn_bwd_rows(Q, K, V, dO, batch: int, seq: int, heads: int, d: int, causal: bool, scale: float,
+                  b: int, h: int, rows) -> Dict[str, np.ndarray]:
+    """dQ, dK, dV at positions ``rows`` of one (batch, head), at full sequence
+    length.  The same sums as attn_bwd restricted to those rows: a dQ row
+    needs its own row of P and dP; a dK or dV row needs the column of P and
+    dP at that key, i.e. every query's log-sum-exp and D."""
+    rows = np.asarray(rows)
+    q, k, v, do = (_heads(M, batch, seq, heads, d)[b, h] for M in (Q, K, V, dO))
+    f = attn_fwd(q, k, v, 1, seq, 1, d, causal, scale)
+    lse, o = f["lse"][0], f["O"]
+    D = (do * o).sum(axis=1)
+    pos = np.arange(seq)
+    Sr = np.matmul(q[rows], k.T) * scale
+    Sc = np.matmul(q, k[rows].T) * scale
+    if causal:
+        Sr = np.where(pos[None, :] > rows[:, None], -np.inf, Sr)
+        Sc = np.where(rows[None, :] > pos[:, None], -np.inf, Sc)
+    Pr = np.exp(Sr - lse[rows][:, None])
+    dSr = Pr * (np.matmul(do[rows], v.T) - D[rows][:, None])
+    Pc = np.exp(Sc - lse[:, None])
+    dSc = Pc * (np.matmul(do, v[rows].T) - D[:, None])
+    return {"dQ": np.matmul(dSr, k) * scale, "dK": np.matmul(dSc.T, q) * scale, "dV": np.matmul(Pc.T, do)}
+
 def _shard_cols(heads: int, d: int, tp: int, i: int) -> slice:
     if heads % tp:
         raise ValueError(f"heads={heads} is not divisible by tp={tp}")

@@ -149,6 +149,16 @@ def pin_online_softmax_and_rows(at):
     fr = at.attn_fwd_rows(Q, K, V, B, S, H, d, True, scale, 0, 0, rows)
     _close(fr["O"], f["O"][rows], 1e-13, "rows view")
     _close(fr["lse"], f["lse"][0][rows], 1e-13, "rows lse")
+    # sampled backward rows against the whole backward, two sequences and two heads
+    B, S, H = 2, 23, 2
+    Q, K, V, dO = _case(9, B, S, H, d)
+    for causal in (False, True):
+        g = at.attn_bwd(Q, K, V, dO, B, S, H, d, causal, scale)
+        for b, hd, rr in ((0, 1, [0, 7, 22]), (1, 0, [3, 4, 21])):
+            gr = at.attn_bwd_rows(Q, K, V, dO, B, S, H, d, causal, scale, b, hd, rr)
+            idx = [b * S + r for r in rr]
+            for k in ("dQ", "dK", "dV"):
+                _close(gr[k], g[k][idx, hd * d:(hd + 1) * d], 1e-12, f"rows view {k} causal={causal}")
 
 
 def _block_case(seed, B, S, H, d):

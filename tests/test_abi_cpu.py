@@ -166,3 +166,20 @@ def test_attn_validation():
     assert b(*args, P + 16, 1 << 20) == E_ALIGN
     args[15] = None   # lse is required by the backward
     assert b(*args, P, 1 << 20) == E_NULL
+
+
+def test_attn_block_validation():
+    f = tl.lib.tp_attn_fwd
+    # (stream, batch, seq, h, heads, head_dim, tp, causal, scale, X, Wqkv, Wo, QKV, O, lse, Z): refused on the host
+    assert f(None, 1, 8, 512, 4, 128, 3, 1, 0.1, P, P, P, P, P, P, P) == E_DIV       # 4 heads over 3 shards
+    assert f(None, 1, 8, 512, 4, 64, 2, 1, 0.1, P, P, P, P, P, P, P) == E_SHAPE      # head_dim 64
+    assert f(None, 1, 8, 512, 4, 128, 2, 3, 0.1, P, P, P, P, P, P, P) == E_VALUE     # causal not 0/1
+    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, None, P) == E_NULL   # lse required
+    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P + 8, P, P, P, P) == E_ALIGN
+    assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 3) == 0
+    assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 2) >= 8 * 256 * 2 * 4
+    b = tl.lib.tp_attn_bwd
+    args = [None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, P, P, P, P, P]
+    assert b(*args, P, 16) == E_WS
+    assert b(*args, None, 1 << 20) == E_NULL
+    assert b(*args, P + 16, 1 << 20) == E_ALIGN

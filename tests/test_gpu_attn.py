@@ -28,9 +28,9 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _lse_close(got, want, what):
+def _lse_close(got, want, what, tol=1e-4):
     err = np.abs(np.asarray(got) - want) / np.maximum(1.0, np.abs(want))
-    assert np.all(np.isfinite(got)) and err.max() <= 1e-4, f"{what}: lse error {err.max():.3e}"
+    assert np.all(np.isfinite(got)) and err.max() <= tol, f"{what}: lse error {err.max():.3e}"
 
 
 def _qkv(seed, T, heads, std=1.0):
@@ -172,3 +172,114 @@ def test_attn_bwd_workload_two_heads():
         assert_close(g[:, :w][:, cs], ref["dQ"], "bf16", f"dQ head {hd}")
         assert_close(g[:, w:2 * w][:, cs], ref["dK"], "bf16", f"dK head {hd}")
         assert_close(g[:, 2 * w:][:, cs], ref["dV"], "bf16", f"dV head {hd}")
+
+
+# ----------------------------------------------------------------------------
+# The head-sharded attention block: QKV projection, attention over the shard's
+# heads, O-projection partial, and its backward, through tp_attn_fwd/bwd.
+
+def _block_run(raw, batch, seq, heads, tp, i, causal):
+    """Shard i of the block on the GPU; returns every output as a device tensor."""
+    T, h = raw["X"].shape
+    w = heads // tp * D
+    c = slice(i * w, (i + 1) * w)
+    Wqkv = np.ascontiguousarray(np.concatenate([raw[n][:, c] for n in ("Wq", "Wk", "Wv")], axis=1))
+    X, Wq, Wo, dZ = (to_dev(a, "bf16") for a in (raw["X"], Wqkv, np.ascontiguousarray(raw["Wo"][c]), raw["dZ"]))
+    out = {"QKV": empty((T, 3 * w), "bf16"), "O": empty((T, w), "bf16"), "lse": empty_f32((heads // tp, T)),
+           "Z": empty_f32((T, h)), "dX": empty_f32((T, h)), "dWqkv": empty_f32((h, 3 * w)),
+           "dWo": empty_f32((w, h))}
+    tl.tp_attn_fwd(X, Wq, Wo, out["QKV"], out["O"], out["lse"], out["Z"], batch, seq, heads, tp, causal=causal)
+    tl.tp_attn_bwd(X, Wq, Wo, out["QKV"], out["O"], out["lse"], dZ, out["dX"], out["dWqkv"], out["dWo"], batch, seq,
+                   heads, tp, causal=causal)
+    sync()
+    return out
+
+
+@pytest.mark.parametrize("batch,seq,heads,tp,shard,causal", [(2, 77, 4, 2, 1, True), (1, 200, 2, 1, 0, False),
+                                                             (3, 64, 4, 4, 3, True)])
+def test_attn_block_small(batch, seq, heads, tp, shard, causal):
+    need_gpu()
+    _say(f"attn block batch={batch} seq={seq} heads={heads} tp={tp} shard={shard} causal={causal}")
+    T, h = batch * seq, heads * D
+    r = np.random.default_rng(seq + 7 * heads)
+    raw = {"X": synth.bf16_round_bits(r.standard_normal((T, h)).astype(np.float32)),
+           "dZ": synth.bf16_round_bits(r.standard_normal((T, h)).astype(np.float32))}
+    for n in ("Wq", "Wk", "Wv", "Wo"):
+        raw[n] = synth.bf16_round_bits((r.standard_normal((h, h)) / np.sqrt(h)).astype(np.float32))
+    g = _block_run(raw, batch, seq, heads, tp, shard, causal)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    ref = oat.tp_attn_block_bwd_shard(f["X"], f["Wq"], f["Wk"], f["Wv"], f["Wo"], f["dZ"], batch, seq, heads, D, tp,
+                                      shard, causal, D ** -0.5)
+    for k in ("QKV", "O", "Z", "dX", "dWqkv", "dWo"):
+        assert_close(to_f64(g[k]), ref[k], "bf16", k)
+    _block_lse_close(to_f64(g["lse"]), ref["QKV"], ref["lse"], batch, seq, heads // tp, causal)
+
+
+def _block_lse_close(got, QKV, want, batch, seq, hs, causal):
+    """The block's attention reads the bf16-rounded QKV its projection wrote, so
+    each score q.k * scale may move by up to 2^-7 * scale * sum_d |q_d| |k_d|
+    (two roundings of unit 2^-8), and the log-sum-exp, a softmax-weighted
+    mean of those moves, by no more than their maximum over the row's keys;
+    fp32 arithmetic adds the 1e-4 * max(1, |lse|) of the core's own bar."""
+    w = hs * D
+    for b in range(batch):
+        rs = slice(b * seq, (b + 1) * seq)
+        for hd in range(hs):
+            cs = slice(hd * D, (hd + 1) * D)
+            aq, ak = np.abs(QKV[rs, cs]), np.abs(QKV[rs, w:2 * w][:, cs])
+            m = aq @ ak.T
+            if causal:
+                m = np.where(np.tril(np.ones((seq, seq), dtype=bool)), m, 0.0)
+            bound = 2.0 ** -7 * D ** -0.5 * m.max(axis=1) + 1e-4 * np.maximum(1.0, np.abs(want[hd, rs]))
+            err = np.abs(got[hd, rs] - want[hd, rs])
+            assert np.all(np.isfinite(got[hd, rs])) and np.all(err <= bound), \
+                f"lse b={b} head={hd}: worst err/bound {np.max(err / bound):.3f}"
+
+
+@pytest.mark.slow
+def test_attn_block_workload_sampled():
+    """T=4096 (one causal sequence), h=5120, 40 heads of 128, tp=4, shard 0, the workload's own inputs:
+    sampled rows of every output, sampled columns of the weight gradients."""
+    need_gpu()
+    wl = synth.WORKLOADS["attn_proj_bf16"]
+    _say(f"attn block workload {wl.name}")
+    raw = synth.proj_inputs(wl, which=("X", "Wq", "Wk", "Wv", "Wo", "dOut"))
+    raw["dZ"] = raw.pop("dOut")
+    T, heads, tp = wl.T, wl.heads, wl.tp
+    hs, w = heads // tp, heads // tp * D
+    g = _block_run(raw, 1, T, heads, tp, 0, True)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    rows = np.array(sorted(set(np.random.default_rng(11).choice(T, 20, replace=False).tolist()) | {0, 127, T - 1}))
+    Wqkv = oat.qkv_shard_weight(f["Wq"], f["Wk"], f["Wv"], heads, D, tp, 0)
+    Wo = f["Wo"][:w]
+    QKV = f["X"] @ Wqkv
+    assert_close(to_f64(g["QKV"][torch.as_tensor(rows, device="cuda")]), QKV[rows], "bf16", "QKV rows")
+    Q, K, V = QKV[:, :w], QKV[:, w:2 * w], QKV[:, 2 * w:]
+    dO = f["dZ"] @ Wo.T
+    O_rows = np.zeros((len(rows), w))
+    dQKV_rows = np.zeros((len(rows), 3 * w))
+    for hd in range(hs):
+        cs = slice(hd * D, (hd + 1) * D)
+        fr = oat.attn_fwd_rows(Q, K, V, 1, T, hs, D, True, D ** -0.5, 0, hd, rows)
+        O_rows[:, cs] = fr["O"]
+        _lse_close(to_f64(g["lse"])[hd, rows], fr["lse"], f"lse head {hd}")
+        br = oat.attn_bwd_rows(Q, K, V, dO, 1, T, hs, D, True, D ** -0.5, 0, hd, rows)
+        for k, name in enumerate(("dQ", "dK", "dV")):
+            dQKV_rows[:, k * w + hd * D:k * w + (hd + 1) * D] = br[name]
+    sel = torch.as_tensor(rows, device="cuda")
+    assert_close(to_f64(g["O"][sel]), O_rows, "bf16", "O rows")
+    assert_close(to_f64(g["Z"][sel]), O_rows @ Wo, "bf16", "Z rows")
+    assert_close(to_f64(g["dX"][sel]), dQKV_rows @ Wqkv.T, "bf16", "dX rows")
+    # weight-gradient columns: dWo needs all of O, dWqkv the whole dQ/dK/dV of head 3
+    cols = np.random.default_rng(12).choice(wl.h, 24, replace=False)
+    O_full = np.concatenate([oat.attn_fwd(Q[:, hd * D:(hd + 1) * D], K[:, hd * D:(hd + 1) * D],
+                                          V[:, hd * D:(hd + 1) * D], 1, T, 1, D, True, D ** -0.5)["O"]
+                             for hd in range(hs)], axis=1)
+    assert_close(to_f64(g["dWo"][:, torch.as_tensor(cols, device="cuda")]), O_full.T @ f["dZ"][:, cols], "bf16",
+                 "dWo cols")
+    cs = slice(3 * D, 4 * D)
+    b3 = oat.attn_bwd(Q[:, cs], K[:, cs], V[:, cs], dO[:, cs], 1, T, 1, D, True, D ** -0.5)
+    for k, name in enumerate(("dQ", "dK", "dV")):
+        qc = k * w + 3 * D + np.array([0, 17, 64, 127])
+        assert_close(to_f64(g["dWqkv"][:, torch.as_tensor(qc, device="cuda")]),
+                     f["X"].T @ b3[name][:, [0, 17, 64, 127]], "bf16", f"dWqkv {name} cols of head 3")
