@@ -23,6 +23,8 @@
 //   fragment needs, the same exchange the GEMM epilogues use for stores.
 #pragma once
 
+#include <utility>
+
 #include "gemm_bf16.hpp"
 
 namespace tpmlp {
@@ -49,6 +51,36 @@ constexpr int kAttnStage = 2 * AttnKTile::BYTES + AttnVTile::BYTES;  // 32 KB
 __device__ __forceinline__ f32x16_t mfma_bf16(const u32x4_t& b, const u32x4_t& a, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b), __builtin_bit_cast(bf16x8_t, a),
                                                   c, 0, 0, 0);
+}
+
+// f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// The same product with the accumulator pinned to accumulation registers
+// (AGPRs) for long-lived sums.  The compiler does not see into the asm, so it
+// covers the hazards itself: NOP_A wait states before the product when `a`
+// may just have been written by a VALU op (which needs 2), and
+// agpr_acc_drain before any VALU read of the sums (the product's passes + 2).
+template <int NOP_A>
+__device__ __forceinline__ void mfma_bf16_agpr(const u32x4_t& b, const u32x4_t& a, f32x16_t& c) {
+  if constexpr (NOP_A > 0)
+    asm volatile("s_nop %3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a), "n"(NOP_A - 1));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+
+// 24 wait states after the last product into any of the sums, ordered before
+// every later use of them.
+__device__ __forceinline__ void agpr_acc_drain(f32x16_t (&x)[4], f32x16_t (&y)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
 }
 
 // Lane-pair exchange of two register groups g0 = (x0, x1) and g1 = (y0, y1),
@@ -334,28 +366,60 @@ struct AttnRowTile {
 };
 
 // acc[f] += B(tile rows as n) x A over the 8 d-substeps: C[m][n] with m from a, n = tile row.
-template <int S, int NF, class Tile>
+// The B fragments of substep S + 2 are read while substep S multiplies, so
+// the LDS latency hides behind the MFMAs.
+template <int NF, int R = 3, class Tile>
 __device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int lane, const u32x4_t (&a)[8],
                                         f32x16_t (&acc)[NF]) {
-  if constexpr (NF >= 1) acc[0] = mfma_bf16(t.template row<0, S>(src, lane), a[S], acc[0]);
-  if constexpr (NF >= 2) acc[1] = mfma_bf16(t.template row<1, S>(src, lane), a[S], acc[1]);
-  if constexpr (S + 1 < 8) mm_rows<S + 1, NF>(t, src, lane, a, acc);
+  static_assert(R == 2 || R == 3, "ring depth in substeps");
+  u32x4_t b[R][NF];
+  auto fetch = [&](auto SC) {
+    constexpr int S = decltype(SC)::value;
+    b[S % R][0] = t.template row<0, S>(src, lane);
+    if constexpr (NF >= 2) b[S % R][1] = t.template row<1, S>(src, lane);
+  };
+  fetch(std::integral_constant<int, 0>{});
+  if constexpr (R == 3) fetch(std::integral_constant<int, 1>{});
+  auto step = [&](auto SC) {
+    constexpr int S = decltype(SC)::value;
+    if constexpr (S + R - 1 < 8) fetch(std::integral_constant<int, S + R - 1>{});
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = mfma_bf16(b[S % R][f], a[S], acc[f]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead: the scheduler would sink them to their use
+  };
+  step(std::integral_constant<int, 0>{});
+  step(std::integral_constant<int, 1>{});
+  step(std::integral_constant<int, 2>{});
+  step(std::integral_constant<int, 3>{});
+  step(std::integral_constant<int, 4>{});
+  step(std::integral_constant<int, 5>{});
+  step(std::integral_constant<int, 6>{});
+  step(std::integral_constant<int, 7>{});
 }
 
-// acc[F] += B(tile rows as k, d block F as n) x A over NT row-substeps of 16.
-template <int T, int NT, class Tile>
+// acc[F] += B(tile rows as k, d block F as n) x A over NT row-substeps of 16,
+// reading the next substep's four B fragments while this one multiplies.
+// The 4 NT products run in the order (T, F); the B fragment of product i + D
+// is read while product i multiplies (a ring of D + 1 fragments).
+template <int NT, bool AGPR = false, int D = 4, class Tile>
 __device__ __forceinline__ void mm_cols(const Tile& t, const lds_char* src, const u32x4_t (&a)[NT],
                                         f32x16_t (&acc)[4]) {
-#pragma unroll
-  for (int F = 0; F < 4; ++F) {
-    u32x4_t b;
-    if (F == 0) b = t.template col<0, T>(src);
-    else if (F == 1) b = t.template col<1, T>(src);
-    else if (F == 2) b = t.template col<2, T>(src);
-    else b = t.template col<3, T>(src);
-    acc[F] = mfma_bf16(b, a[T], acc[F]);
-  }
-  if constexpr (T + 1 < NT) mm_cols<T + 1, NT>(t, src, a, acc);
+  static_assert(NT <= 4 && D >= 1 && D <= 7, "at most 4 row-substeps");
+  constexpr int N = 4 * NT, R = D + 1;
+  u32x4_t b[R];
+  auto fetch = [&](auto IC) {
+    constexpr int I = decltype(IC)::value;
+    if constexpr (I < N) b[I % R] = t.template col<I % 4, I / 4>(src);
+  };
+  static_for<D>(fetch);
+  auto step = [&](auto IC) {
+    constexpr int I = decltype(IC)::value;
+    fetch(std::integral_constant<int, I + D>{});
+    if constexpr (AGPR) mfma_bf16_agpr<(I % 4 == 0) ? 3 : 0>(b[I % R], a[I / 4], acc[I % 4]);  // first use of a[I/4]
+    else acc[I % 4] = mfma_bf16(b[I % R], a[I / 4], acc[I % 4]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead: the scheduler would sink them to their use
+  };
+  static_for<N>(step);
 }
 
 // A fragments of a 32 x 32k block held in accumulator layout (row = lane & 31,
@@ -387,7 +451,21 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16_t (&acc)[4], float 
 
 constexpr int kAttnBwdBQ = 64;   // query rows per block in the key-stationary kernel
 using AttnQTile = AttnRowTile<kAttnBwdBQ, 2>;   // 64 rows, 2 waves load it
-constexpr int kAttnDkvStage = 2 * AttnQTile::BYTES;  // Q and dO: 32 KB
+constexpr int kAttnDkvRows = 2 * AttnQTile::BYTES;        // Q and dO tiles: 32 KB
+constexpr int kAttnDkvStage = kAttnDkvRows + 2 * 256;     // + the block's 64 lse and 64 D values
+
+// 64 consecutive floats (one per lane) from global memory into LDS through the
+// buffer unit; lanes past `nbytes` read zero.
+__device__ __forceinline__ void lds_dma_f32x64(const float* base, uint32_t nbytes, lds_char* dst, int lane) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  const i32x4_t rsrc = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffffu), (int)nbytes, kBufferWord3};
+  const uint32_t voff = (uint32_t)lane * 4u;
+  const uint32_t lds = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 // dK, dV for 64 keys of one head (2 waves x 32 keys), over all query blocks
 // that see them.  K and V rows stay in registers as A fragments.
@@ -422,22 +500,30 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
   ot.init(wave, lane, p.lddo);
   const bf16_t* Qh = p.Q + row_base * p.ldq + head * kAttnD;
   const bf16_t* dOh = p.dO + row_base * p.lddo + head * kAttnD;
+  const float* lse_h = p.lse + (int64_t)head * T + row_base;
+  const float* D_h = p.D + (int64_t)head * T + row_base;
+  // One stage: the query block's Q and dO tiles, then its lse and D values
+  // (wave 0 fetches lse, wave 1 fetches D), all through the LDS DMA so a
+  // single vmcnt wait covers the whole next stage.
   auto issue = [&](int qb, lds_char* dst) {
     const int q0 = qb * kAttnBwdBQ;
     const int rows = min(kAttnBwdBQ, seq - q0);
     qt.load(Qh + (int64_t)q0 * p.ldq, (uint32_t)(((int64_t)(rows - 1) * p.ldq + kAttnD) * 2), dst, wave);
     ot.load(dOh + (int64_t)q0 * p.lddo, (uint32_t)(((int64_t)(rows - 1) * p.lddo + kAttnD) * 2),
             dst + AttnQTile::BYTES, wave);
+    lds_dma_f32x64((wave == 0 ? lse_h : D_h) + q0, (uint32_t)rows * 4u, dst + kAttnDkvRows + 256 * wave, lane);
   };
-  const float* lse_h = p.lse + (int64_t)head * T + row_base;
-  const float* D_h = p.D + (int64_t)head * T + row_base;
   const float log2e = 1.4426950408889634f;
 
   f32x16_t dk[4], dv[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 4; ++f) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) dk[f][v] = dv[f][v] = 0.0f;
+    // Move the sums to accumulation registers once, where the loop keeps them.
+    asm volatile("" : "+a"(dk[f]));
+    asm volatile("" : "+a"(dv[f]));
+  }
 
   const int nqb = (seq + kAttnBwdBQ - 1) / kAttnBwdBQ;
   const int qb0 = p.causal ? k0 / kAttnBwdBQ : 0;
@@ -451,49 +537,74 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     lds_char* nxt = ((qb - qb0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
     if (qb + 1 < nqb) issue(qb + 1, nxt);
     const int q0 = qb * kAttnBwdBQ;
-    // S^T (keys x queries) and dP^T = V dO^T
-    f32x16_t st[2], dpt[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[f][v] = dpt[f][v] = 0.0f;
-    mm_rows<0, 2>(qt, cur, lane, kf, st);
-    mm_rows<0, 2>(ot, cur + AttnQTile::BYTES, lane, vf, dpt);
-    // P^T and dS^T; columns are queries q0 + 32 f + 8 g + 4 h + e
-    float pt[2][16], dst_[2][16];
     const bool edge = q0 + kAttnBwdBQ > seq || (p.causal && q0 < kw0 + 31);
+    const lds_char* lse_s = cur + kAttnDkvRows;
+    const lds_char* d_s = cur + kAttnDkvRows + 256;
+    // Accumulator layout: lane holds key krow and queries q0 + 32 f + 8 g + 4 h + e
+    // in register 4 g + e of block f.  Only one score-sized accumulator is live
+    // at a time: P^T is kept as packed bf16 pairs (pk) for dS.
+    uint32_t pk[2][8];
+    u32x4_t af[4];
+    {
+      f32x16_t sacc[2];   // S^T = K Q^T
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qc = q0 + 32 * f + 8 * g + 4 * h;
-        float l4[4] = {0.f, 0.f, 0.f, 0.f}, d4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < 16; ++v) sacc[f][v] = 0.0f;
+      mm_rows<2>(qt, cur, lane, kf, sacc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)   // scalar loads: head * T + row_base need not be a multiple of 4
-          if (qc + e < seq) {
-            l4[e] = lse_h[qc + e];
-            d4[e] = D_h[qc + e];
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qo = (32 * f + 8 * g + 4 * h) * 4;   // byte offset of the 4 queries in the lse row
+          const f32x4_t l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(lse_s + qo);
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - l4[e] * log2e);
+            if (edge) {
+              const int q = q0 + 32 * f + 8 * g + 4 * h + e;
+              if (q >= seq || krow >= seq || (p.causal && q < krow)) pv[e] = 0.0f;
+            }
           }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g + e;
-          float pv = __builtin_amdgcn_exp2f(st[f][v] * p.scale_log2 - l4[e] * log2e);
-          if (edge) {
-            const int q = qc + e;
-            if (q >= seq || krow >= seq || (p.causal && q < krow)) pv = 0.0f;
-          }
-          pt[f][v] = pv;
-          dst_[f][v] = pv * (dpt[f][v] - d4[e]);
+          pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
+          pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
         }
-      }
-    u32x4_t pa[4], da[4];
-    acc_to_afrag<2>(pt, pa);
-    acc_to_afrag<2>(dst_, da);
-    mm_cols<0, 4>(ot, cur + AttnQTile::BYTES, pa, dv);   // dV += P^T dO
-    mm_cols<0, 4>(qt, cur, da, dk);                      // dK += dS^T Q
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      af[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
+                        pk[t >> 1][4 * (t & 1) + 3]);
+    mm_cols<4, true>(ot, cur + AttnQTile::BYTES, af, dv);   // dV += P^T dO
+    {
+      f32x16_t dacc[2];   // dP^T = V dO^T
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dacc[f][v] = 0.0f;
+      mm_rows<2>(ot, cur + AttnQTile::BYTES, lane, vf, dacc);
+      // dS^T = P^T * (dP^T - D), with P^T from its bf16 copy
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qo = (32 * f + 8 * g + 4 * h) * 4;
+          const f32x4_t d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(d_s + qo);
+          const uint32_t p01 = pk[f][2 * g], p23 = pk[f][2 * g + 1];
+          pk[f][2 * g] = pack_bf16x2(bf16lo(p01) * (dacc[f][4 * g] - d4[0]), bf16hi(p01) * (dacc[f][4 * g + 1] - d4[1]));
+          pk[f][2 * g + 1] =
+              pack_bf16x2(bf16lo(p23) * (dacc[f][4 * g + 2] - d4[2]), bf16hi(p23) * (dacc[f][4 * g + 3] - d4[3]));
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      af[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
+                        pk[t >> 1][4 * (t & 1) + 3]);
+    mm_cols<4, true>(qt, cur, af, dk);   // dK += dS^T Q
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
+  agpr_acc_drain(dk, dv);   // the last products into dk, dv have retired before VALU reads them
   if (krow < seq) {
     store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
     store_rows_bf16(dk, p.scale, p.dK + (row_base + krow) * p.lddk + head * kAttnD, h);
@@ -562,29 +673,58 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     if (j + 1 < nkb) issue(j + 1, nxt);
     const int kv0 = j * kAttnBK;
     if (!(p.causal && kv0 > wq0 + 31)) {
-      f32x16_t s[2], dp[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[f][v] = dp[f][v] = 0.0f;
-      mm_rows<0, 2>(ktile, cur, lane, qf, s);                       // S = Q K^T
-      mm_rows<0, 2>(vtile, cur + AttnKVTile::BYTES, lane, of, dp);  // dP = dO V^T
       const bool edge = kv0 + kAttnBK > seq || (p.causal && kv0 + kAttnBK - 1 > wq0);
-      float ds[2][16];
+      // P = exp(S * scale - lse), kept as packed bf16 pairs in accumulator
+      // layout (lane: query qrow, keys kv0 + 32 f + 8 g + 4 h + e).
+      uint32_t pk[2][8];
+      {
+        f32x16_t sacc[2];   // S = Q K^T
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float pv = __builtin_amdgcn_exp2f(s[f][v] * p.scale_log2 - lse2);
-          if (edge) {
-            const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (kv >= seq || (p.causal && kv > qrow)) pv = 0.0f;
+          for (int v = 0; v < 16; ++v) sacc[f][v] = 0.0f;
+        mm_rows<2, 2>(ktile, cur, lane, qf, sacc);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float pv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - lse2);
+              if (edge) {
+                const int kv = kv0 + 32 * f + 8 * g + 4 * h + e;
+                if (kv >= seq || (p.causal && kv > qrow)) pv[e] = 0.0f;
+              }
+            }
+            pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
+            pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
           }
-          ds[f][v] = pv * (dp[f][v] - Dq);
-        }
+      }
+      {
+        f32x16_t dacc[2];   // dP = dO V^T
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) dacc[f][v] = 0.0f;
+        mm_rows<2, 2>(vtile, cur + AttnKVTile::BYTES, lane, of, dacc);
+        // dS = P * (dP - D)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t p01 = pk[f][2 * g], p23 = pk[f][2 * g + 1];
+            pk[f][2 * g] = pack_bf16x2(bf16lo(p01) * (dacc[f][4 * g] - Dq), bf16hi(p01) * (dacc[f][4 * g + 1] - Dq));
+            pk[f][2 * g + 1] =
+                pack_bf16x2(bf16lo(p23) * (dacc[f][4 * g + 2] - Dq), bf16hi(p23) * (dacc[f][4 * g + 3] - Dq));
+          }
+      }
       u32x4_t da[4];
-      acc_to_afrag<2>(ds, da);
-      mm_cols<0, 4>(ktile, cur, da, dq);   // dQ += dS K
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        da[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
+                          pk[t >> 1][4 * (t & 1) + 3]);
+      mm_cols<4, false, 3>(ktile, cur, da, dq);   // dQ += dS K
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
