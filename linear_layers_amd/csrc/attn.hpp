@@ -368,9 +368,16 @@ struct AttnRowTile {
 // acc[f] += B(tile rows as n) x A over the 8 d-substeps: C[m][n] with m from a, n = tile row.
 // The B fragments of substep S + 2 are read while substep S multiplies, so
 // the LDS latency hides behind the MFMAs.
-template <int NF, int R = 3, class Tile>
+struct NoSide {
+  template <class I>
+  __device__ __forceinline__ void operator()(I) const {}
+};
+
+// side(std::integral_constant<int, S>{}) runs after substep S's products are
+// issued: independent VALU work placed there executes under the MFMAs.
+template <int NF, int R = 3, class Tile, class Side = NoSide>
 __device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int lane, const u32x4_t (&a)[8],
-                                        f32x16_t (&acc)[NF]) {
+                                        f32x16_t (&acc)[NF], Side side = Side{}) {
   static_assert(R == 2 || R == 3, "ring depth in substeps");
   u32x4_t b[R][NF];
   auto fetch = [&](auto SC) {
@@ -385,6 +392,7 @@ __device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int 
     if constexpr (S + R - 1 < 8) fetch(std::integral_constant<int, S + R - 1>{});
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = mfma_bf16(b[S % R][f], a[S], acc[f]);
+    side(SC);
     __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead: the scheduler would sink them to their use
   };
   step(std::integral_constant<int, 0>{});
@@ -401,9 +409,9 @@ __device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int 
 // reading the next substep's four B fragments while this one multiplies.
 // The 4 NT products run in the order (T, F); the B fragment of product i + D
 // is read while product i multiplies (a ring of D + 1 fragments).
-template <int NT, bool AGPR = false, int D = 4, class Tile>
+template <int NT, bool AGPR = false, int D = 4, class Tile, class Side = NoSide>
 __device__ __forceinline__ void mm_cols(const Tile& t, const lds_char* src, const u32x4_t (&a)[NT],
-                                        f32x16_t (&acc)[4]) {
+                                        f32x16_t (&acc)[4], Side side = Side{}) {
   static_assert(NT <= 4 && D >= 1 && D <= 7, "at most 4 row-substeps");
   constexpr int N = 4 * NT, R = D + 1;
   u32x4_t b[R];
@@ -417,6 +425,7 @@ __device__ __forceinline__ void mm_cols(const Tile& t, const lds_char* src, cons
     fetch(std::integral_constant<int, I + D>{});
     if constexpr (AGPR) mfma_bf16_agpr<(I % 4 == 0) ? 3 : 0>(b[I % R], a[I / 4], acc[I % 4]);  // first use of a[I/4]
     else acc[I % 4] = mfma_bf16(b[I % R], a[I / 4], acc[I % 4]);
+    side(IC);
     __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead: the scheduler would sink them to their use
   };
   static_for<N>(step);
@@ -541,61 +550,60 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     const lds_char* lse_s = cur + kAttnDkvRows;
     const lds_char* d_s = cur + kAttnDkvRows + 256;
     // Accumulator layout: lane holds key krow and queries q0 + 32 f + 8 g + 4 h + e
-    // in register 4 g + e of block f.  Only one score-sized accumulator is live
-    // at a time: P^T is kept as packed bf16 pairs (pk) for dS.
-    uint32_t pk[2][8];
-    u32x4_t af[4];
-    {
-      f32x16_t sacc[2];   // S^T = K Q^T
+    // in register 4 g + e of block f.  The VALU work runs under the MFMAs of
+    // the next product: P^T under dP^T, dS^T under dV.  P^T and dS^T are kept
+    // as packed bf16 pairs (pk) in accumulator layout.
+    f32x16_t sacc[2], dacc[2];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[f][v] = 0.0f;
-      mm_rows<2>(qt, cur, lane, kf, sacc);
+      for (int v = 0; v < 16; ++v) sacc[f][v] = dacc[f][v] = 0.0f;
+    // This block's lse and D values for the lane's queries, read before the
+    // products so that no later wait on them also drains the fragment reads.
+    f32x4_t l4s[8], d4s[8];
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qo = (32 * f + 8 * g + 4 * h) * 4;   // byte offset of the 4 queries in the lse row
-          const f32x4_t l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(lse_s + qo);
-          float pv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - l4[e] * log2e);
-            if (edge) {
-              const int q = q0 + 32 * f + 8 * g + 4 * h + e;
-              if (q >= seq || krow >= seq || (p.causal && q < krow)) pv[e] = 0.0f;
-            }
-          }
-          pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
-          pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
-        }
+    for (int k = 0; k < 8; ++k) {
+      const int qo = (32 * (k / 4) + 8 * (k % 4) + 4 * h) * 4;
+      l4s[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(lse_s + qo);
+      d4s[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(d_s + qo);
     }
+    mm_rows<2>(qt, cur, lane, kf, sacc);   // S^T = K Q^T
+    uint32_t pk[2][8];
+    // P^T = exp(S^T * scale - lse), slice (f, g) = (S / 4, S % 4) under substep S of dP^T
+    auto p_slice = [&](auto SC) {
+      constexpr int f = decltype(SC)::value / 4, g = decltype(SC)::value % 4;
+      const f32x4_t l4 = l4s[4 * f + g];
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - l4[e] * log2e);
+        if (edge) {
+          const int q = q0 + 32 * f + 8 * g + 4 * h + e;
+          if (q >= seq || krow >= seq || (p.causal && q < krow)) pv[e] = 0.0f;
+        }
+      }
+      pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
+      pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
+    };
+    mm_rows<2>(ot, cur + AttnQTile::BYTES, lane, vf, dacc, p_slice);   // dP^T = V dO^T
+    u32x4_t af[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       af[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
                         pk[t >> 1][4 * (t & 1) + 3]);
-    mm_cols<4, true>(ot, cur + AttnQTile::BYTES, af, dv);   // dV += P^T dO
-    {
-      f32x16_t dacc[2];   // dP^T = V dO^T
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dacc[f][v] = 0.0f;
-      mm_rows<2>(ot, cur + AttnQTile::BYTES, lane, vf, dacc);
-      // dS^T = P^T * (dP^T - D), with P^T from its bf16 copy
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qo = (32 * f + 8 * g + 4 * h) * 4;
-          const f32x4_t d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(d_s + qo);
-          const uint32_t p01 = pk[f][2 * g], p23 = pk[f][2 * g + 1];
-          pk[f][2 * g] = pack_bf16x2(bf16lo(p01) * (dacc[f][4 * g] - d4[0]), bf16hi(p01) * (dacc[f][4 * g + 1] - d4[1]));
-          pk[f][2 * g + 1] =
-              pack_bf16x2(bf16lo(p23) * (dacc[f][4 * g + 2] - d4[2]), bf16hi(p23) * (dacc[f][4 * g + 3] - d4[3]));
-        }
-    }
+    // dS^T = P^T * (dP^T - D) from the bf16 P^T, slice (f, g) = (I / 8, (I / 2) % 4) under product I of dV
+    auto ds_slice = [&](auto IC) {
+      constexpr int I = decltype(IC)::value;
+      if constexpr (I % 2 == 0) {
+        constexpr int f = I / 8, g = (I / 2) % 4;
+        const f32x4_t d4 = d4s[4 * f + g];
+        const uint32_t p01 = pk[f][2 * g], p23 = pk[f][2 * g + 1];
+        pk[f][2 * g] = pack_bf16x2(bf16lo(p01) * (dacc[f][4 * g] - d4[0]), bf16hi(p01) * (dacc[f][4 * g + 1] - d4[1]));
+        pk[f][2 * g + 1] =
+            pack_bf16x2(bf16lo(p23) * (dacc[f][4 * g + 2] - d4[2]), bf16hi(p23) * (dacc[f][4 * g + 3] - d4[3]));
+      }
+    };
+    mm_cols<4, true>(ot, cur + AttnQTile::BYTES, af, dv, ds_slice);   // dV += P^T dO
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       af[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
