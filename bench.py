@@ -64,10 +64,20 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_fingerprint() -> str:
-    """Hash of the kernel sources: counters taken on other sources are stale."""
+# Kernel sources that cannot affect a workload's kernels (they hold other
+# kernels only), left out of its fingerprint.
+_UNRELATED_SOURCES = {"mlp": {"attn.hpp"}, "swiglu": {"attn.hpp"}, "sp_mlp": {"attn.hpp"},
+                      "proj": {"sp.hpp", "swiglu.hpp"}}
+
+
+def kernel_fingerprint(kind: str) -> str:
+    """Hash of the kernel sources a workload's kernels are built from: counters
+    taken on other sources are stale."""
     h = hashlib.sha256()
+    skip = _UNRELATED_SOURCES.get(kind, set())
     for f in sorted(glob.glob(os.path.join(ROOT, "linear_layers_amd", "csrc", "*"))):
+        if os.path.basename(f) in skip:
+            continue
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
@@ -520,6 +530,11 @@ def step_roles(tl, step, torch):
     return order
 
 
+def synth_kind(workload: str) -> str:
+    import synth
+    return synth.WORKLOADS[workload].kind
+
+
 def load_traffic(workload: str, symbol: str, role: str):
     """Calibrated HBM bytes per launch of (role, symbol), if measured on these sources."""
     try:
@@ -527,7 +542,7 @@ def load_traffic(workload: str, symbol: str, role: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None, "no traffic table"
-    if t.get("fingerprint") != kernel_fingerprint():
+    if t.get("fingerprint") != kernel_fingerprint(synth_kind(workload)):
         return None, "kernel sources changed since the counters were taken"
     e = t.get("launches", {}).get(role)
     if not e or e.get("kernel") != symbol:
@@ -685,7 +700,7 @@ def run_profile_pass(args):
     torch.cuda.synchronize()
     order = step_roles(tl, step, torch)   # the last step: its launches in order
     with open(args.profile_pass, "w") as f:
-        json.dump({"workload": wl.name, "order": order, "fingerprint": kernel_fingerprint()}, f)
+        json.dump({"workload": wl.name, "order": order, "fingerprint": kernel_fingerprint(wl.kind)}, f)
     print(json.dumps({"profile_pass": args.profile_pass, "launches": len(order)}), flush=True)
 
 
