@@ -127,7 +127,7 @@ def proj_role_flops(wl, T=None):
 def role_flops(wl, role):
     if wl.kind == "proj":
         return proj_role_flops(wl).get(role, 0.0)
-    return ROLE_UNITS[wl.kind][role] * 2.0 * wl.T * wl.h * wl.Fs
+    return ROLE_UNITS[wl.kind].get(role, 0) * 2.0 * wl.T * wl.h * wl.Fs
 
 
 def step_flops(wl, T=None):
