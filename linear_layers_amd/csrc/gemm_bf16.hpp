@@ -438,35 +438,40 @@ gemm_bf16_kernel(const GemmArgs p) {
       bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
       const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
       const int h = lane >> 5;
+      // Bias of the lane's columns: register group g = 2pr + q holds columns
+      // c + 8q + 4h .. + 3 of the 16-column block c = ... + 32 j + 16 pr.
+      float bv[FN][4][4];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          // Register groups g = 2pr (columns c + 4h..) and 2pr+1 (c + 8 + 4h..);
-          // after the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
-          const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-          float bv[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-          if (bias) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int cq = c + 8 * q + 4 * h;
-              if (cq < N) {
-                const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
-                bv[q][0] = bf16lo(w[0]); bv[q][1] = bf16hi(w[0]); bv[q][2] = bf16lo(w[1]); bv[q][3] = bf16hi(w[1]);
-              }
-            }
+        for (int g = 0; g < 4; ++g) {
+          const int cq = n0 + wn * WTN + 32 * j + 8 * g + 4 * h;
+          bv[j][g][0] = bv[j][g][1] = bv[j][g][2] = bv[j][g][3] = 0.f;
+          if (bias && cq < N) {
+            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
+            bv[j][g][0] = bf16lo(w[0]); bv[j][g][1] = bf16hi(w[0]); bv[j][g][2] = bf16lo(w[1]); bv[j][g][3] = bf16hi(w[1]);
           }
-          const int cs = c + 8 * h;
+        }
+      // Rows outermost: the four 32-byte pieces of each 128-byte line of a row
+      // (two j blocks x two 16-column halves) are stored back to back, so L2
+      // merges them before it evicts the line.
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = mrow + 32 * i;
+      for (int i = 0; i < FM; ++i) {
+        const int row = mrow + 32 * i;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            // After the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
+            const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+            const int cs = c + 8 * h;
             uint32_t aw[2][2], hw[2][2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
               const int g = 2 * pr + q;
               float hv[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[q][e];
+              for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[j][g][e];
               if constexpr (kGelu) {
                 aw[q][0] = pack_bf16x2(gelu_tanh(hv[0]), gelu_tanh(hv[1]));
                 aw[q][1] = pack_bf16x2(gelu_tanh(hv[2]), gelu_tanh(hv[3]));
@@ -493,7 +498,7 @@ gemm_bf16_kernel(const GemmArgs p) {
                     u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
             }
           }
-        }
+      }
     };
     if (p.act == kActGeluTanh) epilogue(std::true_type{});
     else epilogue(std::false_type{});
@@ -506,12 +511,13 @@ gemm_bf16_kernel(const GemmArgs p) {
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);   // [M, N/2]
     bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);  // [M, N] packed, or null
     const int h = lane >> 5;
+    // Rows outermost: the pieces of each 128-byte line are stored back to back.
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int c0 = n0 + wn * WTN + 32 * j;  // packed column, a multiple of 32
+    for (int i = 0; i < FM; ++i) {
+      const int row = mrow + 32 * i;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = mrow + 32 * i;
+      for (int j = 0; j < FN; ++j) {
+        const int c0 = n0 + wn * WTN + 32 * j;  // packed column, a multiple of 32
         uint32_t aw[2][2], hw[2][2][2];
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
@@ -566,14 +572,15 @@ gemm_bf16_kernel(const GemmArgs p) {
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);        // [M, 2N] packed
     const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);  // [M, 2N] packed
     const int h = lane >> 5;
+    // Rows outermost: the pieces of each 128-byte line are read and stored back to back.
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c8 = n0 + wn * WTN + 32 * j + 8 * g;  // output column 8q
+      for (int j = 0; j < FN; ++j) {
+        const int row = mrow + 32 * i;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = mrow + 32 * i;
+        for (int g = 0; g < 4; ++g) {
+          const int c8 = n0 + wn * WTN + 32 * j + 8 * g;  // output column 8q
           float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
           if (row < M && c8 < N) {
             const bf16_t* src = Hs + (int64_t)row * p.ldh + 2 * c8 + 4 * h;
@@ -608,16 +615,26 @@ gemm_bf16_kernel(const GemmArgs p) {
       bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
       const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
       const int h = lane >> 5;
+      float csum[FN][2][2][4];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-          float csum[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-          const int cs = c + 8 * h;
+        for (int pr = 0; pr < 2; ++pr)
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = mrow + 32 * i;
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) csum[j][pr][q][e] = 0.f;
+      // Rows outermost, so the pieces of each 128-byte line of H and dH are
+      // read and stored back to back.
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = mrow + 32 * i;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const int c = n0 + wn * WTN + 32 * j + 16 * pr;
+            const int cs = c + 8 * h;
             uint32_t dw[2][2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -635,7 +652,7 @@ gemm_bf16_kernel(const GemmArgs p) {
                   for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e];
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) csum[q][e] += d[e];
+                for (int e = 0; e < 4; ++e) csum[j][pr][q][e] += d[e];
               }
               dw[q][0] = pack_bf16x2(d[0], d[1]);
               dw[q][1] = pack_bf16x2(d[2], d[3]);
@@ -649,23 +666,33 @@ gemm_bf16_kernel(const GemmArgs p) {
             if (row < M && cs < N)
               *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
           }
-          // Sum over the 32 rows held by lanes with the same lane/32.
+      }
+      if (p.colsum) {
+        // Sum over the 32 rows held by lanes with the same lane/32.
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+          for (int pr = 0; pr < 2; ++pr)
 #pragma unroll
-              for (int x = 1; x < 32; x <<= 1) csum[q][e] += __shfl_xor(csum[q][e], x);
-            }
-          if ((lane & 31) == 0) {
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+              for (int e = 0; e < 4; ++e) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[q][e];
-            }
-          }
+                for (int x = 1; x < 32; x <<= 1) csum[j][pr][q][e] += __shfl_xor(csum[j][pr][q][e], x);
+              }
+        if ((lane & 31) == 0) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[j][pr][q][e];
+              }
         }
+      }
     };
     if (p.act == kActGeluTanh) epilogue(std::true_type{});
     else epilogue(std::false_type{});
