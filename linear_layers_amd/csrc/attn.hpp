@@ -82,6 +82,9 @@ __device__ __forceinline__ void agpr_acc_drain(f32x16_t (&x)[4], f32x16_t (&y)[4
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]), "+a"(y[3]));
 }
+__device__ __forceinline__ void agpr_acc_drain(f32x16_t (&x)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]));
+}
 
 // Lane-pair exchange of two register groups g0 = (x0, x1) and g1 = (y0, y1),
 // each 4 bf16 of columns 4h..4h+3 of their 8-column group: afterwards lane
@@ -123,7 +126,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const int qb = p.causal ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;  // longest rows first when causal
+  // Causal: workgroup x takes query blocks nqb - 1 - x and x, whose key ranges add
+  // up to the same work for every workgroup; otherwise block x alone.
+  const int nvb = (p.causal && (int)blockIdx.x != nqb - 1 - (int)blockIdx.x) ? 2 : 1;
+  for (int vb = 0; vb < nvb; ++vb) {
+  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
+  const int qb = p.causal ? (vb == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x) : (int)blockIdx.x;
   const int head = blockIdx.y;
   const int64_t row_base = (int64_t)blockIdx.z * seq;
   const int q0 = qb * kAttnBQ;
@@ -245,6 +253,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     if (p.lse != nullptr && h == 0)
       p.lse[(int64_t)head * p.batch * seq + row_base + qrow] = (m_i + __log2f(l_i)) * 0.69314718055994531f;
   }
+  }  // query blocks
 }
 
 // ================================================================ backward --
@@ -486,7 +495,12 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nkb = (seq + 63) / 64;
-  const int kb = p.causal ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x;  // most query blocks first
+  // Causal: workgroup x takes key blocks x and nkb - 1 - x, whose query ranges add
+  // up to the same work for every workgroup; otherwise block x alone.
+  const int nvb = (p.causal && (int)blockIdx.x != nkb - 1 - (int)blockIdx.x) ? 2 : 1;
+  for (int vb = 0; vb < nvb; ++vb) {
+  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
+  const int kb = p.causal ? (vb == 0 ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
   const int head = blockIdx.y;
   const int64_t T = (int64_t)p.batch * seq;
   const int64_t row_base = (int64_t)blockIdx.z * seq;
@@ -617,6 +631,7 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
     store_rows_bf16(dk, p.scale, p.dK + (row_base + krow) * p.lddk + head * kAttnD, h);
   }
+  }  // key blocks
 }
 
 using AttnKVTile = AttnRowTile<kAttnBK, 4>;   // 64 key rows x 128, 4 waves load it
@@ -631,7 +646,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const int qb = p.causal ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  // Causal: workgroup x takes query blocks nqb - 1 - x and x, whose key ranges add
+  // up to the same work for every workgroup; otherwise block x alone.
+  const int nvb = (p.causal && (int)blockIdx.x != nqb - 1 - (int)blockIdx.x) ? 2 : 1;
+  for (int vb = 0; vb < nvb; ++vb) {
+  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
+  const int qb = p.causal ? (vb == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x) : (int)blockIdx.x;
   const int head = blockIdx.y;
   const int64_t T = (int64_t)p.batch * seq;
   const int64_t row_base = (int64_t)blockIdx.z * seq;
@@ -667,9 +687,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
 
   f32x16_t dq[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 4; ++f) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) dq[f][v] = 0.0f;
+  }
   const int kv_end = p.causal ? min(seq, q0 + kAttnBQ) : seq;
   const int nkb = (kv_end + kAttnBK - 1) / kAttnBK;
   issue(0, (lds_char*)st0);
@@ -732,12 +753,13 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
       for (int t = 0; t < 4; ++t)
         da[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
                           pk[t >> 1][4 * (t & 1) + 3]);
-      mm_cols<4, false, 3>(ktile, cur, da, dq);   // dQ += dS K
+      mm_cols<4, false, 2>(ktile, cur, da, dq);   // dQ += dS K
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
   if (qrow < seq) store_rows_bf16(dq, p.scale, p.dQ + (row_base + qrow) * p.lddq + head * kAttnD, h);
+  }  // query blocks
 }
 
 }  // namespace tpmlp

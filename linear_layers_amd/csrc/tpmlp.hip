@@ -953,7 +953,9 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.heads = heads;
   a.causal = causal;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const dim3 grid((unsigned)((seq + kAttnBQ - 1) / kAttnBQ), (unsigned)heads, (unsigned)batch);
+  // Causal: each workgroup takes a long and a short query block (pairs x, n-1-x).
+  const int64_t nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const dim3 grid((unsigned)(causal ? (nqb + 1) / 2 : nqb), (unsigned)heads, (unsigned)batch);
   return launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), (hipStream_t)stream, a);
 }
 
@@ -1013,10 +1015,12 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   const int64_t items = T * heads;
   TPMLP_TRY(launch("attn_bwd_dot", "attn_bwd_dot_kernel", attn_bwd_dot_kernel, dim3((unsigned)((items + 15) / 16)),
                    dim3(256), s, a));
+  // Causal: each workgroup takes a long and a short block (pairs x, n-1-x).
+  const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
   TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
-                   dim3((unsigned)((seq + 63) / 64), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
+                   dim3((unsigned)(causal ? (nkb + 1) / 2 : nkb), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
   return launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
-                dim3((unsigned)((seq + kAttnBQ - 1) / kAttnBQ), (unsigned)heads, (unsigned)batch), dim3(256), s, a);
+                dim3((unsigned)(causal ? (nqb + 1) / 2 : nqb), (unsigned)heads, (unsigned)batch), dim3(256), s, a);
 }
 
 // ------------------------------------------- head-sharded attention block --
