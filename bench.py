@@ -307,6 +307,18 @@ class Step:
         tl.tp_mlp_bwd(s.X, s.W1s[i], s.W2s[i], s.H, s.A, s.dZ, s.wl.tp, s.dXp[i], s.dW1, s.dW2, db1_shard=s.db1,
                       workspace=s.ws, stream=s.stream)
 
+    def parts(self):
+        """Shard 0's forward call and backward call alone, with their GEMM flops."""
+        tl, s, u = self.tl, self, 2.0 * self.wl.T * self.wl.h * self.wl.Fs
+
+        def fwd():
+            tl.tp_mlp_fwd(s.X, s.W1s[0], s.b1s[0], s.W2s[0], s.wl.tp, s.A, s.Zp[0], H_save=s.H, stream=s.stream)
+
+        def bwd():
+            tl.tp_mlp_bwd(s.X, s.W1s[0], s.W2s[0], s.H, s.A, s.dZ, s.wl.tp, s.dXp[0], s.dW1, s.dW2, db1_shard=s.db1,
+                          workspace=s.ws, stream=s.stream)
+        return {"tp_mlp_fwd": (fwd, 2 * u), "tp_mlp_bwd": (bwd, 4 * u)}
+
     def __call__(self):
         tl, s = self.tl, self
         tl.tp_mlp_fwd(s.X, s.W1s[0], s.b1s[0], s.W2s[0], s.wl.tp, s.A, s.Zp[0], H_save=s.H, stream=s.stream)
@@ -361,6 +373,10 @@ class SwiGLUStep:
         s = self
         s.tl.tp_swiglu_bwd(s.X, s.Wgus[i], s.Wds[i], s.GU, s.A, s.dZ, s.wl.tp, s.dXp[i], s.dWgu, s.dWd,
                            workspace=s.ws, stream=s.stream)
+
+    def parts(self):
+        u = 2.0 * self.wl.T * self.wl.h * self.wl.Fs
+        return {"tp_swiglu_fwd": (lambda: self.fwd(0), 3 * u), "tp_swiglu_bwd": (lambda: self.bwd(0), 6 * u)}
 
     def __call__(self):
         s = self
@@ -495,6 +511,11 @@ class AttnBlockStep:
         s.tl.tp_attn_bwd(s.X, s.Wqkv[i], s.Wo[i], s.QKV, s.O, s.lse, s.dZ, s.dXp[i], s.dWqkv, s.dWo, 1, s.wl.T,
                          s.wl.heads, s.wl.tp, causal=True, workspace=s.ws, stream=s.stream)
 
+    def parts(self):
+        r = proj_role_flops(self.wl)
+        f = r["gemm.attn_qkv"] + r["attn_fwd"] + r["gemm.attn_out"]
+        return {"tp_attn_fwd": (lambda: self.fwd(0), f), "tp_attn_bwd": (lambda: self.bwd(0), step_flops(self.wl) - f)}
+
     def __call__(self):
         s = self
         s.fwd(0)
@@ -620,6 +641,23 @@ def run_bench(args):
     flops_step = step_flops(wl)
     value = flops_step / (ms_step * 1e-3) / 1e12
 
+    # The step's forward and backward calls, each timed alone (after the timed
+    # region, so they do not change it): same launches, same stream.
+    parts = {}
+    if hasattr(step, "parts"):
+        for name, (fn, pflops) in step.parts().items():
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1) / args.steps
+            ptf = pflops / (pms * 1e-3) / 1e12
+            parts[name] = {"us": round(pms * 1e3, 2), "tflops": round(ptf, 2),
+                           "pct_of_peak": round(100 * ptf / PEAK_BF16_TFLOPS, 2)}
+
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
     n_launch, dom_ms, dom_sym, dom_clocks = timed[dom_key]
@@ -672,6 +710,7 @@ def run_bench(args):
                    "global_batch": T, "seq_len": None, "parallelism": f"tp{tp} shard simulated on 1 GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
+        "parts": parts,
         "kernels_warmup": kernels,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 2),
