@@ -278,7 +278,21 @@ struct AttnBwdArgs {
   int64_t lddq, lddk, lddv;
   int batch, seq, heads, causal;
   float scale, scale_log2;
+  float* dq_part;     // causal: [batch][heads][query blocks][chunks][128][128] fp32 partial dQ
+  int dq_chunks;      // key chunks of the longest query block (1: no partials)
 };
+
+// Causal dQ work is split along keys: a query block of 128 rows sees up to
+// 2 (b + 1) key blocks of 64; they are taken in chunks of kAttnDqChunk key
+// blocks, one workgroup per (block, chunk), so no workgroup does more than
+// kAttnDqChunk iterations.  Chunk c exists for blocks b >= kAttnDqChunkRows * c.
+constexpr int kAttnDqChunk = 16;
+constexpr int kAttnDqChunkRows = kAttnDqChunk * 64 / 128;
+
+__device__ __forceinline__ int attn_dq_chunks(int b, int seq) {
+  const int kv_end = min(seq, (b + 1) * 128);
+  return ((kv_end + 63) / 64 + kAttnDqChunk - 1) / kAttnDqChunk;
+}
 
 // D[head][t] = sum over the head's 128 columns of dO * O; 16 lanes per (row, head).
 __global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const AttnBwdArgs p) {
@@ -646,12 +660,20 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  // Causal: workgroup x takes query blocks nqb - 1 - x and x, whose key ranges add
-  // up to the same work for every workgroup; otherwise block x alone.
-  const int nvb = (p.causal && (int)blockIdx.x != nqb - 1 - (int)blockIdx.x) ? 2 : 1;
-  for (int vb = 0; vb < nvb; ++vb) {
-  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
-  const int qb = p.causal ? (vb == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x) : (int)blockIdx.x;
+  // Causal: workgroup x is chunk c of query block qb, enumerated chunk by chunk
+  // (c = 0 for every block, then c = 1 for the blocks that have it, ...), the
+  // blocks of one chunk from the last (longest) down.  Otherwise block x, all keys.
+  int qb = (int)blockIdx.x, chunk = 0;
+  if (p.causal) {
+    int id = (int)blockIdx.x;
+    // The grid holds exactly the chunks that exist; the bound only guards the loop.
+    while (chunk < p.dq_chunks && id >= nqb - kAttnDqChunkRows * chunk) {
+      id -= nqb - kAttnDqChunkRows * chunk;
+      ++chunk;
+    }
+    if (chunk >= p.dq_chunks) return;   // uniform across the workgroup, before any barrier
+    qb = nqb - 1 - id;
+  }
   const int head = blockIdx.y;
   const int64_t T = (int64_t)p.batch * seq;
   const int64_t row_base = (int64_t)blockIdx.z * seq;
@@ -692,14 +714,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     for (int v = 0; v < 16; ++v) dq[f][v] = 0.0f;
   }
   const int kv_end = p.causal ? min(seq, q0 + kAttnBQ) : seq;
-  const int nkb = (kv_end + kAttnBK - 1) / kAttnBK;
-  issue(0, (lds_char*)st0);
+  const int j0 = p.causal ? chunk * kAttnDqChunk : 0;
+  const int j1 = p.causal ? min((kv_end + kAttnBK - 1) / kAttnBK, j0 + kAttnDqChunk) : (kv_end + kAttnBK - 1) / kAttnBK;
+  issue(j0, (lds_char*)st0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    lds_char* cur = (j & 1) ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = (j & 1) ? (lds_char*)st0 : (lds_char*)st1;
-    if (j + 1 < nkb) issue(j + 1, nxt);
+  for (int j = j0; j < j1; ++j) {
+    lds_char* cur = ((j - j0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = ((j - j0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+    if (j + 1 < j1) issue(j + 1, nxt);
     const int kv0 = j * kAttnBK;
     if (!(p.causal && kv0 > wq0 + 31)) {
       const bool edge = kv0 + kAttnBK > seq || (p.causal && kv0 + kAttnBK - 1 > wq0);
@@ -758,8 +781,55 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
-  if (qrow < seq) store_rows_bf16(dq, p.scale, p.dQ + (row_base + qrow) * p.lddq + head * kAttnD, h);
-  }  // query blocks
+  if (p.causal && attn_dq_chunks(qb, seq) > 1) {
+    // one of several chunks: its fp32 partial (unscaled) for attn_bwd_dq_sum_kernel
+    float* dst = p.dq_part +
+                 ((((int64_t)blockIdx.z * p.heads + head) * nqb + qb) * p.dq_chunks + chunk) * (kAttnBQ * kAttnD) +
+                 (int64_t)(32 * wave + (lane & 31)) * kAttnD + 4 * h;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * f + 8 * g) =
+            f32x4_t{dq[f][4 * g], dq[f][4 * g + 1], dq[f][4 * g + 2], dq[f][4 * g + 3]};
+  } else if (qrow < seq) {
+    store_rows_bf16(dq, p.scale, p.dQ + (row_base + qrow) * p.lddq + head * kAttnD, h);
+  }
+}
+
+// dQ of the causal query blocks that were split into several key chunks: the
+// chunks' partials added in chunk order, scaled, rounded to bf16.  Workgroup
+// (x, head, sequence) covers 16 rows of block kAttnDqChunkRows + x / 8; each
+// thread owns 8 consecutive columns of one row.
+__global__ void __launch_bounds__(256) attn_bwd_dq_sum_kernel(const AttnBwdArgs p) {
+  const int seq = p.seq;
+  const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const int qb = kAttnDqChunkRows + (int)blockIdx.x / 8;
+  const int r = 16 * ((int)blockIdx.x % 8) + (int)threadIdx.x / 16;   // row within the block
+  const int c8 = 8 * ((int)threadIdx.x % 16);                          // first of 8 columns
+  const int head = blockIdx.y;
+  const int nch = attn_dq_chunks(qb, seq);
+  const float* src = p.dq_part +
+                     (((int64_t)blockIdx.z * p.heads + head) * nqb + qb) * p.dq_chunks * (kAttnBQ * kAttnD) +
+                     r * kAttnD + c8;
+  f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src);
+  f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+  for (int c = 1; c < nch; ++c) {
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * (kAttnBQ * kAttnD));
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * (kAttnBQ * kAttnD) + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a0[e] += x0[e];
+      a1[e] += x1[e];
+    }
+  }
+  const int q = qb * kAttnBQ + r;
+  if (q < seq) {
+    const float sc = p.scale;
+    *reinterpret_cast<u32x4_t*>(p.dQ + ((int64_t)blockIdx.z * seq + q) * p.lddq + head * kAttnD + c8) =
+        u32x4_t{pack_bf16x2(a0[0] * sc, a0[1] * sc), pack_bf16x2(a0[2] * sc, a0[3] * sc),
+                pack_bf16x2(a1[0] * sc, a1[1] * sc), pack_bf16x2(a1[2] * sc, a1[3] * sc)};
+  }
 }
 
 }  // namespace tpmlp

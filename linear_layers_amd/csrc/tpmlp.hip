@@ -959,9 +959,32 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   return launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), (hipStream_t)stream, a);
 }
 
+namespace {
+// Causal dQ chunks of the longest query block (see attn_dq_chunks).
+int64_t attn_dq_chunks_max(int64_t seq) {
+  return seq > 0 ? ((seq + 63) / 64 + kAttnDqChunk - 1) / kAttnDqChunk : 0;
+}
+
+struct AttnBwdWs {
+  size_t d_bytes, part_off, total;
+};
+
+// D [heads, T] fp32, then (when some causal query block has several key
+// chunks) the fp32 dQ partials [batch][heads][query blocks][chunks][128][128].
+AttnBwdWs attn_bwd_ws(int64_t batch, int64_t seq, int64_t heads) {
+  AttnBwdWs w;
+  w.d_bytes = align256((size_t)batch * seq * heads * sizeof(float));
+  w.part_off = w.d_bytes;
+  const int64_t ch = attn_dq_chunks_max(seq), nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const size_t part = ch > 1 ? (size_t)batch * heads * nqb * ch * kAttnBQ * kAttnD * sizeof(float) : 0;
+  w.total = w.part_off + align256(part);
+  return w;
+}
+}  // namespace
+
 size_t attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads) {
   if (batch < 0 || seq < 0 || heads < 1 || batch * seq > kMaxDim) return 0;
-  return align256((size_t)batch * seq * heads * sizeof(float));
+  return attn_bwd_ws(batch, seq, heads).total;
 }
 
 int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
@@ -982,7 +1005,8 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   if (T == 0) return TPMLP_OK;
   if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd || lddo >= kMaxLd)
     return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
-  const size_t need = align256((size_t)T * heads * sizeof(float));
+  const AttnBwdWs W = attn_bwd_ws(batch, seq, heads);
+  const size_t need = W.total;
   if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
   if (workspace_bytes < need) return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
@@ -1011,16 +1035,29 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.dq_chunks = (int)attn_dq_chunks_max(seq);
+  a.dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + W.part_off);
   hipStream_t s = (hipStream_t)stream;
   const int64_t items = T * heads;
   TPMLP_TRY(launch("attn_bwd_dot", "attn_bwd_dot_kernel", attn_bwd_dot_kernel, dim3((unsigned)((items + 15) / 16)),
                    dim3(256), s, a));
-  // Causal: each workgroup takes a long and a short block (pairs x, n-1-x).
+  // Causal dK/dV: each workgroup takes a long and a short block (pairs x, n-1-x).
+  // Causal dQ: one workgroup per (query block, key chunk); blocks with several
+  // chunks are summed by attn_bwd_dq_sum_kernel.
   const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  int64_t dq_items = nqb;
+  if (causal) {
+    dq_items = 0;
+    for (int64_t c = 0; kAttnDqChunkRows * c < nqb; ++c) dq_items += nqb - kAttnDqChunkRows * c;
+  }
   TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
                    dim3((unsigned)(causal ? (nkb + 1) / 2 : nkb), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
-  return launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
-                dim3((unsigned)(causal ? (nqb + 1) / 2 : nqb), (unsigned)heads, (unsigned)batch), dim3(256), s, a);
+  TPMLP_TRY(launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
+                   dim3((unsigned)dq_items, (unsigned)heads, (unsigned)batch), dim3(256), s, a));
+  if (causal && a.dq_chunks > 1 && nqb > kAttnDqChunkRows)
+    TPMLP_TRY(launch("attn_bwd_dq_sum", "attn_bwd_dq_sum_kernel", attn_bwd_dq_sum_kernel,
+                     dim3((unsigned)(8 * (nqb - kAttnDqChunkRows)), (unsigned)heads, (unsigned)batch), dim3(256), s, a));
+  return TPMLP_OK;
 }
 
 // ------------------------------------------- head-sharded attention block --
@@ -1044,12 +1081,14 @@ struct AttnBlockWs {
   size_t do_off, dqkv_off, d_off, total;
 };
 
-AttnBlockWs attn_block_ws(int64_t T, int64_t w, int64_t hs) {
+// dO and dQKV (bf16), then the attention backward's own workspace.
+AttnBlockWs attn_block_ws(int64_t batch, int64_t seq, int64_t w, int64_t hs) {
+  const int64_t T = batch * seq;
   AttnBlockWs L;
   L.do_off = 0;
   L.dqkv_off = align256((size_t)T * w * 2);
   L.d_off = L.dqkv_off + align256((size_t)T * 3 * w * 2);
-  L.total = L.d_off + align256((size_t)T * hs * sizeof(float));
+  L.total = L.d_off + attn_bwd_ws(batch, seq, hs).total;
   return L;
 }
 }  // namespace
@@ -1082,7 +1121,7 @@ size_t tp_attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int he
       batch * seq > kMaxDim)
     return 0;
   const int64_t hs = heads / tp_size;
-  return attn_block_ws(batch * seq, hs * head_dim, hs).total;
+  return attn_block_ws(batch, seq, hs * head_dim, hs).total;
 }
 
 int tp_attn_bwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
@@ -1102,7 +1141,7 @@ int tp_attn_bwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, 
   TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
   TPMLP_TRY(check_mat("dWqkv_shard", dWqkv_shard, h, 3 * w, 3 * w, 4));
   TPMLP_TRY(check_mat("dWo_shard", dWo_shard, w, h, h, 4));
-  const AttnBlockWs L = attn_block_ws(T, w, d.hs);
+  const AttnBlockWs L = attn_block_ws(batch, seq, w, d.hs);
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     TPMLP_TRY(fill_zero(dWqkv_shard, h, 3 * w, 3 * w, s));

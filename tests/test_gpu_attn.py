@@ -126,7 +126,10 @@ def _bwd_case(batch, seq, heads, causal, seed, scale=None):
 
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 130, 1, False), (3, 128, 1, True),
-                                                    (1, 1000, 2, True), (1, 1000, 1, False)])
+                                                    (1, 1000, 2, True), (1, 1000, 1, False),
+                                                    # causal query blocks past row 1024 split their keys into
+                                                    # chunks of 1024 (2 and 3 chunks here, ragged last block)
+                                                    (2, 1100, 1, True), (1, 2100, 2, True)])
 def test_attn_bwd(batch, seq, heads, causal):
     need_gpu()
     _say(f"attn bwd batch={batch} seq={seq} heads={heads} causal={causal}")
