@@ -350,11 +350,17 @@ int partial_sum(int tp, int64_t T, int64_t N, const float* P, int64_t stride, in
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
   const int nvec = (int)(N / 4);
-  constexpr int U = 2;
-  const int64_t per_row = (nvec + 256 * U - 1) / (256 * U);
-  const int64_t blocks = T * per_row;
+  // Four 16-byte groups per thread for wide rows (measured 6.3 vs 6.1 TB/s at
+  // N = 4096), two otherwise.
+  if (nvec >= 1024) {
+    const int64_t blocks = T * ((nvec + 1023) / 1024);
+    const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * 16);
+    return launch(role, "partial_sum_kernel<4>", partial_sum_kernel<4>, dim3(grid), dim3(256), s, P, stride, ldp,
+                  out, ldo, tp, (int)T, nvec);
+  }
+  const int64_t blocks = T * ((nvec + 511) / 512);
   const unsigned grid = (unsigned)std::min<int64_t>(blocks, (int64_t)cus * 16);
-  return launch(role, "partial_sum_kernel<2>", partial_sum_kernel<U>, dim3(grid), dim3(256), s, P, stride, ldp,
+  return launch(role, "partial_sum_kernel<2>", partial_sum_kernel<2>, dim3(grid), dim3(256), s, P, stride, ldp,
                 out, ldo, tp, (int)T, nvec);
 }
 
