@@ -6,7 +6,8 @@
 // a query block's attention accumulated key block by key block).  Heads are
 // independent (damodev.csdn.net/6a43867610ee7a33f284fb9e.html, 1.2.2; the
 // head-sharded projections on io.zouht.com/197.html, 2.2.1), so the grid is
-// (query blocks, heads, batch).
+// (query blocks, heads, batch); when causal, a workgroup takes two query
+// blocks, a long and a short one, so that all do the same work.
 //
 // Layout: T = batch * seq token rows; head h reads columns [128h, 128h+128)
 // of Q, K and V (each with its own row stride, e.g. the three blocks of the
@@ -258,10 +259,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
 
 // ================================================================ backward --
 // With P = softmax(S) and D_q = sum_d dO[q,d] O[q,d]: dV = P^T dO, dP = dO V^T,
-// dS = P * (dP - D), dQ = dS K * scale, dK = dS^T Q * scale.  Two kernels,
-// no atomics: one owns a block of keys and loops over query blocks (dK, dV),
-// the other owns a block of queries and loops over key blocks (dQ); both
-// recompute P from the saved log-sum-exp.
+// dS = P * (dP - D), dQ = dS K * scale, dK = dS^T Q * scale.  No atomics:
+// after D (attn_bwd_dot_kernel), one kernel owns a block of keys and loops
+// over query blocks (dK, dV), another owns a block of queries and loops over
+// key blocks (dQ); both recompute P from the saved log-sum-exp.  Causal dQ
+// work is cut into key chunks whose partials attn_bwd_dq_sum_kernel adds.
 
 struct AttnBwdArgs {
   const bf16_t* Q;
@@ -428,8 +430,7 @@ __device__ __forceinline__ void mm_rows(const Tile& t, const lds_char* src, int 
   step(std::integral_constant<int, 7>{});
 }
 
-// acc[F] += B(tile rows as k, d block F as n) x A over NT row-substeps of 16,
-// reading the next substep's four B fragments while this one multiplies.
+// acc[F] += B(tile rows as k, d block F as n) x A over NT row-substeps of 16.
 // The 4 NT products run in the order (T, F); the B fragment of product i + D
 // is read while product i multiplies (a ring of D + 1 fragments).
 template <int NT, bool AGPR = false, int D = 4, class Tile, class Side = NoSide>
@@ -500,7 +501,8 @@ __device__ __forceinline__ void lds_dma_f32x64(const float* base, uint32_t nbyte
 }
 
 // dK, dV for 64 keys of one head (2 waves x 32 keys), over all query blocks
-// that see them.  K and V rows stay in registers as A fragments.
+// that see them (causal: two key blocks per workgroup, a long and a short
+// one).  K and V rows stay in registers as A fragments.
 __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char st0[kAttnDkvStage];
   __shared__ __attribute__((aligned(1024))) char st1[kAttnDkvStage];
@@ -651,7 +653,8 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
 using AttnKVTile = AttnRowTile<kAttnBK, 4>;   // 64 key rows x 128, 4 waves load it
 constexpr int kAttnDqStage = 2 * AttnKVTile::BYTES;  // K and V: 32 KB
 
-// dQ for 128 query rows of one head (4 waves x 32), over the key blocks they see.
+// dQ for 128 query rows of one head (4 waves x 32), over the key blocks they
+// see (causal: over one chunk of at most kAttnDqChunk key blocks).
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char st0[kAttnDqStage];
   __shared__ __attribute__((aligned(1024))) char st1[kAttnDqStage];
