@@ -51,9 +51,10 @@ struct GemmArgs {
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id.  Renumber
 // them so that each XCD (with its own L2) works on a contiguous run of tiles,
 // then walk tiles in groups of 8 tile-rows so that neighbours share B panels.
-__device__ __forceinline__ void map_tile(const GemmArgs& p, int& tm, int& tn, int& ks) {
-  const int nwg = gridDim.x;
-  int pid = blockIdx.x;
+// pid / nwg: the workgroup's index among the nwg workgroups of this product
+// (the whole grid, or one product's share of a paired launch, whose start is
+// a multiple of 8 so that pid & 7 still names the XCD).
+__device__ __forceinline__ void map_tile(const GemmArgs& p, int pid, int nwg, int& tm, int& tn, int& ks) {
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
   const int per = p.tiles_m * p.tiles_n;
   ks = pid / per;
@@ -66,6 +67,10 @@ __device__ __forceinline__ void map_tile(const GemmArgs& p, int& tm, int& tn, in
   const int r = t - gid * width;
   tm = first + r % gsz;
   tn = r / gsz;
+}
+
+__device__ __forceinline__ void map_tile(const GemmArgs& p, int& tm, int& tn, int& ks) {
+  map_tile(p, (int)blockIdx.x, (int)gridDim.x, tm, tn, ks);
 }
 
 // Moves one operand tile (ROWS M- or N-indices x BK) from global memory into

@@ -200,9 +200,9 @@ struct FragLoop<NF, NF, S> {
   __device__ __forceinline__ static void run(const Tile&, const lds_char*, u32x4_t*) {}
 };
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
-__global__ void __launch_bounds__(128 * WGN, OCC)
-gemm_bf16_kernel(const GemmArgs p) {
+// One workgroup's tile: workgroup pid of the nwg that compute product p.
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC, int BKT, int WGN>
+__device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int nwg) {
   constexpr int WGM = 2;                     // waves along M
   constexpr int NW = WGM * WGN, NT = 64 * NW;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -239,13 +239,13 @@ gemm_bf16_kernel(const GemmArgs p) {
 
   // Profiling only: the shader clock over workgroup 0's main loop.
   unsigned long long clk0 = 0, ref0 = 0;
-  if (p.clk != nullptr && blockIdx.x == 0) {
+  if (p.clk != nullptr && pid == 0) {
     clk0 = __builtin_amdgcn_s_memtime();
     ref0 = __builtin_amdgcn_s_memrealtime();
   }
 
   int tmi, tni, ks;
-  map_tile(p, tmi, tni, ks);
+  map_tile(p, pid, nwg, tmi, tni, ks);
   const int m0 = tmi * BM, n0 = tni * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int kbeg = ks * p.k_per_split;
@@ -402,7 +402,7 @@ gemm_bf16_kernel(const GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the loads the compiler does not see
   __syncthreads();
-  if (p.clk != nullptr && blockIdx.x == 0 && tid == 0) {
+  if (p.clk != nullptr && pid == 0 && tid == 0) {
     p.clk[0] = __builtin_amdgcn_s_memtime() - clk0;
     p.clk[1] = __builtin_amdgcn_s_memrealtime() - ref0;
   }
@@ -703,6 +703,24 @@ gemm_bf16_kernel(const GemmArgs p) {
       }
     }
   }
+}
+
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
+__global__ void __launch_bounds__(128 * WGN, OCC)
+gemm_bf16_kernel(const GemmArgs p) {
+  gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Two independent products of the same shape class in one launch: workgroups
+// [0, n0) compute p0, the rest p1 (n0 a multiple of 8).  Used where each alone
+// would leave CUs idle and together they fill the chip once.
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
+__global__ void __launch_bounds__(128 * WGN, OCC)
+gemm_bf16_pair_kernel(const GemmArgs p0, const GemmArgs p1, int n0) {
+  if ((int)blockIdx.x < n0)
+    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p0, (int)blockIdx.x, n0);
+  else
+    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
 }
 
 }  // namespace tpmlp

@@ -289,6 +289,37 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
 // a K-contiguous operand (or 64 K-rows of an M/N-contiguous one).
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
 
+// The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
+// launch of 256x256 tiles (eight waves, K step 64, two stages) when together
+// they fill the chip once (at least 3/4 of the CUs, at most all of them) and
+// the first product's tile count is a multiple of 8 (so each workgroup keeps
+// its XCD within its product).  *done reports whether the pair ran; when it
+// did not, nothing was launched.
+int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStream_t s, bool* done) {
+  *done = false;
+  if (dtype != TPMLP_BF16 || a0.M <= 0 || a0.N <= 0 || a1.M <= 0 || a1.N <= 0) return TPMLP_OK;
+  if (a0.lda >= kMaxLd || a0.ldb >= kMaxLd || a1.lda >= kMaxLd || a1.ldb >= kMaxLd) return TPMLP_OK;
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  constexpr int BM = 256, BN = 256, BKT = 64;
+  auto prep = [&](GemmArgs& a) {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    a.group_m = std::max(1, std::min(a.tiles_m, (cus / 8) / a.tiles_n));
+    a.splits = 1;
+    a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
+    a.clk = nullptr;
+    return (int64_t)a.tiles_m * a.tiles_n;
+  };
+  const int64_t n0 = prep(a0), n1 = prep(a1);
+  if (n0 % 8 != 0 || n0 + n1 > cus || 4 * (n0 + n1) < 3 * (int64_t)cus) return TPMLP_OK;
+  a0.clk = prof_clock_slot(role);   // the clock of the first product's workgroup 0
+  *done = true;
+  return launch(role, "gemm_bf16_pair_kernel<256,256,0,0,0,2,1,64,4>",
+                gemm_bf16_pair_kernel<BM, BN, false, false, kEpiF32, 2, 1, BKT, 4>, dim3((unsigned)(n0 + n1)),
+                dim3(512), s, a0, a1, (int)n0);
+}
+
 template <bool AK, bool BKM, int EPI>
 int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return TPMLP_OK;
@@ -578,16 +609,20 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
     TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 255) / 256)),
                      dim3(256), s, (const float*)cs, rows, (int)Fs, db1_shard));
   }
-  // dW2_i = A_i^T dZ
-  a = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
-  a.C = dW2_shard;
-  a.ldc = h;
-  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad2", dtype, a, s)));
-  // dW1_i = X^T dH_i
-  a = gemm_args(X, h, dH, Fs, h, Fs, T);
-  a.C = dW1_shard;
-  a.ldc = Fs;
-  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad1", dtype, a, s)));
+  // dW2_i = A_i^T dZ and dW1_i = X^T dH_i: one paired launch when together
+  // they fill the chip once, else one launch each.
+  GemmArgs w2 = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
+  w2.C = dW2_shard;
+  w2.ldc = h;
+  GemmArgs w1 = gemm_args(X, h, dH, Fs, h, Fs, T);
+  w1.C = dW1_shard;
+  w1.ldc = Fs;
+  bool paired = false;
+  TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
+  if (!paired) {
+    TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad2", dtype, w2, s)));
+    TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad1", dtype, w1, s)));
+  }
   // dX_i = dH_i W1_i^T
   a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
   a.C = dX_partial;

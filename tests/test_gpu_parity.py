@@ -34,6 +34,9 @@ SHAPES = [
     ("bf16", 513, 512, 2048, 4),
     ("bf16", 1, 16, 32, 2),
     ("bf16", 77, 136, 24, 3),
+    # h = 4096, F/tp = 2048: the two weight gradients run as one paired launch
+    # (128 + 128 tiles of 256x256), with a ragged K = T
+    ("bf16", 300, 4096, 4096, 2),
     ("f32", 128, 256, 1024, 2),
     ("f32", 45, 20, 24, 2),
 ]
