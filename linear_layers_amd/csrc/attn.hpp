@@ -280,20 +280,21 @@ struct AttnBwdArgs {
   int64_t lddq, lddk, lddv;
   int batch, seq, heads, causal;
   float scale, scale_log2;
-  float* dq_part;     // causal: [batch][heads][query blocks][chunks][128][128] fp32 partial dQ
+  float* dq_part;     // causal: [batch][heads][dq_items][128][128] fp32 partial dQ, one per work item
   int dq_chunks;      // key chunks of the longest query block (1: no partials)
+  int dq_kc;          // key blocks per chunk (even)
+  int dq_items;       // work items (workgroups) per (sequence, head)
 };
 
-// Causal dQ work is split along keys: a query block of 128 rows sees up to
-// 2 (b + 1) key blocks of 64; they are taken in chunks of kAttnDqChunk key
-// blocks, one workgroup per (block, chunk), so no workgroup does more than
-// kAttnDqChunk iterations.  Chunk c exists for blocks b >= kAttnDqChunkRows * c.
-constexpr int kAttnDqChunk = 16;
-constexpr int kAttnDqChunkRows = kAttnDqChunk * 64 / 128;
-
-__device__ __forceinline__ int attn_dq_chunks(int b, int seq) {
+// Causal dQ work is split along keys: a query block b of 128 rows sees up to
+// 2 (b + 1) key blocks of 64; they are taken in chunks of kc key blocks (kc
+// even: 16, or more so that no block has more than 8 chunks), one workgroup
+// per (block, chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items
+// are numbered chunk by chunk, the blocks of one chunk from the last down:
+// item(b, c) = sum over c' < c of (nqb - c' kc / 2), plus nqb - 1 - b.
+__device__ __forceinline__ int attn_dq_chunks(int b, int seq, int kc) {
   const int kv_end = min(seq, (b + 1) * 128);
-  return ((kv_end + 63) / 64 + kAttnDqChunk - 1) / kAttnDqChunk;
+  return ((kv_end + 63) / 64 + kc - 1) / kc;
 }
 
 // D[head][t] = sum over the head's 128 columns of dO * O; 16 lanes per (row, head).
@@ -670,8 +671,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   if (p.causal) {
     int id = (int)blockIdx.x;
     // The grid holds exactly the chunks that exist; the bound only guards the loop.
-    while (chunk < p.dq_chunks && id >= nqb - kAttnDqChunkRows * chunk) {
-      id -= nqb - kAttnDqChunkRows * chunk;
+    while (chunk < p.dq_chunks && id >= nqb - (p.dq_kc / 2) * chunk) {
+      id -= nqb - (p.dq_kc / 2) * chunk;
       ++chunk;
     }
     if (chunk >= p.dq_chunks) return;   // uniform across the workgroup, before any barrier
@@ -717,8 +718,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     for (int v = 0; v < 16; ++v) dq[f][v] = 0.0f;
   }
   const int kv_end = p.causal ? min(seq, q0 + kAttnBQ) : seq;
-  const int j0 = p.causal ? chunk * kAttnDqChunk : 0;
-  const int j1 = p.causal ? min((kv_end + kAttnBK - 1) / kAttnBK, j0 + kAttnDqChunk) : (kv_end + kAttnBK - 1) / kAttnBK;
+  const int j0 = p.causal ? chunk * p.dq_kc : 0;
+  const int j1 = p.causal ? min((kv_end + kAttnBK - 1) / kAttnBK, j0 + p.dq_kc) : (kv_end + kAttnBK - 1) / kAttnBK;
   issue(j0, (lds_char*)st0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
@@ -784,10 +785,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
-  if (p.causal && attn_dq_chunks(qb, seq) > 1) {
-    // one of several chunks: its fp32 partial (unscaled) for attn_bwd_dq_sum_kernel
+  if (p.causal && attn_dq_chunks(qb, seq, p.dq_kc) > 1) {
+    // one of several chunks: its fp32 partial (unscaled) in this item's slot, for attn_bwd_dq_sum_kernel
     float* dst = p.dq_part +
-                 ((((int64_t)blockIdx.z * p.heads + head) * nqb + qb) * p.dq_chunks + chunk) * (kAttnBQ * kAttnD) +
+                 (((int64_t)blockIdx.z * p.heads + head) * p.dq_items + blockIdx.x) * (kAttnBQ * kAttnD) +
                  (int64_t)(32 * wave + (lane & 31)) * kAttnD + 4 * h;
 #pragma unroll
     for (int f = 0; f < 4; ++f)
@@ -802,24 +803,28 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
 
 // dQ of the causal query blocks that were split into several key chunks: the
 // chunks' partials added in chunk order, scaled, rounded to bf16.  Workgroup
-// (x, head, sequence) covers 16 rows of block kAttnDqChunkRows + x / 8; each
-// thread owns 8 consecutive columns of one row.
+// (x, head, sequence) covers 16 rows of block kc / 2 + x / 8 (the first block
+// with two chunks); each thread owns 8 consecutive columns of one row.
 __global__ void __launch_bounds__(256) attn_bwd_dq_sum_kernel(const AttnBwdArgs p) {
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const int qb = kAttnDqChunkRows + (int)blockIdx.x / 8;
+  const int half = p.dq_kc / 2;
+  const int qb = half + (int)blockIdx.x / 8;
   const int r = 16 * ((int)blockIdx.x % 8) + (int)threadIdx.x / 16;   // row within the block
   const int c8 = 8 * ((int)threadIdx.x % 16);                          // first of 8 columns
   const int head = blockIdx.y;
-  const int nch = attn_dq_chunks(qb, seq);
-  const float* src = p.dq_part +
-                     (((int64_t)blockIdx.z * p.heads + head) * nqb + qb) * p.dq_chunks * (kAttnBQ * kAttnD) +
-                     r * kAttnD + c8;
+  const int nch = attn_dq_chunks(qb, seq, p.dq_kc);
+  const float* base = p.dq_part + ((int64_t)blockIdx.z * p.heads + head) * p.dq_items * (kAttnBQ * kAttnD) +
+                      r * kAttnD + c8;
+  // slot of chunk c of block qb: the items of chunks before c, then nqb - 1 - qb
+  int slot = nqb - 1 - qb;
+  const float* src = base + (int64_t)slot * (kAttnBQ * kAttnD);
   f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src);
   f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + 4);
   for (int c = 1; c < nch; ++c) {
-    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * (kAttnBQ * kAttnD));
-    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + (int64_t)c * (kAttnBQ * kAttnD) + 4);
+    slot += nqb - half * (c - 1);
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(base + (int64_t)slot * (kAttnBQ * kAttnD));
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(base + (int64_t)slot * (kAttnBQ * kAttnD) + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       a0[e] += x0[e];

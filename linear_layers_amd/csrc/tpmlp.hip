@@ -1001,9 +1001,22 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
 }
 
 namespace {
-// Causal dQ chunks of the longest query block (see attn_dq_chunks).
-int64_t attn_dq_chunks_max(int64_t seq) {
-  return seq > 0 ? ((seq + 63) / 64 + kAttnDqChunk - 1) / kAttnDqChunk : 0;
+// Causal dQ key chunks (see attn_dq_chunks): kc key blocks per chunk, 16 or
+// more (even) so that the longest query block has at most 8 chunks; the
+// chunk count of that block; and the work items per (sequence, head).
+struct AttnDqPlan {
+  int64_t kc, chunks, items;
+};
+
+AttnDqPlan attn_dq_plan(int64_t seq) {
+  AttnDqPlan pl{16, 0, 0};
+  if (seq <= 0) return pl;
+  const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const int64_t need = (nkb + 7) / 8;
+  if (need > pl.kc) pl.kc = need + (need & 1);
+  pl.chunks = (nkb + pl.kc - 1) / pl.kc;
+  for (int64_t c = 0; c < pl.chunks && (pl.kc / 2) * c < nqb; ++c) pl.items += nqb - (pl.kc / 2) * c;
+  return pl;
 }
 
 struct AttnBwdWs {
@@ -1016,8 +1029,8 @@ AttnBwdWs attn_bwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnBwdWs w;
   w.d_bytes = align256((size_t)batch * seq * heads * sizeof(float));
   w.part_off = w.d_bytes;
-  const int64_t ch = attn_dq_chunks_max(seq), nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const size_t part = ch > 1 ? (size_t)batch * heads * nqb * ch * kAttnBQ * kAttnD * sizeof(float) : 0;
+  const AttnDqPlan pl = attn_dq_plan(seq);
+  const size_t part = pl.chunks > 1 ? (size_t)batch * heads * pl.items * kAttnBQ * kAttnD * sizeof(float) : 0;
   w.total = w.part_off + align256(part);
   return w;
 }
@@ -1076,7 +1089,10 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.dq_chunks = (int)attn_dq_chunks_max(seq);
+  const AttnDqPlan dqp = attn_dq_plan(seq);
+  a.dq_chunks = (int)dqp.chunks;
+  a.dq_kc = (int)dqp.kc;
+  a.dq_items = (int)dqp.items;
   a.dq_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + W.part_off);
   hipStream_t s = (hipStream_t)stream;
   const int64_t items = T * heads;
@@ -1086,18 +1102,14 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   // Causal dQ: one workgroup per (query block, key chunk); blocks with several
   // chunks are summed by attn_bwd_dq_sum_kernel.
   const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  int64_t dq_items = nqb;
-  if (causal) {
-    dq_items = 0;
-    for (int64_t c = 0; kAttnDqChunkRows * c < nqb; ++c) dq_items += nqb - kAttnDqChunkRows * c;
-  }
+  const int64_t dq_items = causal ? dqp.items : nqb;
   TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
                    dim3((unsigned)(causal ? (nkb + 1) / 2 : nkb), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
   TPMLP_TRY(launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
                    dim3((unsigned)dq_items, (unsigned)heads, (unsigned)batch), dim3(256), s, a));
-  if (causal && a.dq_chunks > 1 && nqb > kAttnDqChunkRows)
+  if (causal && dqp.chunks > 1 && nqb > dqp.kc / 2)
     TPMLP_TRY(launch("attn_bwd_dq_sum", "attn_bwd_dq_sum_kernel", attn_bwd_dq_sum_kernel,
-                     dim3((unsigned)(8 * (nqb - kAttnDqChunkRows)), (unsigned)heads, (unsigned)batch), dim3(256), s, a));
+                     dim3((unsigned)(8 * (nqb - dqp.kc / 2)), (unsigned)heads, (unsigned)batch), dim3(256), s, a));
   return TPMLP_OK;
 }
 

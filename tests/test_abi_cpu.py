@@ -176,6 +176,9 @@ def test_attn_block_validation():
     assert f(None, 1, 8, 512, 4, 128, 2, 3, 0.1, P, P, P, P, P, P, P) == E_VALUE     # causal not 0/1
     assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, None, P) == E_NULL   # lse required
     assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P + 8, P, P, P, P) == E_ALIGN
+    # causal dQ partials: none up to 1024 tokens; at 32K tokens at most 8 key chunks per query block
+    assert tl.attn_bwd_workspace_bytes(1, 1024, 10) == 1024 * 10 * 4
+    assert tl.attn_bwd_workspace_bytes(1, 32768, 10) <= 32768 * 10 * 4 + 256 * 10 * 4.5 * 65536
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 3) == 0
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 2) >= 8 * 256 * 2 * 4
     b = tl.lib.tp_attn_bwd

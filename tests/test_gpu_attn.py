@@ -177,6 +177,28 @@ def test_attn_bwd_workload_two_heads():
         assert_close(g[:, 2 * w:][:, cs], ref["dV"], "bf16", f"dV head {hd}")
 
 
+@pytest.mark.slow
+def test_attn_bwd_long_sequence_sampled():
+    """8400 tokens (ragged), 2 sequences, 2 heads, causal: past 8192 tokens the causal dQ key chunks grow
+    (18 key blocks of 64 here, 8 chunks for the last query block).  Sampled rows of dQ, dK, dV of two
+    (sequence, head) pairs against the oracle, rows on both sides of the chunk edges (every 1152 keys)."""
+    need_gpu()
+    batch, seq, heads = 2, 8400, 2
+    _say(f"attn bwd long batch={batch} seq={seq} heads={heads}")
+    qkv, dO, dqkv = _bwd_case(batch, seq, heads, True, seed=8400)
+    w = heads * D
+    f, fd, g = synth.to_f64(qkv, "bf16"), synth.to_f64(dO, "bf16"), to_f64(dqkv)
+    rows = np.array([0, 1, 127, 1151, 1152, 1153, 2303, 2304, 4607, 4608, 6000, 8063, 8064, 8270, 8271, 8399])
+    for b, hd in ((0, 0), (1, 1)):
+        ref = oat.attn_bwd_rows(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], fd, batch, seq, heads, D, True, D ** -0.5,
+                                b, hd, rows)
+        r = b * seq + rows
+        cs = slice(hd * D, (hd + 1) * D)
+        assert_close(g[r][:, :w][:, cs], ref["dQ"], "bf16", f"dQ seq {b} head {hd}")
+        assert_close(g[r][:, w:2 * w][:, cs], ref["dK"], "bf16", f"dK seq {b} head {hd}")
+        assert_close(g[r][:, 2 * w:][:, cs], ref["dV"], "bf16", f"dV seq {b} head {hd}")
+
+
 # ----------------------------------------------------------------------------
 # The head-sharded attention block: QKV projection, attention over the shard's
 # heads, O-projection partial, and its backward, through tp_attn_fwd/bwd.
