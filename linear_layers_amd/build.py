@@ -13,8 +13,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpmlp.so")
 SOURCES = [os.path.join(CSRC, "tpmlp.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("common.hpp", "gemm.hpp", "reduce.hpp")] + [
-    os.path.join(ROOT, "include", "tpmlp.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

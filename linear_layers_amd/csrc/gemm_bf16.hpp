@@ -15,9 +15,10 @@
 //     (chunk c of row r at position c ^ ((r >> 2) & 3)) and read with
 //     ds_read_b128: one read gives a lane 8 consecutive K values.
 //   * An M/N-contiguous tile is stored as 32 K-rows of BM (or BN) elements
-//     (16-byte chunk q of K-row k at position q ^ 4*(k&3)) and read with
-//     ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit values across
-//     groups of 16 lanes, so two reads give a lane its 8 K values.
+//     (16-byte chunk q of K-row k at position q ^ 4*(k&3); in a row whose
+//     chunk count is not a multiple of 16, the last 8 chunks at q ^ 4*(k&1))
+//     and read with ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit
+//     values across groups of 16 lanes, so two reads give a lane its 8 K values.
 //   * The MFMA takes the B fragment as its first operand and the A fragment
 //     as its second, so each lane's accumulators hold 4 consecutive output
 //     columns of one row, which the epilogue stores as 8- or 16-byte vectors.
@@ -58,10 +59,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Position of 16-byte chunk q of K-row k in an M/N-contiguous tile.
-__device__ __forceinline__ int swz_t(int k, int q) { return q ^ ((k & 3) << 2); }
-
-template <int ROWS, bool KMAJ, int BKT, int NW = 4>
+// ROWS (M or N) x BKT (K) operand tile; NF fragment blocks of 32 rows per wave.
+template <int ROWS, bool KMAJ, int BKT, int NW = 4, int NF = 4>
 struct Bf16Tile {
   // One operand tile of ROWS (M or N) x BKT (K) bf16 = ROWS * BKT * 2 bytes.
   static constexpr int CPR = BKT / 8;           // 16-byte chunks per K-contiguous row
@@ -69,12 +68,22 @@ struct Bf16Tile {
   static constexpr int SLOTS = ROWS * CPR;      // 16-byte slots
   static constexpr int INSTR = SLOTS / (64 * NW);  // buffer loads per wave
   static constexpr int QPR = ROWS / 8;          // chunks per K-row (M/N-contiguous layout)
+  static constexpr int QPR16 = QPR & ~15;       // chunks under the 4-row swizzle; the rest (8) under a 2-row one
+  static constexpr int NFB = KMAJ ? 4 : (NF > 4 ? NF : 4);
   static_assert(BKT == 32 || BKT == 64, "K step of 32 or 64");
   static_assert(SLOTS % (64 * NW) == 0, "tile too small for the waves");
-  static_assert(KMAJ || ROWS >= 128, "the K-row swizzle needs at least 16 chunks per K-row");
+  static_assert(KMAJ || (ROWS >= 128 && (QPR - QPR16 == 0 || QPR - QPR16 == 8)),
+                "the K-row swizzle needs at least 16 chunks per K-row, in groups of 16 and at most one of 8");
 
   uint32_t voff[INSTR];   // per-lane byte offsets in the re-based buffer
-  uint32_t fbase[4];      // per-lane LDS offsets of the MFMA fragments
+  uint32_t fbase[NFB];    // per-lane LDS offsets of the MFMA fragments
+
+  // Position of 16-byte chunk q of K-row k in an M/N-contiguous tile: an XOR
+  // that stays inside q's group of 16 chunks (or the trailing group of 8), so
+  // it is an involution on the row.
+  static __device__ __forceinline__ int swz_t(int k, int q) {
+    return q < QPR16 ? q ^ ((k & 3) << 2) : q ^ ((k & 1) << 2);
+  }
 
   // Position of chunk c of row r in a K-contiguous tile: conflict-free for
   // one row written as CPR chunks and for 16 consecutive rows read at one chunk.
@@ -95,7 +104,7 @@ struct Bf16Tile {
         voff[j] = (uint32_t)(((int64_t)k * ld + q * 8) * 2);
       }
     }
-    // Fragment rows are w0 + 32 f + (lane & 31) with w0 a multiple of 64.
+    // Fragment rows are w0 + 32 f + (lane & 31) with w0 a multiple of 32.
     if constexpr (KMAJ) {
       const uint32_t lb = (uint32_t)(w0 + (lane & 31)) * (uint32_t)(CPR * 16);
       if constexpr (CPR == 4) {
@@ -106,22 +115,26 @@ struct Bf16Tile {
         fbase[2] = fbase[3] = 0;
       } else {
         // chunk 2S + lane/32 of row r at (2S + lane/32) ^ (r & 7) ^ ((r >> 3) & 7); with
-        // r = w0 + 32 f + (lane & 31) the XOR term is L ^ 4 (f & 1), so the bases are
-        // indexed by X = (2S ^ 4(f&1)) / 2.
-        const int L = (lane >> 5) ^ (lane & 7) ^ ((lane & 31) >> 3);
+        // r = w0 + 32 f + (lane & 31) the XOR term is L ^ 4 (f & 1) (L takes the
+        // parity of w0 / 32), so the bases are indexed by X = (2S ^ 4(f&1)) / 2.
+        const int L = (lane >> 5) ^ (lane & 7) ^ ((lane & 31) >> 3) ^ (((w0 >> 5) & 1) << 2);
 #pragma unroll
         for (int x = 0; x < 4; ++x) fbase[x] = lb + (uint32_t)((L ^ (2 * x)) << 4);
       }
     } else {
       // 16-lane group g reads K-rows kb + j/4 (j = lane & 15) at column
       // w0 + 32 f + 16 (g&1) + 4 (j&3); the transpose hands lane j the 4 K
-      // values of column w0 + 32 f + 16 (g&1) + j.  (k & 3) = j >> 2.
+      // values of column w0 + 32 f + 16 (g&1) + j.  (k & 3) = j >> 2.  The
+      // four chunks of fragment f start at a multiple of 4, in one swizzle group.
       const int g = lane >> 4, j = lane & 15;
       const int qlow = 2 * (g & 1) + ((j & 3) >> 1);
       const int kl = 8 * (g >> 1) + (j >> 2);
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        fbase[f] = (uint32_t)((kl * QPR + ((((w0 >> 3) + 4 * f) ^ (j & 12)) | qlow)) * 16 + (j & 1) * 8);
+      for (int f = 0; f < NFB; ++f) {
+        const int qb = (w0 >> 3) + 4 * f;
+        const int x = qb < QPR16 ? (j & 12) : (j & 4);
+        fbase[f] = (uint32_t)((kl * QPR + ((qb ^ x) | qlow)) * 16 + (j & 1) * 8);
+      }
     }
   }
 
@@ -172,7 +185,7 @@ struct Bf16Tile {
       constexpr int X = CPR == 4 ? S : (((2 * S) ^ (4 * (F & 1))) >> 1);
       return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src + fbase[X] + F * 32 * CPR * 16);
     } else {
-      static_assert(F < 4, "too many fragment blocks");
+      static_assert(F < NFB, "too many fragment blocks");
       const lds_char* p0 = src + fbase[F] + 16 * S * QPR * 16;
       const lds_char* p1 = p0 + 4 * QPR * 16;
       const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p0);
@@ -201,15 +214,15 @@ struct FragLoop<NF, NF, S> {
 };
 
 // One workgroup's tile: workgroup pid of the nwg that compute product p.
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC, int BKT, int WGN>
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC, int BKT, int WGN, int WGM>
 __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int nwg) {
-  constexpr int WGM = 2;                     // waves along M
-  constexpr int NW = WGM * WGN, NT = 64 * NW;
+  constexpr int NW = WGM * WGN, NT = 64 * NW;  // WGM x WGN waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
+  static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles of whole 32x32 blocks");
   constexpr int NSUB = BKT / 16;             // MFMA K-substeps per step
-  using TA = Bf16Tile<BM, A_KMAJ, BKT, NW>;
-  using TB = Bf16Tile<BN, B_KMAJ, BKT, NW>;
+  using TA = Bf16Tile<BM, A_KMAJ, BKT, NW, FM>;
+  using TB = Bf16Tile<BN, B_KMAJ, BKT, NW, FN>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;
   constexpr int LPS = TA::INSTR + TB::INSTR;  // buffer loads per wave per step
   static_assert(NS >= 2 && NS <= 6, "2..6 stages");
@@ -699,28 +712,34 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
     if (p.colsum) {
       __syncthreads();
       for (int c = tid; c < BN; c += NT) {
-        if (n0 + c < N) p.colsum[(int64_t)tmi * N + n0 + c] = red[c] + red[BN + c];
+        float t = red[c];
+#pragma unroll
+        for (int r = 1; r < WGM; ++r) t += red[r * BN + c];   // wave rows in order
+        if (n0 + c < N) p.colsum[(int64_t)tmi * N + n0 + c] = t;
       }
     }
   }
 }
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
-__global__ void __launch_bounds__(128 * WGN, OCC)
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2,
+          int WGM = 2>
+__global__ void __launch_bounds__(64 * WGM * WGN, OCC)
 gemm_bf16_kernel(const GemmArgs p) {
-  gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p, (int)blockIdx.x, (int)gridDim.x);
+  gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Two independent products of the same shape class in one launch: workgroups
 // [0, n0) compute p0, the rest p1 (n0 a multiple of 8).  Used where each alone
 // would leave CUs idle and together they fill the chip once.
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2>
-__global__ void __launch_bounds__(128 * WGN, OCC)
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2,
+          int WGM = 2>
+__global__ void __launch_bounds__(64 * WGM * WGN, OCC)
 gemm_bf16_pair_kernel(const GemmArgs p0, const GemmArgs p1, int n0) {
   if ((int)blockIdx.x < n0)
-    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p0, (int)blockIdx.x, n0);
+    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p0, (int)blockIdx.x, n0);
   else
-    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN>(p1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
+    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p1, (int)blockIdx.x - n0,
+                                                                      (int)gridDim.x - n0);
 }
 
 }  // namespace tpmlp
