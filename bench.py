@@ -501,6 +501,8 @@ class AttnBlockStep:
         self.dWqkv = torch.empty((h, 3 * w), dtype=torch.float32, device=dev)
         self.dWo = torch.empty((w, h), dtype=torch.float32, device=dev)
         self.ws = torch.empty(tl.tp_attn_bwd_workspace_bytes(1, T, wl.heads, tp), dtype=torch.uint8, device=dev)
+        self.fws = torch.empty(max(1, tl.tp_attn_fwd_workspace_bytes(1, T, wl.heads, tp)), dtype=torch.uint8,
+                               device=dev)
         for i in range(1, tp):
             self.fwd(i)
             self.bwd(i)
@@ -508,7 +510,7 @@ class AttnBlockStep:
     def fwd(self, i):
         s = self
         s.tl.tp_attn_fwd(s.X, s.Wqkv[i], s.Wo[i], s.QKV, s.O, s.lse, s.Zp[i], 1, s.wl.T, s.wl.heads, s.wl.tp,
-                         causal=True, stream=s.stream)
+                         causal=True, workspace=s.fws, stream=s.stream)
 
     def bwd(self, i):
         s = self

@@ -295,10 +295,22 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
  * Q, K, V (bf16, row strides ldq, ldk, ldv — e.g. the three blocks of the
  * fused QKV output, ld = 3*heads*head_dim) and writes the same columns of O
  * (bf16, ldo).  head_dim must be 128.  lse [heads, T] fp32 (row h*T + t)
- * receives log(sum_j exp(s_tj)) of each query row, or pass NULL. */
+ * receives log(sum_j exp(s_tj)) of each query row, or pass NULL.
+ * workspace: device memory of at least attn_fwd_workspace_bytes() bytes,
+ * 256-byte aligned, owned by the caller; causal calls on sequences longer
+ * than 1024 keep per-chunk partial results there (the key range of a query
+ * block is split over several workgroups and merged by log-sum-exp).  It may
+ * be NULL (with workspace_bytes 0) when that size is 0 or causal = 0. */
 int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
              const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, void* O,
-             int64_t ldo, float* lse);
+             int64_t ldo, float* lse, void* workspace, size_t workspace_bytes);
+
+/* Bytes of device workspace a causal attn_fwd needs (0 on bad args, and for
+ * sequences of at most 1024): fp32 partial O tiles of 64 KB plus 512 bytes
+ * of row log-sum-exp per chunk of the query blocks whose keys are split
+ * (2.5 tiles per query block of 128 rows, per head and sequence, at 4096
+ * tokens; at most 8 chunks per block). */
+size_t attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads);
 
 /* Bytes of device workspace attn_bwd needs (0 on bad args): fp32 [heads, T]
  * row sums and, for causal sequences longer than 1024, fp32 partial dQ tiles
@@ -335,10 +347,16 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
  *   O_save       [T, w] (ld w) bf16: the attention output of the shard's heads
  *   lse          [H/tp, T] fp32: log-sum-exp of each query row (as attn_fwd)
  *   Z_partial    [T, h] fp32 (ld h): this shard's partial of the output
- * causal and scale as in attn_fwd. */
+ * causal and scale as in attn_fwd; workspace as attn_fwd's for the shard's
+ * H/tp heads, at least tp_attn_fwd_workspace_bytes() bytes (checked before
+ * anything is launched). */
 int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
                 int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
-                void* QKV_save, void* O_save, float* lse, float* Z_partial);
+                void* QKV_save, void* O_save, float* lse, float* Z_partial, void* workspace,
+                size_t workspace_bytes);
+
+/* Bytes of device workspace tp_attn_fwd needs (0 on bad args or when none). */
+size_t tp_attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int head_dim, int tp_size);
 
 /* Bytes of device workspace tp_attn_bwd needs (0 on bad args). */
 size_t tp_attn_bwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int head_dim, int tp_size);

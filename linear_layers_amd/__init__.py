@@ -25,7 +25,8 @@ __all__ = [
     "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
     "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "attn_bwd",
-    "attn_bwd_workspace_bytes", "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace_bytes", "profile_enable",
+    "attn_bwd_workspace_bytes", "attn_fwd_workspace_bytes", "tp_attn_fwd", "tp_attn_fwd_workspace_bytes",
+    "tp_attn_bwd", "tp_attn_bwd_workspace_bytes", "profile_enable",
     "profile_collect", "status_string", "version",
 ]
 
@@ -59,11 +60,13 @@ _SIGNATURES = {
     "sp_partial_sum_dropout_residual": [_vp, _int, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp,
                                         _i64],
     "sp_dropout_bwd": [_vp, _i64, _i64, _vp, _i64, _f32, _u64, _i64, _vp, _i64],
-    "attn_fwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
+    "attn_fwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _sz],
+    "attn_fwd_workspace_bytes": [_i64, _i64, _int],
     "attn_bwd_workspace_bytes": [_i64, _i64, _int],
     "attn_bwd": [_vp, _i64, _i64, _int, _int, _int, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                  _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz],
-    "tp_attn_fwd": [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_attn_fwd": [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz],
+    "tp_attn_fwd_workspace_bytes": [_i64, _i64, _int, _int, _int],
     "tp_attn_bwd_workspace_bytes": [_i64, _i64, _int, _int, _int],
     "tp_attn_bwd": [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                     _vp, _vp, _sz],
@@ -73,7 +76,9 @@ _SIGNATURES = {
     "tpmlp_profile_enable": [ctypes.c_char_p],
     "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
 }
-_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_attn_bwd_workspace_bytes": _sz, "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_attn_bwd_workspace_bytes": _sz,
+             "attn_fwd_workspace_bytes": _sz, "tp_attn_fwd_workspace_bytes": _sz,
+             "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
              "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
 
 
@@ -333,13 +338,23 @@ def sp_dropout_bwd(dOut, dZ, p: float, seed: int, row0: int, stream=None) -> Non
                                      _ptr(dZ), _ld(dZ, h)))
 
 
+def attn_fwd_workspace_bytes(batch: int, seq: int, heads: int) -> int:
+    return int(_get_lib().attn_fwd_workspace_bytes(batch, seq, heads))
+
+
 def attn_fwd(Q, K, V, O, batch: int, seq: int, heads: int, causal: bool = True, scale: Optional[float] = None,
-             lse=None, head_dim: int = 128, stream=None) -> None:
-    """O = softmax(Q K^T * scale) V per head (bf16; head h in columns [128h, 128h+128)); lse [heads, T] fp32."""
+             lse=None, workspace=None, head_dim: int = 128, stream=None) -> None:
+    """O = softmax(Q K^T * scale) V per head (bf16; head h in columns [128h, 128h+128)); lse [heads, T] fp32;
+    workspace a device uint8 tensor (allocated here if None and needed)."""
     w = heads * head_dim
     sc = head_dim ** -0.5 if scale is None else scale
+    if workspace is None and causal:
+        n = attn_fwd_workspace_bytes(batch, seq, heads)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=Q.device)
     _check(_get_lib().attn_fwd(_stream(stream, O), batch, seq, heads, head_dim, int(bool(causal)), sc, _ptr(Q),
-                               _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(lse)))
+                               _ld(Q, w), _ptr(K), _ld(K, w), _ptr(V), _ld(V, w), _ptr(O), _ld(O, w), _ptr(lse),
+                               _ptr(workspace), 0 if workspace is None else workspace.numel()))
 
 
 def attn_bwd_workspace_bytes(batch: int, seq: int, heads: int) -> int:
@@ -360,18 +375,27 @@ def attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, batch: int, seq: int, heads: int, 
                                _ld(dV, w), _ptr(workspace), workspace.numel()))
 
 
+def tp_attn_fwd_workspace_bytes(batch: int, seq: int, heads: int, tp_size: int, head_dim: int = 128) -> int:
+    return int(_get_lib().tp_attn_fwd_workspace_bytes(batch, seq, heads, head_dim, tp_size))
+
+
 def tp_attn_fwd(X, Wqkv_shard, Wo_shard, QKV_save, O_save, lse, Z_partial, batch: int, seq: int, heads: int,
-                tp_size: int, causal: bool = True, scale: Optional[float] = None, head_dim: int = 128,
-                stream=None) -> None:
-    """One shard of the head-sharded attention block (contiguous tensors; heads = all heads of the layer)."""
+                tp_size: int, causal: bool = True, scale: Optional[float] = None, workspace=None,
+                head_dim: int = 128, stream=None) -> None:
+    """One shard of the head-sharded attention block (contiguous tensors; heads = all heads of the layer);
+    workspace a device uint8 tensor (allocated here if None and needed)."""
     h = X.shape[1]
     sc = head_dim ** -0.5 if scale is None else scale
     for n, t in (("X", X), ("Wqkv_shard", Wqkv_shard), ("Wo_shard", Wo_shard), ("QKV_save", QKV_save),
                  ("O_save", O_save), ("lse", lse), ("Z_partial", Z_partial)):
         _require_contiguous(n, t)
+    if workspace is None and causal:
+        n = tp_attn_fwd_workspace_bytes(batch, seq, heads, tp_size, head_dim)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=X.device)
     _check(_get_lib().tp_attn_fwd(_stream(stream, X), batch, seq, h, heads, head_dim, tp_size, int(bool(causal)), sc,
                                   _ptr(X), _ptr(Wqkv_shard), _ptr(Wo_shard), _ptr(QKV_save), _ptr(O_save), _ptr(lse),
-                                  _ptr(Z_partial)))
+                                  _ptr(Z_partial), _ptr(workspace), 0 if workspace is None else workspace.numel()))
 
 
 def tp_attn_bwd_workspace_bytes(batch: int, seq: int, heads: int, tp_size: int, head_dim: int = 128) -> int:

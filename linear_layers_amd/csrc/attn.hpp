@@ -6,8 +6,11 @@
 // a query block's attention accumulated key block by key block).  Heads are
 // independent (damodev.csdn.net/6a43867610ee7a33f284fb9e.html, 1.2.2; the
 // head-sharded projections on io.zouht.com/197.html, 2.2.1), so the grid is
-// (query blocks, heads, batch); when causal, a workgroup takes two query
-// blocks, a long and a short one, so that all do the same work.
+// (work items, heads, batch).  When causal, a query block's keys are cut into
+// chunks (one workgroup each) so that no workgroup's share is much longer than
+// another's and the grid holds enough workgroups to fill the chip; the
+// normalised partial results of a block's chunks are merged by their
+// log-sum-exp (attn_fwd_combine_kernel).
 //
 // Layout: T = batch * seq token rows; head h reads columns [128h, 128h+128)
 // of Q, K and V (each with its own row stride, e.g. the three blocks of the
@@ -40,11 +43,26 @@ struct AttnArgs {
   float* lse;         // [heads, batch * seq] natural-log row log-sum-exp, or null
   int batch, seq, heads, causal;
   float scale_log2;   // scale * log2(e): scores are kept in base-2 units
+  // causal key chunks (see attn_key_chunks); partials of blocks with several
+  float* o_part;      // [batch][heads][items][128][128] fp32 O of one chunk, normalised by its own sum
+  float* lse_part;    // [batch][heads][items][128] base-2 log-sum-exp of that chunk
+  int chunks, kc, items;
 };
 
 constexpr int kAttnD = 128;   // head_dim
 constexpr int kAttnBQ = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kAttnBK = 64;   // keys per block
+
+// Causal work split along keys: query block b of 128 rows sees up to 2 (b + 1)
+// key blocks of 64; they are taken in chunks of kc key blocks (kc even: 16, or
+// more so that no block has more than 8 chunks), one workgroup per (block,
+// chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items are numbered
+// chunk by chunk, the blocks of one chunk from the last down:
+// item(b, c) = sum over c' < c of (nqb - c' kc / 2), plus nqb - 1 - b.
+__device__ __forceinline__ int attn_key_chunks(int b, int seq, int kc) {
+  const int kv_end = min(seq, (b + 1) * 128);
+  return ((kv_end + 63) / 64 + kc - 1) / kc;
+}
 using AttnKTile = Bf16Tile<kAttnBK, true, 64, 4>;   // 64 keys x 64 of d, K-contiguous
 using AttnVTile = Bf16Tile<kAttnD, false, 64, 4>;   // 64 key rows x 128 of d, d contiguous
 constexpr int kAttnStage = 2 * AttnKTile::BYTES + AttnVTile::BYTES;  // 32 KB
@@ -127,12 +145,19 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  // Causal: workgroup x takes query blocks nqb - 1 - x and x, whose key ranges add
-  // up to the same work for every workgroup; otherwise block x alone.
-  const int nvb = (p.causal && (int)blockIdx.x != nqb - 1 - (int)blockIdx.x) ? 2 : 1;
-  for (int vb = 0; vb < nvb; ++vb) {
-  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
-  const int qb = p.causal ? (vb == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x) : (int)blockIdx.x;
+  // Causal: workgroup x is chunk c of query block qb (see attn_key_chunks);
+  // otherwise block x, all keys.
+  int qb = (int)blockIdx.x, chunk = 0;
+  if (p.causal) {
+    int id = (int)blockIdx.x;
+    // The grid holds exactly the chunks that exist; the bound only guards the loop.
+    while (chunk < p.chunks && id >= nqb - (p.kc / 2) * chunk) {
+      id -= nqb - (p.kc / 2) * chunk;
+      ++chunk;
+    }
+    if (chunk >= p.chunks) return;   // uniform across the workgroup, before any barrier
+    qb = nqb - 1 - id;
+  }
   const int head = blockIdx.y;
   const int64_t row_base = (int64_t)blockIdx.z * seq;
   const int q0 = qb * kAttnBQ;
@@ -166,7 +191,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   };
 
   const int kv_end = p.causal ? min(seq, q0 + kAttnBQ) : seq;
-  const int nkb = (kv_end + kAttnBK - 1) / kAttnBK;
+  const int j0 = p.causal ? chunk * p.kc : 0;
+  const int j1 = p.causal ? min((kv_end + kAttnBK - 1) / kAttnBK, j0 + p.kc) : (kv_end + kAttnBK - 1) / kAttnBK;
   float m_i = -INFINITY, l_i = 0.0f;
   f32x16_t o[4];
 #pragma unroll
@@ -174,13 +200,13 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[f][v] = 0.0f;
 
-  issue(0, (lds_char*)st0);
+  issue(j0, (lds_char*)st0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    lds_char* cur = (j & 1) ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = (j & 1) ? (lds_char*)st0 : (lds_char*)st1;
-    if (j + 1 < nkb) issue(j + 1, nxt);
+  for (int j = j0; j < j1; ++j) {
+    lds_char* cur = ((j - j0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = ((j - j0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+    if (j + 1 < j1) issue(j + 1, nxt);
     const int kv0 = j * kAttnBK;
     // A wave whose rows all precede this block (causal) has nothing to add.
     if (!(p.causal && kv0 > wq0 + 31)) {
@@ -236,8 +262,24 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     __syncthreads();                            // ... everyone's; and stage cur is free again
   }
 
-  // O = acc / l, stored as bf16 (8 consecutive columns of d per lane and 16-byte stores)
-  if (qrow < seq) {
+  // Every row of a chunk sees at least one key (chunk c starts at key
+  // 64 c kc <= the block's first row), so l_i > 0 here.
+  if (qrow < seq && p.causal && attn_key_chunks(qb, seq, p.kc) > 1) {
+    // one of several chunks: its normalised partial and base-2 log-sum-exp in
+    // this item's slot, for attn_fwd_combine_kernel
+    const float inv = 1.0f / l_i;
+    const int64_t slot = ((int64_t)blockIdx.z * p.heads + head) * p.items + blockIdx.x;
+    const int r = 32 * wave + (lane & 31);
+    float* dst = p.o_part + slot * (kAttnBQ * kAttnD) + (int64_t)r * kAttnD + 4 * h;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4_t*>(dst + 32 * f + 8 * g) =
+            f32x4_t{o[f][4 * g] * inv, o[f][4 * g + 1] * inv, o[f][4 * g + 2] * inv, o[f][4 * g + 3] * inv};
+    if (h == 0) p.lse_part[slot * kAttnBQ + r] = m_i + __log2f(l_i);
+  } else if (qrow < seq) {
+    // O = acc / l, stored as bf16 (8 consecutive columns of d per lane and 16-byte stores)
     const float inv = 1.0f / l_i;
     bf16_t* op = p.O + (row_base + qrow) * p.ldo + head * kAttnD + 8 * h;
 #pragma unroll
@@ -254,7 +296,56 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     if (p.lse != nullptr && h == 0)
       p.lse[(int64_t)head * p.batch * seq + row_base + qrow] = (m_i + __log2f(l_i)) * 0.69314718055994531f;
   }
-  }  // query blocks
+}
+
+// O and lse of the causal query blocks whose keys were split into chunks: with
+// chunk c's normalised partial O_c and base-2 log-sum-exp L_c, and M = max L_c,
+// O = sum_c 2^(L_c - M) O_c / sum_c 2^(L_c - M) and lse = M + log2 sum_c
+// 2^(L_c - M) (in natural-log units), the chunks taken in order.  Workgroup
+// (x, head, sequence) covers 16 rows of block kc / 2 + x / 8 (the first block
+// with two chunks); each thread owns 8 consecutive columns of one row.
+__global__ void __launch_bounds__(256) attn_fwd_combine_kernel(const AttnArgs p) {
+  const int seq = p.seq;
+  const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const int half = p.kc / 2;
+  const int qb = half + (int)blockIdx.x / 8;
+  const int r = 16 * ((int)blockIdx.x % 8) + (int)threadIdx.x / 16;   // row within the block
+  const int c8 = 8 * ((int)threadIdx.x % 16);                          // first of 8 columns
+  const int head = blockIdx.y;
+  const int qrow = qb * kAttnBQ + r;
+  if (qrow >= seq) return;   // no barrier below
+  const int nch = attn_key_chunks(qb, seq, p.kc);
+  const int64_t hslot = ((int64_t)blockIdx.z * p.heads + head) * p.items;
+  // slot of chunk c of block qb: the items of chunks before c, then nqb - 1 - qb
+  float mx = -INFINITY;
+  int slot = nqb - 1 - qb;
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) slot += nqb - half * (c - 1);
+    mx = fmaxf(mx, p.lse_part[(hslot + slot) * kAttnBQ + r]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.0f;
+  slot = nqb - 1 - qb;
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) slot += nqb - half * (c - 1);
+    const float wgt = __builtin_amdgcn_exp2f(p.lse_part[(hslot + slot) * kAttnBQ + r] - mx);
+    sum += wgt;
+    const float* src = p.o_part + (hslot + slot) * (kAttnBQ * kAttnD) + (int64_t)r * kAttnD + c8;
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(src);
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += wgt * x0[e];
+      acc[4 + e] += wgt * x1[e];
+    }
+  }
+  const float inv = 1.0f / sum;
+  const int64_t row = (int64_t)blockIdx.z * seq + qrow;
+  *reinterpret_cast<u32x4_t*>(p.O + row * p.ldo + head * kAttnD + c8) =
+      u32x4_t{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  if (p.lse != nullptr && c8 == 0)
+    p.lse[(int64_t)head * p.batch * seq + row] = (mx + __log2f(sum)) * 0.69314718055994531f;
 }
 
 // ================================================================ backward --
@@ -286,16 +377,7 @@ struct AttnBwdArgs {
   int dq_items;       // work items (workgroups) per (sequence, head)
 };
 
-// Causal dQ work is split along keys: a query block b of 128 rows sees up to
-// 2 (b + 1) key blocks of 64; they are taken in chunks of kc key blocks (kc
-// even: 16, or more so that no block has more than 8 chunks), one workgroup
-// per (block, chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items
-// are numbered chunk by chunk, the blocks of one chunk from the last down:
-// item(b, c) = sum over c' < c of (nqb - c' kc / 2), plus nqb - 1 - b.
-__device__ __forceinline__ int attn_dq_chunks(int b, int seq, int kc) {
-  const int kv_end = min(seq, (b + 1) * 128);
-  return ((kv_end + 63) / 64 + kc - 1) / kc;
-}
+// Causal dQ work is split along keys in the forward's chunks (attn_key_chunks).
 
 // D[head][t] = sum over the head's 128 columns of dO * O; 16 lanes per (row, head).
 __global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const AttnBwdArgs p) {
@@ -785,7 +867,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
-  if (p.causal && attn_dq_chunks(qb, seq, p.dq_kc) > 1) {
+  if (p.causal && attn_key_chunks(qb, seq, p.dq_kc) > 1) {
     // one of several chunks: its fp32 partial (unscaled) in this item's slot, for attn_bwd_dq_sum_kernel
     float* dst = p.dq_part +
                  (((int64_t)blockIdx.z * p.heads + head) * p.dq_items + blockIdx.x) * (kAttnBQ * kAttnD) +
@@ -813,7 +895,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_sum_kernel(const AttnBwdArgs 
   const int r = 16 * ((int)blockIdx.x % 8) + (int)threadIdx.x / 16;   // row within the block
   const int c8 = 8 * ((int)threadIdx.x % 16);                          // first of 8 columns
   const int head = blockIdx.y;
-  const int nch = attn_dq_chunks(qb, seq, p.dq_kc);
+  const int nch = attn_key_chunks(qb, seq, p.dq_kc);
   const float* base = p.dq_part + ((int64_t)blockIdx.z * p.heads + head) * p.dq_items * (kAttnBQ * kAttnD) +
                       r * kAttnD + c8;
   // slot of chunk c of block qb: the items of chunks before c, then nqb - 1 - qb

@@ -976,6 +976,41 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
 
 // ------------------------------------------------------ attention core --
 namespace {
+// Causal key chunks (see attn_key_chunks): kc key blocks per chunk, 16 or more
+// (even) so that the longest query block has at most 8 chunks; the chunk count
+// of that block; and the work items per (sequence, head).  The forward and the
+// dQ pass use the same chunks.
+struct AttnChunkPlan {
+  int64_t kc, chunks, items;
+};
+
+AttnChunkPlan attn_chunk_plan(int64_t seq) {
+  AttnChunkPlan pl{16, 0, 0};
+  if (seq <= 0) return pl;
+  const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
+  const int64_t need = (nkb + 7) / 8;
+  if (need > pl.kc) pl.kc = need + (need & 1);
+  pl.chunks = (nkb + pl.kc - 1) / pl.kc;
+  for (int64_t c = 0; c < pl.chunks && (pl.kc / 2) * c < nqb; ++c) pl.items += nqb - (pl.kc / 2) * c;
+  return pl;
+}
+
+// Causal forward partials when some query block has several key chunks: fp32
+// O [batch][heads][items][128][128], then fp32 base-2 lse [batch][heads][items][128].
+struct AttnFwdWs {
+  size_t lse_off, total;
+};
+
+AttnFwdWs attn_fwd_ws(int64_t batch, int64_t seq, int64_t heads) {
+  AttnFwdWs w{0, 0};
+  const AttnChunkPlan pl = attn_chunk_plan(seq);
+  if (pl.chunks <= 1) return w;
+  const size_t slots = (size_t)batch * heads * pl.items;
+  w.lse_off = align256(slots * kAttnBQ * kAttnD * sizeof(float));
+  w.total = w.lse_off + align256(slots * kAttnBQ * sizeof(float));
+  return w;
+}
+
 int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale) {
   if (head_dim != kAttnD) return fail(TPMLP_E_SHAPE, "head_dim %d: this build takes head_dim 128", head_dim);
   if (heads < 1 || heads > 65535) return fail(TPMLP_E_SHAPE, "heads = %d out of range [1, 65535]", heads);
@@ -988,9 +1023,14 @@ int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, 
 }
 }  // namespace
 
+size_t attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads) {
+  if (batch < 0 || seq < 0 || heads < 1 || batch * seq > kMaxDim) return 0;
+  return attn_fwd_ws(batch, seq, heads).total;
+}
+
 int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
              const void* Q, int64_t ldq, const void* K, int64_t ldk, const void* V, int64_t ldv, void* O,
-             int64_t ldo, float* lse) {
+             int64_t ldo, float* lse, void* workspace, size_t workspace_bytes) {
   TPMLP_TRY(check_attn(batch, seq, heads, head_dim, causal, scale));
   const int64_t T = batch * seq, w = (int64_t)heads * head_dim;
   TPMLP_TRY(check_mat("Q", Q, T, w, ldq, 8));
@@ -1001,6 +1041,16 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   if (T == 0) return TPMLP_OK;
   if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd)
     return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
+  // Only causal calls with more than one key chunk per block use the workspace.
+  const AttnChunkPlan pl = attn_chunk_plan(seq);
+  const AttnFwdWs W = causal ? attn_fwd_ws(batch, seq, heads) : AttnFwdWs{0, 0};
+  if (W.total > 0) {
+    if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+    if (workspace_bytes < W.total)
+      return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, W.total);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  }
   AttnArgs a;
   a.Q = static_cast<const bf16_t*>(Q);
   a.K = static_cast<const bf16_t*>(K);
@@ -1016,42 +1066,35 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.heads = heads;
   a.causal = causal;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  // Causal: each workgroup takes a long and a short query block (pairs x, n-1-x).
+  a.chunks = (int)pl.chunks;
+  a.kc = (int)pl.kc;
+  a.items = (int)pl.items;
+  a.o_part = W.total > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.lse_part = W.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + W.lse_off) : nullptr;
+  // Causal: one workgroup per (query block, key chunk); blocks with several
+  // chunks are merged by attn_fwd_combine_kernel.
   const int64_t nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const dim3 grid((unsigned)(causal ? (nqb + 1) / 2 : nqb), (unsigned)heads, (unsigned)batch);
-  return launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), (hipStream_t)stream, a);
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)(causal ? pl.items : nqb), (unsigned)heads, (unsigned)batch);
+  TPMLP_TRY(launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), s, a));
+  if (W.total > 0 && nqb > pl.kc / 2)
+    TPMLP_TRY(launch("attn_fwd_combine", "attn_fwd_combine_kernel", attn_fwd_combine_kernel,
+                     dim3((unsigned)(8 * (nqb - pl.kc / 2)), (unsigned)heads, (unsigned)batch), dim3(256), s, a));
+  return TPMLP_OK;
 }
 
 namespace {
-// Causal dQ key chunks (see attn_dq_chunks): kc key blocks per chunk, 16 or
-// more (even) so that the longest query block has at most 8 chunks; the
-// chunk count of that block; and the work items per (sequence, head).
-struct AttnDqPlan {
-  int64_t kc, chunks, items;
-};
-
-AttnDqPlan attn_dq_plan(int64_t seq) {
-  AttnDqPlan pl{16, 0, 0};
-  if (seq <= 0) return pl;
-  const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  const int64_t need = (nkb + 7) / 8;
-  if (need > pl.kc) pl.kc = need + (need & 1);
-  pl.chunks = (nkb + pl.kc - 1) / pl.kc;
-  for (int64_t c = 0; c < pl.chunks && (pl.kc / 2) * c < nqb; ++c) pl.items += nqb - (pl.kc / 2) * c;
-  return pl;
-}
-
 struct AttnBwdWs {
   size_t d_bytes, part_off, total;
 };
 
 // D [heads, T] fp32, then (when some causal query block has several key
-// chunks) the fp32 dQ partials [batch][heads][query blocks][chunks][128][128].
+// chunks) the fp32 dQ partials [batch][heads][work items][128][128].
 AttnBwdWs attn_bwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnBwdWs w;
   w.d_bytes = align256((size_t)batch * seq * heads * sizeof(float));
   w.part_off = w.d_bytes;
-  const AttnDqPlan pl = attn_dq_plan(seq);
+  const AttnChunkPlan pl = attn_chunk_plan(seq);
   const size_t part = pl.chunks > 1 ? (size_t)batch * heads * pl.items * kAttnBQ * kAttnD * sizeof(float) : 0;
   w.total = w.part_off + align256(part);
   return w;
@@ -1111,7 +1154,7 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const AttnDqPlan dqp = attn_dq_plan(seq);
+  const AttnChunkPlan dqp = attn_chunk_plan(seq);
   a.dq_chunks = (int)dqp.chunks;
   a.dq_kc = (int)dqp.kc;
   a.dq_items = (int)dqp.items;
@@ -1168,9 +1211,17 @@ AttnBlockWs attn_block_ws(int64_t batch, int64_t seq, int64_t w, int64_t hs) {
 }
 }  // namespace
 
+size_t tp_attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads, int head_dim, int tp_size) {
+  if (batch < 0 || seq < 0 || heads < 1 || head_dim != kAttnD || tp_size < 1 || heads % tp_size != 0 ||
+      batch * seq > kMaxDim)
+    return 0;
+  return attn_fwd_ws(batch, seq, heads / tp_size).total;
+}
+
 int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, int head_dim, int tp_size,
                 int causal, float scale, const void* X, const void* Wqkv_shard, const void* Wo_shard,
-                void* QKV_save, void* O_save, float* lse, float* Z_partial) {
+                void* QKV_save, void* O_save, float* lse, float* Z_partial, void* workspace,
+                size_t workspace_bytes) {
   AttnBlockDims d;
   TPMLP_TRY(check_attn_block(batch, seq, h, heads, head_dim, tp_size, causal, scale, &d));
   const int64_t T = d.T, w = d.w;
@@ -1182,12 +1233,21 @@ int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, 
   TPMLP_TRY(check_vec("lse", lse, T * d.hs, true));
   TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
   if (T == 0) return TPMLP_OK;
+  // The attention core's workspace is checked here, before the first launch.
+  const size_t need = causal ? attn_fwd_ws(batch, seq, d.hs).total : 0;
+  if (need > 0) {
+    if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
+    if (workspace_bytes < need)
+      return fail(TPMLP_E_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
+  }
   hipStream_t s = (hipStream_t)stream;
   TPMLP_TRY(col_fwd(s, TPMLP_BF16, kActNone, T, h, 3 * w, X, h, Wqkv_shard, 3 * w, nullptr, QKV_save, 3 * w,
                     nullptr, 0, "gemm.attn_qkv"));
   const bf16_t* qkv = static_cast<const bf16_t*>(QKV_save);
   TPMLP_TRY(attn_fwd(stream, batch, seq, (int)d.hs, head_dim, causal, scale, qkv, 3 * w, qkv + w, 3 * w,
-                     qkv + 2 * w, 3 * w, O_save, w, lse));
+                     qkv + 2 * w, 3 * w, O_save, w, lse, workspace, workspace_bytes));
   return row_fwd(s, TPMLP_BF16, T, w, h, O_save, w, Wo_shard, h, Z_partial, h, "gemm.attn_out");
 }
 

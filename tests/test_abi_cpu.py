@@ -151,14 +151,22 @@ def test_sp_validation():
 
 def test_attn_validation():
     f = tl.lib.attn_fwd
-    # (stream, batch, seq, heads, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, O, ldo, lse): refused on the host
-    assert f(None, 1, 8, 1, 64, 1, 0.1, P, 64, P, 64, P, 64, P, 64, None) == E_SHAPE
-    assert f(None, 1, 8, 1, 128, 2, 0.1, P, 128, P, 128, P, 128, P, 128, None) == E_VALUE
-    assert f(None, 1, 8, 1, 128, 1, float("inf"), P, 128, P, 128, P, 128, P, 128, None) == E_VALUE
-    assert f(None, 1, 8, 0, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None) == E_SHAPE
-    assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None) == E_SHAPE   # ldq < heads*128
-    assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None) == E_NULL
-    assert f(None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P + 8, 128, None) == E_ALIGN
+    # (stream, batch, seq, heads, head_dim, causal, scale, Q, ldq, K, ldk, V, ldv, O, ldo, lse, workspace, bytes):
+    # refused on the host
+    assert f(None, 1, 8, 1, 64, 1, 0.1, P, 64, P, 64, P, 64, P, 64, None, None, 0) == E_SHAPE
+    assert f(None, 1, 8, 1, 128, 2, 0.1, P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_VALUE
+    assert f(None, 1, 8, 1, 128, 1, float("inf"), P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_VALUE
+    assert f(None, 1, 8, 0, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_SHAPE
+    assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None, None, 0) == E_SHAPE   # ldq < heads*128
+    assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None, None, 0) == E_NULL
+    assert f(None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P + 8, 128, None, None, 0) == E_ALIGN
+    # causal, 2048 tokens: key chunks need the workspace (checked after the shapes)
+    need = tl.attn_fwd_workspace_bytes(1, 2048, 1)
+    assert need >= 2 * 2 * 128 * 128 * 4 and tl.attn_fwd_workspace_bytes(1, 1024, 1) == 0
+    fw = [None, 1, 2048, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None]
+    assert f(*fw, None, 0) == E_NULL
+    assert f(*fw, P, need - 1) == E_WS
+    assert f(*fw, P + 16, need) == E_ALIGN
     b = tl.lib.attn_bwd
     args = [None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, P, 128, P, P, 128, P, 128, P, 128]
     assert b(*args, P, 16) == E_WS
@@ -170,12 +178,19 @@ def test_attn_validation():
 
 def test_attn_block_validation():
     f = tl.lib.tp_attn_fwd
-    # (stream, batch, seq, h, heads, head_dim, tp, causal, scale, X, Wqkv, Wo, QKV, O, lse, Z): refused on the host
-    assert f(None, 1, 8, 512, 4, 128, 3, 1, 0.1, P, P, P, P, P, P, P) == E_DIV       # 4 heads over 3 shards
-    assert f(None, 1, 8, 512, 4, 64, 2, 1, 0.1, P, P, P, P, P, P, P) == E_SHAPE      # head_dim 64
-    assert f(None, 1, 8, 512, 4, 128, 2, 3, 0.1, P, P, P, P, P, P, P) == E_VALUE     # causal not 0/1
-    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, None, P) == E_NULL   # lse required
-    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P + 8, P, P, P, P) == E_ALIGN
+    # (stream, batch, seq, h, heads, head_dim, tp, causal, scale, X, Wqkv, Wo, QKV, O, lse, Z, workspace, bytes):
+    # refused on the host
+    assert f(None, 1, 8, 512, 4, 128, 3, 1, 0.1, P, P, P, P, P, P, P, None, 0) == E_DIV       # 4 heads over 3 shards
+    assert f(None, 1, 8, 512, 4, 64, 2, 1, 0.1, P, P, P, P, P, P, P, None, 0) == E_SHAPE      # head_dim 64
+    assert f(None, 1, 8, 512, 4, 128, 2, 3, 0.1, P, P, P, P, P, P, P, None, 0) == E_VALUE     # causal not 0/1
+    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, None, P, None, 0) == E_NULL   # lse required
+    assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P + 8, P, P, P, P, None, 0) == E_ALIGN
+    # the attention core's workspace is checked before the QKV projection is launched
+    need = tl.tp_attn_fwd_workspace_bytes(1, 2048, 4, 2)
+    assert need == tl.attn_fwd_workspace_bytes(1, 2048, 2) > 0
+    fw = [None, 1, 2048, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, P, P]
+    assert f(*fw, None, 0) == E_NULL
+    assert f(*fw, P, need - 1) == E_WS
     # causal dQ partials: none up to 1024 tokens; at 32K tokens at most 8 key chunks per query block
     assert tl.attn_bwd_workspace_bytes(1, 1024, 10) == 1024 * 10 * 4
     assert tl.attn_bwd_workspace_bytes(1, 32768, 10) <= 32768 * 10 * 4 + 256 * 10 * 4.5 * 65536

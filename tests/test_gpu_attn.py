@@ -41,7 +41,11 @@ def _qkv(seed, T, heads, std=1.0):
 
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 300, 2, False), (3, 128, 1, True),
-                                                    (1, 1000, 2, True)])
+                                                    (1, 1000, 2, True),
+                                                    # causal query blocks past row 1024 split their keys into
+                                                    # chunks of 1024, merged by log-sum-exp (2 and 3 chunks,
+                                                    # ragged last block)
+                                                    (2, 1100, 1, True), (1, 2100, 2, True), (1, 2100, 1, False)])
 def test_attn_fwd_fused_qkv(batch, seq, heads, causal):
     need_gpu()
     _say(f"attn fwd batch={batch} seq={seq} heads={heads} causal={causal}")
@@ -72,6 +76,58 @@ def test_attn_fwd_separate_strided_and_scale():
     ref = oat.attn_fwd(*f, batch, seq, heads, D, False, scale)
     assert_close(to_f64(O[:, :w]), ref["O"], "bf16", "O")
     assert torch.isnan(O[:, w:]).all(), "columns past the heads were written"
+
+
+def test_attn_fwd_split_workspace():
+    """Causal, 2100 tokens: the chunked forward is bitwise repeatable; a workspace below
+    attn_fwd_workspace_bytes is refused before anything is written."""
+    need_gpu()
+    batch, seq, heads = 1, 2100, 2
+    T, w = batch * seq, heads * D
+    dev = to_dev(_qkv(21, T, heads), "bf16")
+    Q, K, V = dev[:, :w], dev[:, w:2 * w], dev[:, 2 * w:]
+    outs = []
+    for _ in range(2):
+        O, lse = empty((T, w), "bf16"), empty_f32((heads, T))
+        tl.attn_fwd(Q, K, V, O, batch, seq, heads, causal=True, lse=lse)
+        sync()
+        outs.append((O, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    need = tl.attn_fwd_workspace_bytes(batch, seq, heads)
+    assert need > 0
+    O = empty((T, w), "bf16")
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tl.TpmlpError) as e:
+        tl.attn_fwd(Q, K, V, O, batch, seq, heads, causal=True, workspace=small)
+    assert e.value.status == 7
+    sync()
+    assert torch.isnan(O).all(), "O was written by a refused call"
+
+
+@pytest.mark.slow
+def test_attn_fwd_long_sequence_sampled():
+    """8400 tokens (ragged), 2 sequences, 2 heads, causal: past 8192 tokens the key chunks grow (18 key
+    blocks here, 8 chunks for the last query block).  Sampled rows of O and lse of every (sequence, head)
+    against the oracle, on both sides of the chunk edges (every 1152 keys)."""
+    need_gpu()
+    batch, seq, heads = 2, 8400, 2
+    _say(f"attn fwd long batch={batch} seq={seq} heads={heads}")
+    T, w = batch * seq, heads * D
+    qkv = _qkv(8401, T, heads)
+    dev = to_dev(qkv, "bf16")
+    O, lse = empty((T, w), "bf16"), empty_f32((heads, T))
+    tl.attn_fwd(dev[:, :w], dev[:, w:2 * w], dev[:, 2 * w:], O, batch, seq, heads, causal=True, lse=lse)
+    sync()
+    f = synth.to_f64(qkv, "bf16")
+    Og, Lg = to_f64(O), to_f64(lse)
+    rows = np.array([0, 1, 1151, 1152, 1153, 2303, 2304, 4607, 4608, 6000, 8063, 8064, 8270, 8271, 8399])
+    for b in range(batch):
+        for hd in range(heads):
+            ref = oat.attn_fwd_rows(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], batch, seq, heads, D, True, D ** -0.5,
+                                    b, hd, rows)
+            r = b * seq + rows
+            assert_close(Og[r, hd * D:(hd + 1) * D], ref["O"], "bf16", f"O seq {b} head {hd}")
+            _lse_close(Lg[hd, r], ref["lse"], f"lse seq {b} head {hd}")
 
 
 def test_attn_empty_and_errors():
