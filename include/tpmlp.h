@@ -298,7 +298,7 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
  * receives log(sum_j exp(s_tj)) of each query row, or pass NULL.
  * workspace: device memory of at least attn_fwd_workspace_bytes() bytes,
  * 256-byte aligned, owned by the caller; causal calls on sequences longer
- * than 1024 keep per-chunk partial results there (the key range of a query
+ * than 2048 keep per-chunk partial results there (the key range of a query
  * block is split over several workgroups and merged by log-sum-exp).  It may
  * be NULL (with workspace_bytes 0) when that size is 0 or causal = 0. */
 int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale,
@@ -306,10 +306,9 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
              int64_t ldo, float* lse, void* workspace, size_t workspace_bytes);
 
 /* Bytes of device workspace a causal attn_fwd needs (0 on bad args, and for
- * sequences of at most 1024): fp32 partial O tiles of 64 KB plus 512 bytes
- * of row log-sum-exp per chunk of the query blocks whose keys are split
- * (2.5 tiles per query block of 128 rows, per head and sequence, at 4096
- * tokens; at most 8 chunks per block). */
+ * sequences of at most 2048): fp32 partial O tiles of 64 KB plus 512 bytes
+ * of row log-sum-exp per work item (1.5 per query block of 128 rows, per
+ * head and sequence, at 4096 tokens; at most 8 chunks per block). */
 size_t attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads);
 
 /* Bytes of device workspace attn_bwd needs (0 on bad args): fp32 [heads, T]

@@ -160,10 +160,10 @@ def test_attn_validation():
     assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None, None, 0) == E_SHAPE   # ldq < heads*128
     assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None, None, 0) == E_NULL
     assert f(None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P + 8, 128, None, None, 0) == E_ALIGN
-    # causal, 2048 tokens: key chunks need the workspace (checked after the shapes)
-    need = tl.attn_fwd_workspace_bytes(1, 2048, 1)
-    assert need >= 2 * 2 * 128 * 128 * 4 and tl.attn_fwd_workspace_bytes(1, 1024, 1) == 0
-    fw = [None, 1, 2048, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None]
+    # causal, 4096 tokens: key chunks need the workspace (checked after the shapes)
+    need = tl.attn_fwd_workspace_bytes(1, 4096, 1)
+    assert need >= 2 * 16 * 128 * 128 * 4 and tl.attn_fwd_workspace_bytes(1, 2048, 1) == 0
+    fw = [None, 1, 4096, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None]
     assert f(*fw, None, 0) == E_NULL
     assert f(*fw, P, need - 1) == E_WS
     assert f(*fw, P + 16, need) == E_ALIGN
@@ -186,9 +186,9 @@ def test_attn_block_validation():
     assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, None, P, None, 0) == E_NULL   # lse required
     assert f(None, 1, 8, 512, 4, 128, 2, 1, 0.1, P, P, P + 8, P, P, P, P, None, 0) == E_ALIGN
     # the attention core's workspace is checked before the QKV projection is launched
-    need = tl.tp_attn_fwd_workspace_bytes(1, 2048, 4, 2)
-    assert need == tl.attn_fwd_workspace_bytes(1, 2048, 2) > 0
-    fw = [None, 1, 2048, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, P, P]
+    need = tl.tp_attn_fwd_workspace_bytes(1, 4096, 4, 2)
+    assert need == tl.attn_fwd_workspace_bytes(1, 4096, 2) > 0
+    fw = [None, 1, 4096, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, P, P]
     assert f(*fw, None, 0) == E_NULL
     assert f(*fw, P, need - 1) == E_WS
     # causal dQ partials: none up to 1024 tokens; at 32K tokens at most 8 key chunks per query block

@@ -42,10 +42,11 @@ def _qkv(seed, T, heads, std=1.0):
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 300, 2, False), (3, 128, 1, True),
                                                     (1, 1000, 2, True),
-                                                    # causal query blocks past row 1024 split their keys into
-                                                    # chunks of 1024, merged by log-sum-exp (2 and 3 chunks,
+                                                    # causal query blocks past row 2048 split their keys into
+                                                    # chunks of 2048, merged by log-sum-exp (2 and 3 chunks,
                                                     # ragged last block)
-                                                    (2, 1100, 1, True), (1, 2100, 2, True), (1, 2100, 1, False)])
+                                                    (2, 1100, 1, True), (1, 2100, 2, True), (1, 2100, 1, False),
+                                                    (1, 4200, 1, True)])
 def test_attn_fwd_fused_qkv(batch, seq, heads, causal):
     need_gpu()
     _say(f"attn fwd batch={batch} seq={seq} heads={heads} causal={causal}")
@@ -79,8 +80,8 @@ def test_attn_fwd_separate_strided_and_scale():
 
 
 def test_attn_fwd_split_workspace():
-    """Causal, 2100 tokens: the chunked forward is bitwise repeatable; a workspace below
-    attn_fwd_workspace_bytes is refused before anything is written."""
+    """Causal, 2100 tokens (two key chunks for the last query block): the chunked forward is bitwise
+    repeatable; a workspace below attn_fwd_workspace_bytes is refused before anything is written."""
     need_gpu()
     batch, seq, heads = 1, 2100, 2
     T, w = batch * seq, heads * D
@@ -105,12 +106,12 @@ def test_attn_fwd_split_workspace():
 
 
 @pytest.mark.slow
-def test_attn_fwd_long_sequence_sampled():
-    """8400 tokens (ragged), 2 sequences, 2 heads, causal: past 8192 tokens the key chunks grow (18 key
-    blocks here, 8 chunks for the last query block).  Sampled rows of O and lse of every (sequence, head)
-    against the oracle, on both sides of the chunk edges (every 1152 keys)."""
+@pytest.mark.parametrize("batch,seq,heads,chunk", [(2, 8400, 2, 2048), (1, 16500, 1, 2176)])
+def test_attn_fwd_long_sequence_sampled(batch, seq, heads, chunk):
+    """Long causal sequences (ragged): 8400 tokens take 5 key chunks of 2048; past 16384 tokens the chunks
+    grow (34 key blocks of 64 at 16500, 8 chunks for the last query block).  Sampled rows of O and lse of
+    every (sequence, head) against the oracle, on both sides of the chunk edges."""
     need_gpu()
-    batch, seq, heads = 2, 8400, 2
     _say(f"attn fwd long batch={batch} seq={seq} heads={heads}")
     T, w = batch * seq, heads * D
     qkv = _qkv(8401, T, heads)
@@ -120,7 +121,8 @@ def test_attn_fwd_long_sequence_sampled():
     sync()
     f = synth.to_f64(qkv, "bf16")
     Og, Lg = to_f64(O), to_f64(lse)
-    rows = np.array([0, 1, 1151, 1152, 1153, 2303, 2304, 4607, 4608, 6000, 8063, 8064, 8270, 8271, 8399])
+    edges = [e for c in range(1, 8) for e in (c * chunk - 1, c * chunk) if c * chunk < seq]
+    rows = np.array(sorted({0, 1, seq // 2, seq - 129, seq - 128, seq - 2, seq - 1, *edges}))
     for b in range(batch):
         for hd in range(heads):
             ref = oat.attn_fwd_rows(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], batch, seq, heads, D, True, D ** -0.5,
