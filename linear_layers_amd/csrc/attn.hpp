@@ -54,9 +54,9 @@ constexpr int kAttnBQ = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kAttnBK = 64;   // keys per block
 
 // Causal work split along keys: query block b of 128 rows sees up to 2 (b + 1)
-// key blocks of 64; they are taken in chunks of kc key blocks (kc even: at
-// least 16 in the dQ pass and 32 in the forward, more where a block would
-// otherwise have more than 8 chunks), one workgroup per (block, chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items are numbered
+// key blocks of 64; they are taken in chunks of kc key blocks (kc even: 32,
+// more where a block would otherwise have more than 8 chunks), one workgroup
+// per (block, chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items are numbered
 // chunk by chunk, the blocks of one chunk from the last down:
 // item(b, c) = sum over c' < c of (nqb - c' kc / 2), plus nqb - 1 - b.
 __device__ __forceinline__ int attn_key_chunks(int b, int seq, int kc) {

@@ -978,8 +978,7 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
 namespace {
 // Causal key chunks (see attn_key_chunks): kc key blocks per chunk, min_kc or
 // more (even) so that the longest query block has at most 8 chunks; the chunk
-// count of that block; and the work items per (sequence, head).  The dQ pass
-// takes chunks of at least 16 key blocks, the forward of at least 32.
+// count of that block; and the work items per (sequence, head).
 struct AttnChunkPlan {
   int64_t kc, chunks, items;
 };
@@ -1001,10 +1000,12 @@ struct AttnFwdWs {
   size_t lse_off, total;
 };
 
-// Key blocks per forward chunk (at least): 32 (2048 keys) measured best for
-// 4096 causal tokens (forward 80 + merge 8 us, against 87 + 13 at 16 and
-// 83 + 20 at 8).
+// Key blocks per chunk (at least): 32 (2048 keys) measured best for 4096
+// causal tokens, for the forward (80 + 8 us merge, against 87 + 13 at 16 and
+// 83 + 20 at 8) and for dQ (101 + 7.5 us sum, against 102 + 9 at 24 and
+// 107 + 11 at 16).
 constexpr int64_t kAttnFwdMinKc = 32;
+constexpr int64_t kAttnDqMinKc = 32;
 
 AttnFwdWs attn_fwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnFwdWs w{0, 0};
@@ -1099,7 +1100,7 @@ AttnBwdWs attn_bwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnBwdWs w;
   w.d_bytes = align256((size_t)batch * seq * heads * sizeof(float));
   w.part_off = w.d_bytes;
-  const AttnChunkPlan pl = attn_chunk_plan(seq);
+  const AttnChunkPlan pl = attn_chunk_plan(seq, kAttnDqMinKc);
   const size_t part = pl.chunks > 1 ? (size_t)batch * heads * pl.items * kAttnBQ * kAttnD * sizeof(float) : 0;
   w.total = w.part_off + align256(part);
   return w;
@@ -1159,7 +1160,7 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const AttnChunkPlan dqp = attn_chunk_plan(seq);
+  const AttnChunkPlan dqp = attn_chunk_plan(seq, kAttnDqMinKc);
   a.dq_chunks = (int)dqp.chunks;
   a.dq_kc = (int)dqp.kc;
   a.dq_items = (int)dqp.items;

@@ -185,9 +185,9 @@ def _bwd_case(batch, seq, heads, causal, seed, scale=None):
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 130, 1, False), (3, 128, 1, True),
                                                     (1, 1000, 2, True), (1, 1000, 1, False),
-                                                    # causal query blocks past row 1024 split their keys into
-                                                    # chunks of 1024 (2 and 3 chunks here, ragged last block)
-                                                    (2, 1100, 1, True), (1, 2100, 2, True)])
+                                                    # causal query blocks past row 2048 split their keys into
+                                                    # chunks of 2048 (2 and 3 chunks here, ragged last block)
+                                                    (2, 1100, 1, True), (1, 2100, 2, True), (1, 4200, 1, True)])
 def test_attn_bwd(batch, seq, heads, causal):
     need_gpu()
     _say(f"attn bwd batch={batch} seq={seq} heads={heads} causal={causal}")
@@ -204,9 +204,10 @@ def test_attn_bwd(batch, seq, heads, causal):
 
 def test_attn_bwd_deterministic_and_workspace():
     need_gpu()
-    a = _bwd_case(1, 200, 2, True, seed=9)[2]
-    b = _bwd_case(1, 200, 2, True, seed=9)[2]
-    assert torch.equal(a, b)
+    for seq in (200, 2100):   # one key chunk; two (partials summed in order)
+        a = _bwd_case(1, seq, 2, True, seed=9)[2]
+        b = _bwd_case(1, seq, 2, True, seed=9)[2]
+        assert torch.equal(a, b)
     assert tl.attn_bwd_workspace_bytes(2, 100, 3) >= 2 * 100 * 3 * 4
     Z = torch.zeros((4, D), dtype=torch.bfloat16, device="cuda")
     L = torch.zeros((1, 4), device="cuda")
@@ -237,16 +238,16 @@ def test_attn_bwd_workload_two_heads():
 
 @pytest.mark.slow
 def test_attn_bwd_long_sequence_sampled():
-    """8400 tokens (ragged), 2 sequences, 2 heads, causal: past 8192 tokens the causal dQ key chunks grow
-    (18 key blocks of 64 here, 8 chunks for the last query block).  Sampled rows of dQ, dK, dV of two
-    (sequence, head) pairs against the oracle, rows on both sides of the chunk edges (every 1152 keys)."""
+    """8400 tokens (ragged), 2 sequences, 2 heads, causal: 5 dQ key chunks of 2048 for the last query
+    block.  Sampled rows of dQ, dK, dV of two (sequence, head) pairs against the oracle, rows on both sides
+    of the chunk edges."""
     need_gpu()
     batch, seq, heads = 2, 8400, 2
     _say(f"attn bwd long batch={batch} seq={seq} heads={heads}")
     qkv, dO, dqkv = _bwd_case(batch, seq, heads, True, seed=8400)
     w = heads * D
     f, fd, g = synth.to_f64(qkv, "bf16"), synth.to_f64(dO, "bf16"), to_f64(dqkv)
-    rows = np.array([0, 1, 127, 1151, 1152, 1153, 2303, 2304, 4607, 4608, 6000, 8063, 8064, 8270, 8271, 8399])
+    rows = np.array([0, 1, 127, 2047, 2048, 2049, 4095, 4096, 6143, 6144, 8191, 8192, 8270, 8271, 8399])
     for b, hd in ((0, 0), (1, 1)):
         ref = oat.attn_bwd_rows(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], fd, batch, seq, heads, D, True, D ** -0.5,
                                 b, hd, rows)
