@@ -225,9 +225,13 @@ struct TileCfg {
 // 128x128; per CU, 256x192 runs at 0.80 of 256x256's rate when B is
 // K-contiguous (8192x1536x4096 138 vs 149 us) but at 0.72-0.77 when B goes
 // through the transposing reads (2048x6144x12288 337 vs 322 us), so it is
-// kept to the former.
+// kept to the former.  Two 128x128 workgroups per CU run at about 0.72 of a
+// 256x256 workgroup's rate (the GPT-3 shard's 2048x12288x6144 and
+// 6144x12288x2048 products: 328 vs 358 us and 335 vs 421 us with 256x256
+// tiles although they leave a round partly idle), so they win only where
+// the larger tiles would leave much of the chip idle.
 constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f, false, false},
-                                {128, 128, 2, 0.98f, 0.90f, false, false},
+                                {128, 128, 2, 0.72f, 0.72f, false, false},
                                 {256, 320, 1, 0.95f, 0.95f, true, false},
                                 {256, 192, 1, 0.80f, 0.80f, false, true}};
 constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f, false, false}, {64, 64, 1, 0.60f, 0.60f, false, false}};
