@@ -60,13 +60,23 @@ partial_sum_kernel(const float* __restrict__ P, int64_t shard_stride, int64_t ld
   }
 }
 
-// out[n] = sum_{t < rows} part[t*N + n] in ascending t.
-__global__ void __launch_bounds__(256)
+// out[n] = sum_{t < rows} part[t*N + n] in ascending t.  One thread per
+// column; eight rows are loaded before they are added, so the loads overlap
+// (the sum is latency-bound: a few dozen rows of a few thousand columns).
+__global__ void __launch_bounds__(64)
 colsum_reduce_kernel(const float* __restrict__ part, int rows, int N, float* __restrict__ out) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int n = blockIdx.x * 64 + threadIdx.x;
   if (n >= N) return;
   float s = 0.0f;
-  for (int t = 0; t < rows; ++t) s += part[(int64_t)t * N + n];
+  int t = 0;
+  for (; t + 8 <= rows; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(t + u) * N + n];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; t < rows; ++t) s += part[(int64_t)t * N + n];
   out[n] = s;
 }
 

@@ -378,6 +378,46 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   }
 }
 
+// A weight gradient whose 128x128 output tiles fill at most half of the
+// chip's 512 workgroup slots (256 CUs x 2) is split along its long K = T
+// into S slices of at least 1024 (fp32, in the workspace) that one launch
+// computes side by side, then summed in slice order.  S depends on the
+// shapes alone, so the workspace size does too.
+constexpr int64_t kSplitSlots = 512;
+int wgrad_splits(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (dtype != TPMLP_BF16) return 1;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = 1;
+  while (S < 8 && tiles * 2 * S <= kSplitSlots && K / (2 * S) >= 1024) S *= 2;
+  return S;
+}
+
+int partial_sum(int tp, int64_t T, int64_t N, const float* P, int64_t stride, int64_t ldp, float* out,
+                int64_t ldo, hipStream_t s, const char* role);
+
+// A weight gradient (both operands M/N-contiguous, fp32 output) with its K
+// split as wgrad_splits decides: the slices go to `slices` (M x N each, ld N)
+// and are summed into a.C; unsplit, the planner's launch writes a.C directly.
+int run_wgrad_split(const char* role, const char* sum_role, int dtype, GemmArgs a, float* slices,
+                    hipStream_t s) {
+  const int S = wgrad_splits(dtype, a.M, a.N, a.K);
+  if (S == 1 || a.M <= 0 || a.N <= 0) return run_gemm<false, false, kEpiF32>(role, dtype, a, s);
+  if (a.lda >= kMaxLd || a.ldb >= kMaxLd)
+    return fail(TPMLP_E_SHAPE, "%s: leading dimension above 2^22 elements", role);
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  float* out = a.C;
+  const int64_t ldo = a.ldc;
+  a.C = slices;
+  a.ldc = a.N;
+  a.splits = S;
+  a.split_stride = (int64_t)a.M * a.N;
+  const int tiles_m = (a.M + 127) / 128, tiles_n = (a.N + 127) / 128;
+  const int group = std::max(1, std::min(tiles_m, (cus / 8) * 2 / tiles_n));
+  TPMLP_TRY((run_gemm_bf16<128, 128, false, false, kEpiF32, 2, 2, 64>(role, a, s, group)));
+  return partial_sum(S, a.M, a.N, slices, a.split_stride, a.N, out, ldo, s, sum_role);
+}
+
 GemmArgs gemm_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K) {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -448,16 +488,20 @@ int row_fwd(hipStream_t s, int dtype, int64_t T, int64_t Ks, int64_t N, const vo
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t dh_off, cs_off, total;
+  size_t dh_off, cs_off, split_off, total;
 };
 
-BwdLayout bwd_layout(int dtype, int64_t T, int64_t Fs) {
+BwdLayout bwd_layout(int dtype, int64_t T, int64_t h, int64_t Fs) {
   BwdLayout L;
   L.dh_off = 0;
   const size_t dh = align256((size_t)T * Fs * elem_size(dtype));
   L.cs_off = dh;
   const size_t cs = align256((size_t)((T + kMinBM - 1) / kMinBM) * Fs * sizeof(float));
-  L.total = dh + cs;
+  L.split_off = dh + cs;
+  // both weight gradients have h x Fs outputs
+  const int S = std::max(wgrad_splits(dtype, Fs, h, T), wgrad_splits(dtype, h, Fs, T));
+  const size_t split = S > 1 ? align256((size_t)S * h * Fs * sizeof(float)) : 0;
+  L.total = L.split_off + split;
   return L;
 }
 
@@ -573,8 +617,7 @@ size_t tpmlp_bwd_workspace_bytes(int dtype, int64_t T, int64_t h, int64_t F, int
   if ((dtype != TPMLP_BF16 && dtype != TPMLP_F32) || tp_size < 1 || T < 0 || T > kMaxDim || h < 1 || F < 1 ||
       F % tp_size != 0)
     return 0;
-  (void)h;
-  return bwd_layout(dtype, T, F / tp_size).total;
+  return bwd_layout(dtype, T, h, F / tp_size).total;
 }
 
 int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
@@ -598,7 +641,7 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
   TPMLP_TRY(check_mat("dW1_shard", dW1_shard, h, Fs, Fs, 4));
   TPMLP_TRY(check_vec("db1_shard", db1_shard, Fs, false));
   TPMLP_TRY(check_mat("dW2_shard", dW2_shard, Fs, h, h, 4));
-  const BwdLayout L = bwd_layout(dtype, T, Fs);
+  const BwdLayout L = bwd_layout(dtype, T, h, Fs);
   if (T > 0) {
     if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
     if (workspace_bytes < L.total)
@@ -632,8 +675,8 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
     const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, true, cus);
     const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
     const int rows = (int)((T + bm - 1) / bm);
-    TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 255) / 256)),
-                     dim3(256), s, (const float*)cs, rows, (int)Fs, db1_shard));
+    TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 63) / 64)),
+                     dim3(64), s, (const float*)cs, rows, (int)Fs, db1_shard));
   }
   // dW2_i = A_i^T dZ and dW1_i = X^T dH_i: one paired launch when together
   // they fill the chip once, else one launch each.
@@ -646,8 +689,9 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
   bool paired = false;
   TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
   if (!paired) {
-    TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad2", dtype, w2, s)));
-    TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.mlp_wgrad1", dtype, w1, s)));
+    float* slices = reinterpret_cast<float*>(ws + L.split_off);
+    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad2", "wgrad_split_sum", dtype, w2, slices, s));
+    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad1", "wgrad_split_sum", dtype, w1, slices, s));
   }
   // dX_i = dH_i W1_i^T
   a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);

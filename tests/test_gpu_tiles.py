@@ -151,3 +151,30 @@ def test_swiglu_256x192():
     assert_close(to_f64(dX), b["dX"], "bf16", "dX")
     assert_close(to_f64(dW_gu), b["dW_gu"], "bf16", "dW_gu")
     assert_close(to_f64(dW_down), b["dW_down"], "bf16", "dW_down")
+
+
+@pytest.mark.parametrize("T", [2048, 2100])
+def test_tp_mlp_bwd_split_k_weight_gradients(T):
+    """h = 512, F/tp = 1024: the weight gradients (1024 x 512 and 512 x 1024) fill a sixteenth of the
+    chip, so each runs as two K slices of T/2 (a partial last K step at T = 2100), summed in order."""
+    need_gpu()
+    h, F = 512, 1024
+    _say(f"mlp bwd split-K T={T} h={h} F={F}")
+    wl = synth.Workload("t", 37, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
+    raw = synth.mlp_inputs(wl)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    X, W1, W2, b1, dZ = (to_dev(raw[k], "bf16") for k in ("X", "W1", "W2", "b1", "dZ"))
+    A, H, Z = empty((T, F), "bf16"), empty((T, F), "bf16"), empty_f32((T, h))
+    dX, dW1, db1, dW2 = empty_f32((T, h)), empty_f32((h, F)), empty_f32((F,)), empty_f32((F, h))
+    tl.tp_mlp_fwd(X, W1, b1, W2, 1, A, Z, H_save=H)
+    tl.profile_enable("")
+    try:
+        tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
+        sync()
+        roles = [r for r, _ in tl.profile_collect(ordered=True)]
+    finally:
+        tl.profile_enable(None)
+    assert roles.count("wgrad_split_sum") == 2, roles
+    g = ref.tp_mlp_bwd_shard(f["X"], f["W1"], f["b1"], f["W2"], f["dZ"], 1, 0)
+    for name, got in (("dX", dX), ("dW1", dW1), ("db1", db1), ("dW2", dW2)):
+        assert_close(to_f64(got), g[name], "bf16", name)
