@@ -289,8 +289,8 @@ int sp_dropout_bwd(void* stream, int64_t rows, int64_t h, const void* dOut, int6
  * Between the head-sharded QKV (column) and O (row) projections each shard
  * computes its own heads independently [csdn 1.2.2; zouht 2.2.1 多头注意力机制;
  * wangyu 注意力机制中的张量并行]: per head and sequence
- * O = softmax(Q K^T * scale) V, with keys j > i masked for query i when
- * causal = 1.  T = batch * seq token rows (sequence b is rows
+ * O = softmax(Q K^T * scale) V (scale > 0, finite), with keys j > i masked
+ * for query i when causal = 1.  T = batch * seq token rows (sequence b is rows
  * [b*seq, (b+1)*seq)); head h reads columns [h*head_dim, (h+1)*head_dim) of
  * Q, K, V (bf16, row strides ldq, ldk, ldv — e.g. the three blocks of the
  * fused QKV output, ld = 3*heads*head_dim) and writes the same columns of O

@@ -216,24 +216,36 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[f][v] = 0.0f;
       attn_qk_step<0>(kt, cur, qf, s);
-      // scores in base-2 units, masked past the sequence and above the diagonal
+      // Raw scores, masked past the sequence and above the diagonal; the
+      // (positive) scale goes into the exponent's FMA, so the row maximum is
+      // taken before scaling.
       const bool edge = kv0 + kAttnBK > seq || (p.causal && kv0 + kAttnBK - 1 > wq0);
       float mloc = -INFINITY;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float x = s[f][v] * p.scale_log2;
           if (edge) {
             const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (kv >= seq || (p.causal && kv > qrow)) x = -INFINITY;
+            if (kv >= seq || (p.causal && kv > qrow)) s[f][v] = -INFINITY;
           }
-          s[f][v] = x;
-          mloc = fmaxf(mloc, x);
+          mloc = fmaxf(mloc, s[f][v]);
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_i, mloc);
-      const float alpha = m_i == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_i - m_new);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;   // this block's row maximum, base 2
+      // The reference m_i moves only when some row of the wave exceeds it by
+      // more than 8 (or has none yet): otherwise P = 2^(s - m_i) <= 256 and the
+      // rescaling of l and O is skipped.  l and O are sums against the same
+      // reference either way, so O = acc / l and lse = m_i + log2 l hold.
+      if (__builtin_amdgcn_ballot_w64(mloc > m_i + 8.0f) != 0) {
+        const float m_new = fmaxf(m_i, mloc);
+        const float alpha = m_i == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_i - m_new);
+        l_i *= alpha;
+        m_i = m_new;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[f][v] *= alpha;
+      }
       float lsum = 0.0f;
       u32x4_t pf[4];
 #pragma unroll
@@ -243,19 +255,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int v = 4 * g0 + e;   // groups g0 (e < 4) and g0 + 1 (e >= 4)
-          pv[e] = __builtin_amdgcn_exp2f(s[f][v] - m_new);
+          pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[f][v], p.scale_log2, -m_i));
           lsum += pv[e];
         }
         pf[t] = swap_pack(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                           pack_bf16x2(pv[6], pv[7]));
       }
       lsum += __shfl_xor(lsum, 32);
-      l_i = l_i * alpha + lsum;
-      m_i = m_new;
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[f][v] *= alpha;
+      l_i += lsum;
       attn_pv_step<0>(vt, cur + 2 * AttnKTile::BYTES, pf, o);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // block j + 1 has landed (this wave's part)

@@ -1072,7 +1072,7 @@ int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, 
   TPMLP_TRY(check_rows("seq", seq));
   if (batch * seq > kMaxDim) return fail(TPMLP_E_SHAPE, "batch * seq above 2^31 - 1");
   if (causal != 0 && causal != 1) return fail(TPMLP_E_VALUE, "causal = %d must be 0 or 1", causal);
-  if (!std::isfinite(scale)) return fail(TPMLP_E_VALUE, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(TPMLP_E_VALUE, "scale must be finite and positive");
   return TPMLP_OK;
 }
 }  // namespace

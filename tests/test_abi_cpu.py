@@ -155,7 +155,8 @@ def test_attn_validation():
     # refused on the host
     assert f(None, 1, 8, 1, 64, 1, 0.1, P, 64, P, 64, P, 64, P, 64, None, None, 0) == E_SHAPE
     assert f(None, 1, 8, 1, 128, 2, 0.1, P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_VALUE
-    assert f(None, 1, 8, 1, 128, 1, float("inf"), P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_VALUE
+    for bad in (float("inf"), 0.0, -0.1):   # the scale must be finite and positive
+        assert f(None, 1, 8, 1, 128, 1, bad, P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_VALUE
     assert f(None, 1, 8, 0, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None, None, 0) == E_SHAPE
     assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None, None, 0) == E_SHAPE   # ldq < heads*128
     assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None, None, 0) == E_NULL
