@@ -220,17 +220,21 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
       // (positive) scale goes into the exponent's FMA, so the row maximum is
       // taken before scaling.
       const bool edge = kv0 + kAttnBK > seq || (p.causal && kv0 + kAttnBK - 1 > wq0);
+      if (edge) {   // one uniform branch per block; selects inside
+        const bool causal = p.causal != 0;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+            s[f][v] = ((kv >= seq) | (causal & (kv > qrow))) ? -INFINITY : s[f][v];
+          }
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (edge) {
-            const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (kv >= seq || (p.causal && kv > qrow)) s[f][v] = -INFINITY;
-          }
-          mloc = fmaxf(mloc, s[f][v]);
-        }
+        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[f][v]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;   // this block's row maximum, base 2
       // The reference m_i moves only when some row of the wave exceeds it by
       // more than 8 (or has none yet): otherwise P = 2^(s - m_i) <= 256 and the
@@ -688,6 +692,16 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
       d4s[k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(d_s + qo);
     }
     mm_rows<2>(qt, cur, lane, kf, sacc);   // S^T = K Q^T
+    if (edge) {   // masked scores -inf, so P^T = 0 there (the scale is positive); one uniform branch
+      const bool causal = p.causal != 0, kout = krow >= seq;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int q = q0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+          sacc[f][v] = ((q >= seq) | kout | (causal & (q < krow))) ? -INFINITY : sacc[f][v];
+        }
+    }
     uint32_t pk[2][8];
     // P^T = exp(S^T * scale - lse), slice (f, g) = (S / 4, S % 4) under substep S of dP^T
     auto p_slice = [&](auto SC) {
@@ -695,13 +709,8 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
       const f32x4_t l4 = l4s[4 * f + g];
       float pv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - l4[e] * log2e);
-        if (edge) {
-          const int q = q0 + 32 * f + 8 * g + 4 * h + e;
-          if (q >= seq || krow >= seq || (p.causal && q < krow)) pv[e] = 0.0f;
-        }
-      }
+      for (int e = 0; e < 4; ++e)
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[f][4 * g + e], p.scale_log2, -l4[e] * log2e));
       pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
       pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
     };
@@ -829,19 +838,23 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
 #pragma unroll
           for (int v = 0; v < 16; ++v) sacc[f][v] = 0.0f;
         mm_rows<2, 2>(ktile, cur, lane, qf, sacc);
+        if (edge) {   // masked scores -inf, so P = 0 there (the scale is positive)
+          const bool causal = p.causal != 0;
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int kv = kv0 + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+              sacc[f][v] = ((kv >= seq) | (causal & (kv > qrow))) ? -INFINITY : sacc[f][v];
+            }
+        }
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float pv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pv[e] = __builtin_amdgcn_exp2f(sacc[f][4 * g + e] * p.scale_log2 - lse2);
-              if (edge) {
-                const int kv = kv0 + 32 * f + 8 * g + 4 * h + e;
-                if (kv >= seq || (p.causal && kv > qrow)) pv[e] = 0.0f;
-              }
-            }
+            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[f][4 * g + e], p.scale_log2, -lse2));
             pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
             pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
           }
