@@ -665,9 +665,12 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   }
-  for (int qb = qb0; qb < nqb; ++qb) {
-    lds_char* cur = ((qb - qb0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = ((qb - qb0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+  // One query block in stage cur (st1 when ODD, else st0; a compile-time
+  // choice, so every LDS address below is a fixed offset from a per-lane base).
+  auto block = [&](const int qb, auto OddC) {
+    constexpr bool kOdd = decltype(OddC)::value;
+    lds_char* cur = kOdd ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = kOdd ? (lds_char*)st0 : (lds_char*)st1;
     if (qb + 1 < nqb) issue(qb + 1, nxt);
     const int q0 = qb * kAttnBwdBQ;
     const bool edge = q0 + kAttnBwdBQ > seq || (p.causal && q0 < kw0 + 31);
@@ -740,7 +743,14 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     mm_cols<4, true>(qt, cur, af, dk);   // dK += dS^T Q
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+  };
+  // Blocks qb0, qb0 + 2, ... use st0, the others st1.
+  int qb = qb0;
+  for (; qb + 1 < nqb; qb += 2) {
+    block(qb, std::false_type{});
+    block(qb + 1, std::true_type{});
   }
+  if (qb < nqb) block(qb, std::false_type{});
   agpr_acc_drain(dk, dv);   // the last products into dk, dv have retired before VALU reads them
   if (krow < seq) {
     store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
