@@ -203,9 +203,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   issue(j0, (lds_char*)st0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    lds_char* cur = ((j - j0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = ((j - j0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+  // One key block in stage cur (st1 when ODD, else st0; a compile-time
+  // choice, so every LDS address below is a fixed offset from a per-lane base).
+  auto block = [&](const int j, auto OddC) {
+    constexpr bool kOdd = decltype(OddC)::value;
+    lds_char* cur = kOdd ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = kOdd ? (lds_char*)st0 : (lds_char*)st1;
     if (j + 1 < j1) issue(j + 1, nxt);
     const int kv0 = j * kAttnBK;
     // A wave whose rows all precede this block (causal) has nothing to add.
@@ -271,7 +274,14 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // block j + 1 has landed (this wave's part)
     __syncthreads();                            // ... everyone's; and stage cur is free again
+  };
+  // Blocks j0, j0 + 2, ... use st0, the others st1.
+  int jj = j0;
+  for (; jj + 1 < j1; jj += 2) {
+    block(jj, std::false_type{});
+    block(jj + 1, std::true_type{});
   }
+  if (jj < j1) block(jj, std::false_type{});
 
   // Every row of a chunk sees at least one key (chunk c starts at key
   // 64 c kc <= the block's first row), so l_i > 0 here.
@@ -831,9 +841,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   issue(j0, (lds_char*)st0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    lds_char* cur = ((j - j0) & 1) ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = ((j - j0) & 1) ? (lds_char*)st0 : (lds_char*)st1;
+  // One key block in stage cur (st1 when ODD, else st0; a compile-time
+  // choice, so every LDS address below is a fixed offset from a per-lane base).
+  auto block = [&](const int j, auto OddC) {
+    constexpr bool kOdd = decltype(OddC)::value;
+    lds_char* cur = kOdd ? (lds_char*)st1 : (lds_char*)st0;
+    lds_char* nxt = kOdd ? (lds_char*)st0 : (lds_char*)st1;
     if (j + 1 < j1) issue(j + 1, nxt);
     const int kv0 = j * kAttnBK;
     if (!(p.causal && kv0 > wq0 + 31)) {
@@ -896,7 +909,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+  };
+  // Blocks j0, j0 + 2, ... use st0, the others st1.
+  int jj = j0;
+  for (; jj + 1 < j1; jj += 2) {
+    block(jj, std::false_type{});
+    block(jj + 1, std::true_type{});
   }
+  if (jj < j1) block(jj, std::false_type{});
   if (p.causal && attn_key_chunks(qb, seq, p.dq_kc) > 1) {
     // one of several chunks: its fp32 partial (unscaled) in this item's slot, for attn_bwd_dq_sum_kernel
     float* dst = p.dq_part +
