@@ -439,14 +439,15 @@ struct AttnRowTile {
 
   static __device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-  __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
+  // `off`: a byte offset added to every read address (a per-wave LDS region).
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld, uint32_t off = 0) {
 #pragma unroll
     for (int j = 0; j < INSTR; ++j) {
       const int s = (wave * INSTR + j) * 64 + lane;
       const int r = s >> 4, q = (s & 15) ^ sw(r);
       voff[j] = (uint32_t)(((int64_t)r * ld + q * 8) * 2);
     }
-    kb = (uint32_t)(lane & 31) * 256u;
+    kb = (uint32_t)(lane & 31) * 256u + off;
     ksw = (uint32_t)sw(lane & 31);
     const int g = lane >> 4, j = lane & 15;
 #pragma unroll
@@ -455,7 +456,7 @@ struct AttnRowTile {
       for (int pp = 0; pp < 2; ++pp) {
         const int kr = 8 * (g >> 1) + (j >> 2) + 4 * pp;     // row within a 16-row substep
         const int q = 4 * F + 2 * (g & 1) + ((j & 3) >> 1);
-        tb[F][pp] = (uint32_t)(kr * 256 + ((q ^ sw(kr)) << 4) + 8 * (j & 1));
+        tb[F][pp] = (uint32_t)(kr * 256 + ((q ^ sw(kr)) << 4) + 8 * (j & 1)) + off;
       }
   }
 
@@ -604,28 +605,34 @@ __device__ __forceinline__ void lds_dma_f32x64(const float* base, uint32_t nbyte
                : "memory", "m0");
 }
 
-// dK, dV for 64 keys of one head (2 waves x 32 keys), over all query blocks
-// that see them (causal: two key blocks per workgroup, a long and a short
-// one).  K and V rows stay in registers as A fragments.
-__global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs p) {
-  __shared__ __attribute__((aligned(1024))) char st0[kAttnDkvStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kAttnDkvStage];
+constexpr int kAttnDkvStride = (kAttnDkvStage + 1023) / 1024 * 1024;   // stage pitch in LDS
+
+// dK, dV for 64 keys of one head, over all query blocks that see them.  The
+// workgroup's 4 waves form two pairs; each pair holds the 64 keys (2 waves x
+// 32, K and V rows in registers as A fragments) and takes half of the query
+// blocks, through its own two LDS stages; at the end the second pair's sums
+// go through LDS and the first pair adds them (fixed order) and stores.  With
+// one wave per SIMD (the sums and K, V need most of a SIMD's registers), a
+// workgroup per key block and the halved query ranges keep every SIMD busy
+// with balanced work even when causal.
+__global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) char stg[4 * kAttnDkvStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wave >> 1, wp = wave & 1;   // pair, wave within the pair
   const int seq = p.seq;
-  const int nkb = (seq + 63) / 64;
-  // Causal: workgroup x takes key blocks x and nkb - 1 - x, whose query ranges add
-  // up to the same work for every workgroup; otherwise block x alone.
-  const int nvb = (p.causal && (int)blockIdx.x != nkb - 1 - (int)blockIdx.x) ? 2 : 1;
-  for (int vb = 0; vb < nvb; ++vb) {
-  if (vb > 0) __syncthreads();   // the first block's last stage reads are done
-  const int kb = p.causal ? (vb == 0 ? (int)blockIdx.x : nkb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int head = blockIdx.y;
+  // Workgroup x is key block x / (heads * batch) of head x % heads and sequence
+  // (x / heads) % batch: the key blocks that see the most queries (causal: the
+  // first) of every head and sequence are dispatched first.
+  const int hb = p.heads * p.batch;
+  const int kb = (int)blockIdx.x / hb;
+  const int head = ((int)blockIdx.x % hb) % p.heads;
+  const int z = ((int)blockIdx.x % hb) / p.heads;
   const int64_t T = (int64_t)p.batch * seq;
-  const int64_t row_base = (int64_t)blockIdx.z * seq;
+  const int64_t row_base = (int64_t)z * seq;
   const int k0 = kb * 64;
-  const int kw0 = k0 + 32 * wave;
+  const int kw0 = k0 + 32 * wp;
   const int krow = kw0 + (lane & 31);
 
   u32x4_t kf[8], vf[8];
@@ -638,23 +645,26 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
       vf[s] = krow < seq ? *reinterpret_cast<const u32x4_t*>(vp + 16 * s) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  // Pair pr's stages are stg + (2 pr + parity) * stride; the pair offset goes
+  // into the tiles' read bases, so reads address stg + parity * stride.
+  const uint32_t pair_off = (uint32_t)(2 * pr * kAttnDkvStride);
   AttnQTile qt, ot;
-  qt.init(wave, lane, p.ldq);
-  ot.init(wave, lane, p.lddo);
+  qt.init(wp, lane, p.ldq, pair_off);
+  ot.init(wp, lane, p.lddo, pair_off);
   const bf16_t* Qh = p.Q + row_base * p.ldq + head * kAttnD;
   const bf16_t* dOh = p.dO + row_base * p.lddo + head * kAttnD;
   const float* lse_h = p.lse + (int64_t)head * T + row_base;
   const float* D_h = p.D + (int64_t)head * T + row_base;
   // One stage: the query block's Q and dO tiles, then its lse and D values
-  // (wave 0 fetches lse, wave 1 fetches D), all through the LDS DMA so a
-  // single vmcnt wait covers the whole next stage.
+  // (the pair's wave 0 fetches lse, wave 1 fetches D), all through the LDS DMA
+  // so a single vmcnt wait covers the whole next stage.
   auto issue = [&](int qb, lds_char* dst) {
     const int q0 = qb * kAttnBwdBQ;
     const int rows = min(kAttnBwdBQ, seq - q0);
-    qt.load(Qh + (int64_t)q0 * p.ldq, (uint32_t)(((int64_t)(rows - 1) * p.ldq + kAttnD) * 2), dst, wave);
+    qt.load(Qh + (int64_t)q0 * p.ldq, (uint32_t)(((int64_t)(rows - 1) * p.ldq + kAttnD) * 2), dst, wp);
     ot.load(dOh + (int64_t)q0 * p.lddo, (uint32_t)(((int64_t)(rows - 1) * p.lddo + kAttnD) * 2),
-            dst + AttnQTile::BYTES, wave);
-    lds_dma_f32x64((wave == 0 ? lse_h : D_h) + q0, (uint32_t)rows * 4u, dst + kAttnDkvRows + 256 * wave, lane);
+            dst + AttnQTile::BYTES, wp);
+    lds_dma_f32x64((wp == 0 ? lse_h : D_h) + q0, (uint32_t)rows * 4u, dst + kAttnDkvRows + 256 * wp, lane);
   };
   const float log2e = 1.4426950408889634f;
 
@@ -668,24 +678,33 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
     asm volatile("" : "+a"(dv[f]));
   }
 
+  // Query blocks [qb0, nqb) (causal: from the key block's own), the first
+  // ceil(n/2) to pair 0, the rest to pair 1; both pairs run ceil(n/2)
+  // iterations (pair 1's last may be empty) so that they meet the same barriers.
   const int nqb = (seq + kAttnBwdBQ - 1) / kAttnBwdBQ;
   const int qb0 = p.causal ? k0 / kAttnBwdBQ : 0;
-  if (qb0 < nqb) {
-    issue(qb0, (lds_char*)st0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-  }
-  // One query block in stage cur (st1 when ODD, else st0; a compile-time
-  // choice, so every LDS address below is a fixed offset from a per-lane base).
-  auto block = [&](const int qb, auto OddC) {
+  const int nit = (nqb - qb0 + 1) / 2;
+  const int my0 = pr == 0 ? qb0 : qb0 + nit;
+  const int my1 = pr == 0 ? qb0 + nit : nqb;
+  lds_char* const st = (lds_char*)stg;
+  auto pstage = [&](int parity) { return st + (2 * pr + parity) * kAttnDkvStride; };   // this pair's stage
+  if (my0 < my1) issue(my0, pstage(0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+  // Iteration i: query block my0 + i in the pair's stage i & 1 (ODD; a
+  // compile-time choice, so the tiles' reads are fixed offsets from their
+  // per-lane bases, which carry the pair offset).
+  auto block = [&](const int i, auto OddC) {
     constexpr bool kOdd = decltype(OddC)::value;
-    lds_char* cur = kOdd ? (lds_char*)st1 : (lds_char*)st0;
-    lds_char* nxt = kOdd ? (lds_char*)st0 : (lds_char*)st1;
-    if (qb + 1 < nqb) issue(qb + 1, nxt);
+    const lds_char* cur = st + (kOdd ? kAttnDkvStride : 0);   // + pair_off inside the tiles
+    lds_char* const mine = pstage(kOdd ? 1 : 0);
+    const int qb = my0 + i;
+    if (qb + 1 < my1) issue(qb + 1, pstage(kOdd ? 0 : 1));
+    if (qb < my1) {
     const int q0 = qb * kAttnBwdBQ;
     const bool edge = q0 + kAttnBwdBQ > seq || (p.causal && q0 < kw0 + 31);
-    const lds_char* lse_s = cur + kAttnDkvRows;
-    const lds_char* d_s = cur + kAttnDkvRows + 256;
+    const lds_char* lse_s = mine + kAttnDkvRows;
+    const lds_char* d_s = mine + kAttnDkvRows + 256;
     // Accumulator layout: lane holds key krow and queries q0 + 32 f + 8 g + 4 h + e
     // in register 4 g + e of block f.  The VALU work runs under the MFMAs of
     // the next product: P^T under dP^T, dS^T under dV.  P^T and dS^T are kept
@@ -751,22 +770,43 @@ __global__ void __launch_bounds__(128, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
       af[t] = swap_pack(pk[t >> 1][4 * (t & 1)], pk[t >> 1][4 * (t & 1) + 1], pk[t >> 1][4 * (t & 1) + 2],
                         pk[t >> 1][4 * (t & 1) + 3]);
     mm_cols<4, true>(qt, cur, af, dk);   // dK += dS^T Q
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
   };
-  // Blocks qb0, qb0 + 2, ... use st0, the others st1.
-  int qb = qb0;
-  for (; qb + 1 < nqb; qb += 2) {
-    block(qb, std::false_type{});
-    block(qb + 1, std::true_type{});
+  int i = 0;
+  for (; i + 1 < nit; i += 2) {
+    block(i, std::false_type{});
+    block(i + 1, std::true_type{});
   }
-  if (qb < nqb) block(qb, std::false_type{});
+  if (i < nit) block(i, std::false_type{});
   agpr_acc_drain(dk, dv);   // the last products into dk, dv have retired before VALU reads them
-  if (krow < seq) {
-    store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
-    store_rows_bf16(dk, p.scale, p.dK + (row_base + krow) * p.lddk + head * kAttnD, h);
+  // Pair 1's sums into LDS (free: the last iteration ended with a barrier),
+  // element-major so that each read and write is one dword per lane.
+  float* const red = reinterpret_cast<float*>(stg);
+  if (pr == 1) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        red[(wp * 128 + 16 * f + v) * 64 + lane] = dk[f][v];
+        red[(wp * 128 + 64 + 16 * f + v) * 64 + lane] = dv[f][v];
+      }
   }
-  }  // key blocks
+  __syncthreads();
+  if (pr == 0) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        dk[f][v] += red[(wp * 128 + 16 * f + v) * 64 + lane];
+        dv[f][v] += red[(wp * 128 + 64 + 16 * f + v) * 64 + lane];
+      }
+    if (krow < seq) {
+      store_rows_bf16(dv, 1.0f, p.dV + (row_base + krow) * p.lddv + head * kAttnD, h);
+      store_rows_bf16(dk, p.scale, p.dK + (row_base + krow) * p.lddk + head * kAttnD, h);
+    }
+  }
 }
 
 using AttnKVTile = AttnRowTile<kAttnBK, 4>;   // 64 key rows x 128, 4 waves load it

@@ -1178,6 +1178,8 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   if (T == 0) return TPMLP_OK;
   if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd || lddo >= kMaxLd)
     return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
+  if ((seq + 63) / 64 * heads * batch > kMaxDim)
+    return fail(TPMLP_E_SHAPE, "key blocks x heads x batch above 2^31 - 1");
   const AttnBwdWs W = attn_bwd_ws(batch, seq, heads);
   const size_t need = W.total;
   if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
@@ -1223,7 +1225,7 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   const int64_t nkb = (seq + 63) / 64, nqb = (seq + kAttnBQ - 1) / kAttnBQ;
   const int64_t dq_items = causal ? dqp.items : nqb;
   TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
-                   dim3((unsigned)(causal ? (nkb + 1) / 2 : nkb), (unsigned)heads, (unsigned)batch), dim3(128), s, a));
+                   dim3((unsigned)(nkb * heads * batch)), dim3(256), s, a));
   TPMLP_TRY(launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
                    dim3((unsigned)dq_items, (unsigned)heads, (unsigned)batch), dim3(256), s, a));
   if (causal && dqp.chunks > 1 && nqb > dqp.kc / 2)
