@@ -813,7 +813,7 @@ using AttnKVTile = AttnRowTile<kAttnBK, 4>;   // 64 key rows x 128, 4 waves load
 constexpr int kAttnDqStage = 2 * AttnKVTile::BYTES;  // K and V: 32 KB
 
 // dQ for 128 query rows of one head (4 waves x 32), over the key blocks they
-// see (causal: over one chunk of at most kAttnDqChunk key blocks).
+// see (causal: over one key chunk, see attn_key_chunks).
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char st0[kAttnDqStage];
   __shared__ __attribute__((aligned(1024))) char st1[kAttnDqStage];
