@@ -8,11 +8,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/tpmlp.h"
+
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
 #include "reduce.hpp"
@@ -306,6 +308,14 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 320 rows of
 // a K-contiguous operand (or 64 K-rows of an M/N-contiguous one).
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
+
+// Entry points that launch several GEMMs check every operand's leading
+// dimension before the first launch, so that no error can follow a launch.
+int check_lds(std::initializer_list<int64_t> lds) {
+  for (const int64_t ld : lds)
+    if (ld >= kMaxLd) return fail(TPMLP_E_SHAPE, "leading dimension %lld above 2^22 elements", (long long)ld);
+  return TPMLP_OK;
+}
 
 // The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
 // launch of 256x256 tiles (eight waves, K step 64, two stages) when together
@@ -607,6 +617,7 @@ int tp_mlp_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
   TPMLP_TRY(check_mat("H_save", H_save, T, Fs, Fs, v, false));
   TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, v));
   TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
+  TPMLP_TRY(check_lds({h, ldw1, Fs}));
   hipStream_t s = (hipStream_t)stream;
   TPMLP_TRY(col_fwd(s, dtype, TPMLP_ACT_GELU_TANH, T, h, Fs, X, h, W1_shard, ldw1, b1_shard, A_save, Fs, H_save, Fs,
                     "gemm.mlp_fwd1"));
@@ -649,6 +660,7 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
   }
+  TPMLP_TRY(check_lds({h, ldw1, Fs}));
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     TPMLP_TRY(fill_zero(dW1_shard, h, Fs, Fs, s));
@@ -716,6 +728,7 @@ int column_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N
   TPMLP_TRY(check_mat("dX_partial", dX_partial, T, K, lddx, 4));
   TPMLP_TRY(check_mat("dW_shard", dW_shard, K, Ns, lddw, 4));
   TPMLP_TRY(check_vec("db_shard", db_shard, Ns, false));
+  TPMLP_TRY(check_lds({ldx, ldw, lddy}));
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     TPMLP_TRY(fill_zero(dW_shard, K, Ns, lddw, s));
@@ -757,6 +770,7 @@ int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, i
   TPMLP_TRY(check_mat("dY", dY, T, N, lddy, v));
   TPMLP_TRY(check_mat("dX_shard", dX_shard, T, Ks, lddx, 4));
   TPMLP_TRY(check_mat("dW_shard", dW_shard, Ks, N, lddw, 4));
+  TPMLP_TRY(check_lds({ldx, ldw, lddy}));
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) return fill_zero(dW_shard, Ks, N, lddw, s);
   // dX_i = dY W_i^T
@@ -835,6 +849,7 @@ int tp_swiglu_fwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
   TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, 8));
   TPMLP_TRY(check_mat("Z_partial", Z_partial, T, h, h, 4));
   if (T == 0) return TPMLP_OK;
+  TPMLP_TRY(check_lds({h, 2 * Fs}));
   hipStream_t s = (hipStream_t)stream;
   // [gate | up] = X W_gu (packed), A = silu(gate) * up
   GemmArgs a = gemm_args(X, h, W_gu_shard, 2 * Fs, T, 2 * Fs, h);
@@ -885,6 +900,7 @@ int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
   }
+  TPMLP_TRY(check_lds({h, 2 * Fs}));
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     TPMLP_TRY(fill_zero(dW_gu_shard, h, 2 * Fs, 2 * Fs, s));
@@ -1298,6 +1314,7 @@ int tp_attn_fwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, 
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
   }
+  TPMLP_TRY(check_lds({h, 3 * w}));
   hipStream_t s = (hipStream_t)stream;
   TPMLP_TRY(col_fwd(s, TPMLP_BF16, kActNone, T, h, 3 * w, X, h, Wqkv_shard, 3 * w, nullptr, QKV_save, 3 * w,
                     nullptr, 0, "gemm.attn_qkv"));
@@ -1333,6 +1350,7 @@ int tp_attn_bwd(void* stream, int64_t batch, int64_t seq, int64_t h, int heads, 
   TPMLP_TRY(check_mat("dWqkv_shard", dWqkv_shard, h, 3 * w, 3 * w, 4));
   TPMLP_TRY(check_mat("dWo_shard", dWo_shard, w, h, h, 4));
   const AttnBlockWs L = attn_block_ws(batch, seq, w, d.hs);
+  TPMLP_TRY(check_lds({h, 3 * w}));
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
     TPMLP_TRY(fill_zero(dWqkv_shard, h, 3 * w, 3 * w, s));

@@ -50,6 +50,8 @@ def call_fwd(dtype=1, T=64, h=64, F=128, tp=2, X=P, W1=P, ldw1=64, b1=None, W2=P
     (dict(X=None), E_NULL), (dict(W1=None), E_NULL), (dict(A=None), E_NULL), (dict(Z=None), E_NULL),
     (dict(X=P + 2), E_ALIGN), (dict(Z=P + 4), E_ALIGN), (dict(h=60), E_ALIGN), (dict(ldw1=68), E_ALIGN),
     (dict(F=2 * 60), E_ALIGN), (dict(dtype=2), E_DTYPE), (dict(dtype=0, h=62), E_ALIGN),
+    # a leading dimension of 2^22 elements or more is refused before the first of the two GEMMs
+    (dict(ldw1=1 << 22), E_SHAPE), (dict(h=1 << 22, ldw1=64), E_SHAPE),
 ])
 def test_tp_mlp_fwd_validation(kw, status):
     assert call_fwd(**kw) == status
@@ -93,6 +95,11 @@ def test_bwd_validation_and_workspace_size():
     assert f(*args, P + 16, 1 << 30) == E_ALIGN
     assert tl.lib.column_parallel_bwd(None, 1, 8, 16, 30, 4, P, 16, P, 8, P, 8, P, 16, P, 8, None) == E_DIV
     assert tl.lib.row_parallel_bwd(None, 1, 8, 32, 16, 2, P, 16, P, 16, P, 16, P, 16, P, 8) == E_SHAPE
+    # two GEMMs each: every leading dimension is checked before the first launch
+    assert tl.lib.column_parallel_bwd(None, 1, 8, 16, 32, 2, P, 1 << 22, P, 16, P, 16, P, 16, P, 16, None) == E_SHAPE
+    assert tl.lib.row_parallel_bwd(None, 1, 8, 32, 16, 2, P, 16, P, 16, P, 1 << 22, P, 16, P, 16) == E_SHAPE
+    big = [None, 1, 64, 64, 128, 2, P, P, 1 << 22, P, P, P, P, P, P, None, P]
+    assert f(*big, P, 1 << 30) == E_SHAPE
 
 
 def test_swiglu_validation():
