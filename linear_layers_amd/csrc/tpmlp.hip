@@ -1087,6 +1087,8 @@ int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, 
   if (batch < 0 || batch > 65535) return fail(TPMLP_E_SHAPE, "batch = %lld out of range", (long long)batch);
   TPMLP_TRY(check_rows("seq", seq));
   if (batch * seq > kMaxDim) return fail(TPMLP_E_SHAPE, "batch * seq above 2^31 - 1");
+  if ((seq + 63) / 64 * heads * batch > kMaxDim)   // the dK/dV grid: key blocks x heads x batch
+    return fail(TPMLP_E_SHAPE, "key blocks x heads x batch above 2^31 - 1");
   if (causal != 0 && causal != 1) return fail(TPMLP_E_VALUE, "causal = %d must be 0 or 1", causal);
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(TPMLP_E_VALUE, "scale must be finite and positive");
   return TPMLP_OK;
@@ -1194,8 +1196,6 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   if (T == 0) return TPMLP_OK;
   if (ldq >= kMaxLd || ldk >= kMaxLd || ldv >= kMaxLd || lddo >= kMaxLd)
     return fail(TPMLP_E_SHAPE, "leading dimension above 2^22 elements");
-  if ((seq + 63) / 64 * heads * batch > kMaxDim)
-    return fail(TPMLP_E_SHAPE, "key blocks x heads x batch above 2^31 - 1");
   const AttnBwdWs W = attn_bwd_ws(batch, seq, heads);
   const size_t need = W.total;
   if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
