@@ -145,11 +145,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int seq = p.seq;
   const int nqb = (seq + kAttnBQ - 1) / kAttnBQ;
-  // Causal: workgroup x is chunk c of query block qb (see attn_key_chunks);
-  // otherwise block x, all keys.
-  int qb = (int)blockIdx.x, chunk = 0;
+  // Workgroup x is work item x / (heads * batch) of head x % heads and
+  // sequence (x / heads) % batch, so the longest items of all heads go first.
+  // Causal: item i is chunk c of query block qb (see attn_key_chunks);
+  // otherwise block i, all keys.
+  const int hb = p.heads * p.batch;
+  const int item = (int)blockIdx.x / hb;
+  const int head = ((int)blockIdx.x % hb) % p.heads;
+  const int zb = ((int)blockIdx.x % hb) / p.heads;
+  int qb = item, chunk = 0;
   if (p.causal) {
-    int id = (int)blockIdx.x;
+    int id = item;
     // The grid holds exactly the chunks that exist; the bound only guards the loop.
     while (chunk < p.chunks && id >= nqb - (p.kc / 2) * chunk) {
       id -= nqb - (p.kc / 2) * chunk;
@@ -158,8 +164,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     if (chunk >= p.chunks) return;   // uniform across the workgroup, before any barrier
     qb = nqb - 1 - id;
   }
-  const int head = blockIdx.y;
-  const int64_t row_base = (int64_t)blockIdx.z * seq;
+  const int64_t row_base = (int64_t)zb * seq;
   const int q0 = qb * kAttnBQ;
   const int wq0 = q0 + 32 * wave;                 // this wave's first query row
   const int qrow = wq0 + (lane & 31);             // this lane's query row
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(const AttnArgs p) {
     // one of several chunks: its normalised partial and base-2 log-sum-exp in
     // this item's slot, for attn_fwd_combine_kernel
     const float inv = 1.0f / l_i;
-    const int64_t slot = ((int64_t)blockIdx.z * p.heads + head) * p.items + blockIdx.x;
+    const int64_t slot = ((int64_t)zb * p.heads + head) * p.items + item;
     const int r = 32 * wave + (lane & 31);
     float* dst = p.o_part + slot * (kAttnBQ * kAttnD) + (int64_t)r * kAttnD + 4 * h;
 #pragma unroll
@@ -825,9 +830,15 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   // Causal: workgroup x is chunk c of query block qb, enumerated chunk by chunk
   // (c = 0 for every block, then c = 1 for the blocks that have it, ...), the
   // blocks of one chunk from the last (longest) down.  Otherwise block x, all keys.
-  int qb = (int)blockIdx.x, chunk = 0;
+  // The grid is item-major as in the forward: workgroup x is item
+  // x / (heads * batch) of head x % heads and sequence (x / heads) % batch.
+  const int hb = p.heads * p.batch;
+  const int item = (int)blockIdx.x / hb;
+  const int head = ((int)blockIdx.x % hb) % p.heads;
+  const int zb = ((int)blockIdx.x % hb) / p.heads;
+  int qb = item, chunk = 0;
   if (p.causal) {
-    int id = (int)blockIdx.x;
+    int id = item;
     // The grid holds exactly the chunks that exist; the bound only guards the loop.
     while (chunk < p.dq_chunks && id >= nqb - (p.dq_kc / 2) * chunk) {
       id -= nqb - (p.dq_kc / 2) * chunk;
@@ -836,9 +847,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
     if (chunk >= p.dq_chunks) return;   // uniform across the workgroup, before any barrier
     qb = nqb - 1 - id;
   }
-  const int head = blockIdx.y;
   const int64_t T = (int64_t)p.batch * seq;
-  const int64_t row_base = (int64_t)blockIdx.z * seq;
+  const int64_t row_base = (int64_t)zb * seq;
   const int q0 = qb * kAttnBQ;
   const int wq0 = q0 + 32 * wave;
   const int qrow = wq0 + (lane & 31);
@@ -960,7 +970,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(const AttnBwdArgs p
   if (p.causal && attn_key_chunks(qb, seq, p.dq_kc) > 1) {
     // one of several chunks: its fp32 partial (unscaled) in this item's slot, for attn_bwd_dq_sum_kernel
     float* dst = p.dq_part +
-                 (((int64_t)blockIdx.z * p.heads + head) * p.dq_items + blockIdx.x) * (kAttnBQ * kAttnD) +
+                 (((int64_t)zb * p.heads + head) * p.dq_items + item) * (kAttnBQ * kAttnD) +
                  (int64_t)(32 * wave + (lane & 31)) * kAttnD + 4 * h;
 #pragma unroll
     for (int f = 0; f < 4; ++f)

@@ -1087,8 +1087,10 @@ int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, 
   if (batch < 0 || batch > 65535) return fail(TPMLP_E_SHAPE, "batch = %lld out of range", (long long)batch);
   TPMLP_TRY(check_rows("seq", seq));
   if (batch * seq > kMaxDim) return fail(TPMLP_E_SHAPE, "batch * seq above 2^31 - 1");
-  if ((seq + 63) / 64 * heads * batch > kMaxDim)   // the dK/dV grid: key blocks x heads x batch
-    return fail(TPMLP_E_SHAPE, "key blocks x heads x batch above 2^31 - 1");
+  // One-dimensional grids: key blocks (dK/dV) or work items (forward, dQ; at
+  // most 4 per key block plus 8) times heads times batch.
+  if (((seq + 63) / 64 * 4 + 8) * heads * batch > kMaxDim)
+    return fail(TPMLP_E_SHAPE, "(4 * key blocks + 8) x heads x batch above 2^31 - 1");
   if (causal != 0 && causal != 1) return fail(TPMLP_E_VALUE, "causal = %d must be 0 or 1", causal);
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(TPMLP_E_VALUE, "scale must be finite and positive");
   return TPMLP_OK;
@@ -1147,7 +1149,7 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   // chunks are merged by attn_fwd_combine_kernel.
   const int64_t nqb = (seq + kAttnBQ - 1) / kAttnBQ;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)(causal ? pl.items : nqb), (unsigned)heads, (unsigned)batch);
+  const dim3 grid((unsigned)((causal ? pl.items : nqb) * heads * batch));
   TPMLP_TRY(launch("attn_fwd", "attn_fwd_kernel", attn_fwd_kernel, grid, dim3(256), s, a));
   if (W.total > 0 && nqb > pl.kc / 2)
     TPMLP_TRY(launch("attn_fwd_combine", "attn_fwd_combine_kernel", attn_fwd_combine_kernel,
@@ -1243,7 +1245,7 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   TPMLP_TRY(launch("attn_bwd_dkdv", "attn_bwd_dkdv_kernel", attn_bwd_dkdv_kernel,
                    dim3((unsigned)(nkb * heads * batch)), dim3(256), s, a));
   TPMLP_TRY(launch("attn_bwd_dq", "attn_bwd_dq_kernel", attn_bwd_dq_kernel,
-                   dim3((unsigned)dq_items, (unsigned)heads, (unsigned)batch), dim3(256), s, a));
+                   dim3((unsigned)(dq_items * heads * batch)), dim3(256), s, a));
   if (causal && dqp.chunks > 1 && nqb > dqp.kc / 2)
     TPMLP_TRY(launch("attn_bwd_dq_sum", "attn_bwd_dq_sum_kernel", attn_bwd_dq_sum_kernel,
                      dim3((unsigned)(8 * (nqb - dqp.kc / 2)), (unsigned)heads, (unsigned)batch), dim3(256), s, a));
