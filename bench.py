@@ -66,8 +66,8 @@ def parse():
 
 # Kernel sources that cannot affect a workload's kernels (they hold other
 # kernels only), left out of its fingerprint.
-_UNRELATED_SOURCES = {"mlp": {"attn.hpp"}, "swiglu": {"attn.hpp"}, "sp_mlp": {"attn.hpp"},
-                      "proj": {"sp.hpp", "swiglu.hpp"}}
+_UNRELATED_SOURCES = {"mlp": {"attn.hpp", "sp.hpp", "swiglu.hpp"}, "swiglu": {"attn.hpp", "sp.hpp"},
+                      "sp_mlp": {"attn.hpp", "swiglu.hpp"}, "proj": {"sp.hpp", "swiglu.hpp"}}
 
 
 def kernel_fingerprint(kind: str) -> str:

@@ -215,6 +215,10 @@ __global__ void __launch_bounds__(256) layernorm_bwd_kernel(const bf16_t* __rest
 // dgamma[c] = sum_r dY[r,c] * xhat[r,c], dbeta[c] = sum_r dY[r,c].  A
 // workgroup owns 16 columns (4 chunks of 4) and 64 row lanes; lane l adds rows
 // l, l + 64, ... in order, then the 64 lane sums are added in order.
+// Workgroups are dealt to the 8 XCDs in turn, and a 128-byte line of X spans
+// four column groups (of dY, two): column group g therefore goes to the
+// workgroup on XCD g / q (q = full groups per XCD), so the groups that share
+// lines run on one XCD and read them through its L2 once.
 __global__ void __launch_bounds__(256) layernorm_param_grad_kernel(const bf16_t* __restrict__ X, int64_t ldx,
                                                                    int rows, int h, const float* __restrict__ mean,
                                                                    const float* __restrict__ rstd,
@@ -223,7 +227,9 @@ __global__ void __launch_bounds__(256) layernorm_param_grad_kernel(const bf16_t*
                                                                    float* __restrict__ dbeta) {
   __shared__ float pg[64][16], pb[64][16];
   const int cl = threadIdx.x & 3, rl = threadIdx.x >> 2;
-  const int c0 = blockIdx.x * 16 + 4 * cl;
+  const int q = (int)(gridDim.x >> 3), b = (int)blockIdx.x;
+  const int grp = b < 8 * q ? (b & 7) * q + (b >> 3) : b;
+  const int c0 = grp * 16 + 4 * cl;
   float sg[4] = {0.f, 0.f, 0.f, 0.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
   if (c0 < h) {
 #pragma unroll 4
@@ -251,7 +257,7 @@ __global__ void __launch_bounds__(256) layernorm_param_grad_kernel(const bf16_t*
     const bool beta_half = threadIdx.x >= 16;
     float t = 0.0f;
     for (int l = 0; l < 64; ++l) t += beta_half ? pb[l][col] : pg[l][col];
-    const int n = blockIdx.x * 16 + col;
+    const int n = grp * 16 + col;
     if (n < h) {
       if (beta_half) {
         if (dbeta) dbeta[n] = t;
