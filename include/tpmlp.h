@@ -311,8 +311,9 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
  * head and sequence, at 4096 tokens; at most 8 chunks per block). */
 size_t attn_fwd_workspace_bytes(int64_t batch, int64_t seq, int heads);
 
-/* Bytes of device workspace attn_bwd needs (0 on bad args): fp32 [heads, T]
- * row sums and, for causal sequences longer than 2048, fp32 partial dQ tiles
+/* Bytes of device workspace attn_bwd needs (0 on bad args): two fp32
+ * [heads, T] arrays (the row sums D and the log-sum-exp in base 2) and, for
+ * causal sequences longer than 2048, fp32 partial dQ tiles
  * of 64 KB, one per work item of the query blocks whose keys are split into
  * chunks (at most 8 chunks per block; about 4.5 tiles per query block of 128
  * rows, per head and sequence, at 32K tokens). */

@@ -391,6 +391,7 @@ struct AttnBwdArgs {
   int64_t ldq, ldk, ldv, ldo, lddo;
   const float* lse;   // [heads, T] natural log
   float* D;           // [heads, T] workspace: sum_d dO * O
+  float* L2;          // [heads, T] workspace: lse * log2(e), the base-2 form the dK/dV kernel stages
   bf16_t* dQ;
   bf16_t* dK;
   bf16_t* dV;
@@ -406,6 +407,8 @@ struct AttnBwdArgs {
 // Causal dQ work is split along keys in the forward's chunks (attn_key_chunks).
 
 // D[head][t] = sum over the head's 128 columns of dO * O; 16 lanes per (row, head).
+// The same pass stores lse in base 2 (L2), so the dK/dV kernel, whose queries
+// change every iteration, takes it ready instead of scaling it per element.
 __global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const AttnBwdArgs p) {
   const int64_t T = (int64_t)p.batch * p.seq;
   const int64_t item = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (row, head) = (item / heads, item % heads)
@@ -423,7 +426,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const AttnBwdArgs p) 
   }
 #pragma unroll
   for (int x = 8; x >= 1; x >>= 1) acc += __shfl_xor(acc, x);
-  if (live && j == 0) p.D[(int64_t)head * T + t] = acc;
+  if (live && j == 0) {
+    p.D[(int64_t)head * T + t] = acc;
+    p.L2[(int64_t)head * T + t] = p.lse[(int64_t)head * T + t] * 1.4426950408889634f;
+  }
 }
 
 // A tile of ROWS token rows x 128 of d in LDS, read two ways: 8 consecutive d
@@ -658,9 +664,9 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
   ot.init(wp, lane, p.lddo, pair_off);
   const bf16_t* Qh = p.Q + row_base * p.ldq + head * kAttnD;
   const bf16_t* dOh = p.dO + row_base * p.lddo + head * kAttnD;
-  const float* lse_h = p.lse + (int64_t)head * T + row_base;
+  const float* lse_h = p.L2 + (int64_t)head * T + row_base;
   const float* D_h = p.D + (int64_t)head * T + row_base;
-  // One stage: the query block's Q and dO tiles, then its lse and D values
+  // One stage: the query block's Q and dO tiles, then its base-2 lse and D values
   // (the pair's wave 0 fetches lse, wave 1 fetches D), all through the LDS DMA
   // so a single vmcnt wait covers the whole next stage.
   auto issue = [&](int qb, lds_char* dst) {
@@ -671,7 +677,6 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
             dst + AttnQTile::BYTES, wp);
     lds_dma_f32x64((wp == 0 ? lse_h : D_h) + q0, (uint32_t)rows * 4u, dst + kAttnDkvRows + 256 * wp, lane);
   };
-  const float log2e = 1.4426950408889634f;
 
   f32x16_t dk[4], dv[4];
 #pragma unroll
@@ -747,7 +752,7 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(const AttnBwdArgs
       float pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[f][4 * g + e], p.scale_log2, -l4[e] * log2e));
+        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[f][4 * g + e], p.scale_log2, -l4[e]));
       pk[f][2 * g] = pack_bf16x2(pv[0], pv[1]);
       pk[f][2 * g + 1] = pack_bf16x2(pv[2], pv[3]);
     };

@@ -1159,15 +1159,17 @@ int attn_fwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
 
 namespace {
 struct AttnBwdWs {
-  size_t d_bytes, part_off, total;
+  size_t d_bytes, l2_off, part_off, total;
 };
 
-// D [heads, T] fp32, then (when some causal query block has several key
-// chunks) the fp32 dQ partials [batch][heads][work items][128][128].
+// D [heads, T] fp32, the base-2 lse [heads, T] fp32, then (when some causal
+// query block has several key chunks) the fp32 dQ partials
+// [batch][heads][work items][128][128].
 AttnBwdWs attn_bwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnBwdWs w;
   w.d_bytes = align256((size_t)batch * seq * heads * sizeof(float));
-  w.part_off = w.d_bytes;
+  w.l2_off = w.d_bytes;
+  w.part_off = w.l2_off + w.d_bytes;
   const AttnChunkPlan pl = attn_chunk_plan(seq, kAttnDqMinKc);
   const size_t part = pl.chunks > 1 ? (size_t)batch * heads * pl.items * kAttnBQ * kAttnD * sizeof(float) : 0;
   w.total = w.part_off + align256(part);
@@ -1216,6 +1218,7 @@ int attn_bwd(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, 
   a.lddo = lddo;
   a.lse = lse;
   a.D = static_cast<float*>(workspace);
+  a.L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + W.l2_off);
   a.dQ = static_cast<bf16_t*>(dQ);
   a.dK = static_cast<bf16_t*>(dK);
   a.dV = static_cast<bf16_t*>(dV);

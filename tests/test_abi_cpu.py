@@ -200,8 +200,8 @@ def test_attn_block_validation():
     assert f(*fw, None, 0) == E_NULL
     assert f(*fw, P, need - 1) == E_WS
     # causal dQ partials: none up to 2048 tokens; at 32K tokens at most 8 key chunks per query block
-    assert tl.attn_bwd_workspace_bytes(1, 2048, 10) == 2048 * 10 * 4
-    assert tl.attn_bwd_workspace_bytes(1, 32768, 10) <= 32768 * 10 * 4 + 256 * 10 * 4.5 * 65536
+    assert tl.attn_bwd_workspace_bytes(1, 2048, 10) == 2 * 2048 * 10 * 4
+    assert tl.attn_bwd_workspace_bytes(1, 32768, 10) <= 2 * 32768 * 10 * 4 + 256 * 10 * 4.5 * 65536
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 3) == 0
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 2) >= 8 * 256 * 2 * 4
     b = tl.lib.tp_attn_bwd

@@ -208,7 +208,7 @@ def test_attn_bwd_deterministic_and_workspace():
         a = _bwd_case(1, seq, 2, True, seed=9)[2]
         b = _bwd_case(1, seq, 2, True, seed=9)[2]
         assert torch.equal(a, b)
-    assert tl.attn_bwd_workspace_bytes(2, 100, 3) >= 2 * 100 * 3 * 4
+    assert tl.attn_bwd_workspace_bytes(2, 100, 3) >= 2 * 2 * 100 * 3 * 4
     Z = torch.zeros((4, D), dtype=torch.bfloat16, device="cuda")
     L = torch.zeros((1, 4), device="cuda")
     small = torch.zeros(8, dtype=torch.uint8, device="cuda")
