@@ -350,10 +350,38 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
 
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];  // fragments of even / odd K-substeps
 
+  // 256x256 tiles with K steps of 64 (the input and weight gradients) spread
+  // the next substep's LDS reads between the current substep's MFMAs instead
+  // of issuing them as one burst: the burst filled the LDS command queue.
+  // The reads go out in the order the MFMAs consume them (A block 0, the B
+  // blocks, the other A blocks); a transposing fragment is two reads.
+  // (Measured in isolation: input gradients 1-3%, weight gradients 5%
+  // faster; K steps of 32 measured slower this way and keep the burst.)
+  constexpr bool kIlv = BM == 256 && BN == 256 && BKT == 64;
+  auto rd = [&](auto SC, const lds_char* src, u32x4_t (&af)[FM], u32x4_t (&bfr)[FN]) {
+    constexpr int S = decltype(SC)::value;
+    FragLoop<0, 1, S>::run(ta, src, af);
+    FragLoop<0, FN, S>::run(tb, src + TA::BYTES, bfr);
+    FragLoop<1, FM, S>::run(ta, src, af);
+  };
+  auto ilv = [&]() {
+    constexpr int nds = FM * (A_KMAJ ? 1 : 2) + FN * (B_KMAJ ? 1 : 2);   // LDS reads of one substep
+    constexpr int slots = FM * FN - 2;   // the last two MFMAs give the last reads time to land
+    constexpr int per = (nds + slots - 1) / slots;
+    constexpr int used = (nds + per - 1) / per;
+    static_assert(!kIlv || (nds % per == 0 && used <= FM * FN), "reads in equal groups under the MFMAs");
+#pragma unroll
+    for (int i = 0; i < used; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, per, 0);   // then `per` LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - used, 0);
+  };
+
   // One step in stage ST (compile time) with its substep-0 fragments in
   // a0/b0.  Order (kept by the scheduling barriers): loads of step kt+NS-1;
-  // then for each substep s the reads of substep s+1 go out before the MFMAs
-  // of substep s; before the last substep's MFMAs the kernel waits for step
+  // then for each substep s the reads of substep s+1 go out before (kIlv:
+  // between) the MFMAs of substep s; before the last substep's MFMAs the kernel waits for step
   // kt+1, passes the barrier and reads that step's substep-0 fragments.
   auto step = [&](auto STc, int kt) {
     constexpr int ST = decltype(STc)::value;
@@ -361,22 +389,37 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
     lds_char* nxt = stage(std::integral_constant<int, (ST + 1) % NS>{});
     if (kt + NS - 1 < nkp) issue(kt + NS - 1, stage(std::integral_constant<int, (ST + NS - 1) % NS>{}));
     __builtin_amdgcn_sched_barrier(0);
-    FragLoop<0, FM, 1>::run(ta, cur, a1);
-    FragLoop<0, FN, 1>::run(tb, cur + TA::BYTES, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NSUB == 4) {
-      FragLoop<0, FM, 2>::run(ta, cur, a0);
-      FragLoop<0, FN, 2>::run(tb, cur + TA::BYTES, b0);
+    if constexpr (kIlv) {
+      rd(std::integral_constant<int, 1>{}, cur, a1, b1);
+      mfmas(a0, b0);
+      ilv();
       __builtin_amdgcn_sched_barrier(0);
+      rd(std::integral_constant<int, 2>{}, cur, a0, b0);
       mfmas(a1, b1);
+      ilv();
       __builtin_amdgcn_sched_barrier(0);
-      FragLoop<0, FM, 3>::run(ta, cur, a1);
-      FragLoop<0, FN, 3>::run(tb, cur + TA::BYTES, b1);
+      rd(std::integral_constant<int, 3>{}, cur, a1, b1);
+      mfmas(a0, b0);
+      ilv();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      FragLoop<0, FM, 1>::run(ta, cur, a1);
+      FragLoop<0, FN, 1>::run(tb, cur + TA::BYTES, b1);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(a0, b0);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NSUB == 4) {
+        FragLoop<0, FM, 2>::run(ta, cur, a0);
+        FragLoop<0, FN, 2>::run(tb, cur + TA::BYTES, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        FragLoop<0, FM, 3>::run(ta, cur, a1);
+        FragLoop<0, FN, 3>::run(tb, cur + TA::BYTES, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (kt + 1 < nkp) {
       wait_landed(kt + 1);
