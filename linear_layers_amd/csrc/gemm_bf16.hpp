@@ -350,14 +350,15 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
 
   u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];  // fragments of even / odd K-substeps
 
-  // 256x256 tiles with K steps of 64 (the input and weight gradients) spread
-  // the next substep's LDS reads between the current substep's MFMAs instead
-  // of issuing them as one burst: the burst filled the LDS command queue.
-  // The reads go out in the order the MFMAs consume them (A block 0, the B
-  // blocks, the other A blocks); a transposing fragment is two reads.
-  // (Measured in isolation: input gradients 1-3%, weight gradients 5%
-  // faster; K steps of 32 measured slower this way and keep the burst.)
-  constexpr bool kIlv = BM == 256 && BN == 256 && BKT == 64;
+  // With K steps of 64 the next substep's LDS reads are spread between the
+  // current substep's MFMAs instead of going out as one burst (which filled
+  // the LDS command queue), in the order the MFMAs use them: A block 0, the
+  // B blocks, the other A blocks; a transposing fragment is two reads.
+  // (Measured: 1-4% faster on the tile shapes with K steps of 64, neutral on
+  // 256x192; the 256x320 weight gradient, both operands through transposing
+  // reads, ran 2.7% slower inside the attention block, and 256x256 tiles with
+  // K steps of 32 ran slower in isolation: those keep the burst.)
+  constexpr bool kIlv = BKT == 64 && !(BN == 320 && !A_KMAJ && !B_KMAJ);
   auto rd = [&](auto SC, const lds_char* src, u32x4_t (&af)[FM], u32x4_t (&bfr)[FN]) {
     constexpr int S = decltype(SC)::value;
     FragLoop<0, 1, S>::run(ta, src, af);
@@ -367,15 +368,19 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
   auto ilv = [&]() {
     constexpr int nds = FM * (A_KMAJ ? 1 : 2) + FN * (B_KMAJ ? 1 : 2);   // LDS reads of one substep
     constexpr int slots = FM * FN - 2;   // the last two MFMAs give the last reads time to land
-    constexpr int per = (nds + slots - 1) / slots;
-    constexpr int used = (nds + per - 1) / per;
-    static_assert(!kIlv || (nds % per == 0 && used <= FM * FN), "reads in equal groups under the MFMAs");
+    static_assert(!kIlv || slots >= 1, "at least three MFMAs per substep");
+    constexpr int per = slots >= 1 ? (nds + slots - 1) / slots : nds;
+    constexpr int full = nds / per, rest = nds - full * per;   // groups of `per` reads, then one of `rest`
 #pragma unroll
-    for (int i = 0; i < used; ++i) {
+    for (int i = 0; i < full; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, per, 0);   // then `per` LDS reads
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - used, 0);
+    if constexpr (rest > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, rest, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - full - (rest > 0 ? 1 : 0), 0);
   };
 
   // One step in stage ST (compile time) with its substep-0 fragments in
