@@ -311,6 +311,29 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
     }
   };
 
+  // The same loads in two halves (A, then B), for the split below; steps past
+  // the end of K zero both tiles in the first half.
+  auto issue_a = [&](int kt, lds_char* dst) {
+    if (kt < nk) {
+      const bf16_t* pa;
+      const bf16_t* pb;
+      uint32_t na, nb;
+      bases(kt, pa, na, pb, nb);
+      ta.load(pa, na, dst, wave);
+    } else if (kt < nkp) {
+      ta.zero(dst, wave, lane);
+      tb.zero(dst + TA::BYTES, wave, lane);
+    }
+  };
+  auto issue_b = [&](int kt, lds_char* dst) {
+    if (kt < nk) {
+      const bf16_t* pa;
+      const bf16_t* pb;
+      uint32_t na, nb;
+      bases(kt, pa, na, pb, nb);
+      tb.load(pb, nb, dst + TA::BYTES, wave);
+    }
+  };
   // Wait until this wave's loads of step `next` have landed: the loads of
   // the real steps after it that are already issued (at most NS-2) may stay
   // in flight.
@@ -359,6 +382,13 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
   // reads, ran 2.7% slower inside the attention block, and 256x256 tiles with
   // K steps of 32 ran slower in isolation: those keep the burst.)
   constexpr bool kIlv = BKT == 64 && !(BN == 320 && !A_KMAJ && !B_KMAJ);
+  // 256x256 weight gradients (both operands through transposing reads) also
+  // issue the next step's B loads one substep after its A loads (measured 2%
+  // faster in isolation; input gradients measured slower so).  With two
+  // stages every wait for a step's loads is a full vmcnt(0), so the split
+  // leaves the load accounting as it is.
+  constexpr bool kSplit = kIlv && BM == 256 && BN == 256 && !A_KMAJ && !B_KMAJ;
+  static_assert(!kSplit || NS == 2, "the split loads assume two stages");
   auto rd = [&](auto SC, const lds_char* src, u32x4_t (&af)[FM], u32x4_t (&bfr)[FN]) {
     constexpr int S = decltype(SC)::value;
     FragLoop<0, 1, S>::run(ta, src, af);
@@ -392,13 +422,22 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
     constexpr int ST = decltype(STc)::value;
     lds_char* cur = stage(STc);
     lds_char* nxt = stage(std::integral_constant<int, (ST + 1) % NS>{});
-    if (kt + NS - 1 < nkp) issue(kt + NS - 1, stage(std::integral_constant<int, (ST + NS - 1) % NS>{}));
+    lds_char* const ahead = stage(std::integral_constant<int, (ST + NS - 1) % NS>{});
+    if constexpr (kSplit) {
+      if (kt + NS - 1 < nkp) issue_a(kt + NS - 1, ahead);
+    } else {
+      if (kt + NS - 1 < nkp) issue(kt + NS - 1, ahead);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kIlv) {
       rd(std::integral_constant<int, 1>{}, cur, a1, b1);
       mfmas(a0, b0);
       ilv();
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kSplit) {
+        if (kt + NS - 1 < nkp) issue_b(kt + NS - 1, ahead);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       rd(std::integral_constant<int, 2>{}, cur, a0, b0);
       mfmas(a1, b1);
       ilv();
