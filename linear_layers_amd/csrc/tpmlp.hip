@@ -333,7 +333,14 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
   auto prep = [&](GemmArgs& a) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
-    a.group_m = std::max(1, std::min(a.tiles_m, (cus / 8) / a.tiles_n));
+    // Each product holds about half of an XCD's CUs: its tiles there form
+    // a block of g tile rows, g the power of two nearest the square root of
+    // that count, so they share as few operand blocks as possible (16 tiles
+    // per XCD: 4 x 4, eight 256-row blocks of A and B, instead of 2 x 8, ten).
+    const int per_xcd = std::max(1, (int)((int64_t)a.tiles_m * a.tiles_n / 8));
+    int g = 1;
+    while (g * g < per_xcd) g *= 2;
+    a.group_m = std::max(1, std::min(a.tiles_m, g));
     a.splits = 1;
     a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
     a.clk = nullptr;
