@@ -317,6 +317,19 @@ int check_lds(std::initializer_list<int64_t> lds) {
   return TPMLP_OK;
 }
 
+// Raster rows for tiles that share no operand with other XCDs (the weight
+// gradients, whose operands are both activations): an XCD's `per_xcd` tiles
+// form a block of g rows by ceil(per_xcd / g) columns with g + columns
+// smallest, so they need as few 256-row operand blocks as possible.
+int square_group(int per_xcd, int tiles_m) {
+  int best = 1, cost = 1 << 30;
+  for (int g = 1; g <= std::max(1, std::min(tiles_m, per_xcd)); ++g) {
+    const int c = g + (per_xcd + g - 1) / g;
+    if (c < cost) cost = c, best = g;
+  }
+  return best;
+}
+
 // The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
 // launch of 256x256 tiles (eight waves, K step 64, two stages) when together
 // they fill the chip once (at least 3/4 of the CUs, at most all of them) and
@@ -333,14 +346,10 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
   auto prep = [&](GemmArgs& a) {
     a.tiles_m = (a.M + BM - 1) / BM;
     a.tiles_n = (a.N + BN - 1) / BN;
-    // Each product holds about half of an XCD's CUs: its tiles there form
-    // a block of g tile rows, g the power of two nearest the square root of
-    // that count, so they share as few operand blocks as possible (16 tiles
-    // per XCD: 4 x 4, eight 256-row blocks of A and B, instead of 2 x 8, ten).
-    const int per_xcd = std::max(1, (int)((int64_t)a.tiles_m * a.tiles_n / 8));
-    int g = 1;
-    while (g * g < per_xcd) g *= 2;
-    a.group_m = std::max(1, std::min(a.tiles_m, g));
+    // Each product holds about half of an XCD's CUs; its tiles there form a
+    // square block (16 tiles per XCD: 4 x 4, eight 256-row blocks of A and
+    // B, instead of 2 x 8, ten).
+    a.group_m = square_group(std::max(1, (int)((int64_t)a.tiles_m * a.tiles_n / 8)), a.tiles_m);
     a.splits = 1;
     a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
     a.clk = nullptr;
@@ -368,7 +377,13 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     // whole rows of tiles, so each round of an XCD shares its A rows.
     const int bm = kCfgBf16[cfg].bm, bn = kCfgBf16[cfg].bn;
     const int tiles_m = (a.M + bm - 1) / bm, tiles_n = (a.N + bn - 1) / bn;
-    const int group = std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
+    // Weight gradients (both operands activations, shared by no other XCD)
+    // take a square block of the tiles one XCD runs at once instead.
+    int group = std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
+    if constexpr (!AK && !BKM) {
+      const int64_t slots = (int64_t)cus * kCfgBf16[cfg].occ, tiles = (int64_t)tiles_m * tiles_n;
+      group = square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
+    }
     switch (cfg) {
       case 0:
         // K step 32 with a 4-stage ring when B is read through the transposing
