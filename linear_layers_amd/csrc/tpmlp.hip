@@ -380,7 +380,9 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     // Weight gradients (both operands activations, shared by no other XCD)
     // take a square block of the tiles one XCD runs at once instead.
     int group = std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
-    if constexpr (!AK && !BKM) {
+    // So do products of at most 8 tile rows: whole rows there would make
+    // every XCD stream all of B.
+    if ((!AK && !BKM) || tiles_m <= 8) {
       const int64_t slots = (int64_t)cus * kCfgBf16[cfg].occ, tiles = (int64_t)tiles_m * tiles_n;
       group = square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
     }
