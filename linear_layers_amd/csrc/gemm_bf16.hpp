@@ -729,6 +729,21 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = mrow + 32 * i;
+        // The row block's H loads all go out before any is used, so their
+        // latencies overlap (one wait per row block, not one per load).
+        u32x2_t hq[FN][2][2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int cq = n0 + wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
+              hq[j][pr][q] = u32x2_t{0u, 0u};
+              if constexpr (kGelu) {   // with no activation H is not read (it may be NULL)
+                if (row < M && cq < N) hq[j][pr][q] = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
+              }
+            }
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -742,8 +757,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
               const int cq = c + 8 * q + 4 * h;
               float d[4] = {0.f, 0.f, 0.f, 0.f};
               if (row < M && cq < N) {
-                if constexpr (kGelu) {   // with no activation H is not read (it may be NULL)
-                  const u32x2_t hw = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
+                if constexpr (kGelu) {
+                  const u32x2_t hw = hq[j][pr][q];
                   const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
 #pragma unroll
                   for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e] * gelu_tanh_grad(hv[e]);
