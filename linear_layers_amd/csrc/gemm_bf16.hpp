@@ -540,17 +540,23 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
       const int h = lane >> 5;
       // Bias of the lane's columns: register group g = 2pr + q holds columns
       // c + 8q + 4h .. + 3 of the 16-column block c = ... + 32 j + 16 pr.
-      float bv[FN][4][4];
+      // All of them are loaded before any is converted (one wait, not one per load).
+      u32x2_t bw[FN][4];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int cq = n0 + wn * WTN + 32 * j + 8 * g + 4 * h;
-          bv[j][g][0] = bv[j][g][1] = bv[j][g][2] = bv[j][g][3] = 0.f;
-          if (bias && cq < N) {
-            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(bias + cq);
-            bv[j][g][0] = bf16lo(w[0]); bv[j][g][1] = bf16hi(w[0]); bv[j][g][2] = bf16lo(w[1]); bv[j][g][3] = bf16hi(w[1]);
-          }
+          bw[j][g] = u32x2_t{0u, 0u};
+          if (bias && cq < N) bw[j][g] = *reinterpret_cast<const u32x2_t*>(bias + cq);
+        }
+      float bv[FN][4][4];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2_t w = bw[j][g];
+          bv[j][g][0] = bf16lo(w[0]); bv[j][g][1] = bf16hi(w[0]); bv[j][g][2] = bf16lo(w[1]); bv[j][g][3] = bf16hi(w[1]);
         }
       // Rows outermost: the four 32-byte pieces of each 128-byte line of a row
       // (two j blocks x two 16-column halves) are stored back to back, so L2
