@@ -17,6 +17,7 @@
 
 #include "gemm.hpp"
 #include "gemm_bf16.hpp"
+#include "gemm_w4.hpp"
 #include "reduce.hpp"
 #include "attn.hpp"
 #include "sp.hpp"
@@ -216,37 +217,33 @@ struct TileCfg {
   int bm, bn, occ;   // tile, workgroups per CU
   float eff, eff_act; // measured relative throughput: plain fp32 epilogue / activation epilogues
   bool f32_epi_only;  // too many registers for the activation epilogues
-  bool b_kmaj_only;   // only where B is K-contiguous (plain 16-byte LDS reads)
 };
-// bf16: 256x256 with 8 waves (2 x 4, two per SIMD, so one issues MFMAs while
-// the other waits) is fastest when it fills the chip; 128x128 with 4 waves and
-// two workgroups per CU wins for grids that would leave CUs idle; 256x320 and
-// 256x192 (8 waves as 4 x 2, 64x160 / 64x96 per wave) fill the chip where
-// widths of 5120, 3840, 3072 or 1536 leave 256x256 a fraction of a round
-// short.  Measured inside the model steps: 4096x5120x3840 142 us vs 180 at
-// 128x128; per CU, 256x192 runs at 0.80 of 256x256's rate when B is
-// K-contiguous (8192x1536x4096 138 vs 149 us) but at 0.72-0.77 when B goes
-// through the transposing reads (2048x6144x12288 337 vs 322 us), so it is
-// kept to the former.  Two 128x128 workgroups per CU run at about 0.72 of a
-// 256x256 workgroup's rate (the GPT-3 shard's 2048x12288x6144 and
-// 6144x12288x2048 products: 328 vs 358 us and 335 vs 421 us with 256x256
-// tiles although they leave a round partly idle), so they win only where
-// the larger tiles would leave much of the chip idle.
-constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f, false, false},
-                                {128, 128, 2, 0.72f, 0.72f, false, false},
-                                {256, 320, 1, 0.95f, 0.95f, true, false},
-                                {256, 192, 1, 0.80f, 0.80f, false, true}};
-constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f, false, false}, {64, 64, 1, 0.60f, 0.60f, false, false}};
+// bf16: 256x256 with 4 waves (128x128 per wave, gemm_w4.hpp) is fastest
+// when it fills the chip; the other shapes run on the 8-wave kernel
+// (gemm_bf16.hpp): 128x128 with 4 waves and two workgroups per CU for grids
+// that would leave CUs idle, and 256x320 (8 waves as 4 x 2, 64x160 per wave)
+// for fp32 outputs whose width (5120) leaves 256x256 a fraction of a round
+// short.  Their efficiencies are relative to the 4-wave 256x256 kernel, which
+// runs the MLP products 10-20% faster than the 8-wave 256x256 tile they were
+// first measured against (8192x2048x4096: 107 vs 118-131 us; 8192x4096x2048:
+// 120 vs 141-151 us): against that tile, 4096x5120x3840 ran in 142 us at
+// 256x320 vs 180 at 128x128, and two 128x128 workgroups per CU ran at about
+// 0.72 of its rate.  (A 256x192 tile of the 8-wave kernel, 0.80 of the old
+// 256x256 rate, no longer wins for any shape and was dropped.)
+constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f, false},
+                                {128, 128, 2, 0.62f, 0.62f, false},
+                                {256, 320, 1, 0.82f, 0.82f, true}};
+constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f, false}, {64, 64, 1, 0.60f, 0.60f, false}};
 constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
 
-int plan_cfg(int dtype, int M, int N, int epi, bool b_kmaj, int cus) {
+int plan_cfg(int dtype, int M, int N, int epi, int cus) {
   const TileCfg* cfgs = dtype == TPMLP_BF16 ? kCfgBf16 : kCfgF32;
   const int n = dtype == TPMLP_BF16 ? (int)(sizeof(kCfgBf16) / sizeof(kCfgBf16[0]))
                                     : (int)(sizeof(kCfgF32) / sizeof(kCfgF32[0]));
   int best = 0;
   double best_score = -1.0;
   for (int i = 0; i < n; ++i) {
-    if ((cfgs[i].f32_epi_only && epi != kEpiF32) || (cfgs[i].b_kmaj_only && !b_kmaj)) continue;
+    if (cfgs[i].f32_epi_only && epi != kEpiF32) continue;
     const int64_t tiles = (int64_t)((M + cfgs[i].bm - 1) / cfgs[i].bm) * ((N + cfgs[i].bn - 1) / cfgs[i].bn);
     const int64_t slots = (int64_t)cus * cfgs[i].occ;
     const int64_t rounds = (tiles + slots - 1) / slots;
@@ -305,6 +302,24 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
                 dim3(64 * WGM * WGN), s, a);
 }
 
+// The four-wave 256x256 kernel (K steps of 64, two LDS stages).
+template <bool AK, bool BKM, int EPI>
+int run_gemm_w4(const char* role, GemmArgs a, hipStream_t s, int group) {
+  a.tiles_m = (a.M + 255) / 256;
+  a.tiles_n = (a.N + 255) / 256;
+  a.group_m = group;
+  if (a.splits < 1) a.splits = 1;
+  const int per = (a.K + a.splits - 1) / a.splits;
+  a.k_per_split = ((per + 63) / 64) * 64;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * a.splits;
+  if (grid <= 0) return TPMLP_OK;
+  if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
+  char sym[96];
+  snprintf(sym, sizeof(sym), "gemm_w4_kernel<256,256,%d,%d,%d>", (int)AK, (int)BKM, EPI);
+  a.clk = prof_clock_slot(role);
+  return launch(role, sym, gemm_w4_kernel<256, 256, AK, BKM, EPI>, dim3((unsigned)grid), dim3(256), s, a);
+}
+
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 320 rows of
 // a K-contiguous operand (or 64 K-rows of an M/N-contiguous one).
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
@@ -331,7 +346,7 @@ int square_group(int per_xcd, int tiles_m) {
 }
 
 // The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
-// launch of 256x256 tiles (eight waves, K step 64, two stages) when together
+// launch of 256x256 tiles (the four-wave kernel) when together
 // they fill the chip once (at least 3/4 of the CUs, at most all of them) and
 // the first product's tile count is a multiple of 8 (so each workgroup keeps
 // its XCD within its product).  *done reports whether the pair ran; when it
@@ -359,9 +374,8 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
   if (n0 % 8 != 0 || n0 + n1 > cus || 4 * (n0 + n1) < 3 * (int64_t)cus) return TPMLP_OK;
   a0.clk = prof_clock_slot(role);   // the clock of the first product's workgroup 0
   *done = true;
-  return launch(role, "gemm_bf16_pair_kernel<256,256,0,0,0,2,1,64,4,2>",
-                gemm_bf16_pair_kernel<BM, BN, false, false, kEpiF32, 2, 1, BKT, 4, 2>, dim3((unsigned)(n0 + n1)),
-                dim3(512), s, a0, a1, (int)n0);
+  return launch(role, "gemm_w4_pair_kernel<256,256,0,0,0>", gemm_w4_pair_kernel<BM, BN, false, false, kEpiF32>,
+                dim3((unsigned)(n0 + n1)), dim3(256), s, a0, a1, (int)n0);
 }
 
 template <bool AK, bool BKM, int EPI>
@@ -371,7 +385,7 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     return fail(TPMLP_E_SHAPE, "%s: leading dimension above 2^22 elements", role);
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
-  const int cfg = plan_cfg(dtype, a.M, a.N, EPI, BKM, cus);
+  const int cfg = plan_cfg(dtype, a.M, a.N, EPI, cus);
   if (dtype == TPMLP_BF16) {
     // Raster group: the tiles one XCD runs at once (CUs/8 x occupancy) span
     // whole rows of tiles, so each round of an XCD shares its A rows.
@@ -387,18 +401,11 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
       group = square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
     }
     switch (cfg) {
-      case 0:
-        // K step 32 with a 4-stage ring when B is read through the transposing
-        // LDS reads (more loads in flight hide their latency); 64 x 2 otherwise.
-        if constexpr (AK && !BKM) return run_gemm_bf16<256, 256, AK, BKM, EPI, 4, 1, 32, 4>(role, a, s, group);
-        else return run_gemm_bf16<256, 256, AK, BKM, EPI, 2, 1, 64, 4>(role, a, s, group);
+      case 0: return run_gemm_w4<AK, BKM, EPI>(role, a, s, group);
       case 2:
-        // 320 and 192 rows of 64-element K steps split evenly over 8 waves' loads.
+        // 320 rows of 64-element K steps split evenly over 8 waves' loads.
         if constexpr (EPI == kEpiF32) return run_gemm_bf16<256, 320, AK, BKM, EPI, 2, 1, 64, 2, 4>(role, a, s, group);
         else return fail(TPMLP_E_SHAPE, "%s: no 256x320 tile for this epilogue", role);
-      case 3:
-        if constexpr (BKM) return run_gemm_bf16<256, 192, AK, BKM, EPI, 2, 1, 64, 2, 4>(role, a, s, group);
-        else return fail(TPMLP_E_SHAPE, "%s: no 256x192 tile for an N-contiguous B", role);
       default: return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, group);
     }
   }
@@ -708,7 +715,7 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
   TPMLP_TRY(device_cus(&cus));
   TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.mlp_dgrad_act", dtype, a, s)));
   if (db1_shard) {
-    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, true, cus);
+    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, cus);
     const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
     const int rows = (int)((T + bm - 1) / bm);
     TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 63) / 64)),

@@ -301,6 +301,6 @@ def test_profiler_times_and_clocks():
     roles = {k.split("|")[0] for k in recs}
     assert roles == {"gemm.mlp_fwd1", "gemm.mlp_fwd2"}
     for n, ms, sym, clocks in recs.values():
-        assert n == 1 and ms > 0.0 and sym.startswith("gemm_bf16_kernel<")
+        assert n == 1 and ms > 0.0 and sym.startswith(("gemm_bf16_kernel<", "gemm_w4_kernel<"))
         assert len(clocks) == 1 and 0.05 < clocks[0] < 5.0
     assert tl.profile_collect() == {}

@@ -1,14 +1,15 @@
-"""GPU parity of the wide GEMM tiles (256x320 and 256x192, eight waves as
-4 x 2) against the float64 oracle, through the public entry points.
+"""GPU parity of the GEMM tile shapes that the common MLP cases do not reach,
+against the float64 oracle, through the public entry points.
 
-The planner gives these tiles to widths such as 5120, 3840, 3072 and 1536,
-where 256x256 tiles would leave part of a round idle (256x320 for fp32
-outputs, 256x192 where B is K-contiguous).  Each case is sized so the planner
-picks the tile under test (checked through the launch records), with ragged
-M, N and K, and covers one operand orientation or epilogue: the fp32 partial
-with a K-contiguous A and an N-contiguous B, two K-contiguous operands, two
+The 256x320 tile (eight waves as 4 x 2) serves fp32 outputs whose width
+(5120 and the like) leaves 256x256 tiles part of a round idle; the four-wave
+256x256 kernel's typed epilogues are also run here on ragged shapes whose last
+tile column is partial.  Each case is sized so the planner picks the kernel
+under test (checked through the launch records), with ragged M, N and K, and
+covers one operand orientation or epilogue: the fp32 partial with a
+K-contiguous A and an N-contiguous B, two K-contiguous operands, two
 M/N-contiguous operands (weight gradients, B's K-rows of 40 chunks), GeLU'
-with the bias-gradient column sums summed over four wave rows, and the gated
+with the bias-gradient column sums (two wave rows per tile), and the gated
 MLP's backward epilogue.  Bar: max|err|/max|ref| <= 2e-2 (bf16 storage).
 """
 from __future__ import annotations
@@ -59,7 +60,7 @@ def test_row_parallel_fwd_256x320():
     assert_close(to_f64(Z), want, "bf16", "Z")
 
 
-@pytest.mark.parametrize("T,K,tile", [(4000, 5096, "256,320"), (2600, 3080, "256,192")])
+@pytest.mark.parametrize("T,K,tile", [(4000, 5096, "gemm_bf16_kernel<256,320"), (2600, 3080, "gemm_w4_kernel<256,256")])
 def test_row_parallel_bwd_dgrad_wide(T, K, tile):
     """dX = dY W^T with M = T, N = K, K = 200: both operands K-contiguous."""
     need_gpu()
@@ -70,7 +71,7 @@ def test_row_parallel_bwd_dgrad_wide(T, K, tile):
     X, W, dY = to_dev(Xr, "bf16"), to_dev(Wr, "bf16"), to_dev(dYr, "bf16")
     dX, dW = empty_f32((T, K)), empty_f32((K, N))
     syms = _launched(lambda: tl.row_parallel_bwd(X, W, dY, 1, dX, dW))
-    _has(syms, f"gemm_bf16_kernel<{tile},1,1,0,")
+    _has(syms, f"{tile},1,1,0")
     g = ref.row_parallel_bwd(synth.to_f64(Xr, "bf16"), synth.to_f64(Wr, "bf16"), synth.to_f64(dYr, "bf16"))
     assert_close(to_f64(dX), g["dX"], "bf16", "dX")
     assert_close(to_f64(dW), g["dW"], "bf16", "dW")
@@ -95,9 +96,9 @@ def test_column_parallel_bwd_wgrad_256x320():
     assert_close(to_f64(db), g["db"], "bf16", "db")
 
 
-def test_tp_mlp_bwd_dgrad_act_256x192():
+def test_tp_mlp_bwd_dgrad_act_ragged():
     """The MLP backward with T = 8000, h = 200, F/tp = 1496: dH = (dZ W2^T) * GeLU'(H) and the
-    db1 column sums run on 256x192 tiles (four wave rows summed per tile)."""
+    db1 column sums run on the four-wave 256x256 tiles, the last tile column 216 wide."""
     need_gpu()
     T, h, F = 8000, 200, 1496
     _say(f"mlp bwd T={T} h={h} F={F}")
@@ -113,7 +114,7 @@ def test_tp_mlp_bwd_dgrad_act_256x192():
         tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
 
     syms = _launched(run)
-    _has(syms, "gemm_bf16_kernel<256,192,1,1,2,")
+    _has(syms, "gemm_w4_kernel<256,256,1,1,2>")
     o = ref.tp_mlp_fwd_shard(f["X"], f["W1"], f["b1"], f["W2"], 1, 0)
     assert_close(to_f64(A), o["A"], "bf16", "A")
     assert_close(to_f64(Z), o["Z"], "bf16", "Z")
@@ -122,9 +123,9 @@ def test_tp_mlp_bwd_dgrad_act_256x192():
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
-def test_swiglu_256x192():
+def test_swiglu_bwd_ragged():
     """The gated MLP with T = 8000, h = 136, F/tp = 1496: dA = dZ W_down^T with its gate/up
-    epilogue runs on 256x192 tiles."""
+    epilogue runs on the four-wave 256x256 tiles, the last tile column 216 wide."""
     need_gpu()
     T, h, F = 8000, 136, 1496
     _say(f"swiglu T={T} h={h} F={F}")
@@ -142,7 +143,7 @@ def test_swiglu_256x192():
         tl.tp_swiglu_bwd(X, W_gu, Wd, GU, A, dZ, 1, dX, dW_gu, dW_down)
 
     syms = _launched(run)
-    _has(syms, "gemm_bf16_kernel<256,192,1,1,4,")
+    _has(syms, "gemm_w4_kernel<256,256,1,1,4>")
     o = sw.tp_swiglu_fwd_shard(f["X"], f["W_gate"], f["W_up"], f["W_down"], 1, 0)
     assert_close(to_f64(GU), o["GU"], "bf16", "GU")
     assert_close(to_f64(A), o["A"], "bf16", "A")
