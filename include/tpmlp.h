@@ -155,6 +155,25 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
                float* dW1_shard, float* db1_shard, float* dW2_shard, void* workspace,
                size_t workspace_bytes);
 
+/* tp_mlp_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same operands, outputs and results as tp_mlp_bwd
+ * (the same kernels in the same order); the workspace is a static device
+ * array of tpmlp_noalloc_scratch_bytes() bytes (64 MiB) that the library
+ * holds on each device it runs on until the process ends.  The call makes no
+ * allocation.  Sizes whose workspace (tpmlp_bwd_workspace_bytes) exceeds the
+ * array return TPMLP_E_WORKSPACE before anything is enqueued (a 8192-token,
+ * 2048-wide shard needs 33 MiB).  All calls on one device share the array:
+ * calls that overlap on one device (different streams, or different host
+ * threads) race; calls on one stream are ordered. */
+int tp_mlp_bwd_noalloc(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size,
+                       const void* X, const void* W1_shard, int64_t ldw1, const void* W2_shard,
+                       const void* H_save, const void* A_save, const void* dZ, float* dX_partial,
+                       float* dW1_shard, float* db1_shard, float* dW2_shard);
+
+/* Size in bytes of the static scratch array of tp_mlp_bwd_noalloc. */
+size_t tpmlp_noalloc_scratch_bytes(void);
+
 /* Backward of one column shard Y_i = X W_i (+ b_i) with no activation (the
  * QKV projection), dY_i the gradient of Y_i [wangyu 按列切分, backward]:
  *   dX_partial [T, K] fp32, lddx >= K   dY_i W_i^T (sum over shards = dX)

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "TpmlpError", "lib", "LIB_PATH", "F32", "BF16", "ACT_NONE", "ACT_GELU_TANH",
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
-    "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
+    "tp_mlp_bwd_noalloc", "tpmlp_noalloc_scratch_bytes", "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
     "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_fwd_workspace_bytes", "tp_attn_fwd", "tp_attn_fwd_workspace_bytes",
@@ -46,6 +46,9 @@ _SIGNATURES = {
     "tp_mlp_fwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_mlp_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                    _vp, _sz],
+    "tp_mlp_bwd_noalloc": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp],
+    "tpmlp_noalloc_scratch_bytes": [],
     "column_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                             _i64, _vp],
     "row_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64],
@@ -76,7 +79,7 @@ _SIGNATURES = {
     "tpmlp_profile_enable": [ctypes.c_char_p],
     "tpmlp_profile_collect": [ctypes.c_char_p, _sz],
 }
-_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_attn_bwd_workspace_bytes": _sz,
+_RESTYPES = {"tpmlp_bwd_workspace_bytes": _sz, "tpmlp_noalloc_scratch_bytes": _sz, "attn_bwd_workspace_bytes": _sz, "tp_attn_bwd_workspace_bytes": _sz,
              "attn_fwd_workspace_bytes": _sz, "tp_attn_fwd_workspace_bytes": _sz,
              "tp_swiglu_bwd_workspace_bytes": _sz, "tpmlp_status_string": ctypes.c_char_p,
              "tpmlp_last_error": ctypes.c_char_p, "tpmlp_version": ctypes.c_char_p}
@@ -232,6 +235,24 @@ def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_parti
     _check(_get_lib().tp_mlp_bwd(_stream(stream, X), dt, T, h, F, tp_size, _ptr(X), _ptr(W1_shard), _ld(W1_shard, Fs),
                           _ptr(W2_shard), _ptr(H_save), _ptr(A_save), _ptr(dZ), _ptr(dX_partial), _ptr(dW1_shard),
                           _ptr(db1_shard), _ptr(dW2_shard), _ptr(workspace), workspace.numel()))
+
+
+def tp_mlp_bwd_noalloc(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_partial, dW1_shard, dW2_shard,
+                       db1_shard=None, stream=None) -> None:
+    """tp_mlp_bwd with its workspace in the library's static device scratch array (no allocation)."""
+    T, h = X.shape
+    Fs = W1_shard.shape[1]
+    F = Fs * tp_size
+    for n, t in (("X", X), ("W2_shard", W2_shard), ("H_save", H_save), ("A_save", A_save), ("dZ", dZ),
+                 ("dX_partial", dX_partial), ("dW1_shard", dW1_shard), ("dW2_shard", dW2_shard)):
+        _require_contiguous(n, t)
+    _check(_get_lib().tp_mlp_bwd_noalloc(_stream(stream, X), _dtype(X), T, h, F, tp_size, _ptr(X), _ptr(W1_shard),
+                                         _ld(W1_shard, Fs), _ptr(W2_shard), _ptr(H_save), _ptr(A_save), _ptr(dZ),
+                                         _ptr(dX_partial), _ptr(dW1_shard), _ptr(db1_shard), _ptr(dW2_shard)))
+
+
+def tpmlp_noalloc_scratch_bytes() -> int:
+    return int(_get_lib().tpmlp_noalloc_scratch_bytes())
 
 
 def column_parallel_bwd(X, W_shard, dY, tp_size: int, dX_partial, dW_shard, db_shard=None, stream=None) -> None:

@@ -546,6 +546,121 @@ BwdLayout bwd_layout(int dtype, int64_t T, int64_t h, int64_t Fs) {
   return L;
 }
 
+// Operand checks of one shard's MLP backward (shared by the workspace and
+// the allocation-free entry points).
+int check_mlp_bwd_args(int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X, const void* W1_shard,
+                       int64_t ldw1, const void* W2_shard, const void* H_save, const void* A_save, const void* dZ,
+                       float* dX_partial, float* dW1_shard, float* db1_shard, float* dW2_shard) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_split("F", F, tp_size));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("h", h));
+  TPMLP_TRY(check_dim("F", F));
+  const int64_t Fs = F / tp_size;
+  const int v = chunk_elems(dtype);
+  TPMLP_TRY(check_mat("X", X, T, h, h, v));
+  TPMLP_TRY(check_mat("W1_shard", W1_shard, h, Fs, ldw1, v));
+  TPMLP_TRY(check_mat("W2_shard", W2_shard, Fs, h, h, v));
+  TPMLP_TRY(check_mat("H_save", H_save, T, Fs, Fs, v));
+  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, v));
+  TPMLP_TRY(check_mat("dZ", dZ, T, h, h, v));
+  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
+  TPMLP_TRY(check_mat("dW1_shard", dW1_shard, h, Fs, Fs, 4));
+  TPMLP_TRY(check_vec("db1_shard", db1_shard, Fs, false));
+  TPMLP_TRY(check_mat("dW2_shard", dW2_shard, Fs, h, h, 4));
+  TPMLP_TRY(check_lds({h, ldw1, Fs}));
+  return TPMLP_OK;
+}
+
+// One shard's MLP backward on a validated workspace of bwd_layout(...).total bytes.
+int mlp_bwd_launch(hipStream_t s, int dtype, int64_t T, int64_t h, int64_t Fs, const void* X, const void* W1_shard,
+                   int64_t ldw1, const void* W2_shard, const void* H_save, const void* A_save, const void* dZ,
+                   float* dX_partial, float* dW1_shard, float* db1_shard, float* dW2_shard, void* workspace) {
+  const BwdLayout L = bwd_layout(dtype, T, h, Fs);
+  if (T == 0) {
+    TPMLP_TRY(fill_zero(dW1_shard, h, Fs, Fs, s));
+    TPMLP_TRY(fill_zero(dW2_shard, Fs, h, h, s));
+    return fill_zero(db1_shard, 1, Fs, Fs, s);
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* dH = ws + L.dh_off;
+  float* cs = reinterpret_cast<float*>(ws + L.cs_off);
+
+  // dH = (dZ W2_i^T) * GeLU'(H_i), with per-tile column sums of dH.
+  GemmArgs a = gemm_args(dZ, h, W2_shard, h, T, Fs, h);
+  a.Y = dH;
+  a.ldy = Fs;
+  a.H = const_cast<void*>(H_save);
+  a.ldh = Fs;
+  a.colsum = db1_shard ? cs : nullptr;
+  a.act = kActGeluTanh;
+  // The tile rows used by the plan decide how many column-sum rows exist.
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.mlp_dgrad_act", dtype, a, s)));
+  if (db1_shard) {
+    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, cus);
+    const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
+    const int rows = (int)((T + bm - 1) / bm);
+    TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 63) / 64)),
+                     dim3(64), s, (const float*)cs, rows, (int)Fs, db1_shard));
+  }
+  // dW2_i = A_i^T dZ and dW1_i = X^T dH_i: one paired launch when together
+  // they fill the chip once, else one launch each.
+  GemmArgs w2 = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
+  w2.C = dW2_shard;
+  w2.ldc = h;
+  GemmArgs w1 = gemm_args(X, h, dH, Fs, h, Fs, T);
+  w1.C = dW1_shard;
+  w1.ldc = Fs;
+  bool paired = false;
+  TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
+  if (!paired) {
+    float* slices = reinterpret_cast<float*>(ws + L.split_off);
+    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad2", "wgrad_split_sum", dtype, w2, slices, s));
+    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad1", "wgrad_split_sum", dtype, w1, slices, s));
+  }
+  // dX_i = dH_i W1_i^T
+  a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
+  a.C = dX_partial;
+  a.ldc = h;
+  return run_gemm<true, true, kEpiF32>("gemm.mlp_dgrad1", dtype, a, s);
+}
+
+
+// -------------------------------------------------- allocation-free scratch --
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): tp_mlp_bwd_noalloc keeps
+// its workspace in this file-scope device array instead of a caller buffer.
+// Each device the library runs on holds its own copy until the process ends.
+// In host code the array's name is only a host-side stand-in; its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is passed to kernels.  Calls on one device
+// share the array, so calls that overlap on one device race; nothing in it
+// needs to start at zero (every byte the backward reads it wrote first).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;   // 64 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(TPMLP_E_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TPMLP_OK;
+}
+
 }  // namespace
 
 // ======================================================================= ABI
@@ -666,23 +781,9 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
                const void* W1_shard, int64_t ldw1, const void* W2_shard, const void* H_save, const void* A_save,
                const void* dZ, float* dX_partial, float* dW1_shard, float* db1_shard, float* dW2_shard,
                void* workspace, size_t workspace_bytes) {
-  TPMLP_TRY(check_dtype(dtype));
-  TPMLP_TRY(check_split("F", F, tp_size));
-  TPMLP_TRY(check_rows("T", T));
-  TPMLP_TRY(check_dim("h", h));
-  TPMLP_TRY(check_dim("F", F));
+  TPMLP_TRY(check_mlp_bwd_args(dtype, T, h, F, tp_size, X, W1_shard, ldw1, W2_shard, H_save, A_save, dZ, dX_partial,
+                               dW1_shard, db1_shard, dW2_shard));
   const int64_t Fs = F / tp_size;
-  const int v = chunk_elems(dtype);
-  TPMLP_TRY(check_mat("X", X, T, h, h, v));
-  TPMLP_TRY(check_mat("W1_shard", W1_shard, h, Fs, ldw1, v));
-  TPMLP_TRY(check_mat("W2_shard", W2_shard, Fs, h, h, v));
-  TPMLP_TRY(check_mat("H_save", H_save, T, Fs, Fs, v));
-  TPMLP_TRY(check_mat("A_save", A_save, T, Fs, Fs, v));
-  TPMLP_TRY(check_mat("dZ", dZ, T, h, h, v));
-  TPMLP_TRY(check_mat("dX_partial", dX_partial, T, h, h, 4));
-  TPMLP_TRY(check_mat("dW1_shard", dW1_shard, h, Fs, Fs, 4));
-  TPMLP_TRY(check_vec("db1_shard", db1_shard, Fs, false));
-  TPMLP_TRY(check_mat("dW2_shard", dW2_shard, Fs, h, h, 4));
   const BwdLayout L = bwd_layout(dtype, T, h, Fs);
   if (T > 0) {
     if (workspace == nullptr) return fail(TPMLP_E_NULL, "workspace is NULL");
@@ -691,57 +792,28 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return fail(TPMLP_E_ALIGNMENT, "workspace is not 256-byte aligned");
   }
-  TPMLP_TRY(check_lds({h, ldw1, Fs}));
-  hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {
-    TPMLP_TRY(fill_zero(dW1_shard, h, Fs, Fs, s));
-    TPMLP_TRY(fill_zero(dW2_shard, Fs, h, h, s));
-    return fill_zero(db1_shard, 1, Fs, Fs, s);
-  }
-  char* ws = static_cast<char*>(workspace);
-  void* dH = ws + L.dh_off;
-  float* cs = reinterpret_cast<float*>(ws + L.cs_off);
-
-  // dH = (dZ W2_i^T) * GeLU'(H_i), with per-tile column sums of dH.
-  GemmArgs a = gemm_args(dZ, h, W2_shard, h, T, Fs, h);
-  a.Y = dH;
-  a.ldy = Fs;
-  a.H = const_cast<void*>(H_save);
-  a.ldh = Fs;
-  a.colsum = db1_shard ? cs : nullptr;
-  a.act = kActGeluTanh;
-  // The tile rows used by the plan decide how many column-sum rows exist.
-  int cus = 256;
-  TPMLP_TRY(device_cus(&cus));
-  TPMLP_TRY((run_gemm<true, true, kEpiActBwd>("gemm.mlp_dgrad_act", dtype, a, s)));
-  if (db1_shard) {
-    const int cfg = plan_cfg(dtype, (int)T, (int)Fs, kEpiActBwd, cus);
-    const int bm = dtype == TPMLP_BF16 ? kCfgBf16[cfg].bm : kCfgF32[cfg].bm;
-    const int rows = (int)((T + bm - 1) / bm);
-    TPMLP_TRY(launch("colsum", "colsum_reduce_kernel", colsum_reduce_kernel, dim3((unsigned)((Fs + 63) / 64)),
-                     dim3(64), s, (const float*)cs, rows, (int)Fs, db1_shard));
-  }
-  // dW2_i = A_i^T dZ and dW1_i = X^T dH_i: one paired launch when together
-  // they fill the chip once, else one launch each.
-  GemmArgs w2 = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
-  w2.C = dW2_shard;
-  w2.ldc = h;
-  GemmArgs w1 = gemm_args(X, h, dH, Fs, h, Fs, T);
-  w1.C = dW1_shard;
-  w1.ldc = Fs;
-  bool paired = false;
-  TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
-  if (!paired) {
-    float* slices = reinterpret_cast<float*>(ws + L.split_off);
-    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad2", "wgrad_split_sum", dtype, w2, slices, s));
-    TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad1", "wgrad_split_sum", dtype, w1, slices, s));
-  }
-  // dX_i = dH_i W1_i^T
-  a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
-  a.C = dX_partial;
-  a.ldc = h;
-  return run_gemm<true, true, kEpiF32>("gemm.mlp_dgrad1", dtype, a, s);
+  return mlp_bwd_launch((hipStream_t)stream, dtype, T, h, Fs, X, W1_shard, ldw1, W2_shard, H_save, A_save, dZ,
+                        dX_partial, dW1_shard, db1_shard, dW2_shard, workspace);
 }
+
+int tp_mlp_bwd_noalloc(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_size, const void* X,
+                       const void* W1_shard, int64_t ldw1, const void* W2_shard, const void* H_save,
+                       const void* A_save, const void* dZ, float* dX_partial, float* dW1_shard, float* db1_shard,
+                       float* dW2_shard) {
+  TPMLP_TRY(check_mlp_bwd_args(dtype, T, h, F, tp_size, X, W1_shard, ldw1, W2_shard, H_save, A_save, dZ, dX_partial,
+                               dW1_shard, db1_shard, dW2_shard));
+  const int64_t Fs = F / tp_size;
+  const BwdLayout L = bwd_layout(dtype, T, h, Fs);
+  if (L.total > kNoAllocScratchBytes)
+    return fail(TPMLP_E_WORKSPACE, "tp_mlp_bwd_noalloc: these sizes need %zu bytes of scratch, above the %zu-byte "
+                "static scratch array (use tp_mlp_bwd with a caller workspace)", L.total, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  TPMLP_TRY(noalloc_scratch(&ws));
+  return mlp_bwd_launch((hipStream_t)stream, dtype, T, h, Fs, X, W1_shard, ldw1, W2_shard, H_save, A_save, dZ,
+                        dX_partial, dW1_shard, db1_shard, dW2_shard, ws);
+}
+
+size_t tpmlp_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int column_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, int tp_size, const void* X,
                         int64_t ldx, const void* W_shard, int64_t ldw, const void* dY, int64_t lddy,
