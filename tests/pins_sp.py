@@ -162,5 +162,32 @@ def pin_sp_backward_autograd(sp):
     _close(dbet, gb.numpy(), 1e-11, "SP dbeta (sum over ranks)")
 
 
+def pin_sp_forward_torch(sp):
+    """Forward values against torch (float64, independent of the oracle): the
+    block out = X + Dropout(GeLU_tanh(LayerNorm(X) W1 + b1) W2) with the same
+    keep mask, compared with sp_block_fwd on the whole sequence and with the
+    per-rank reduce-scatter end (partial_sum_dropout_residual over each rank's
+    rows of the TP partials).  The two oracle paths share their formula for
+    the dropout and the residual, so this is the pin that fixes it: dropout
+    applies to the MLP output only, kept values scaled by 1/(1-p), the
+    residual added unscaled (zouht 2.2.2, Dropout and the residual add)."""
+    T, h, F, tp, p, seed = 24, 16, 48, 3, 0.25, 9
+    X, g, b, W1, b1, W2, _ = _mlp_case(8, T, h, F)
+    keep = sp.dropout_keep(seed, 0, T, h, p)
+    t = [torch.tensor(m, dtype=torch.float64) for m in (X, g, b, W1, b1, W2)]
+    Yln = torch.nn.functional.layer_norm(t[0], (h,), t[1], t[2], eps=1e-5)
+    Z = torch.nn.functional.gelu(Yln @ t[3] + t[4], approximate="tanh") @ t[5]
+    out = (t[0] + torch.where(torch.tensor(keep), Z / (1.0 - float(np.float32(p))), torch.zeros_like(Z))).numpy()
+    whole = sp.sp_block_fwd(X, g, b, lambda Yf: ref.mlp_fwd(Yf, W1, b1, W2)["Z"], p, seed)
+    _close(whole["out"], out, 1e-12, "SP block forward vs torch")
+    rows = T // tp
+    parts = [ref.tp_mlp_fwd_shard(Yln.numpy(), W1, b1, W2, tp, j)["Z"] for j in range(tp)]
+    for i in range(tp):
+        r = slice(i * rows, (i + 1) * rows)
+        got = sp.partial_sum_dropout_residual([P[r] for P in parts], X[r], p, seed, i * rows)
+        _close(got, out[r], 1e-12, f"SP reduce-scatter end, rank {i}, vs torch")
+
+
 ALL_PINS = [pin_philox_known_answers, pin_dropout_rate_and_split, pin_layernorm_vs_torch, pin_layernorm_closed_forms,
-            pin_layernorm_brute_and_differences, pin_sp_split_equals_whole, pin_sp_backward_autograd]
+            pin_layernorm_brute_and_differences, pin_sp_split_equals_whole, pin_sp_backward_autograd,
+            pin_sp_forward_torch]

@@ -22,6 +22,19 @@ MUTATIONS = {
     "ln_dgamma_wrong": ("\"dgamma\": (dY * xh).sum(axis=0)", "\"dgamma\": dY.sum(axis=0)"),
     "residual_dropped": ("return np.asarray(residual, dtype=np.float64) + np.where(keep, z * dropout_scale(p), 0.0)",
                          "return np.where(keep, z * dropout_scale(p), 0.0)"),
+    # The same mistake made in both oracle paths (the reduce-scatter end and
+    # the whole-sequence block), which pin each other: only the torch forward
+    # pin can catch these.
+    "dropout_after_residual_both": [
+        ("return np.asarray(residual, dtype=np.float64) + np.where(keep, z * dropout_scale(p), 0.0)",
+         "return np.where(keep, (np.asarray(residual, dtype=np.float64) + z) * dropout_scale(p), 0.0)"),
+        ('"out": np.asarray(X, dtype=np.float64) + np.where(keep, Z * dropout_scale(p), 0.0)',
+         '"out": np.where(keep, (np.asarray(X, dtype=np.float64) + Z) * dropout_scale(p), 0.0)')],
+    "residual_scaled_both": [
+        ("return np.asarray(residual, dtype=np.float64) + np.where(keep, z * dropout_scale(p), 0.0)",
+         "return np.asarray(residual, dtype=np.float64) * dropout_scale(p) + np.where(keep, z * dropout_scale(p), 0.0)"),
+        ('"out": np.asarray(X, dtype=np.float64) + np.where(keep, Z * dropout_scale(p), 0.0)',
+         '"out": np.asarray(X, dtype=np.float64) * dropout_scale(p) + np.where(keep, Z * dropout_scale(p), 0.0)')],
 }
 
 
@@ -30,17 +43,20 @@ def test_pin(pin):
     pin(sp)
 
 
-def _mutant(name, old, new):
+def _mutant(name, edits):
+    """The oracle with each (old, new) edit applied once; edits may be one pair or a list of pairs."""
     src = inspect.getsource(sp)
-    assert src.count(old) >= 1, f"mutation {name} does not apply"
+    for old, new in ([edits] if isinstance(edits, tuple) else edits):
+        assert src.count(old) >= 1, f"mutation {name} does not apply"
+        src = src.replace(old, new, 1)
     mod = types.ModuleType(f"sp_mutant_{name}")
-    exec(compile(src.replace(old, new, 1), f"<mutant {name}>", "exec"), mod.__dict__)
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
     return mod
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_a_pin_catches(name):
-    mod = _mutant(name, *MUTATIONS[name])
+    mod = _mutant(name, MUTATIONS[name])
     caught = []
     for pin in pins_sp.ALL_PINS:
         try:
@@ -48,3 +64,14 @@ def test_a_pin_catches(name):
         except Exception:  # noqa: BLE001 - any failure counts as caught
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", ["dropout_after_residual_both", "residual_scaled_both"])
+def test_consistent_mistakes_need_the_torch_forward_pin(name):
+    """Without pin_sp_forward_torch these two-place mistakes pass every other pin."""
+    mod = _mutant(name, MUTATIONS[name])
+    others = [p for p in pins_sp.ALL_PINS if p is not pins_sp.pin_sp_forward_torch]
+    for pin in others:
+        pin(mod)
+    with pytest.raises(AssertionError):
+        pins_sp.pin_sp_forward_torch(mod)
