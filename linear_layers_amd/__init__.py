@@ -170,11 +170,76 @@ def _require_contiguous(name: str, t: Optional[torch.Tensor]) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+_STORAGE = (torch.bfloat16, torch.float32)
+_F32T, _BF16T, _U8T = torch.float32, torch.bfloat16, torch.uint8
+
+
+def _dims(name: str, t, n: int) -> tuple:
+    """Shape of a tensor argument that must have n dimensions."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != n:
+        raise ValueError(f"{name} must be {n}-D, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _args(*specs) -> None:
+    """Check tensor arguments before any library call (the library cannot see
+    buffer sizes, so a short or mistyped buffer would be read or written past
+    its end on the device).
+
+    Each spec is (name, tensor, shape, dtypes, optional): the exact shape, the
+    allowed dtype(s), and whether None is allowed.  A non-tensor or a wrong
+    dtype raises TypeError; a wrong shape, a tensor not on a CUDA (HIP)
+    device, or tensors on different devices raise ValueError.  Shapes and
+    dtypes are checked for every argument before devices.
+    """
+    present = []
+    for name, t, shape, dtypes, optional in specs:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+        dts = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+        if t.dtype not in dts:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+        present.append((name, t))
+    dev = None
+    for name, t in present:
+        if not t.is_cuda:
+            raise ValueError(f"{name} is on {t.device}; libtpmlp takes device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _storage(name: str, t) -> torch.dtype:
+    """The storage dtype of the call, taken from its first input."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in _STORAGE:
+        raise TypeError(f"unsupported dtype {t.dtype}; libtpmlp takes bfloat16 or float32")
+    return t.dtype
+
+
+def _ws(name: str, t) -> tuple:
+    """Spec of a workspace argument: a 1-D uint8 device buffer of any length."""
+    return (name, t, (t.numel(),) if isinstance(t, torch.Tensor) else (0,), _U8T, False)
+
+
 def column_parallel_fwd(X, W_shard, tp_size: int, Y_shard, bias_shard=None, H_save=None,
                         act="gelu_tanh", stream=None) -> None:
     """Y_shard = Act(X @ W_shard + bias_shard); optionally H_save = X @ W_shard + bias_shard."""
-    T, K = X.shape
-    Ns = W_shard.shape[1]
+    T, K = _dims("X", X, 2)
+    Ns = _dims("W_shard", W_shard, 2)[1]
+    dt = _storage("X", X)
+    _args(("X", X, (T, K), dt, False), ("W_shard", W_shard, (K, Ns), dt, False), ("Y_shard", Y_shard, (T, Ns), dt, False),
+          ("bias_shard", bias_shard, (Ns,), dt, True), ("H_save", H_save, (T, Ns), dt, True))
     _check(_get_lib().column_parallel_fwd(_stream(stream, X), _dtype(X), _ACTS[act], T, K, Ns * tp_size, tp_size,
                                    _ptr(X), _ld(X, K), _ptr(W_shard), _ld(W_shard, Ns), _ptr(bias_shard),
                                    _ptr(Y_shard), _ld(Y_shard, Ns), _ptr(H_save), _ld(H_save, Ns)))
@@ -182,8 +247,11 @@ def column_parallel_fwd(X, W_shard, tp_size: int, Y_shard, bias_shard=None, H_sa
 
 def row_parallel_fwd(X_shard, W_shard, tp_size: int, Z_partial, stream=None) -> None:
     """Z_partial (fp32) = X_shard @ W_shard."""
-    T, Ks = X_shard.shape
-    N = W_shard.shape[1]
+    T, Ks = _dims("X_shard", X_shard, 2)
+    N = _dims("W_shard", W_shard, 2)[1]
+    dt = _storage("X_shard", X_shard)
+    _args(("X_shard", X_shard, (T, Ks), dt, False), ("W_shard", W_shard, (Ks, N), dt, False),
+          ("Z_partial", Z_partial, (T, N), _F32T, False))
     _check(_get_lib().row_parallel_fwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
                                 _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N),
                                 _ptr(Z_partial), _ld(Z_partial, N)))
@@ -195,9 +263,12 @@ def shard_partial_sum(partials, out, tp_size: Optional[int] = None, stream=None)
     ``partials`` is a [tp, T, N] tensor (or a view with any shard stride and
     row stride); ``out`` is [T, N].
     """
-    tp = partials.shape[0] if tp_size is None else tp_size
-    T, N = partials.shape[1], partials.shape[2]
-    if partials.dim() != 3 or (T > 1 and N > 1 and partials.stride(2) != 1):
+    P, T, N = _dims("partials", partials, 3)
+    tp = P if tp_size is None else tp_size
+    if not 1 <= tp <= P:
+        raise ValueError(f"tp_size {tp} outside [1, {P}] (partials holds {P} shards)")
+    _args(("partials", partials, (P, T, N), _F32T, False), ("out", out, (T, N), _F32T, False))
+    if T > 1 and N > 1 and partials.stride(2) != 1:
         raise ValueError("partials must be [tp, T, N] with contiguous rows")
     _check(_get_lib().shard_partial_sum(_stream(stream, out), tp, T, N, _ptr(partials), partials.stride(0),
                                  partials.stride(1) if T > 1 else N, _ptr(out), _ld(out, N)))
@@ -206,13 +277,27 @@ def shard_partial_sum(partials, out, tp_size: Optional[int] = None, stream=None)
 def tp_mlp_fwd(X, W1_shard, b1_shard, W2_shard, tp_size: int, A_save, Z_partial, H_save=None,
                stream=None) -> None:
     """One shard of Z = GeLU(X W1 + b1) W2: writes A_save, H_save (optional) and Z_partial."""
-    T, h = X.shape
-    Fs = W1_shard.shape[1]
+    T, h = _dims("X", X, 2)
+    Fs = _dims("W1_shard", W1_shard, 2)[1]
+    dt = _storage("X", X)
+    _args(("X", X, (T, h), dt, False), ("W1_shard", W1_shard, (h, Fs), dt, False), ("b1_shard", b1_shard, (Fs,), dt, True),
+          ("W2_shard", W2_shard, (Fs, h), dt, False), ("A_save", A_save, (T, Fs), dt, False),
+          ("Z_partial", Z_partial, (T, h), _F32T, False), ("H_save", H_save, (T, Fs), dt, True))
     for n, t in (("X", X), ("W2_shard", W2_shard), ("A_save", A_save), ("Z_partial", Z_partial), ("H_save", H_save)):
         _require_contiguous(n, t)
     _check(_get_lib().tp_mlp_fwd(_stream(stream, X), _dtype(X), T, h, Fs * tp_size, tp_size, _ptr(X), _ptr(W1_shard),
                           _ld(W1_shard, Fs), _ptr(b1_shard), _ptr(W2_shard), _ptr(H_save), _ptr(A_save),
                           _ptr(Z_partial)))
+
+
+def _mlp_bwd_args(X, W1_shard, W2_shard, H_save, A_save, dZ, dX_partial, dW1_shard, dW2_shard, db1_shard, T, h, Fs,
+                  *extra):
+    dt = _storage("X", X)
+    _args(*extra, ("X", X, (T, h), dt, False), ("W1_shard", W1_shard, (h, Fs), dt, False),
+          ("W2_shard", W2_shard, (Fs, h), dt, False), ("H_save", H_save, (T, Fs), dt, False),
+          ("A_save", A_save, (T, Fs), dt, False), ("dZ", dZ, (T, h), dt, False),
+          ("dX_partial", dX_partial, (T, h), _F32T, False), ("dW1_shard", dW1_shard, (h, Fs), _F32T, False),
+          ("dW2_shard", dW2_shard, (Fs, h), _F32T, False), ("db1_shard", db1_shard, (Fs,), _F32T, True))
 
 
 def tpmlp_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: int) -> int:
@@ -222,9 +307,11 @@ def tpmlp_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: int) 
 def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_partial, dW1_shard, dW2_shard,
                db1_shard=None, workspace=None, stream=None) -> None:
     """One shard's backward; workspace is a device uint8 tensor (allocated here if None)."""
-    T, h = X.shape
-    Fs = W1_shard.shape[1]
+    T, h = _dims("X", X, 2)
+    Fs = _dims("W1_shard", W1_shard, 2)[1]
     F = Fs * tp_size
+    _mlp_bwd_args(X, W1_shard, W2_shard, H_save, A_save, dZ, dX_partial, dW1_shard, dW2_shard, db1_shard, T, h, Fs,
+                  *([] if workspace is None else [_ws("workspace", workspace)]))
     for n, t in (("X", X), ("W2_shard", W2_shard), ("H_save", H_save), ("A_save", A_save), ("dZ", dZ),
                  ("dX_partial", dX_partial), ("dW1_shard", dW1_shard), ("dW2_shard", dW2_shard)):
         _require_contiguous(n, t)
@@ -240,9 +327,10 @@ def tp_mlp_bwd(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_parti
 def tp_mlp_bwd_noalloc(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, dX_partial, dW1_shard, dW2_shard,
                        db1_shard=None, stream=None) -> None:
     """tp_mlp_bwd with its workspace in the library's static device scratch array (no allocation)."""
-    T, h = X.shape
-    Fs = W1_shard.shape[1]
+    T, h = _dims("X", X, 2)
+    Fs = _dims("W1_shard", W1_shard, 2)[1]
     F = Fs * tp_size
+    _mlp_bwd_args(X, W1_shard, W2_shard, H_save, A_save, dZ, dX_partial, dW1_shard, dW2_shard, db1_shard, T, h, Fs)
     for n, t in (("X", X), ("W2_shard", W2_shard), ("H_save", H_save), ("A_save", A_save), ("dZ", dZ),
                  ("dX_partial", dX_partial), ("dW1_shard", dW1_shard), ("dW2_shard", dW2_shard)):
         _require_contiguous(n, t)
@@ -257,8 +345,12 @@ def tpmlp_noalloc_scratch_bytes() -> int:
 
 def column_parallel_bwd(X, W_shard, dY, tp_size: int, dX_partial, dW_shard, db_shard=None, stream=None) -> None:
     """dX_partial = dY W_shard^T, dW_shard = X^T dY, db_shard = column sums of dY (fp32 outputs)."""
-    T, K = X.shape
-    Ns = W_shard.shape[1]
+    T, K = _dims("X", X, 2)
+    Ns = _dims("W_shard", W_shard, 2)[1]
+    dt = _storage("X", X)
+    _args(("X", X, (T, K), dt, False), ("W_shard", W_shard, (K, Ns), dt, False), ("dY", dY, (T, Ns), dt, False),
+          ("dX_partial", dX_partial, (T, K), _F32T, False), ("dW_shard", dW_shard, (K, Ns), _F32T, False),
+          ("db_shard", db_shard, (Ns,), _F32T, True))
     _check(_get_lib().column_parallel_bwd(_stream(stream, X), _dtype(X), T, K, Ns * tp_size, tp_size, _ptr(X), _ld(X, K),
                                    _ptr(W_shard), _ld(W_shard, Ns), _ptr(dY), _ld(dY, Ns), _ptr(dX_partial),
                                    _ld(dX_partial, K), _ptr(dW_shard), _ld(dW_shard, Ns), _ptr(db_shard)))
@@ -266,8 +358,12 @@ def column_parallel_bwd(X, W_shard, dY, tp_size: int, dX_partial, dW_shard, db_s
 
 def row_parallel_bwd(X_shard, W_shard, dY, tp_size: int, dX_shard, dW_shard, stream=None) -> None:
     """dX_shard = dY W_shard^T, dW_shard = X_shard^T dY (fp32 outputs)."""
-    T, Ks = X_shard.shape
-    N = W_shard.shape[1]
+    T, Ks = _dims("X_shard", X_shard, 2)
+    N = _dims("W_shard", W_shard, 2)[1]
+    dt = _storage("X_shard", X_shard)
+    _args(("X_shard", X_shard, (T, Ks), dt, False), ("W_shard", W_shard, (Ks, N), dt, False),
+          ("dY", dY, (T, N), dt, False), ("dX_shard", dX_shard, (T, Ks), _F32T, False),
+          ("dW_shard", dW_shard, (Ks, N), _F32T, False))
     _check(_get_lib().row_parallel_bwd(_stream(stream, X_shard), _dtype(X_shard), T, Ks * tp_size, N, tp_size,
                                 _ptr(X_shard), _ld(X_shard, Ks), _ptr(W_shard), _ld(W_shard, N), _ptr(dY),
                                 _ld(dY, N), _ptr(dX_shard), _ld(dX_shard, Ks), _ptr(dW_shard), _ld(dW_shard, N)))
@@ -275,7 +371,12 @@ def row_parallel_bwd(X_shard, W_shard, dY, tp_size: int, dX_shard, dW_shard, str
 
 def swiglu_pack_shard(W_gate, W_up, tp_size: int, shard: int, W_gu_shard, stream=None) -> None:
     """W_gu_shard [h, 2F/tp] = shard `shard` of [W_gate | W_up], interleaved in groups of 8 columns."""
-    h, F = W_gate.shape
+    h, F = _dims("W_gate", W_gate, 2)
+    dt = _storage("W_gate", W_gate)
+    if tp_size < 1 or F % tp_size:
+        raise ValueError(f"F = {F} is not divisible by tp_size {tp_size}")
+    _args(("W_gate", W_gate, (h, F), dt, False), ("W_up", W_up, (h, F), dt, False),
+          ("W_gu_shard", W_gu_shard, (h, 2 * (F // tp_size)), dt, False))
     _require_contiguous("W_gu_shard", W_gu_shard)
     _check(_get_lib().swiglu_pack_shard(_stream(stream, W_gate), _dtype(W_gate), h, F, tp_size, shard,
                                         _ptr(W_gate), _ld(W_gate, F), _ptr(W_up), _ld(W_up, F), _ptr(W_gu_shard)))
@@ -283,7 +384,11 @@ def swiglu_pack_shard(W_gate, W_up, tp_size: int, shard: int, W_gu_shard, stream
 
 def swiglu_unpack_grad(dW_gu_shard, tp_size: int, shard: int, dW_gate, dW_up, stream=None) -> None:
     """Columns of shard `shard` of dW_gate and dW_up [h, F] (fp32) from the packed dW_gu_shard."""
-    h, F = dW_gate.shape
+    h, F = _dims("dW_gate", dW_gate, 2)
+    if tp_size < 1 or F % tp_size:
+        raise ValueError(f"F = {F} is not divisible by tp_size {tp_size}")
+    _args(("dW_gu_shard", dW_gu_shard, (h, 2 * (F // tp_size)), _F32T, False), ("dW_gate", dW_gate, (h, F), _F32T, False),
+          ("dW_up", dW_up, (h, F), _F32T, False))
     _require_contiguous("dW_gu_shard", dW_gu_shard)
     _check(_get_lib().swiglu_unpack_grad(_stream(stream, dW_gu_shard), h, F, tp_size, shard, _ptr(dW_gu_shard),
                                          _ptr(dW_gate), _ld(dW_gate, F), _ptr(dW_up), _ld(dW_up, F)))
@@ -291,8 +396,12 @@ def swiglu_unpack_grad(dW_gu_shard, tp_size: int, shard: int, dW_gate, dW_up, st
 
 def tp_swiglu_fwd(X, W_gu_shard, W_down_shard, tp_size: int, A_save, Z_partial, GU_save=None, stream=None) -> None:
     """One shard of down = (silu(X W_gate) * (X W_up)) W_down: writes A_save, GU_save (optional), Z_partial."""
-    T, h = X.shape
-    Fs = W_down_shard.shape[0]
+    T, h = _dims("X", X, 2)
+    Fs = _dims("W_down_shard", W_down_shard, 2)[0]
+    dt = _storage("X", X)   # the library itself refuses fp32 storage for the gated MLP
+    _args(("X", X, (T, h), dt, False), ("W_gu_shard", W_gu_shard, (h, 2 * Fs), dt, False),
+          ("W_down_shard", W_down_shard, (Fs, h), dt, False), ("A_save", A_save, (T, Fs), dt, False),
+          ("Z_partial", Z_partial, (T, h), _F32T, False), ("GU_save", GU_save, (T, 2 * Fs), dt, True))
     for n, t in (("X", X), ("W_gu_shard", W_gu_shard), ("W_down_shard", W_down_shard), ("A_save", A_save),
                  ("Z_partial", Z_partial), ("GU_save", GU_save)):
         _require_contiguous(n, t)
@@ -308,9 +417,16 @@ def tp_swiglu_bwd_workspace_bytes(dtype: int, T: int, h: int, F: int, tp_size: i
 def tp_swiglu_bwd(X, W_gu_shard, W_down_shard, GU_save, A_save, dZ, tp_size: int, dX_partial, dW_gu_shard,
                   dW_down_shard, workspace=None, stream=None) -> None:
     """One shard's backward of the gated MLP; workspace is a device uint8 tensor (allocated here if None)."""
-    T, h = X.shape
-    Fs = W_down_shard.shape[0]
+    T, h = _dims("X", X, 2)
+    Fs = _dims("W_down_shard", W_down_shard, 2)[0]
     F = Fs * tp_size
+    dt = _storage("X", X)
+    _args(("X", X, (T, h), dt, False), ("W_gu_shard", W_gu_shard, (h, 2 * Fs), dt, False),
+          ("W_down_shard", W_down_shard, (Fs, h), dt, False), ("GU_save", GU_save, (T, 2 * Fs), dt, False),
+          ("A_save", A_save, (T, Fs), dt, False), ("dZ", dZ, (T, h), dt, False),
+          ("dX_partial", dX_partial, (T, h), _F32T, False), ("dW_gu_shard", dW_gu_shard, (h, 2 * Fs), _F32T, False),
+          ("dW_down_shard", dW_down_shard, (Fs, h), _F32T, False),
+          *([] if workspace is None else [_ws("workspace", workspace)]))
     for n, t in (("X", X), ("W_gu_shard", W_gu_shard), ("W_down_shard", W_down_shard), ("GU_save", GU_save),
                  ("A_save", A_save), ("dZ", dZ), ("dX_partial", dX_partial), ("dW_gu_shard", dW_gu_shard),
                  ("dW_down_shard", dW_down_shard)):
@@ -326,14 +442,21 @@ def tp_swiglu_bwd(X, W_gu_shard, W_down_shard, GU_save, A_save, dZ, tp_size: int
 
 def layernorm_fwd(X, gamma, beta, Y, mean, rstd, eps: float = 1e-5, stream=None) -> None:
     """Y = LayerNorm(X) per row (bf16 in/out, fp32 gamma/beta/statistics).  Y may be a row block of a larger buffer."""
-    rows, h = X.shape
+    rows, h = _dims("X", X, 2)
+    _args(("X", X, (rows, h), _BF16T, False), ("gamma", gamma, (h,), _F32T, False), ("beta", beta, (h,), _F32T, False),
+          ("Y", Y, (rows, h), _BF16T, False), ("mean", mean, (rows,), _F32T, False),
+          ("rstd", rstd, (rows,), _F32T, False))
     _check(_get_lib().layernorm_fwd(_stream(stream, X), rows, h, _ptr(X), _ld(X, h), _ptr(gamma), _ptr(beta), eps,
                                     _ptr(Y), _ld(Y, h), _ptr(mean), _ptr(rstd)))
 
 
 def layernorm_bwd(X, gamma, mean, rstd, dY, dX, dgamma=None, dbeta=None, dRes=None, stream=None) -> None:
     """dX (fp32) from dY (fp32), plus dRes (bf16) if given; dgamma/dbeta = this block's sums (fp32)."""
-    rows, h = X.shape
+    rows, h = _dims("X", X, 2)
+    _args(("X", X, (rows, h), _BF16T, False), ("gamma", gamma, (h,), _F32T, False), ("mean", mean, (rows,), _F32T, False),
+          ("rstd", rstd, (rows,), _F32T, False), ("dY", dY, (rows, h), _F32T, False), ("dX", dX, (rows, h), _F32T, False),
+          ("dgamma", dgamma, (h,), _F32T, True), ("dbeta", dbeta, (h,), _F32T, True),
+          ("dRes", dRes, (rows, h), _BF16T, True))
     _check(_get_lib().layernorm_bwd(_stream(stream, X), rows, h, _ptr(X), _ld(X, h), _ptr(gamma), _ptr(mean),
                                     _ptr(rstd), _ptr(dY), _ld(dY, h), _ptr(dRes), _ld(dRes, h), _ptr(dX), _ld(dX, h),
                                     _ptr(dgamma), _ptr(dbeta)))
@@ -342,9 +465,13 @@ def layernorm_bwd(X, gamma, mean, rstd, dY, dX, dgamma=None, dbeta=None, dRes=No
 def sp_partial_sum_dropout_residual(partials, residual, out, p: float, seed: int, row0: int,
                                     tp_size: Optional[int] = None, stream=None) -> None:
     """out = residual + Dropout(sum of partials[s]) over this GPU's rows (partials: [tp, rows, h] view, fp32)."""
-    tp = partials.shape[0] if tp_size is None else tp_size
-    rows, h = partials.shape[1], partials.shape[2]
-    if partials.dim() != 3 or (rows > 1 and h > 1 and partials.stride(2) != 1):
+    P, rows, h = _dims("partials", partials, 3)
+    tp = P if tp_size is None else tp_size
+    if not 1 <= tp <= P:
+        raise ValueError(f"tp_size {tp} outside [1, {P}] (partials holds {P} shards)")
+    _args(("partials", partials, (P, rows, h), _F32T, False), ("residual", residual, (rows, h), _BF16T, False),
+          ("out", out, (rows, h), _BF16T, False))
+    if rows > 1 and h > 1 and partials.stride(2) != 1:
         raise ValueError("partials must be [tp, rows, h] with contiguous rows")
     _check(_get_lib().sp_partial_sum_dropout_residual(_stream(stream, out), tp, rows, h, _ptr(partials),
                                                       partials.stride(0), partials.stride(1) if rows > 1 else h,
@@ -354,7 +481,8 @@ def sp_partial_sum_dropout_residual(partials, residual, out, p: float, seed: int
 
 def sp_dropout_bwd(dOut, dZ, p: float, seed: int, row0: int, stream=None) -> None:
     """dZ = Dropout'(dOut) for this GPU's rows (bf16); dZ may be a row block of the gathered gradient."""
-    rows, h = dOut.shape
+    rows, h = _dims("dOut", dOut, 2)
+    _args(("dOut", dOut, (rows, h), _BF16T, False), ("dZ", dZ, (rows, h), _BF16T, False))
     _check(_get_lib().sp_dropout_bwd(_stream(stream, dOut), rows, h, _ptr(dOut), _ld(dOut, h), p, seed, row0,
                                      _ptr(dZ), _ld(dZ, h)))
 
@@ -368,7 +496,11 @@ def attn_fwd(Q, K, V, O, batch: int, seq: int, heads: int, causal: bool = True, 
     """O = softmax(Q K^T * scale) V per head (bf16; head h in columns [128h, 128h+128)); lse [heads, T] fp32;
     workspace a device uint8 tensor (allocated here if None and needed)."""
     w = heads * head_dim
+    T = batch * seq
     sc = head_dim ** -0.5 if scale is None else scale
+    _args(("Q", Q, (T, w), _BF16T, False), ("K", K, (T, w), _BF16T, False), ("V", V, (T, w), _BF16T, False),
+          ("O", O, (T, w), _BF16T, False), ("lse", lse, (heads, T), _F32T, True),
+          *([] if workspace is None else [_ws("workspace", workspace)]))
     if workspace is None and causal:
         n = attn_fwd_workspace_bytes(batch, seq, heads)
         if n > 0:
@@ -386,7 +518,11 @@ def attn_bwd(Q, K, V, O, dO, lse, dQ, dK, dV, batch: int, seq: int, heads: int, 
              scale: Optional[float] = None, workspace=None, head_dim: int = 128, stream=None) -> None:
     """dQ, dK, dV (bf16) of attn_fwd for upstream dO; workspace a device uint8 tensor (allocated here if None)."""
     w = heads * head_dim
+    T = batch * seq
     sc = head_dim ** -0.5 if scale is None else scale
+    _args(*[(n, t, (T, w), _BF16T, False) for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO), ("dQ", dQ),
+                                                         ("dK", dK), ("dV", dV))],
+          ("lse", lse, (heads, T), _F32T, False), *([] if workspace is None else [_ws("workspace", workspace)]))
     if workspace is None:
         workspace = torch.empty(max(1, attn_bwd_workspace_bytes(batch, seq, heads)), dtype=torch.uint8,
                                 device=Q.device)
@@ -405,7 +541,17 @@ def tp_attn_fwd(X, Wqkv_shard, Wo_shard, QKV_save, O_save, lse, Z_partial, batch
                 head_dim: int = 128, stream=None) -> None:
     """One shard of the head-sharded attention block (contiguous tensors; heads = all heads of the layer);
     workspace a device uint8 tensor (allocated here if None and needed)."""
-    h = X.shape[1]
+    T, h = _dims("X", X, 2)
+    if tp_size < 1 or heads % tp_size:
+        raise ValueError(f"heads = {heads} is not divisible by tp_size {tp_size}")
+    hs = heads // tp_size
+    w = hs * head_dim
+    if T != batch * seq:
+        raise ValueError(f"X has {T} rows, expected batch * seq = {batch * seq}")
+    _args(("X", X, (T, h), _BF16T, False), ("Wqkv_shard", Wqkv_shard, (h, 3 * w), _BF16T, False),
+          ("Wo_shard", Wo_shard, (w, h), _BF16T, False), ("QKV_save", QKV_save, (T, 3 * w), _BF16T, False),
+          ("O_save", O_save, (T, w), _BF16T, False), ("lse", lse, (hs, T), _F32T, False),
+          ("Z_partial", Z_partial, (T, h), _F32T, False), *([] if workspace is None else [_ws("workspace", workspace)]))
     sc = head_dim ** -0.5 if scale is None else scale
     for n, t in (("X", X), ("Wqkv_shard", Wqkv_shard), ("Wo_shard", Wo_shard), ("QKV_save", QKV_save),
                  ("O_save", O_save), ("lse", lse), ("Z_partial", Z_partial)):
@@ -427,7 +573,19 @@ def tp_attn_bwd(X, Wqkv_shard, Wo_shard, QKV_save, O_save, lse, dZ, dX_partial, 
                 batch: int, seq: int, heads: int, tp_size: int, causal: bool = True, scale: Optional[float] = None,
                 workspace=None, head_dim: int = 128, stream=None) -> None:
     """Backward of tp_attn_fwd for dZ; workspace a device uint8 tensor (allocated here if None)."""
-    h = X.shape[1]
+    T, h = _dims("X", X, 2)
+    if tp_size < 1 or heads % tp_size:
+        raise ValueError(f"heads = {heads} is not divisible by tp_size {tp_size}")
+    hs = heads // tp_size
+    w = hs * head_dim
+    if T != batch * seq:
+        raise ValueError(f"X has {T} rows, expected batch * seq = {batch * seq}")
+    _args(("X", X, (T, h), _BF16T, False), ("Wqkv_shard", Wqkv_shard, (h, 3 * w), _BF16T, False),
+          ("Wo_shard", Wo_shard, (w, h), _BF16T, False), ("QKV_save", QKV_save, (T, 3 * w), _BF16T, False),
+          ("O_save", O_save, (T, w), _BF16T, False), ("lse", lse, (hs, T), _F32T, False),
+          ("dZ", dZ, (T, h), _BF16T, False), ("dX_partial", dX_partial, (T, h), _F32T, False),
+          ("dWqkv_shard", dWqkv_shard, (h, 3 * w), _F32T, False), ("dWo_shard", dWo_shard, (w, h), _F32T, False),
+          *([] if workspace is None else [_ws("workspace", workspace)]))
     sc = head_dim ** -0.5 if scale is None else scale
     for n, t in (("X", X), ("Wqkv_shard", Wqkv_shard), ("Wo_shard", Wo_shard), ("QKV_save", QKV_save),
                  ("O_save", O_save), ("lse", lse), ("dZ", dZ), ("dX_partial", dX_partial),
