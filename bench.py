@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 2.4 GHz)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_SCLK_GHZ = 2.4         # the engine clock that peak assumes
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
@@ -47,14 +48,22 @@ PROFILES = os.path.join(ROOT, "profiles")
 def traffic_path(workload: str) -> str:
     return os.path.join(PROFILES, f"{workload}_traffic.json")
 
+
+def mfma_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_mfma.json")
+
+XCDS = 8                    # MI355X: 8 accelerator dies, GRBM_GUI_ACTIVE sums their busy cycles
+COLD_FLUSH_BYTES = 512 << 20   # written between steps by the cold-cache timing
+
 CALIB_BYTES = 256 << 20     # the plain copy used to scale the HBM byte counters
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time for the baseline")
@@ -66,8 +75,10 @@ def parse():
 
 # Kernel sources that cannot affect a workload's kernels (they hold other
 # kernels only), left out of its fingerprint.
-_UNRELATED_SOURCES = {"mlp": {"attn.hpp", "sp.hpp", "swiglu.hpp"}, "swiglu": {"attn.hpp", "sp.hpp"},
-                      "sp_mlp": {"attn.hpp", "swiglu.hpp"}, "proj": {"sp.hpp", "swiglu.hpp"}}
+_UNRELATED_SOURCES = {"mlp": {"attn.hpp", "sp.hpp", "swiglu.hpp", "epilogue.hpp"},
+                      "swiglu": {"attn.hpp", "sp.hpp", "epilogue.hpp"},
+                      "sp_mlp": {"attn.hpp", "swiglu.hpp", "epilogue.hpp"},
+                      "proj": {"sp.hpp", "swiglu.hpp", "epilogue.hpp"}}
 
 
 def kernel_fingerprint(kind: str) -> str:
@@ -139,6 +150,8 @@ def step_flops(wl, T=None):
         r = proj_role_flops(wl, T)
         return sum(v for k, v in r.items() if k.startswith("gemm.")) + 7 * attn_product_flops(wl, T)
     T = wl.T if T is None else T
+    if wl.kind == "mlp" and wl.dz_std is None:      # forward only, every shard on this GPU
+        return wl.tp * 2 * 2.0 * T * wl.h * wl.Fs
     units = sum(u for k, u in ROLE_UNITS[wl.kind].items() if k != "gemm.mlp_wgrad")   # the pair is counted once
     return units * 2.0 * T * wl.h * wl.Fs
 
@@ -180,6 +193,21 @@ def _proj_bytes(wl, role):
             "attn_bwd_dq": T * 4 * w * 2 + 2 * T * hs * 4 + T * w * 2}.get(role)
 
 
+def _time_sample(run, probe, T, target_s):
+    """Rows of the sample and its oracle time: grow the row count toward
+    target_s; when the whole workload takes less than that, repeat it."""
+    dt = run(probe)
+    rows = int(min(T, max(probe, probe * target_s / max(dt, 1e-3))))
+    rows = max(probe, rows - rows % 8) if rows < T else T
+    dt, reps = run(rows), 1
+    if rows == T and dt < target_s:
+        more = min(100000, int(target_s / max(dt, 1e-6)))
+        for _ in range(more - 1):
+            dt += run(rows)
+        reps = max(more, 1)
+    return rows, reps, dt
+
+
 def cpu_baseline(wl, raw, target_s: float):
     """Time the float64 oracle (fwd + bwd of shard 0) on a sample of rows."""
     import synth
@@ -202,7 +230,26 @@ def cpu_baseline(wl, raw, target_s: float):
         W2 = synth.to_f64(raw["W2"][:Fs], wl.dtype)
         b1 = synth.to_f64(raw["b1"][:Fs], wl.dtype) if "b1" in raw else None
 
+    fwd_only = "dZ" not in raw
+
+    def run_fwd(rows):
+        # every shard's forward, then the sum of the partials (the forward-only workload's step)
+        X = synth.to_f64(raw["X"][:rows], wl.dtype)
+        t0 = time.perf_counter()
+        parts = []
+        for i in range(wl.tp):
+            W1i = synth.to_f64(raw["W1"][:, i * Fs:(i + 1) * Fs], wl.dtype)
+            W2i = synth.to_f64(raw["W2"][i * Fs:(i + 1) * Fs], wl.dtype)
+            H = ref.matmul(X, W1i)
+            if "b1" in raw:
+                H = H + synth.to_f64(raw["b1"][i * Fs:(i + 1) * Fs], wl.dtype)[None, :]
+            parts.append(ref.matmul(ref.gelu_tanh(H), W2i))
+        ref.shard_partial_sum(parts)
+        return time.perf_counter() - t0
+
     def run(rows):
+        if fwd_only:
+            return run_fwd(rows)
         X = synth.to_f64(raw["X"][:rows], wl.dtype)
         dZ = synth.to_f64(raw["dZ"][:rows], wl.dtype)
         t0 = time.perf_counter()
@@ -231,15 +278,14 @@ def cpu_baseline(wl, raw, target_s: float):
         del out
         return time.perf_counter() - t0
 
-    probe = min(wl.T, 256)
-    dt = run(probe)
-    rows = int(min(wl.T, max(probe, probe * target_s / max(dt, 1e-3))))
-    rows = max(probe, rows - rows % 8)
-    dt = run(rows)
-    flops = step_flops(wl) * rows / wl.T
+    rows, reps, dt = _time_sample(run, min(wl.T, 256), wl.T, target_s)
+    flops = step_flops(wl) * rows / wl.T * reps
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 numpy oracle, shard 0 fwd+bwd on the first {rows} of {wl.T} token rows "
-                      f"(h={wl.h}, F/tp={Fs}); {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
+            "sample": (f"float64 numpy oracle, all {wl.tp} shards' forward and their partial sum" if fwd_only else
+                       "float64 numpy oracle, shard 0 fwd+bwd") +
+                      f" on the first {rows} of {wl.T} token rows (h={wl.h}, F/tp={Fs})" +
+                      (f", {reps} repetitions" if reps > 1 else "") +
+                      f"; {dt:.2f} s for {flops / 1e9:.1f} GFLOP",
             "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
@@ -259,15 +305,12 @@ def _cpu_baseline_proj(wl, raw, target_s, threads):
                                     wl.tp, 0, True, wl.head_dim ** -0.5)
         return time.perf_counter() - t0
 
-    probe = min(wl.T, 128)
-    dt = run(probe)
-    rows = int(min(wl.T, max(probe, probe * target_s / max(dt, 1e-3))))
-    rows = max(probe, rows - rows % 8)
-    dt = run(rows)
-    flops = step_flops(wl, rows)
+    rows, reps, dt = _time_sample(run, min(wl.T, 128), wl.T, target_s)
+    flops = step_flops(wl, rows) * reps
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle, shard 0 fwd+bwd of the attention block on a causal sequence of the "
-                      f"first {rows} of {wl.T} tokens (h={wl.h}, {wl.heads // wl.tp} heads); {dt:.2f} s for "
+                      f"first {rows} of {wl.T} tokens (h={wl.h}, {wl.heads // wl.tp} heads)" +
+                      (f", {reps} repetitions" if reps > 1 else "") + f"; {dt:.2f} s for "
                       f"{flops / 1e9:.1f} GFLOP",
             "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
@@ -281,7 +324,11 @@ class Step:
         T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
         dev = torch.device("cuda:0")
 
+        f32 = wl.dtype == "f32"
+
         def up(a):
+            if f32:
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
         self.X, self.dZ = up(raw["X"]), up(raw["dZ"])
@@ -289,7 +336,7 @@ class Step:
         self.W1s = [up(np.ascontiguousarray(raw["W1"][:, i * Fs:(i + 1) * Fs])) for i in range(tp)]
         self.W2s = [up(raw["W2"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
         self.b1s = [None if "b1" not in raw else up(raw["b1"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
-        bf = torch.bfloat16
+        bf = torch.float32 if f32 else torch.bfloat16
         self.A = torch.empty((T, Fs), dtype=bf, device=dev)
         self.H = torch.empty((T, Fs), dtype=bf, device=dev)
         self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
@@ -300,7 +347,8 @@ class Step:
         self.dW1 = torch.empty((h, Fs), dtype=torch.float32, device=dev)
         self.dW2 = torch.empty((Fs, h), dtype=torch.float32, device=dev)
         self.db1 = torch.empty((Fs,), dtype=torch.float32, device=dev) if "b1" in raw else None
-        self.ws = torch.empty(tl.tpmlp_bwd_workspace_bytes(tl.BF16, T, h, F, tp), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(1, tl.tpmlp_bwd_workspace_bytes(tl.F32 if f32 else tl.BF16, T, h, F, tp)),
+                              dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream(dev)
         for i in range(1, tp):  # the other shards' partials, computed once
             self.shard(i)
@@ -330,6 +378,39 @@ class Step:
         tl.tp_mlp_bwd(s.X, s.W1s[0], s.W2s[0], s.H, s.A, s.dZ, s.wl.tp, s.dXp[0], s.dW1, s.dW2, db1_shard=s.db1,
                       workspace=s.ws, stream=s.stream)
         tl.shard_partial_sum(s.dXp[:, :s.rows], s.dXsum, stream=s.stream)
+
+
+class FwdStep:
+    """A forward-only MLP workload (the tiny fp32 one): every shard's forward
+    on this GPU in turn, then the sum of all their partials."""
+
+    def __init__(self, wl, raw, tl, torch):
+        self.wl, self.tl = wl, tl
+        T, h, tp, Fs = wl.T, wl.h, wl.tp, wl.Fs
+        dev = torch.device("cuda:0")
+        f32 = wl.dtype == "f32"
+        dt = torch.float32 if f32 else torch.bfloat16
+
+        def up(a):
+            if f32:
+                return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.X = up(raw["X"])
+        self.W1s = [up(np.ascontiguousarray(raw["W1"][:, i * Fs:(i + 1) * Fs])) for i in range(tp)]
+        self.W2s = [up(raw["W2"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        self.b1s = [None if "b1" not in raw else up(raw["b1"][i * Fs:(i + 1) * Fs]) for i in range(tp)]
+        self.A = torch.empty((T, Fs), dtype=dt, device=dev)
+        self.Zp = torch.empty((tp, T, h), dtype=torch.float32, device=dev)
+        self.Z = torch.empty((T, h), dtype=torch.float32, device=dev)
+        self.rows = T
+        self.stream = torch.cuda.current_stream(dev)
+
+    def __call__(self):
+        tl, s = self.tl, self
+        for i in range(s.wl.tp):
+            tl.tp_mlp_fwd(s.X, s.W1s[i], s.b1s[i], s.W2s[i], s.wl.tp, s.A, s.Zp[i], stream=s.stream)
+        tl.shard_partial_sum(s.Zp, s.Z, stream=s.stream)
 
 
 class SwiGLUStep:
@@ -541,10 +622,10 @@ def make_step(wl, tl, torch):
     if wl.kind == "swiglu":
         raw = synth.swiglu_inputs(wl)
         return raw, SwiGLUStep(wl, raw, tl, torch)
-    if wl.kind == "mlp" and wl.dtype == "bf16":
+    if wl.kind == "mlp":
         raw = synth.mlp_inputs(wl)
-        return raw, Step(wl, raw, tl, torch)
-    raise SystemExit(f"workload {wl.name}: the benchmark step covers the bf16 MLP and gated-MLP workloads")
+        return raw, (Step(wl, raw, tl, torch) if wl.dz_std is not None else FwdStep(wl, raw, tl, torch))
+    raise SystemExit(f"workload {wl.name}: no benchmark step")
 
 
 def step_roles(tl, step, torch):
@@ -577,6 +658,61 @@ def load_traffic(workload: str, symbol: str, role: str):
     return e["fetch_bytes"] + e["write_bytes"], "FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
 
 
+def load_mfma(workload: str, symbol: str, role: str):
+    """MFMA-busy fraction of (role, symbol) from the committed counter summary, if taken on these sources."""
+    try:
+        with open(mfma_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, "no MFMA counter table"
+    if t.get("fingerprint") != kernel_fingerprint(synth_kind(workload)):
+        return None, "kernel sources changed since the counters were taken"
+    e = t.get("launches", {}).get(role)
+    if not e or e.get("kernel") != symbol:
+        return None, "no counters for this kernel"
+    return e["mfma_busy"], ("SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / 8 XCDs): the fraction of the "
+                            "kernel's cycles the matrix cores were busy, at whatever clock it ran")
+
+
+def epilogue_ablation(wl, step, tl, torch, n):
+    """The fused bias+GeLU epilogue of the first product against the same
+    product with an fp32 output followed by the standalone epilogue pass, and
+    the standalone GeLU' pass, on shard 0 of the workload (same stream)."""
+    T, Fs = wl.T, wl.Fs
+    stream = step.stream
+    X, W1, b1, A, H = step.X, step.W1s[0], step.b1s[0], step.A, step.H
+    P = torch.empty((T, Fs), dtype=torch.float32, device=X.device)
+    dH = torch.empty_like(A)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    fused = timed(lambda: tl.column_parallel_fwd(X, W1, wl.tp, A, bias_shard=b1, H_save=H, stream=stream))
+    gemm = timed(lambda: tl.row_parallel_fwd(X, W1, 1, P, stream=stream))
+    bgf = timed(lambda: tl.bias_gelu_fwd(P, A, bias=b1, H_out=H, stream=stream))
+    gb = timed(lambda: tl.gelu_bwd(P, H, dH, stream=stream))
+    esz = A.element_size()
+    bgf_bytes = T * Fs * (4 + 2 * esz) + (Fs * esz if b1 is not None else 0)
+    gb_bytes = T * Fs * (4 + 2 * esz)
+    return {"what": f"X W1_0 ({T}x{Fs}, K={wl.h}) with the bias+GeLU epilogue fused vs an fp32 product then "
+                    "bias_gelu_fwd; gelu_bwd over the same [T, F/tp]",
+            "fused_us": round(fused, 2), "unfused_gemm_fp32_us": round(gemm, 2),
+            "bias_gelu_fwd_us": round(bgf, 2), "unfused_total_us": round(gemm + bgf, 2),
+            "fusion_saves_us": round(gemm + bgf - fused, 2),
+            "bias_gelu_fwd_gbs": round(bgf_bytes / (bgf * 1e-6) / 1e9, 1),
+            "gelu_bwd_us": round(gb, 2), "gelu_bwd_gbs": round(gb_bytes / (gb * 1e-6) / 1e9, 1),
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+            "bytes": {"bias_gelu_fwd": bgf_bytes, "gelu_bwd": gb_bytes}}
+
+
 def workload_text(wl):
     T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
     what = {"llama7b_bf16": "the Llama-7B-scale MLP", "gpt2m_bf16": "the GPT-2-medium-scale MLP",
@@ -592,6 +728,11 @@ def workload_text(wl):
                 f"{h}x{3 * hs * wl.head_dim}, flash attention, O projection {hs * wl.head_dim}x{h} into an fp32 "
                 f"partial; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums; bf16 storage, "
                 f"fp32 accumulate")
+    if wl.dz_std is None:
+        return (f"{wl.name}: all {tp} shards of the MLP in turn on this GPU, T={T} tokens, h={h}, F={F}, tp={tp} "
+                f"(F/tp={Fs}), {'fp32' if wl.dtype == 'f32' else 'bf16'} storage, fp32 accumulate; forward only "
+                f"(column-parallel GEMM with bias+GeLU, row-parallel GEMM into an fp32 partial per shard), then "
+                f"the on-device sum of the {tp} partials")
     return (f"{wl.name}: one shard of {what}, T={T} tokens, h={h}, F={F}, tp={tp} (F/tp={Fs}), bf16 storage, "
             f"fp32 accumulate; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums")
 
@@ -646,6 +787,34 @@ def run_bench(args):
 
     flops_step = step_flops(wl)
     value = flops_step / (ms_step * 1e-3) / 1e12
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+
+    # Per-step durations over as many steps again, warm and then cold: the cold
+    # pass writes a 512 MB buffer between steps (off the clock), which evicts
+    # the operands from L2 and the 256 MB Infinity Cache.
+    def per_step(n, flush=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            if flush is not None:
+                flush.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
+    warm_t = per_step(args.steps)
+    step_ms = {"mean": round(ms_step, 4), "median": round(warm_t[len(warm_t) // 2], 4), "min": round(warm_t[0], 4),
+               "steps": len(warm_t)}
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(COLD_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        cold_t = per_step(args.steps, flush)
+        del flush
+        med = cold_t[len(cold_t) // 2]
+        cold = {"median_ms": round(med, 4), "min_ms": round(cold_t[0], 4), "steps": len(cold_t),
+                "value_at_median": round(flops_step / (med * 1e-3) / 1e12, 2),
+                "flush_bytes_between_steps": COLD_FLUSH_BYTES}
 
     # The step's forward and backward calls, each timed alone (after the timed
     # region, so they do not change it): same launches, same stream.
@@ -662,7 +831,9 @@ def run_bench(args):
             pms = e0.elapsed_time(e1) / args.steps
             ptf = pflops / (pms * 1e-3) / 1e12
             parts[name] = {"us": round(pms * 1e3, 2), "tflops": round(ptf, 2),
-                           "pct_of_peak": round(100 * ptf / PEAK_BF16_TFLOPS, 2)}
+                           "pct_of_peak": round(100 * ptf / peak, 2)}
+
+    ablation = epilogue_ablation(wl, step, tl, torch, args.steps) if isinstance(step, Step) else None
 
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
@@ -674,14 +845,15 @@ def run_bench(args):
     # reported beside it, with the peak scaled to that clock.
     sclk = sum(dom_clocks) / len(dom_clocks) if dom_clocks else None
     traffic, traffic_note = load_traffic(wl.name, dom_sym, dominant)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "traffic_note": traffic_note,
+    mfma_busy, mfma_note = load_mfma(wl.name, dom_sym, dominant)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "traffic_note": traffic_note, "mfma_busy": mfma_busy, "mfma_busy_note": mfma_note,
                 "algorithmic_bytes": None, "kernel": dom_sym, "role": dominant, "launches": n_launch,
                 "mean_launch_us": round(per_launch_ms * 1e3, 2), "flop_per_launch": role_flops(wl, dominant),
                 "sclk_ghz": round(sclk, 3) if sclk else None,
-                "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ, 1) if sclk else None,
-                "frac_at_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_GHZ), 4) if sclk else None}
+                "peak_at_sclk": round(peak * sclk / PEAK_SCLK_GHZ, 1) if sclk else None,
+                "frac_at_sclk": round(achieved / (peak * sclk / PEAK_SCLK_GHZ), 4) if sclk else None}
     roofline["algorithmic_bytes"] = algorithmic_bytes(wl, dominant)
 
     kernels = {}
@@ -694,6 +866,9 @@ def run_bench(args):
             entry["tflops"] = round(role_flops(wl, role) / (us * 1e-6) / 1e12, 1)
         elif role == "partial_sum":
             entry["gbs"] = round((tp + 1) * step.rows * h * 4 / (us * 1e-6) / 1e9, 1)
+        elif role == "colsum":
+            # the per-tile column sums of dH (one row per 256-row tile) in, db1 out
+            entry["gbs"] = round((((T + 255) // 256) * Fs + Fs) * 4 / (us * 1e-6) / 1e9, 1)
         kernels[role] = entry
 
     out = {
@@ -710,13 +885,16 @@ def run_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic (seeded normal inputs and random-init weights of the workload's shapes)",
         "config": {"workload": workload_text(wl),
                    "global_batch": T, "seq_len": None, "parallelism": f"tp{tp} shard simulated on 1 GPU"},
-        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_of_peak": round(100 * value / peak, 2),
+        "step_ms": step_ms,
+        "cold": cold,
         "roofline": roofline,
         "parts": parts,
+        "epilogue_ablation": ablation,
         "kernels_warmup": kernels,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 2),
@@ -745,7 +923,8 @@ def run_profile_pass(args):
     torch.cuda.synchronize()
     order = step_roles(tl, step, torch)   # the last step: its launches in order
     with open(args.profile_pass, "w") as f:
-        json.dump({"workload": wl.name, "order": order, "fingerprint": kernel_fingerprint(wl.kind)}, f)
+        json.dump({"workload": wl.name, "order": order, "fingerprint": kernel_fingerprint(wl.kind),
+                   "cus": torch.cuda.get_device_properties(0).multi_processor_count}, f)
     print(json.dumps({"profile_pass": args.profile_pass, "launches": len(order)}), flush=True)
 
 
@@ -760,6 +939,37 @@ def _read_pmc(csv_path, counter):
     return rows
 
 
+def summarize_mfma(d, roles, cmds):
+    """profiles/<workload>_mfma.{txt,json}: MFMA-busy fraction of each kernel role of one step."""
+    csvs = glob.glob(os.path.join(d, "mfma", "**", "*counter_collection.csv"), recursive=True)
+    busy = _read_pmc(csvs[0], "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _read_pmc(csvs[0], "GRBM_GUI_ACTIVE")
+    simds = 4 * int(roles.get("cus", 256))
+    n = len(roles["order"])
+    lib_b = [r for r in busy if "tpmlp::" in r[1]][-n:]
+    lib_g = [r for r in gui if "tpmlp::" in r[1]][-n:]
+    launches = {}
+    lines = [f"# MFMA utilisation per launch, {roles['workload']} step (one launch of each kernel role)", "",
+             f"command: {cmds.get('mfma', 'rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -- python3 bench.py --profile-pass OUT')}",
+             "", f"mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x GRBM_GUI_ACTIVE / {XCDS} XCDs): the share of",
+             "the kernel's cycles in which the matrix cores were busy, at whatever clock the kernel ran",
+             "(against the 2.4 GHz peak, frac = mfma_busy x clock / 2.4 GHz).", "",
+             f"{'role':24s} {'kernel':44s} {'cycles':>9s} {'mfma_busy':>9s}"]
+    for (role, sym), (_, name, b), (_, _, g) in zip(roles["order"], lib_b, lib_g):
+        assert canon(name) == sym, f"launch order mismatch: {canon(name)} != {sym}"
+        cyc = g / XCDS
+        frac = b / (simds * cyc) if cyc > 0 else 0.0
+        if role in launches:   # a role launched twice in the step keeps its first launch
+            continue
+        launches[role] = {"kernel": sym, "mfma_busy": round(frac, 4), "cycles": round(cyc)}
+        lines.append(f"{role:24s} {sym:44s} {cyc:9.0f} {frac:9.3f}")
+    with open(os.path.join(PROFILES, f"{roles['workload']}_mfma.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(mfma_path(roles["workload"]), "w") as f:
+        json.dump({"fingerprint": roles["fingerprint"], "workload": roles["workload"], "simds": simds,
+                   "launches": launches}, f, indent=1)
+
+
 def summarize_profile(d):
     """Write profiles/*.txt and profiles/traffic.json from rocprofv3 output under d."""
     os.makedirs(PROFILES, exist_ok=True)
@@ -769,6 +979,10 @@ def summarize_profile(d):
     if os.path.exists(os.path.join(d, "commands.json")):
         with open(os.path.join(d, "commands.json")) as f:
             cmds = json.load(f)
+    if os.path.isdir(os.path.join(d, "mfma")):
+        summarize_mfma(d, roles, cmds)
+    if not os.path.isdir(os.path.join(d, "fetch_size")):
+        return
     scaled = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         csvs = glob.glob(os.path.join(d, counter.lower(), "**", "*counter_collection.csv"), recursive=True)

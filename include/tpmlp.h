@@ -155,6 +155,26 @@ int tp_mlp_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int tp_
                float* dW1_shard, float* db1_shard, float* dW2_shard, void* workspace,
                size_t workspace_bytes);
 
+/* The epilogues of the column-parallel layer as standalone elementwise
+ * passes over an fp32 product, for the fusion ablation (the GEMM entry points
+ * fuse both into the product's epilogue).  GeLU is elementwise, so it
+ * commutes with the column split [csdn 1.2.1 MLP 模块的张量并行; zouht 2.2.1]
+ * and each shard applies it to its own columns; the tanh form as in
+ * column_parallel_fwd.
+ *   bias_gelu_fwd:  A_out = GeLU(Hin + bias), H_out = Hin + bias (if not NULL)
+ *     Hin [T, N] fp32 (ldin); bias [N] storage dtype or NULL; A_out, H_out
+ *     [T, N] storage dtype (lda, ldh).
+ *   gelu_bwd:       dH_out = dA * GeLU'(H)
+ *     dA [T, N] fp32 (ldda); H [T, N] storage dtype (ldh) as saved by the
+ *     forward; dH_out [T, N] storage dtype (lddh).
+ * N must be a multiple of 8 (TPMLP_E_ALIGNMENT otherwise); the other rules
+ * are the shared conventions above.  HBM-bound: 4 + 2 x element-size bytes
+ * per element. */
+int bias_gelu_fwd(void* stream, int dtype, int64_t T, int64_t N, const float* Hin, int64_t ldin,
+                  const void* bias, void* A_out, int64_t lda, void* H_out, int64_t ldh);
+int gelu_bwd(void* stream, int dtype, int64_t T, int64_t N, const float* dA, int64_t ldda, const void* H,
+             int64_t ldh, void* dH_out, int64_t lddh);
+
 /* tp_mlp_bwd without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same operands, outputs and results as tp_mlp_bwd

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "TpmlpError", "lib", "LIB_PATH", "F32", "BF16", "ACT_NONE", "ACT_GELU_TANH",
     "column_parallel_fwd", "row_parallel_fwd", "shard_partial_sum", "tp_mlp_fwd", "tp_mlp_bwd",
-    "tp_mlp_bwd_noalloc", "tpmlp_noalloc_scratch_bytes", "tpmlp_bwd_workspace_bytes", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
+    "tp_mlp_bwd_noalloc", "tpmlp_noalloc_scratch_bytes", "tpmlp_bwd_workspace_bytes", "bias_gelu_fwd", "gelu_bwd", "column_parallel_bwd", "row_parallel_bwd", "swiglu_pack_shard",
     "swiglu_unpack_grad", "tp_swiglu_fwd", "tp_swiglu_bwd", "tp_swiglu_bwd_workspace_bytes", "layernorm_fwd",
     "layernorm_bwd", "sp_partial_sum_dropout_residual", "sp_dropout_bwd", "attn_fwd", "attn_bwd",
     "attn_bwd_workspace_bytes", "attn_fwd_workspace_bytes", "tp_attn_fwd", "tp_attn_fwd_workspace_bytes",
@@ -49,6 +49,8 @@ _SIGNATURES = {
     "tp_mlp_bwd_noalloc": [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp],
     "tpmlp_noalloc_scratch_bytes": [],
+    "bias_gelu_fwd": [_vp, _int, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64],
+    "gelu_bwd": [_vp, _int, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64],
     "column_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                             _i64, _vp],
     "row_parallel_bwd": [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64],
@@ -337,6 +339,25 @@ def tp_mlp_bwd_noalloc(X, W1_shard, W2_shard, H_save, A_save, dZ, tp_size: int, 
     _check(_get_lib().tp_mlp_bwd_noalloc(_stream(stream, X), _dtype(X), T, h, F, tp_size, _ptr(X), _ptr(W1_shard),
                                          _ld(W1_shard, Fs), _ptr(W2_shard), _ptr(H_save), _ptr(A_save), _ptr(dZ),
                                          _ptr(dX_partial), _ptr(dW1_shard), _ptr(db1_shard), _ptr(dW2_shard)))
+
+
+def bias_gelu_fwd(Hin, A_out, bias=None, H_out=None, stream=None) -> None:
+    """A_out = GeLU(Hin + bias), H_out = Hin + bias (Hin fp32; the rest in A_out's storage dtype)."""
+    T, N = _dims("Hin", Hin, 2)
+    dt = _storage("A_out", A_out)
+    _args(("Hin", Hin, (T, N), _F32T, False), ("A_out", A_out, (T, N), dt, False), ("bias", bias, (N,), dt, True),
+          ("H_out", H_out, (T, N), dt, True))
+    _check(_get_lib().bias_gelu_fwd(_stream(stream, Hin), _dtype(A_out), T, N, _ptr(Hin), _ld(Hin, N), _ptr(bias),
+                                    _ptr(A_out), _ld(A_out, N), _ptr(H_out), _ld(H_out, N)))
+
+
+def gelu_bwd(dA, H, dH_out, stream=None) -> None:
+    """dH_out = dA * GeLU'(H) (dA fp32; H and dH_out in the storage dtype)."""
+    T, N = _dims("dA", dA, 2)
+    dt = _storage("H", H)
+    _args(("dA", dA, (T, N), _F32T, False), ("H", H, (T, N), dt, False), ("dH_out", dH_out, (T, N), dt, False))
+    _check(_get_lib().gelu_bwd(_stream(stream, dA), _dtype(H), T, N, _ptr(dA), _ld(dA, N), _ptr(H), _ld(H, N),
+                               _ptr(dH_out), _ld(dH_out, N)))
 
 
 def tpmlp_noalloc_scratch_bytes() -> int:

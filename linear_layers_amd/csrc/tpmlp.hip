@@ -22,6 +22,7 @@
 #include "attn.hpp"
 #include "sp.hpp"
 #include "swiglu.hpp"
+#include "epilogue.hpp"
 
 using namespace tpmlp;
 
@@ -886,6 +887,56 @@ int row_parallel_bwd(void* stream, int dtype, int64_t T, int64_t K, int64_t N, i
   a.C = dW_shard;
   a.ldc = lddw;
   return run_gemm<false, false, kEpiF32>("gemm.row_wgrad", dtype, a, s);
+}
+
+// ------------------------------------------- unfused GeLU epilogues --
+namespace {
+unsigned elementwise_grid(int64_t items) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, 256 * 32));
+}
+}  // namespace
+
+int bias_gelu_fwd(void* stream, int dtype, int64_t T, int64_t N, const float* Hin, int64_t ldin, const void* bias,
+                  void* A_out, int64_t lda, void* H_out, int64_t ldh) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("N", N));
+  const int v = chunk_elems(dtype);
+  if (N % 8 != 0) return fail(TPMLP_E_ALIGNMENT, "N = %lld is not a multiple of 8", (long long)N);
+  TPMLP_TRY(check_mat("Hin", Hin, T, N, ldin, 4));
+  TPMLP_TRY(check_vec("bias", bias, N, false));
+  TPMLP_TRY(check_mat("A_out", A_out, T, N, lda, v));
+  TPMLP_TRY(check_mat("H_out", H_out, T, N, ldh, v, false));
+  if (T == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned grid = elementwise_grid(T * (N / 8));
+  if (dtype == TPMLP_BF16)
+    return launch("bias_gelu_fwd", "bias_gelu_fwd_kernel<bf16>", bias_gelu_fwd_kernel<bf16_t>, dim3(grid), dim3(256),
+                  s, Hin, ldin, static_cast<const bf16_t*>(bias), static_cast<bf16_t*>(A_out), lda,
+                  static_cast<bf16_t*>(H_out), ldh, (int)T, (int)N);
+  return launch("bias_gelu_fwd", "bias_gelu_fwd_kernel<f32>", bias_gelu_fwd_kernel<float>, dim3(grid), dim3(256), s,
+                Hin, ldin, static_cast<const float*>(bias), static_cast<float*>(A_out), lda,
+                static_cast<float*>(H_out), ldh, (int)T, (int)N);
+}
+
+int gelu_bwd(void* stream, int dtype, int64_t T, int64_t N, const float* dA, int64_t ldda, const void* H,
+             int64_t ldh, void* dH_out, int64_t lddh) {
+  TPMLP_TRY(check_dtype(dtype));
+  TPMLP_TRY(check_rows("T", T));
+  TPMLP_TRY(check_dim("N", N));
+  const int v = chunk_elems(dtype);
+  if (N % 8 != 0) return fail(TPMLP_E_ALIGNMENT, "N = %lld is not a multiple of 8", (long long)N);
+  TPMLP_TRY(check_mat("dA", dA, T, N, ldda, 4));
+  TPMLP_TRY(check_mat("H", H, T, N, ldh, v));
+  TPMLP_TRY(check_mat("dH_out", dH_out, T, N, lddh, v));
+  if (T == 0) return TPMLP_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned grid = elementwise_grid(T * (N / 8));
+  if (dtype == TPMLP_BF16)
+    return launch("gelu_bwd", "gelu_bwd_kernel<bf16>", gelu_bwd_kernel<bf16_t>, dim3(grid), dim3(256), s, dA, ldda,
+                  static_cast<const bf16_t*>(H), ldh, static_cast<bf16_t*>(dH_out), lddh, (int)T, (int)N);
+  return launch("gelu_bwd", "gelu_bwd_kernel<f32>", gelu_bwd_kernel<float>, dim3(grid), dim3(256), s, dA, ldda,
+                static_cast<const float*>(H), ldh, static_cast<float*>(dH_out), lddh, (int)T, (int)N);
 }
 
 // ------------------------------------------------- gated MLP (SwiGLU) --
