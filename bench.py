@@ -12,8 +12,9 @@ One step = the whole per-GPU hot path for shard 0 of the Llama-7B-scale MLP
 Inputs sit in HBM before the timed region starts.  `value` is the GEMM work
 (6 products of 2*T*h*F/tp flops) per second over the timed steps.
 
-Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this build runs on
-one GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: the library runs
+one GPU's shard, and the shards of the other GPUs are simulated in turn on
+that GPU.
 
 Profiling helpers (used with rocprofv3, see the profiles/ summaries):
   --profile-pass OUT.json   a plain copy of known size, then one step; writes
@@ -98,7 +99,7 @@ def canon(name: str) -> str:
     """Kernel name as the library reports it, from a demangled rocprofv3 name."""
     n = name.replace("void tpmlp::", "").replace("tpmlp::", "")
     n = re.sub(r"\(.*\)$", "", n).replace(" ", "").replace("true", "1").replace("false", "0")
-    return n
+    return re.sub(r"\bfloat\b", "f32", n)
 
 
 # GEMMs of one shard's step, in units of 2*T*h*(F/tp) flops: the plain MLP
@@ -1042,8 +1043,9 @@ def main():
         summarize_profile(args.summarize_profile)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs on one GPU only; "
-                                   "the multi-GPU path is a design, not code"}))
+        print(json.dumps({"error": f"--gpus {args.gpus}: the benchmark runs on one GPU only; "
+                                   "other tensor-parallel ranks are simulated on it in turn, "
+                                   "and the multi-GPU path is a design, not code"}))
         sys.exit(2)
     if args.profile_pass:
         run_profile_pass(args)

@@ -27,7 +27,11 @@
  *   fp32.  Partial sums and all gradients of weights and inputs that get
  *   summed are fp32.  Conversion to bf16 rounds to nearest even.
  * - All matrix pointers are DEVICE pointers owned by the caller; the library
- *   never allocates, frees or retains them.  stream is a hipStream_t passed
+ *   never allocates, frees or retains them.  The library's own device memory
+ *   is the workspace the caller passes, except for two allocations it makes
+ *   and keeps until the process ends: the first tpmlp_profile_enable
+ *   hipMallocs a small clock buffer (the profiler only), and
+ *   tp_mlp_bwd_noalloc's scratch is a static device array (no allocation).  stream is a hipStream_t passed
  *   as void* (NULL = the null stream).  Work is enqueued asynchronously on
  *   it; the library never synchronises the stream.  Calls on one stream run
  *   in order; calls on different streams that share an output race.
@@ -45,7 +49,9 @@
  *       (fp32), or a pointer not 16-byte aligned           -> TPMLP_E_ALIGNMENT
  *     unknown dtype / activation                           -> TPMLP_E_DTYPE / TPMLP_E_ACT
  *     workspace too small                                  -> TPMLP_E_WORKSPACE
- *     sizes beyond 2^31-1 elements per dimension           -> TPMLP_E_SHAPE
+ *     sizes beyond 2^31-1 elements per dimension, or any
+ *       leading dimension of 2^22 elements or more (a GEMM
+ *       tile's byte offsets are 32-bit)                    -> TPMLP_E_SHAPE
  *   T == 0 (an empty batch) is valid: forward calls enqueue nothing; backward
  *   calls write zeros to the weight and bias gradients (sums over no rows).
  * - Status detail: tpmlp_last_error() returns a thread-local message about

@@ -1,7 +1,8 @@
 // MFMA GEMM core of libtpmlp for gfx950 (CDNA4), with fused epilogues.
 //
-// C[M,N] = sum_k A(m,k) B(k,n), fp32 accumulate, on v_mfma_f32_32x32x16_bf16
-// (bf16 storage) or v_mfma_f32_32x32x2_f32 (fp32 storage).
+// C[M,N] = sum_k A(m,k) B(k,n) for fp32 storage, fp32 accumulate, on
+// v_mfma_f32_32x32x2_f32.  (The bf16 products have kernels of their own,
+// gemm_bf16.hpp and gemm_w4.hpp; the enums and tile mapping here serve all.)
 //
 // Operand orientation is a template choice, so one kernel body serves all
 // products of the block and its backward (Y = X W; dX = dY W^T; dW = X^T dY):
@@ -145,14 +146,7 @@ struct TileLoader {
   }
 };
 
-template <typename T> struct Mfma;
-template <> struct Mfma<bf16_t> {
-  // One 32x32x16 product: each lane's chunk is 8 consecutive K values.
-  static __device__ __forceinline__ void step(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
-  }
-};
+template <typename T> struct Mfma;   // fp32 only: bf16 products run on gemm_bf16.hpp and gemm_w4.hpp
 template <> struct Mfma<float> {
   // Four 32x32x2 products, one per float of the lane's 4-float chunk.  Each
   // lane group (lane / 32) takes the same K entries for A and B, so the four

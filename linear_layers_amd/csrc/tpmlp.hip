@@ -219,20 +219,20 @@ struct TileCfg {
   float eff, eff_act; // measured relative throughput: plain fp32 epilogue / activation epilogues
   bool f32_epi_only;  // too many registers for the activation epilogues
 };
-// bf16: 256x256 with 4 waves (128x128 per wave, gemm_w4.hpp) is fastest
-// when it fills the chip; the other shapes run on the 8-wave kernel
-// (gemm_bf16.hpp): 128x128 with 4 waves and two workgroups per CU for grids
-// that would leave CUs idle, and 256x320 (8 waves as 4 x 2, 64x160 per wave)
-// for fp32 outputs whose width (5120) leaves 256x256 a fraction of a round
-// short.  Their efficiencies are relative to the 4-wave 256x256 kernel, which
-// runs the MLP products 10-20% faster than the 8-wave 256x256 tile they were
-// first measured against (8192x2048x4096: 107 vs 118-131 us; 8192x4096x2048:
-// 120 vs 141-151 us): against that tile, 4096x5120x3840 ran in 142 us at
-// 256x320 vs 180 at 128x128, and two 128x128 workgroups per CU ran at about
-// 0.72 of its rate.  (A 256x192 tile of the 8-wave kernel, 0.80 of the old
-// 256x256 rate, no longer wins for any shape and was dropped.)
+// bf16: the four-wave kernel (gemm_w4.hpp) at 256x256 (128x128 per wave) is
+// fastest when it fills the chip; at 128x128 (64x64 per wave, two workgroups
+// per CU) it serves grids that 256x256 tiles would leave part idle: with
+// whole rounds on both, 8192x4096x3072 ran 168 us at 256x256 and 224 us at
+// 128x128 (0.75), and at 128x128 it beat the eight-wave kernel's 128x128
+// tile on every MLP and attention product shape measured (by 5-20%; a
+// 256x128 tile, one workgroup per CU, ran at 0.71 and never won by more than
+// 2%).  The eight-wave kernel (gemm_bf16.hpp) keeps 256x320 (8 waves as
+// 4 x 2, 64x160 per wave) for fp32 outputs whose width (5120) leaves 256x256
+// a fraction of a round short: 4096x5120x3840 at 256 tiles of 256x320 ran
+// 134 us in the attention block's step against 172 us at 256x256 (0.82 of
+// the 256x256 rate per tile).
 constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f, false},
-                                {128, 128, 2, 0.62f, 0.62f, false},
+                                {128, 128, 2, 0.75f, 0.75f, false},
                                 {256, 320, 1, 0.82f, 0.82f, true}};
 constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f, false}, {64, 64, 1, 0.60f, 0.60f, false}};
 constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
@@ -303,11 +303,11 @@ int run_gemm_bf16(const char* role, GemmArgs a, hipStream_t s, int group) {
                 dim3(64 * WGM * WGN), s, a);
 }
 
-// The four-wave 256x256 kernel (K steps of 64, two LDS stages).
-template <bool AK, bool BKM, int EPI>
+// The four-wave kernel (K steps of 64, two LDS stages) with BM x BN tiles.
+template <int BM, int BN, bool AK, bool BKM, int EPI>
 int run_gemm_w4(const char* role, GemmArgs a, hipStream_t s, int group) {
-  a.tiles_m = (a.M + 255) / 256;
-  a.tiles_n = (a.N + 255) / 256;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
   a.group_m = group;
   if (a.splits < 1) a.splits = 1;
   const int per = (a.K + a.splits - 1) / a.splits;
@@ -316,9 +316,9 @@ int run_gemm_w4(const char* role, GemmArgs a, hipStream_t s, int group) {
   if (grid <= 0) return TPMLP_OK;
   if (grid > 0x7fffffff) return fail(TPMLP_E_SHAPE, "%s: grid too large", role);
   char sym[96];
-  snprintf(sym, sizeof(sym), "gemm_w4_kernel<256,256,%d,%d,%d>", (int)AK, (int)BKM, EPI);
+  snprintf(sym, sizeof(sym), "gemm_w4_kernel<%d,%d,%d,%d,%d>", BM, BN, (int)AK, (int)BKM, EPI);
   a.clk = prof_clock_slot(role);
-  return launch(role, sym, gemm_w4_kernel<256, 256, AK, BKM, EPI>, dim3((unsigned)grid), dim3(256), s, a);
+  return launch(role, sym, gemm_w4_kernel<BM, BN, AK, BKM, EPI>, dim3((unsigned)grid), dim3(256), s, a);
 }
 
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 320 rows of
@@ -347,36 +347,51 @@ int square_group(int per_xcd, int tiles_m) {
 }
 
 // The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
-// launch of 256x256 tiles (the four-wave kernel) when together
-// they fill the chip once (at least 3/4 of the CUs, at most all of them) and
-// the first product's tile count is a multiple of 8 (so each workgroup keeps
-// its XCD within its product).  *done reports whether the pair ran; when it
-// did not, nothing was launched.
+// launch of the four-wave kernel when together they fill the chip once: at
+// 256x256 (one workgroup per CU) when their tiles cover 3/4 to all of the
+// CUs, else at 128x128 (up to two workgroups per CU) when theirs cover 3/4 of
+// the CUs to all of the workgroup slots.  The first product's tile count must
+// be a multiple of 8 (so each workgroup keeps its XCD within its product).
+// *done reports whether the pair ran; when it did not, nothing was launched.
 int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStream_t s, bool* done) {
   *done = false;
   if (dtype != TPMLP_BF16 || a0.M <= 0 || a0.N <= 0 || a1.M <= 0 || a1.N <= 0) return TPMLP_OK;
   if (a0.lda >= kMaxLd || a0.ldb >= kMaxLd || a1.lda >= kMaxLd || a1.ldb >= kMaxLd) return TPMLP_OK;
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
-  constexpr int BM = 256, BN = 256, BKT = 64;
-  auto prep = [&](GemmArgs& a) {
-    a.tiles_m = (a.M + BM - 1) / BM;
-    a.tiles_n = (a.N + BN - 1) / BN;
-    // Each product holds about half of an XCD's CUs; its tiles there form a
-    // square block (16 tiles per XCD: 4 x 4, eight 256-row blocks of A and
-    // B, instead of 2 x 8, ten).
+  constexpr int BKT = 64;
+  auto prep = [&](GemmArgs& a, int bm, int bn) {
+    a.tiles_m = (a.M + bm - 1) / bm;
+    a.tiles_n = (a.N + bn - 1) / bn;
+    // Each product holds about half of an XCD's workgroups; its tiles there
+    // form a square block (16 tiles per XCD: 4 x 4, eight operand row
+    // blocks of A and B, instead of 2 x 8, ten).
     a.group_m = square_group(std::max(1, (int)((int64_t)a.tiles_m * a.tiles_n / 8)), a.tiles_m);
     a.splits = 1;
     a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
     a.clk = nullptr;
     return (int64_t)a.tiles_m * a.tiles_n;
   };
-  const int64_t n0 = prep(a0), n1 = prep(a1);
-  if (n0 % 8 != 0 || n0 + n1 > cus || 4 * (n0 + n1) < 3 * (int64_t)cus) return TPMLP_OK;
-  a0.clk = prof_clock_slot(role);   // the clock of the first product's workgroup 0
-  *done = true;
-  return launch(role, "gemm_w4_pair_kernel<256,256,0,0,0>", gemm_w4_pair_kernel<BM, BN, false, false, kEpiF32>,
-                dim3((unsigned)(n0 + n1)), dim3(256), s, a0, a1, (int)n0);
+  auto fits = [&](int64_t n0, int64_t n1, int64_t slots) {
+    return n0 % 8 == 0 && n0 + n1 <= slots && 4 * (n0 + n1) >= 3 * (int64_t)cus;
+  };
+  GemmArgs b0 = a0, b1 = a1;
+  int64_t n0 = prep(b0, 256, 256), n1 = prep(b1, 256, 256);
+  if (fits(n0, n1, cus)) {
+    b0.clk = prof_clock_slot(role);   // the clock of the first product's workgroup 0
+    *done = true;
+    return launch(role, "gemm_w4_pair_kernel<256,256,0,0,0>", gemm_w4_pair_kernel<256, 256, false, false, kEpiF32>,
+                  dim3((unsigned)(n0 + n1)), dim3(256), s, b0, b1, (int)n0);
+  }
+  b0 = a0, b1 = a1;
+  n0 = prep(b0, 128, 128), n1 = prep(b1, 128, 128);
+  if (fits(n0, n1, 2 * (int64_t)cus)) {
+    b0.clk = prof_clock_slot(role);
+    *done = true;
+    return launch(role, "gemm_w4_pair_kernel<128,128,0,0,0>", gemm_w4_pair_kernel<128, 128, false, false, kEpiF32>,
+                  dim3((unsigned)(n0 + n1)), dim3(256), s, b0, b1, (int)n0);
+  }
+  return TPMLP_OK;
 }
 
 template <bool AK, bool BKM, int EPI>
@@ -402,12 +417,12 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
       group = square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
     }
     switch (cfg) {
-      case 0: return run_gemm_w4<AK, BKM, EPI>(role, a, s, group);
+      case 0: return run_gemm_w4<256, 256, AK, BKM, EPI>(role, a, s, group);
       case 2:
         // 320 rows of 64-element K steps split evenly over 8 waves' loads.
         if constexpr (EPI == kEpiF32) return run_gemm_bf16<256, 320, AK, BKM, EPI, 2, 1, 64, 2, 4>(role, a, s, group);
         else return fail(TPMLP_E_SHAPE, "%s: no 256x320 tile for this epilogue", role);
-      default: return run_gemm_bf16<128, 128, AK, BKM, EPI, 2, 2, 64>(role, a, s, group);
+      default: return run_gemm_w4<128, 128, AK, BKM, EPI>(role, a, s, group);
     }
   }
   if constexpr (EPI == kEpiSwiGLU || EPI == kEpiSwiGLUBwd) {
@@ -456,7 +471,7 @@ int run_wgrad_split(const char* role, const char* sum_role, int dtype, GemmArgs 
   a.split_stride = (int64_t)a.M * a.N;
   const int tiles_m = (a.M + 127) / 128, tiles_n = (a.N + 127) / 128;
   const int group = std::max(1, std::min(tiles_m, (cus / 8) * 2 / tiles_n));
-  TPMLP_TRY((run_gemm_bf16<128, 128, false, false, kEpiF32, 2, 2, 64>(role, a, s, group)));
+  TPMLP_TRY((run_gemm_w4<128, 128, false, false, kEpiF32>(role, a, s, group)));
   return partial_sum(S, a.M, a.N, slices, a.split_stride, a.N, out, ldo, s, sum_role);
 }
 
@@ -1236,7 +1251,7 @@ AttnFwdWs attn_fwd_ws(int64_t batch, int64_t seq, int64_t heads) {
 }
 
 int check_attn(int64_t batch, int64_t seq, int heads, int head_dim, int causal, float scale) {
-  if (head_dim != kAttnD) return fail(TPMLP_E_SHAPE, "head_dim %d: this build takes head_dim 128", head_dim);
+  if (head_dim != kAttnD) return fail(TPMLP_E_SHAPE, "head_dim %d: the attention kernels take head_dim 128 only", head_dim);
   if (heads < 1 || heads > 65535) return fail(TPMLP_E_SHAPE, "heads = %d out of range [1, 65535]", heads);
   if (batch < 0 || batch > 65535) return fail(TPMLP_E_SHAPE, "batch = %lld out of range", (long long)batch);
   TPMLP_TRY(check_rows("seq", seq));

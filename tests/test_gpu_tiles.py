@@ -3,8 +3,9 @@ against the float64 oracle, through the public entry points.
 
 The 256x320 tile (eight waves as 4 x 2) serves fp32 outputs whose width
 (5120 and the like) leaves 256x256 tiles part of a round idle; the four-wave
-256x256 kernel's typed epilogues are also run here on ragged shapes whose last
-tile column is partial.  Each case is sized so the planner picks the kernel
+kernel's typed epilogues are also run here on ragged shapes whose last tile
+column is partial, at 256x256 and at 128x128 (two workgroups per CU, for grids
+too small for 256x256 tiles), as is the weight-gradient pair at 128x128.  Each case is sized so the planner picks the kernel
 under test (checked through the launch records), with ragged M, N and K, and
 covers one operand orientation or epilogue: the fp32 partial with a
 K-contiguous A and an N-contiguous B, two K-contiguous operands, two
@@ -123,11 +124,45 @@ def test_tp_mlp_bwd_dgrad_act_ragged():
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
-def test_swiglu_bwd_ragged():
-    """The gated MLP with T = 8000, h = 136, F/tp = 1496: dA = dZ W_down^T with its gate/up
-    epilogue runs on the four-wave 256x256 tiles, the last tile column 216 wide."""
+def test_tp_mlp_128x128_tiles_and_weight_gradient_pair():
+    """The MLP with T = 700, h = 1000, F/tp = 2000: every product's 256x256 grid would fill under a
+    tenth of the chip, so the four-wave kernel runs 128x128 tiles (bias+GeLU, GeLU' with column sums,
+    the fp32 partials), and the two weight gradients (2000 x 1000 and 1000 x 2000, 16 x 8 tiles each)
+    run as one paired launch of 128x128 tiles; ragged M, N and K (a partial last K step of T)."""
     need_gpu()
-    T, h, F = 8000, 136, 1496
+    T, h, F = 700, 1000, 2000
+    _say(f"mlp 128x128 T={T} h={h} F={F}")
+    wl = synth.Workload("t", 38, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
+    raw = synth.mlp_inputs(wl)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    X, W1, W2, b1, dZ = (to_dev(raw[k], "bf16") for k in ("X", "W1", "W2", "b1", "dZ"))
+    A, H, Z = empty((T, F), "bf16"), empty((T, F), "bf16"), empty_f32((T, h))
+    dX, dW1, db1, dW2 = empty_f32((T, h)), empty_f32((h, F)), empty_f32((F,)), empty_f32((F, h))
+
+    def run():
+        tl.tp_mlp_fwd(X, W1, b1, W2, 1, A, Z, H_save=H)
+        tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
+
+    syms = _launched(run)
+    for k in ("gemm_w4_kernel<128,128,1,0,1>", "gemm_w4_kernel<128,128,1,0,0>", "gemm_w4_kernel<128,128,1,1,2>",
+              "gemm_w4_pair_kernel<128,128,0,0,0>", "gemm_w4_kernel<128,128,1,1,0>"):
+        _has(syms, k)
+    o = ref.tp_mlp_fwd_shard(f["X"], f["W1"], f["b1"], f["W2"], 1, 0)
+    assert_close(to_f64(A), o["A"], "bf16", "A")
+    assert_close(to_f64(H), o["H"], "bf16", "H")
+    assert_close(to_f64(Z), o["Z"], "bf16", "Z")
+    g = ref.tp_mlp_bwd_shard(f["X"], f["W1"], f["b1"], f["W2"], f["dZ"], 1, 0)
+    for name, got in (("dX", dX), ("dW1", dW1), ("db1", db1), ("dW2", dW2)):
+        assert_close(to_f64(got), g[name], "bf16", name)
+
+
+@pytest.mark.parametrize("T,h,F,tile", [(8000, 136, 1496, "256,256"), (1000, 136, 296, "128,128")])
+def test_swiglu_bwd_ragged(T, h, F, tile):
+    """The gated MLP with h = 136: at T = 8000, F/tp = 1496 dA = dZ W_down^T with its gate/up
+    epilogue runs on the four-wave 256x256 tiles, the last tile column 216 wide; at T = 1000,
+    F/tp = 296 both gated epilogues run on 128x128 tiles, the last column 40 (dA) and 80 (packed
+    gate/up) wide."""
+    need_gpu()
     _say(f"swiglu T={T} h={h} F={F}")
     wl = synth.Workload("t", 36, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, dz_std=1.0, kind="swiglu")
     raw = synth.swiglu_inputs(wl)
@@ -143,7 +178,9 @@ def test_swiglu_bwd_ragged():
         tl.tp_swiglu_bwd(X, W_gu, Wd, GU, A, dZ, 1, dX, dW_gu, dW_down)
 
     syms = _launched(run)
-    _has(syms, "gemm_w4_kernel<256,256,1,1,4>")
+    _has(syms, f"gemm_w4_kernel<{tile},1,1,4>")
+    if tile == "128,128":
+        _has(syms, "gemm_w4_kernel<128,128,1,0,3>")
     o = sw.tp_swiglu_fwd_shard(f["X"], f["W_gate"], f["W_up"], f["W_down"], 1, 0)
     assert_close(to_f64(GU), o["GU"], "bf16", "GU")
     assert_close(to_f64(A), o["A"], "bf16", "A")
