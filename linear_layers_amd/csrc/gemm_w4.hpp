@@ -58,7 +58,7 @@ struct W4Tile {
   static constexpr int QPR = ROWS / 8;         // chunks per K-row (M/N-contiguous)
   static constexpr int NB = KMAJ ? 2 : NFB;    // fragment base registers
   static_assert(SLOTS % (64 * NW) == 0, "tile too small for the waves");
-  static_assert(KMAJ || QPR % 16 == 0, "the K-row swizzle works on groups of 16 chunks");
+  static_assert(KMAJ || QPR % 8 == 0, "the K-row swizzle works on groups of 8 or 16 chunks");
 
   uint32_t voff[INSTR];
   uint32_t fbase[NB];
@@ -72,7 +72,7 @@ struct W4Tile {
         const int row = s / CPR, c = w4::pos_k(row, s % CPR);   // pos_k is an involution in c
         voff[j] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
       } else {
-        const int k = s / QPR, q = w4::pos_t(k, s % QPR);       // so is pos_t in q
+        const int k = s / QPR, q = w4::pos_t(QPR, k, s % QPR);  // so is pos_t in q
         voff[j] = (uint32_t)(((int64_t)k * ld + q * 8) * 2);
       }
     }
@@ -173,7 +173,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
   constexpr int WGM = 2, WGN = 2, NW = 4, NT = 256, BKT = 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 16, FN = WTN / 16;
-  static_assert(WTM % 64 == 0 && WTN % 64 == 0, "wave tiles of whole 64-row groups");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole pairs of 16-row blocks");
   using TA = W4Tile<BM, A_KMAJ, NW, FM>;
   using TB = W4Tile<BN, B_KMAJ, NW, FN>;
   constexpr int STAGE = TA::BYTES + TB::BYTES;

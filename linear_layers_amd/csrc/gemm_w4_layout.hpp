@@ -34,9 +34,22 @@ __host__ __device__ constexpr int swz_k(int r) {
 }
 __host__ __device__ constexpr int pos_k(int r, int c) { return c ^ swz_k(r); }
 
-// M/N-contiguous tile: position of chunk q of K-row k.  An XOR with a value
-// below 16, so an involution that stays inside q's aligned group of 16 chunks.
-__host__ __device__ constexpr int pos_t(int k, int q) { return q ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
+// M/N-contiguous tile of qpr chunks per K-row: position of chunk q of K-row
+// k.  A transposing read cycle (32 lanes) takes 32 bytes (a chunk pair) from
+// each of 8 K-rows, k0..k0+3 and k0+8..k0+11 (k0 a multiple of 4), which must
+// land on the 8 distinct 32-byte bank groups of a 256-byte bank line.
+//   * qpr a multiple of 16 (K-row pitch a multiple of 256 bytes): XOR with
+//     4 (k & 3) + 2 bit3(k), below 16, so the map stays inside q's aligned
+//     group of 16 chunks.
+//   * qpr = 8 (mod 16) (pitch 128 bytes more than a multiple of 256): odd
+//     K-rows sit half a bank line further, so bit 0 of k already splits the
+//     rows in two; XOR with 4 bit1(k) + 2 bit3(k), below 8, separates the 4
+//     rows of each parity and stays inside q's aligned group of 8 chunks.
+// Both are involutions in q and keep chunk pairs (2a, 2a + 1) together.
+__host__ __device__ constexpr int pos_t(int qpr, int k, int q) {
+  return (qpr & 15) == 0 ? q ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1)
+                         : q ^ (((k >> 1) & 1) << 2) ^ (((k >> 3) & 1) << 1);
+}
 
 // Byte offset, in a K-contiguous tile, of the 16 bytes lane `lane` reads for
 // fragment block f (16 rows from the wave's first row w0) of K substep s:
@@ -65,10 +78,10 @@ __host__ __device__ constexpr uint32_t frag_t(int qpr, int w0, int lane, int f, 
   const int g = lane >> 4, j = lane & 15;
   const int k = 32 * s + 8 * g + 4 * r + (j >> 2);
   const int col = w0 + 16 * f + 4 * (j & 3);
-  return (uint32_t)(k * qpr * 16 + pos_t(k, col >> 3) * 16 + (col & 7) * 2);
+  return (uint32_t)(k * qpr * 16 + pos_t(qpr, k, col >> 3) * 16 + (col & 7) * 2);
 }
 // As the kernel forms it: one base per block f (substep 0, read 0), the rest
-// an immediate (32 s + 4 r) K-rows further (k & 3 and (k >> 3) & 1 do not
+// an immediate (32 s + 4 r) K-rows further (bits 0, 1 and 3 of k do not
 // depend on s or r).
 __host__ __device__ constexpr uint32_t frag_t_fast(int qpr, int w0, int lane, int f, int s, int r) {
   return frag_t(qpr, w0, lane, f, 0, 0) + (uint32_t)((32 * s + 4 * r) * qpr * 16);

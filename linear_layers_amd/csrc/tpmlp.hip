@@ -230,10 +230,15 @@ struct TileCfg {
 // 4 x 2, 64x160 per wave) for fp32 outputs whose width (5120) leaves 256x256
 // a fraction of a round short: 4096x5120x3840 at 256 tiles of 256x320 ran
 // 134 us in the attention block's step against 172 us at 256x256 (0.82 of
-// the 256x256 rate per tile).
+// the 256x256 rate per tile).  The four-wave kernel at 256x192 (128x96 per
+// wave) serves widths of 1536, 3072 and 6144 that leave 256x256 a
+// quarter or half round short: per tile it runs at 0.80 of 256x256's rate
+// (2048x6144x12288 with bias+GeLU: 243 us in one round of 256x192 against
+// 258 us in 3/4 of a round of 256x256; 8192x1536x4096: 79 against 92 us).
 constexpr TileCfg kCfgBf16[] = {{256, 256, 1, 1.00f, 1.00f, false},
                                 {128, 128, 2, 0.75f, 0.75f, false},
-                                {256, 320, 1, 0.82f, 0.82f, true}};
+                                {256, 320, 1, 0.82f, 0.82f, true},
+                                {256, 192, 1, 0.80f, 0.80f, false}};
 constexpr TileCfg kCfgF32[] = {{128, 128, 1, 1.00f, 1.00f, false}, {64, 64, 1, 0.60f, 0.60f, false}};
 constexpr int kMinBM = 64;  // smallest BM of any configuration (bounds per-tile column-sum rows)
 
@@ -418,6 +423,7 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
     }
     switch (cfg) {
       case 0: return run_gemm_w4<256, 256, AK, BKM, EPI>(role, a, s, group);
+      case 3: return run_gemm_w4<256, 192, AK, BKM, EPI>(role, a, s, group);
       case 2:
         // 320 rows of 64-element K steps split evenly over 8 waves' loads.
         if constexpr (EPI == kEpiF32) return run_gemm_bf16<256, 320, AK, BKM, EPI, 2, 1, 64, 2, 4>(role, a, s, group);

@@ -61,7 +61,7 @@ static void check_tile(int rows, bool kmaj, int nw, int wave_rows) {
             const int row = s / cpr, c = pos_k(row, s % cpr);
             el = Elem(row, c * 8 + e);
           } else {
-            const int k = s / qpr, q = pos_t(k, s % qpr);
+            const int k = s / qpr, q = pos_t(qpr, k, s % qpr);
             CHECK(q >= 0 && q < qpr, "pos_t leaves the row");
             el = Elem(k, q * 8 + e);
           }
@@ -137,6 +137,7 @@ int main() {
   for (bool kmaj : {true, false}) {
     check_tile(256, kmaj, 4, 128);
     check_tile(128, kmaj, 4, 64);
+    check_tile(192, kmaj, 4, 96);
   }
   if (fails) {
     std::printf("%d failures\n", fails);

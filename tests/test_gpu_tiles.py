@@ -61,7 +61,8 @@ def test_row_parallel_fwd_256x320():
     assert_close(to_f64(Z), want, "bf16", "Z")
 
 
-@pytest.mark.parametrize("T,K,tile", [(4000, 5096, "gemm_bf16_kernel<256,320"), (2600, 3080, "gemm_w4_kernel<256,256")])
+@pytest.mark.parametrize("T,K,tile", [(4000, 5096, "gemm_bf16_kernel<256,320"), (8000, 2000, "gemm_w4_kernel<256,256"),
+                                       (2600, 3080, "gemm_w4_kernel<256,192")])
 def test_row_parallel_bwd_dgrad_wide(T, K, tile):
     """dX = dY W^T with M = T, N = K, K = 200: both operands K-contiguous."""
     need_gpu()
@@ -97,11 +98,14 @@ def test_column_parallel_bwd_wgrad_256x320():
     assert_close(to_f64(db), g["db"], "bf16", "db")
 
 
-def test_tp_mlp_bwd_dgrad_act_ragged():
-    """The MLP backward with T = 8000, h = 200, F/tp = 1496: dH = (dZ W2^T) * GeLU'(H) and the
-    db1 column sums run on the four-wave 256x256 tiles, the last tile column 216 wide."""
+@pytest.mark.parametrize("F,tile", [(2000, "256,256"), (1496, "256,192")])
+def test_tp_mlp_bwd_dgrad_act_ragged(F, tile):
+    """The MLP backward with T = 8000, h = 200: dH = (dZ W2^T) * GeLU'(H) and the db1 column sums
+    run on the four-wave kernel, at F/tp = 2000 on 256x256 tiles (the last tile column 208 wide),
+    at F/tp = 1496 on 256x192 tiles (the last column 152 wide), where the forward's bias+GeLU
+    product also runs on 256x192 tiles with the B tile's K-rows of 24 chunks."""
     need_gpu()
-    T, h, F = 8000, 200, 1496
+    T, h = 8000, 200
     _say(f"mlp bwd T={T} h={h} F={F}")
     wl = synth.Workload("t", 35, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
     raw = synth.mlp_inputs(wl)
@@ -115,7 +119,9 @@ def test_tp_mlp_bwd_dgrad_act_ragged():
         tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
 
     syms = _launched(run)
-    _has(syms, "gemm_w4_kernel<256,256,1,1,2>")
+    _has(syms, f"gemm_w4_kernel<{tile},1,1,2>")
+    if tile == "256,192":
+        _has(syms, "gemm_w4_kernel<256,192,1,0,1>")
     o = ref.tp_mlp_fwd_shard(f["X"], f["W1"], f["b1"], f["W2"], 1, 0)
     assert_close(to_f64(A), o["A"], "bf16", "A")
     assert_close(to_f64(Z), o["Z"], "bf16", "Z")
@@ -156,12 +162,13 @@ def test_tp_mlp_128x128_tiles_and_weight_gradient_pair():
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
-@pytest.mark.parametrize("T,h,F,tile", [(8000, 136, 1496, "256,256"), (1000, 136, 296, "128,128")])
+@pytest.mark.parametrize("T,h,F,tile", [(8000, 136, 2000, "256,256"), (8000, 136, 1496, "256,192"),
+                                         (1000, 136, 296, "128,128")])
 def test_swiglu_bwd_ragged(T, h, F, tile):
-    """The gated MLP with h = 136: at T = 8000, F/tp = 1496 dA = dZ W_down^T with its gate/up
-    epilogue runs on the four-wave 256x256 tiles, the last tile column 216 wide; at T = 1000,
-    F/tp = 296 both gated epilogues run on 128x128 tiles, the last column 40 (dA) and 80 (packed
-    gate/up) wide."""
+    """The gated MLP with h = 136: dA = dZ W_down^T with its gate/up epilogue runs on the four-wave
+    kernel at 256x256 (T = 8000, F/tp = 2000; the last tile column 208 wide), at 256x192 (F/tp =
+    1496, with the forward's joined gate/up product: the last columns 152 and 112 wide) and at
+    128x128 (T = 1000, F/tp = 296; the last columns 40 and 80 wide)."""
     need_gpu()
     _say(f"swiglu T={T} h={h} F={F}")
     wl = synth.Workload("t", 36, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, dz_std=1.0, kind="swiglu")
@@ -179,8 +186,8 @@ def test_swiglu_bwd_ragged(T, h, F, tile):
 
     syms = _launched(run)
     _has(syms, f"gemm_w4_kernel<{tile},1,1,4>")
-    if tile == "128,128":
-        _has(syms, "gemm_w4_kernel<128,128,1,0,3>")
+    if tile != "256,256":
+        _has(syms, f"gemm_w4_kernel<{tile},1,0,3>")
     o = sw.tp_swiglu_fwd_shard(f["X"], f["W_gate"], f["W_up"], f["W_down"], 1, 0)
     assert_close(to_f64(GU), o["GU"], "bf16", "GU")
     assert_close(to_f64(A), o["A"], "bf16", "A")
