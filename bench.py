@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time for the baseline")
     ap.add_argument("--breakdown", action="store_true", help="also print per-kernel timings to stderr")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the step's six products through torch.matmul (hipBLASLt) as a yardstick")
     ap.add_argument("--profile-pass", metavar="OUT_JSON", default=None)
     ap.add_argument("--summarize-profile", metavar="DIR", default=None)
     return ap.parse_args()
@@ -714,6 +716,36 @@ def epilogue_ablation(wl, step, tl, torch, n):
             "bytes": {"bias_gelu_fwd": bgf_bytes, "gelu_bwd": gb_bytes}}
 
 
+def vendor_yardstick(wl, step, torch, n):
+    """The six products of shard 0's MLP step through torch.matmul (hipBLASLt),
+    bf16 in and out, timed one by one on the step's stream: a yardstick for
+    the library's GEMMs, never on its path.  Transposed operands are made
+    contiguous beforehand (outside the timing), so every product runs NN."""
+    X, W1, W2, A, dZ = step.X, step.W1s[0], step.W2s[0], step.A, step.dZ
+    W1T, W2T, XT, AT = (W1.t().contiguous(), W2.t().contiguous(), X.t().contiguous(), A.t().contiguous())
+    stream = step.stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prods = {"fwd1 X W1": (X, W1), "fwd2 A W2": (A, W2), "dgrad_act dZ W2^T": (dZ, W2T),
+             "wgrad2 A^T dZ": (AT, dZ), "wgrad1 X^T dH": (XT, A), "dgrad1 dH W1^T": (A, W1T)}
+    out, total = {}, 0.0
+    with torch.cuda.stream(stream):
+        for name, (a, b) in prods.items():
+            torch.matmul(a, b)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                torch.matmul(a, b)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            fl = 2.0 * a.shape[0] * a.shape[1] * b.shape[1]
+            out[name] = {"us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 1)}
+            total += us
+    return {"what": "torch.matmul (hipBLASLt), bf16 in and out, every product NN with transposes made "
+                    "contiguous beforehand; a yardstick, not the library's path",
+            "products": out, "sum_us": round(total, 2)}
+
+
 def workload_text(wl):
     T, h, F, tp, Fs = wl.T, wl.h, wl.F, wl.tp, wl.Fs
     what = {"llama7b_bf16": "the Llama-7B-scale MLP", "gpt2m_bf16": "the GPT-2-medium-scale MLP",
@@ -835,6 +867,7 @@ def run_bench(args):
                            "pct_of_peak": round(100 * ptf / peak, 2)}
 
     ablation = epilogue_ablation(wl, step, tl, torch, args.steps) if isinstance(step, Step) else None
+    vendor = vendor_yardstick(wl, step, torch, args.steps) if args.vendor and isinstance(step, Step) else None
 
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
@@ -896,6 +929,7 @@ def run_bench(args):
         "roofline": roofline,
         "parts": parts,
         "epilogue_ablation": ablation,
+        "vendor_yardstick": vendor,
         "kernels_warmup": kernels,
         "wall_s_timed": round(wall, 4),
         "setup_s": round(setup_s, 2),
