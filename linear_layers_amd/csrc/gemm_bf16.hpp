@@ -151,6 +151,8 @@ struct Bf16Tile {
 #pragma unroll
     for (int j = 0; j < INSTR; ++j) {
       const uint32_t lds = (uint32_t)(uintptr_t)(dst + (wave * INSTR + j) * 1024);
+      // m0 is set and consumed inside this one statement; no compiler-generated
+      // instruction uses m0 (tests/test_m0_invariant_cpu.py checks the built library).
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
                    : "s"(lds), "v"(voff[j]), "s"(rsrc)

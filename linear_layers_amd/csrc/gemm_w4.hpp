@@ -85,7 +85,11 @@ struct W4Tile {
     }
   }
 
-  // One of this wave's loads (index j) of one step.
+  // One of this wave's loads (index j) of one step.  m0 (the LDS address of
+  // an LDS-DMA load) is set inside the same asm statement that consumes it;
+  // the compiler does not preserve a reserved register listed as clobbered,
+  // which is safe because no compiler-generated instruction of these kernels
+  // uses m0 (checked on the built library by tests/test_m0_invariant_cpu.py).
   __device__ __forceinline__ void load_one(int j, const i32x4_t& rsrc, lds_char* dst, int wave) const {
     const uint32_t lds = (uint32_t)(uintptr_t)(dst + (wave * INSTR + j) * 1024);
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
