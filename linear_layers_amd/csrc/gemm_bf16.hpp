@@ -1,5 +1,9 @@
-// bf16 MFMA GEMM of libtpmlp for gfx950 (CDNA4): C[M,N] = sum_k A(m,k) B(k,n),
-// fp32 accumulate on v_mfma_f32_32x32x16_bf16, with fused epilogues.
+// Eight-wave bf16 MFMA GEMM of libtpmlp for gfx950 (CDNA4): C[M,N] = sum_k
+// A(m,k) B(k,n), fp32 accumulate on v_mfma_f32_32x32x16_bf16, fp32 output.
+// The library runs it at one configuration only, 256x320 tiles of 8 waves as
+// 4 x 2 (64x160 per wave): fp32 outputs whose width (5120) leaves 256x256
+// tiles a fraction of a round short.  Every other bf16 product runs on the
+// four-wave kernel (gemm_w4.hpp), which shares this file's tile helpers.
 //
 // Operand orientation (template flags), as in the products of the block:
 //   A_KMAJ: A(m,k) = A[m*lda + k]   else A(m,k) = A[k*lda + m]
@@ -508,14 +512,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
     p.clk[0] = __builtin_amdgcn_s_memtime() - clk0;
     p.clk[1] = __builtin_amdgcn_s_memrealtime() - ref0;
   }
-  float* red = reinterpret_cast<float*>(st0);  // epilogue scratch (LDS is free now)
-  (void)red;
-
   // ------------------------------------------------------------ epilogue --
   // Lane l, block (i, j), register v: row m0 + wm*WTM + 32 i + (l & 31),
   // column n0 + wn*WTN + 32 j + 8 (v/4) + 4 (l/32) + v%4.
   const int mrow = m0 + wm * WTM + (lane & 31);
   const int ncol = n0 + wn * WTN + 4 * (lane >> 5);
+  static_assert(EPI == kEpiF32, "this kernel keeps the fp32 epilogue only");
   if constexpr (EPI == kEpiF32) {
     float* __restrict__ C = p.C + (int64_t)ks * p.split_stride;
 #pragma unroll
@@ -532,302 +534,6 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
                 f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         }
     }
-  } else if constexpr (EPI == kEpiBiasAct) {
-    // The activation is a compile-time choice inside, taken by one uniform branch.
-    auto epilogue = [&](auto GeluC) {
-      constexpr bool kGelu = decltype(GeluC)::value;
-      bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
-      bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);
-      const bf16_t* __restrict__ bias = static_cast<const bf16_t*>(p.bias);
-      const int h = lane >> 5;
-      // Bias of the lane's columns: register group g = 2pr + q holds columns
-      // c + 8q + 4h .. + 3 of the 16-column block c = ... + 32 j + 16 pr.
-      // All of them are loaded before any is converted (one wait, not one per load).
-      u32x2_t bw[FN][4];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cq = n0 + wn * WTN + 32 * j + 8 * g + 4 * h;
-          bw[j][g] = u32x2_t{0u, 0u};
-          if (bias && cq < N) bw[j][g] = *reinterpret_cast<const u32x2_t*>(bias + cq);
-        }
-      float bv[FN][4][4];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2_t w = bw[j][g];
-          bv[j][g][0] = bf16lo(w[0]); bv[j][g][1] = bf16hi(w[0]); bv[j][g][2] = bf16lo(w[1]); bv[j][g][3] = bf16hi(w[1]);
-        }
-      // Rows outermost: the four 32-byte pieces of each 128-byte line of a row
-      // (two j blocks x two 16-column halves) are stored back to back, so L2
-      // merges them before it evicts the line.
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = mrow + 32 * i;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            // After the swap lane h holds the 8 columns c + 8h .. c + 8h + 7.
-            const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-            const int cs = c + 8 * h;
-            uint32_t aw[2][2], hw[2][2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int g = 2 * pr + q;
-              float hv[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) hv[e] = acc[i][j][4 * g + e] + bv[j][g][e];
-              if constexpr (kGelu) {
-                aw[q][0] = pack_bf16x2(gelu_tanh(hv[0]), gelu_tanh(hv[1]));
-                aw[q][1] = pack_bf16x2(gelu_tanh(hv[2]), gelu_tanh(hv[3]));
-              } else {
-                aw[q][0] = pack_bf16x2(hv[0], hv[1]);
-                aw[q][1] = pack_bf16x2(hv[2], hv[3]);
-              }
-              hw[q][0] = pack_bf16x2(hv[0], hv[1]);
-              hw[q][1] = pack_bf16x2(hv[2], hv[3]);
-            }
-#pragma unroll
-            for (int w = 0; w < 2; ++w) {
-              const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
-              aw[0][w] = ra[0];
-              aw[1][w] = ra[1];
-              const auto rh = __builtin_amdgcn_permlane32_swap(hw[0][w], hw[1][w], false, false);
-              hw[0][w] = rh[0];
-              hw[1][w] = rh[1];
-            }
-            if (row < M && cs < N) {
-              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
-              if (Hs)
-                *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) =
-                    u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
-            }
-          }
-      }
-    };
-    if (p.act == kActGeluTanh) epilogue(std::true_type{});
-    else epilogue(std::false_type{});
-  } else if constexpr (EPI == kEpiSwiGLU) {
-    // Packed column 16q + r holds gate (r < 8) or up (r >= 8) of output
-    // column 8q + r % 8.  In a 32-column block, register groups g = 2p (gate)
-    // and 2p + 1 (up) of a lane hold the same 4 output columns, so
-    // silu(gate) * up needs no data from other lanes; lane-pair swaps then
-    // give every lane 8 consecutive columns for one 16-byte store.
-    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);   // [M, N/2]
-    bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);  // [M, N] packed, or null
-    const int h = lane >> 5;
-    // Rows outermost: the pieces of each 128-byte line are stored back to back.
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = mrow + 32 * i;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int c0 = n0 + wn * WTN + 32 * j;  // packed column, a multiple of 32
-        uint32_t aw[2][2], hw[2][2][2];
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          float av[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = acc[i][j][8 * pr + e], u = acc[i][j][8 * pr + 4 + e];
-            av[e] = g * sigmoidf_fast(g) * u;
-          }
-          aw[pr][0] = pack_bf16x2(av[0], av[1]);
-          aw[pr][1] = pack_bf16x2(av[2], av[3]);
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            hw[pr][q][0] = pack_bf16x2(acc[i][j][8 * pr + 4 * q], acc[i][j][8 * pr + 4 * q + 1]);
-            hw[pr][q][1] = pack_bf16x2(acc[i][j][8 * pr + 4 * q + 2], acc[i][j][8 * pr + 4 * q + 3]);
-          }
-        }
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const auto ra = __builtin_amdgcn_permlane32_swap(aw[0][w], aw[1][w], false, false);
-          aw[0][w] = ra[0];
-          aw[1][w] = ra[1];
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const auto rh = __builtin_amdgcn_permlane32_swap(hw[pr][0][w], hw[pr][1][w], false, false);
-            hw[pr][0][w] = rh[0];
-            hw[pr][1][w] = rh[1];
-          }
-        }
-        if (row < M) {
-          // lane h: output columns c0/2 + 8h .. +7 (from block half p = h)
-          if (c0 + 16 * h < N)
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + c0 / 2 + 8 * h) =
-                u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
-          if (Hs) {
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr)
-              if (c0 + 16 * pr < N)
-                *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + c0 + 16 * pr + 8 * h) =
-                    u32x4_t{hw[pr][0][0], hw[pr][0][1], hw[pr][1][0], hw[pr][1][1]};
-          }
-        }
-      }
-    }
-  } else if constexpr (EPI == kEpiSwiGLUBwd) {
-    // acc = dA for output columns c (N of them).  Column c = 8q + r reads
-    // gate and up at packed columns 16q + r and 16q + 8 + r of H and writes
-    // dgate = dA * up * silu'(gate) and dup = dA * silu(gate) to the same
-    // packed columns of Y.  A lane holds r = 4h .. 4h+3 of one q per register
-    // group; the lane-pair swap gives lane h = 0 the 8 dgate values and lane
-    // h = 1 the 8 dup values of that q.
-    bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);        // [M, 2N] packed
-    const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);  // [M, 2N] packed
-    const int h = lane >> 5;
-    // Rows outermost: the pieces of each 128-byte line are read and stored back to back.
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = mrow + 32 * i;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c8 = n0 + wn * WTN + 32 * j + 8 * g;  // output column 8q
-          float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
-          if (row < M && c8 < N) {
-            const bf16_t* src = Hs + (int64_t)row * p.ldh + 2 * c8 + 4 * h;
-            const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(src);
-            const u32x2_t uw = *reinterpret_cast<const u32x2_t*>(src + 8);
-            const float gv[4] = {bf16lo(gw[0]), bf16hi(gw[0]), bf16lo(gw[1]), bf16hi(gw[1])};
-            const float uv[4] = {bf16lo(uw[0]), bf16hi(uw[0]), bf16lo(uw[1]), bf16hi(uw[1])};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float sl, sg;
-              silu_and_grad(gv[e], sl, sg);
-              const float da = acc[i][j][4 * g + e];
-              dg[e] = da * uv[e] * sg;
-              du[e] = da * sl;
-            }
-          }
-          uint32_t x[2] = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          uint32_t y[2] = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto r = __builtin_amdgcn_permlane32_swap(x[w], y[w], false, false);
-            x[w] = r[0];
-            y[w] = r[1];
-          }
-          if (row < M && c8 < N)
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + 2 * c8 + 8 * h) = u32x4_t{x[0], x[1], y[0], y[1]};
-        }
-      }
-  } else {  // kEpiActBwd: dH = acc * Act'(H) and per-tile column sums of dH
-    auto epilogue = [&](auto GeluC) {
-      constexpr bool kGelu = decltype(GeluC)::value;
-      bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
-      const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
-      const int h = lane >> 5;
-      float csum[FN][2][2][4];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) csum[j][pr][q][e] = 0.f;
-      // Rows outermost, so the pieces of each 128-byte line of H and dH are
-      // read and stored back to back.
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = mrow + 32 * i;
-        // The row block's H loads all go out before any is used, so their
-        // latencies overlap (one wait per row block, not one per load).
-        u32x2_t hq[FN][2][2];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int cq = n0 + wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
-              hq[j][pr][q] = u32x2_t{0u, 0u};
-              if constexpr (kGelu) {   // with no activation H is not read (it may be NULL)
-                if (row < M && cq < N) hq[j][pr][q] = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + cq);
-              }
-            }
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const int c = n0 + wn * WTN + 32 * j + 16 * pr;
-            const int cs = c + 8 * h;
-            uint32_t dw[2][2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int g = 2 * pr + q;
-              const int cq = c + 8 * q + 4 * h;
-              float d[4] = {0.f, 0.f, 0.f, 0.f};
-              if (row < M && cq < N) {
-                if constexpr (kGelu) {
-                  const u32x2_t hw = hq[j][pr][q];
-                  const float hv[4] = {bf16lo(hw[0]), bf16hi(hw[0]), bf16lo(hw[1]), bf16hi(hw[1])};
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e] * gelu_tanh_grad(hv[e]);
-                } else {
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) d[e] = acc[i][j][4 * g + e];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) csum[j][pr][q][e] += d[e];
-              }
-              dw[q][0] = pack_bf16x2(d[0], d[1]);
-              dw[q][1] = pack_bf16x2(d[2], d[3]);
-            }
-#pragma unroll
-            for (int w = 0; w < 2; ++w) {
-              const auto r = __builtin_amdgcn_permlane32_swap(dw[0][w], dw[1][w], false, false);
-              dw[0][w] = r[0];
-              dw[1][w] = r[1];
-            }
-            if (row < M && cs < N)
-              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
-          }
-      }
-      if (p.colsum) {
-        // Sum over the 32 rows held by lanes with the same lane/32.
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                for (int x = 1; x < 32; x <<= 1) csum[j][pr][q][e] += __shfl_xor(csum[j][pr][q][e], x);
-              }
-        if ((lane & 31) == 0) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                const int cl = wn * WTN + 32 * j + 16 * pr + 8 * q + 4 * h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) red[wm * BN + cl + e] = csum[j][pr][q][e];
-              }
-        }
-      }
-    };
-    if (p.act == kActGeluTanh) epilogue(std::true_type{});
-    else epilogue(std::false_type{});
-    if (p.colsum) {
-      __syncthreads();
-      for (int c = tid; c < BN; c += NT) {
-        float t = red[c];
-#pragma unroll
-        for (int r = 1; r < WGM; ++r) t += red[r * BN + c];   // wave rows in order
-        if (n0 + c < N) p.colsum[(int64_t)tmi * N + n0 + c] = t;
-      }
-    }
   }
 }
 
@@ -836,20 +542,6 @@ template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1
 __global__ void __launch_bounds__(64 * WGM * WGN, OCC)
 gemm_bf16_kernel(const GemmArgs p) {
   gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p, (int)blockIdx.x, (int)gridDim.x);
-}
-
-// Two independent products of the same shape class in one launch: workgroups
-// [0, n0) compute p0, the rest p1 (n0 a multiple of 8).  Used where each alone
-// would leave CUs idle and together they fill the chip once.
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC = 1, int BKT = 32, int WGN = 2,
-          int WGM = 2>
-__global__ void __launch_bounds__(64 * WGM * WGN, OCC)
-gemm_bf16_pair_kernel(const GemmArgs p0, const GemmArgs p1, int n0) {
-  if ((int)blockIdx.x < n0)
-    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p0, (int)blockIdx.x, n0);
-  else
-    gemm_bf16_body<BM, BN, A_KMAJ, B_KMAJ, EPI, NS, OCC, BKT, WGN, WGM>(p1, (int)blockIdx.x - n0,
-                                                                      (int)gridDim.x - n0);
 }
 
 }  // namespace tpmlp
