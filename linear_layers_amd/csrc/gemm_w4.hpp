@@ -471,25 +471,27 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
     if (p.act == kActGeluTanh) epilogue(std::true_type{});
     else epilogue(std::false_type{});
   } else if constexpr (EPI == kEpiActBwd) {
+    // Lanes take their sums to the store layout first (a permlane16_swap of
+    // the fp32 values of block pair (2jj, 2jj+1): 8 consecutive columns from
+    // 32 jj + coff), so H is read as one 16-byte load per block pair.
     auto epilogue = [&](auto GeluC) {
       constexpr bool kGelu = decltype(GeluC)::value;
       bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);
       const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);
-      float csum[FN][4];
+      float csum[FN / 2][8];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int jj = 0; jj < FN / 2; ++jj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) csum[j][e] = 0.f;
-      // H of row block i goes out two blocks ahead of its use, so the load
-      // latency overlaps the work of the blocks before it.
-      u32x2_t hq[FM][FN];
+        for (int e = 0; e < 8; ++e) csum[jj][e] = 0.f;
+      // H of row block i goes out two blocks ahead of its use.
+      u32x4_t hq[FM][FN / 2];
       auto load_h = [&](int i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          hq[i][j] = u32x2_t{0u, 0u};
-          if constexpr (kGelu) {   // with no activation H is not read (it may be NULL)
-            const int row = mrow + 16 * i, c = ncol + 16 * j;
-            if (row < M && c < N) hq[i][j] = *reinterpret_cast<const u32x2_t*>(Hs + (int64_t)row * p.ldh + c);
+        for (int jj = 0; jj < FN / 2; ++jj) {
+          hq[i][jj] = u32x4_t{0u, 0u, 0u, 0u};
+          if constexpr (kGelu) {
+            const int row = mrow + 16 * i, cs = n0 + wn * WTN + 32 * jj + coff;
+            if (row < M && cs < N) hq[i][jj] = *reinterpret_cast<const u32x4_t*>(Hs + (int64_t)row * p.ldh + cs);
           }
         }
       };
@@ -500,55 +502,52 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
         row_block(i);
         if (i + 2 < FM) load_h(i + 2);
         const int row = mrow + 16 * i;
-        const u32x2_t* hrow = hq[i];
 #pragma unroll
         for (int jj = 0; jj < FN / 2; ++jj) {
-          uint32_t dw[2][2];
+          float x[8];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int j = 2 * jj + q;
-            const int c = ncol + 16 * j;
-            float d[4] = {0.f, 0.f, 0.f, 0.f};
-            if (row < M && c < N) {
-              if constexpr (kGelu) {
-                const float hv[4] = {bf16lo(hrow[j][0]), bf16hi(hrow[j][0]), bf16lo(hrow[j][1]), bf16hi(hrow[j][1])};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) d[e] = acc[i][j][e] * gelu_tanh_grad(hv[e]);
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) d[e] = acc[i][j][e];
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) csum[j][e] += d[e];
-            }
-            dw[q][0] = pack_bf16x2(d[0], d[1]);
-            dw[q][1] = pack_bf16x2(d[2], d[3]);
-          }
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto r = __builtin_amdgcn_permlane16_swap(dw[0][w], dw[1][w], false, false);
-            dw[0][w] = r[0];
-            dw[1][w] = r[1];
+          for (int e = 0; e < 4; ++e) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][2 * jj][e]),
+                                                            __float_as_uint(acc[i][2 * jj + 1][e]), false, false);
+            x[e] = __uint_as_float(r[0]);
+            x[4 + e] = __uint_as_float(r[1]);
           }
           const int cs = n0 + wn * WTN + 32 * jj + coff;
-          if (row < M && cs < N)
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{dw[0][0], dw[0][1], dw[1][0], dw[1][1]};
+          float d[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d[e] = 0.f;
+          if (row < M && cs < N) {
+            if constexpr (kGelu) {
+              const u32x4_t hw = hq[i][jj];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float hv = (e & 1) ? bf16hi(hw[e >> 1]) : bf16lo(hw[e >> 1]);
+                d[e] = x[e] * gelu_tanh_grad(hv);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) d[e] = x[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) csum[jj][e] += d[e];
+            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) =
+                u32x4_t{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])};
+          }
         }
       }
       if (p.colsum) {
-        // sum over the 16 rows of a lane group (lanes with equal lane >> 4)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int jj = 0; jj < FN / 2; ++jj)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
 #pragma unroll
-            for (int x = 1; x < 16; x <<= 1) csum[j][e] += __shfl_xor(csum[j][e], x);
+            for (int x = 1; x < 16; x <<= 1) csum[jj][e] += __shfl_xor(csum[jj][e], x);
           }
         if ((lane & 15) == 0) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+          for (int jj = 0; jj < FN / 2; ++jj)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wm * BN + wn * WTN + 16 * j + 4 * g4 + e] = csum[j][e];
+            for (int e = 0; e < 8; ++e) red[wm * BN + wn * WTN + 32 * jj + coff + e] = csum[jj][e];
         }
       }
     };
@@ -619,21 +618,23 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
   } else {  // kEpiSwiGLUBwd
     // acc = dA for output columns c (N of them).  Column c = 8q + r reads gate
     // and up at packed columns 16q + r and 16q + 8 + r of H and writes dgate
-    // and dup to the same packed columns of Y.  A lane's 4 columns of block j
-    // are c = 16 j + 4 g + e: q = 2 j + g/2, r = 4 (g & 1) + e.
+    // and dup to the same packed columns of Y.  Lanes take their sums to the
+    // store layout first (a permlane16_swap of the fp32 values of block pair
+    // (2jj, 2jj+1)): 8 consecutive columns from c0 = 32 jj + coff, one whole
+    // q, so gate, up, dgate and dup each move as one 16-byte access.
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);               // [M, 2N] packed
     const bf16_t* __restrict__ Hs = static_cast<const bf16_t*>(p.H);  // [M, 2N] packed
     // gate and up of row block i go out one block ahead of their use
-    u32x2_t gq[FM][FN], uq[FM][FN];
+    u32x4_t gq[FM][FN / 2], uq[FM][FN / 2];
     auto load_gu = [&](int i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = mrow + 16 * i, c = ncol + 16 * j;
-        gq[i][j] = uq[i][j] = u32x2_t{0u, 0u};
-        if (row < M && c < N) {
-          const bf16_t* src = Hs + (int64_t)row * p.ldh + 2 * (c & ~7) + (c & 7);
-          gq[i][j] = *reinterpret_cast<const u32x2_t*>(src);
-          uq[i][j] = *reinterpret_cast<const u32x2_t*>(src + 8);
+      for (int jj = 0; jj < FN / 2; ++jj) {
+        const int row = mrow + 16 * i, c0 = n0 + wn * WTN + 32 * jj + coff;
+        gq[i][jj] = uq[i][jj] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row < M && c0 < N) {
+          const bf16_t* src = Hs + (int64_t)row * p.ldh + 2 * c0;
+          gq[i][jj] = *reinterpret_cast<const u32x4_t*>(src);
+          uq[i][jj] = *reinterpret_cast<const u32x4_t*>(src + 8);
         }
       }
     };
@@ -644,22 +645,36 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
       if (i + 1 < FM) load_gu(i + 1);
       const int row = mrow + 16 * i;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int c = ncol + 16 * j;
-        if (row < M && c < N) {
-          const float gv[4] = {bf16lo(gq[i][j][0]), bf16hi(gq[i][j][0]), bf16lo(gq[i][j][1]), bf16hi(gq[i][j][1])};
-          const float uv[4] = {bf16lo(uq[i][j][0]), bf16hi(uq[i][j][0]), bf16lo(uq[i][j][1]), bf16hi(uq[i][j][1])};
-          float dg[4], du[4];
+      for (int jj = 0; jj < FN / 2; ++jj) {
+        float x[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float sl, sg;
-            silu_and_grad(gv[e], sl, sg);
-            dg[e] = acc[i][j][e] * uv[e] * sg;
-            du[e] = acc[i][j][e] * sl;
+        for (int e = 0; e < 4; ++e) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][2 * jj][e]),
+                                                          __float_as_uint(acc[i][2 * jj + 1][e]), false, false);
+          x[e] = __uint_as_float(r[0]);
+          x[4 + e] = __uint_as_float(r[1]);
+        }
+        const int c0 = n0 + wn * WTN + 32 * jj + coff;
+        if (row < M && c0 < N) {
+          uint32_t dgw[4], duw[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float dg[2], du[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float gv = h ? bf16hi(gq[i][jj][w]) : bf16lo(gq[i][jj][w]);
+              const float uv = h ? bf16hi(uq[i][jj][w]) : bf16lo(uq[i][jj][w]);
+              float sl, sg;
+              silu_and_grad(gv, sl, sg);
+              dg[h] = x[2 * w + h] * uv * sg;
+              du[h] = x[2 * w + h] * sl;
+            }
+            dgw[w] = pack_bf16x2(dg[0], dg[1]);
+            duw[w] = pack_bf16x2(du[0], du[1]);
           }
-          bf16_t* dst = Y + (int64_t)row * p.ldy + 2 * (c & ~7) + (c & 7);
-          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          *reinterpret_cast<u32x2_t*>(dst + 8) = u32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          bf16_t* dst = Y + (int64_t)row * p.ldy + 2 * c0;
+          *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{dgw[0], dgw[1], dgw[2], dgw[3]};
+          *reinterpret_cast<u32x4_t*>(dst + 8) = u32x4_t{duw[0], duw[1], duw[2], duw[3]};
         }
       }
     }
