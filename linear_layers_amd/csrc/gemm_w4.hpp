@@ -164,6 +164,14 @@ struct W4Slot {
   static constexpr int read = is_read ? (t - R0) / RS : 0;
 };
 
+// The two LDS stages of a tile size: one array per size, so every
+// orientation of a tile size in one kernel (gemm_w4_trio_kernel) shares it.
+template <int BYTES>
+__device__ __forceinline__ char* w4_lds() {
+  __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+  return buf;
+}
+
 // One workgroup's tile (workgroup pid of the nwg that compute product p).
 // K steps of 64 (two 32-deep substeps) through two LDS stages.  Step k:
 //   substep 0: MFMAs of (k, 0); reads of (k, 1)'s fragments from stage k.
@@ -184,8 +192,8 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
   constexpr int LPS = TA::INSTR + TB::INSTR;  // buffer loads per wave per step
   static_assert(2 * STAGE <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  char* const st0 = w4_lds<2 * STAGE>();
+  char* const st1 = st0 + STAGE;
   auto stage = [&](auto I) -> lds_char* {
     if constexpr (decltype(I)::value == 0) return (lds_char*)st0;
     else return (lds_char*)st1;
@@ -694,6 +702,22 @@ __global__ void __launch_bounds__(256, 1) gemm_w4_pair_kernel(const GemmArgs p0,
     gemm_w4_body<BM, BN, A_KMAJ, B_KMAJ, EPI>(p0, (int)blockIdx.x, n0);
   else
     gemm_w4_body<BM, BN, A_KMAJ, B_KMAJ, EPI>(p1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
+}
+
+// The MLP backward's two weight gradients (both operands M/N-contiguous) and
+// its input gradient (both K-contiguous), independent of each other, in one
+// launch: workgroups [0, n0) compute p0, [n0, n0 + n1) p1, the rest p2 (n0
+// and n1 multiples of 8, so each workgroup keeps its XCD within its product).
+template <int BM, int BN>
+__global__ void __launch_bounds__(256, 1)
+gemm_w4_trio_kernel(const GemmArgs p0, const GemmArgs p1, const GemmArgs p2, int n0, int n1) {
+  const int b = (int)blockIdx.x;
+  if (b < n0)
+    gemm_w4_body<BM, BN, false, false, kEpiF32>(p0, b, n0);
+  else if (b < n0 + n1)
+    gemm_w4_body<BM, BN, false, false, kEpiF32>(p1, b - n0, n1);
+  else
+    gemm_w4_body<BM, BN, true, true, kEpiF32>(p2, b - n0 - n1, (int)gridDim.x - n0 - n1);
 }
 
 }  // namespace tpmlp

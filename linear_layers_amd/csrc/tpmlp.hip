@@ -399,6 +399,47 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
   return TPMLP_OK;
 }
 
+// The MLP backward's two weight gradients and its input gradient dX = dH W1^T
+// (all three need only dH) in one launch of 128x128 tiles, when the weight
+// gradients would run as the 128x128 pair (their 256x256 tiles too few) and
+// all three together fit one round of two workgroups per CU: the pair alone
+// leaves half of the workgroup slots empty, and dX then runs as a launch of
+// its own (GPT-2-medium shard: 128 + 128 + 256 tiles).  *done reports
+// whether the launch ran; when it did not, nothing was launched.
+int run_bwd_trio(const char* role, int dtype, GemmArgs a0, GemmArgs a1, GemmArgs a2, hipStream_t s, bool* done) {
+  *done = false;
+  if (dtype != TPMLP_BF16) return TPMLP_OK;
+  for (const GemmArgs* a : {&a0, &a1, &a2}) {
+    if (a->M <= 0 || a->N <= 0) return TPMLP_OK;
+    if (a->lda >= kMaxLd || a->ldb >= kMaxLd) return TPMLP_OK;
+  }
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  auto tiles = [](const GemmArgs& a, int b) { return (int64_t)((a.M + b - 1) / b) * ((a.N + b - 1) / b); };
+  const int64_t w256 = tiles(a0, 256) + tiles(a1, 256);
+  if (tiles(a0, 256) % 8 == 0 && w256 <= cus && 4 * w256 >= 3 * (int64_t)cus) return TPMLP_OK;   // the 256x256 pair
+  constexpr int B = 128, BKT = 64;
+  auto prep = [&](GemmArgs& a, bool square) {
+    a.tiles_m = (a.M + B - 1) / B;
+    a.tiles_n = (a.N + B - 1) / B;
+    const int64_t t = (int64_t)a.tiles_m * a.tiles_n;
+    a.group_m = square || a.tiles_m <= 8 ? square_group(std::max(1, (int)(t / 8)), a.tiles_m)
+                                         : std::max(1, std::min(a.tiles_m, (cus / 8) * 2 / a.tiles_n));
+    a.splits = 1;
+    a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
+    a.clk = nullptr;
+    return t;
+  };
+  const int64_t n0 = prep(a0, true), n1 = prep(a1, true), n2 = prep(a2, false);
+  if (n0 % 8 != 0 || n1 % 8 != 0 || n0 + n1 > 2 * (int64_t)cus || 4 * (n0 + n1) < 3 * (int64_t)cus ||
+      n0 + n1 + n2 > 2 * (int64_t)cus)
+    return TPMLP_OK;
+  a0.clk = prof_clock_slot(role);   // the clock of the first product's workgroup 0
+  *done = true;
+  return launch(role, "gemm_w4_trio_kernel<128,128>", gemm_w4_trio_kernel<B, B>, dim3((unsigned)(n0 + n1 + n2)),
+                dim3(256), s, a0, a1, a2, (int)n0, (int)n1);
+}
+
 template <bool AK, bool BKM, int EPI>
 int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return TPMLP_OK;
@@ -628,13 +669,21 @@ int mlp_bwd_launch(hipStream_t s, int dtype, int64_t T, int64_t h, int64_t Fs, c
                      dim3(64), s, (const float*)cs, rows, (int)Fs, db1_shard));
   }
   // dW2_i = A_i^T dZ and dW1_i = X^T dH_i: one paired launch when together
-  // they fill the chip once, else one launch each.
+  // they fill the chip once (joined by dX_i when all three fit one round of
+  // 128x128 tiles), else one launch each.
   GemmArgs w2 = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
   w2.C = dW2_shard;
   w2.ldc = h;
   GemmArgs w1 = gemm_args(X, h, dH, Fs, h, Fs, T);
   w1.C = dW1_shard;
   w1.ldc = Fs;
+  // dX_i = dH_i W1_i^T
+  a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
+  a.C = dX_partial;
+  a.ldc = h;
+  bool joined = false;
+  TPMLP_TRY(run_bwd_trio("gemm.mlp_bwd_trio", dtype, w2, w1, a, s, &joined));
+  if (joined) return TPMLP_OK;
   bool paired = false;
   TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
   if (!paired) {
@@ -642,10 +691,6 @@ int mlp_bwd_launch(hipStream_t s, int dtype, int64_t T, int64_t h, int64_t Fs, c
     TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad2", "wgrad_split_sum", dtype, w2, slices, s));
     TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad1", "wgrad_split_sum", dtype, w1, slices, s));
   }
-  // dX_i = dH_i W1_i^T
-  a = gemm_args(dH, Fs, W1_shard, ldw1, T, h, Fs);
-  a.C = dX_partial;
-  a.ldc = h;
   return run_gemm<true, true, kEpiF32>("gemm.mlp_dgrad1", dtype, a, s);
 }
 

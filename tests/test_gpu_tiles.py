@@ -130,13 +130,15 @@ def test_tp_mlp_bwd_dgrad_act_ragged(F, tile):
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
-def test_tp_mlp_128x128_tiles_and_weight_gradient_pair():
-    """The MLP with T = 700, h = 1000, F/tp = 2000: every product's 256x256 grid would fill under a
-    tenth of the chip, so the four-wave kernel runs 128x128 tiles (bias+GeLU, GeLU' with column sums,
-    the fp32 partials), and the two weight gradients (2000 x 1000 and 1000 x 2000, 16 x 8 tiles each)
-    run as one paired launch of 128x128 tiles; ragged M, N and K (a partial last K step of T)."""
+@pytest.mark.parametrize("T,joined", [(700, "gemm_w4_trio_kernel<128,128>"), (4200, "gemm_w4_pair_kernel<128,128,0,0,0>")])
+def test_tp_mlp_128x128_tiles_and_weight_gradient_pair(T, joined):
+    """The MLP with h = 1000, F/tp = 2000: at T = 700 the four-wave kernel runs 128x128 tiles
+    (bias+GeLU, GeLU' with column sums, the fp32 partials), and the two weight gradients (2000 x 1000 and 1000 x 2000,
+    16 x 8 tiles each) run in one launch of 128x128 tiles: at T = 700 joined by dX = dH W1^T (48 more
+    tiles, one round of two workgroups per CU), at T = 4200 (264 dX tiles, more than the round holds)
+    as a pair, dX on its own; ragged M, N and K (a partial last K step of T)."""
     need_gpu()
-    T, h, F = 700, 1000, 2000
+    h, F = 1000, 2000
     _say(f"mlp 128x128 T={T} h={h} F={F}")
     wl = synth.Workload("t", 38, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
     raw = synth.mlp_inputs(wl)
@@ -150,9 +152,12 @@ def test_tp_mlp_128x128_tiles_and_weight_gradient_pair():
         tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
 
     syms = _launched(run)
-    for k in ("gemm_w4_kernel<128,128,1,0,1>", "gemm_w4_kernel<128,128,1,0,0>", "gemm_w4_kernel<128,128,1,1,2>",
-              "gemm_w4_pair_kernel<128,128,0,0,0>", "gemm_w4_kernel<128,128,1,1,0>"):
-        _has(syms, k)
+    _has(syms, joined)
+    if "pair" in joined:      # the forward products are large enough for 256x192 tiles here
+        _has(syms, "gemm_w4_kernel<128,128,1,1,0>")
+    else:
+        for k in ("gemm_w4_kernel<128,128,1,0,1>", "gemm_w4_kernel<128,128,1,0,0>", "gemm_w4_kernel<128,128,1,1,2>"):
+            _has(syms, k)
     o = ref.tp_mlp_fwd_shard(f["X"], f["W1"], f["b1"], f["W2"], 1, 0)
     assert_close(to_f64(A), o["A"], "bf16", "A")
     assert_close(to_f64(H), o["H"], "bf16", "H")
