@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import gc
 import glob
 import hashlib
 import json
@@ -794,6 +795,16 @@ def run_bench(args):
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
+    # Python's cyclic garbage collector is kept out of the measured loops: a
+    # full pass over the interpreter's heap (torch alone holds ~170k tracked
+    # objects) stops the host for tens of ms, and a step's launches queue
+    # behind it, so one pass landing inside a timed region stretched that
+    # step by 20-30 ms.  Everything alive now is frozen out of later passes
+    # and collection stays off until the measurements are taken.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+
     # Warm-up, with every kernel timed once to find the dominant one.
     tl.profile_enable("")
     for _ in range(max(1, args.warmup)):
@@ -876,6 +887,7 @@ def run_bench(args):
 
     ablation = epilogue_ablation(wl, step, tl, torch, args.steps) if isinstance(step, Step) else None
     vendor = vendor_yardstick(wl, step, torch, args.steps) if args.vendor and isinstance(step, Step) else None
+    gc.enable()
 
     # Dominant kernel: algorithmic flops per launch / mean launch duration.
     dom_key = max((k for k in timed if k.startswith(dominant + "|")), key=lambda k: timed[k][1])
