@@ -400,12 +400,16 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
 }
 
 // The MLP backward's two weight gradients and its input gradient dX = dH W1^T
-// (all three need only dH) in one launch of 128x128 tiles, when the weight
-// gradients would run as the 128x128 pair (their 256x256 tiles too few) and
-// all three together fit one round of two workgroups per CU: the pair alone
-// leaves half of the workgroup slots empty, and dX then runs as a launch of
-// its own (GPT-2-medium shard: 128 + 128 + 256 tiles).  *done reports
-// whether the launch ran; when it did not, nothing was launched.
+// (all three need only dH) in one launch:
+//  * at 256x256 when the weight gradients fill one round of 256x256 tiles
+//    (the 256x256 pair) and dX plans 256x256 tiles: dX's tiles follow the
+//    pair's in the same grid (Llama-7B shard: 128 + 128 + 512 tiles);
+//  * at 128x128 when the weight gradients would run as the 128x128 pair
+//    (their 256x256 tiles too few) and all three together fit one round of
+//    two workgroups per CU: the pair alone leaves half of the workgroup slots
+//    empty, and dX then runs as a launch of its own (GPT-2-medium shard:
+//    128 + 128 + 256 tiles).
+// *done reports whether the launch ran; when it did not, nothing was launched.
 int run_bwd_trio(const char* role, int dtype, GemmArgs a0, GemmArgs a1, GemmArgs a2, hipStream_t s, bool* done) {
   *done = false;
   if (dtype != TPMLP_BF16) return TPMLP_OK;
@@ -416,9 +420,37 @@ int run_bwd_trio(const char* role, int dtype, GemmArgs a0, GemmArgs a1, GemmArgs
   int cus = 256;
   TPMLP_TRY(device_cus(&cus));
   auto tiles = [](const GemmArgs& a, int b) { return (int64_t)((a.M + b - 1) / b) * ((a.N + b - 1) / b); };
+  constexpr int BKT = 64;
   const int64_t w256 = tiles(a0, 256) + tiles(a1, 256);
-  if (tiles(a0, 256) % 8 == 0 && w256 <= cus && 4 * w256 >= 3 * (int64_t)cus) return TPMLP_OK;   // the 256x256 pair
-  constexpr int B = 128, BKT = 64;
+  if (tiles(a0, 256) % 8 == 0 && w256 <= cus && 4 * w256 >= 3 * (int64_t)cus) {
+    // The weight gradients fill one round of 256x256 tiles: dX joins them in
+    // the same launch when its own plan is 256x256 too.  Its tiles come after
+    // the pair's (the pair's workgroups are dispatched first and hold every
+    // CU), so they start on each CU as soon as its weight-gradient tile ends,
+    // with no launch boundary between the products.
+    if (plan_cfg(dtype, a2.M, a2.N, kEpiF32, cus) != 0) return TPMLP_OK;
+    auto prep256 = [&](GemmArgs& a, int group) {
+      a.tiles_m = (a.M + 255) / 256;
+      a.tiles_n = (a.N + 255) / 256;
+      a.group_m = group;
+      a.splits = 1;
+      a.k_per_split = ((a.K + BKT - 1) / BKT) * BKT;
+      a.clk = nullptr;
+      return (int64_t)a.tiles_m * a.tiles_n;
+    };
+    const int64_t m0 = prep256(a0, square_group(std::max(1, (int)(tiles(a0, 256) / 8)), (int)((a0.M + 255) / 256)));
+    const int64_t m1 = prep256(a1, square_group(std::max(1, (int)(tiles(a1, 256) / 8)), (int)((a1.M + 255) / 256)));
+    // dX: whole tile rows per XCD, as its own launch would take them.
+    const int tm2 = (int)((a2.M + 255) / 256), tn2 = (int)((a2.N + 255) / 256);
+    const int g2 = tm2 <= 8 ? square_group(std::max(1, (int)std::min<int64_t>((int64_t)tm2 * tn2, cus) / 8), tm2)
+                            : std::max(1, std::min(tm2, (cus / 8) / tn2));
+    const int64_t m2 = prep256(a2, g2);
+    a0.clk = prof_clock_slot(role);
+    *done = true;
+    return launch(role, "gemm_w4_trio_kernel<256,256>", gemm_w4_trio_kernel<256, 256>, dim3((unsigned)(m0 + m1 + m2)),
+                  dim3(256), s, a0, a1, a2, (int)m0, (int)m1);
+  }
+  constexpr int B = 128;
   auto prep = [&](GemmArgs& a, bool square) {
     a.tiles_m = (a.M + B - 1) / B;
     a.tiles_n = (a.N + B - 1) / B;

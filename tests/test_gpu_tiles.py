@@ -167,6 +167,34 @@ def test_tp_mlp_128x128_tiles_and_weight_gradient_pair(T, joined):
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
+def test_tp_mlp_bwd_trio_256x256_ragged():
+    """The MLP backward with h = 4000, F/tp = 2000, T = 3400: the two weight gradients fill one round of
+    256x256 tiles (128 + 128) and dX = dH W1^T plans 256x256 tiles too (14 x 16), so all three run in one
+    launch of the 256x256 four-wave kernel, dX's tiles after the pair's; ragged M, N and K in every
+    product (3400 = 13 x 256 + 72 rows, 4000 = 15 x 256 + 160, 2000 = 7 x 256 + 208; K = 3400 and 2000
+    end in partial 64-deep steps)."""
+    need_gpu()
+    T, h, F = 3400, 4000, 2000
+    _say(f"mlp 256x256 trio T={T} h={h} F={F}")
+    wl = synth.Workload("t", 41, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
+    raw = synth.mlp_inputs(wl)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    X, W1, W2, b1, dZ = (to_dev(raw[k], "bf16") for k in ("X", "W1", "W2", "b1", "dZ"))
+    A, H, Z = empty((T, F), "bf16"), empty((T, F), "bf16"), empty_f32((T, h))
+    dX, dW1, db1, dW2 = empty_f32((T, h)), empty_f32((h, F)), empty_f32((F,)), empty_f32((F, h))
+    tl.tp_mlp_fwd(X, W1, b1, W2, 1, A, Z, H_save=H)
+
+    def run():
+        tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
+
+    syms = _launched(run)
+    _has(syms, "gemm_w4_trio_kernel<256,256>")
+    assert not any("pair" in k or "1,1,0>" in k for k in syms), syms
+    g = ref.tp_mlp_bwd_shard(f["X"], f["W1"], f["b1"], f["W2"], f["dZ"], 1, 0)
+    for name, got in (("dX", dX), ("dW1", dW1), ("db1", db1), ("dW2", dW2)):
+        assert_close(to_f64(got), g[name], "bf16", name)
+
+
 @pytest.mark.parametrize("T,h,F,tile", [(8000, 136, 2000, "256,256"), (8000, 136, 1496, "256,192"),
                                          (1000, 136, 296, "128,128")])
 def test_swiglu_bwd_ragged(T, h, F, tile):
