@@ -148,6 +148,8 @@ JOINED_ROLES = {"gemm.mlp_wgrad", "gemm.mlp_bwd_trio"}
 
 
 def role_flops(wl, role):
+    if "+" in role:      # products joined in one launch: the sum of their parts
+        return sum(role_flops(wl, r) for r in role.split("+"))
     if wl.kind == "proj":
         return proj_role_flops(wl).get(role, 0.0)
     return ROLE_UNITS[wl.kind].get(role, 0) * 2.0 * wl.T * wl.h * wl.Fs
@@ -167,7 +169,11 @@ def step_flops(wl, T=None):
 
 
 def algorithmic_bytes(wl, role):
-    """The GEMM's operands and outputs, each read or written once."""
+    """The GEMM's operands and outputs, each read or written once (for products
+    joined in one launch, role names joined by '+', the sum of their parts)."""
+    if "+" in role:
+        parts = [algorithmic_bytes(wl, r) for r in role.split("+")]
+        return None if any(p is None for p in parts) else sum(parts)
     T, h, Fs = wl.T, wl.h, wl.Fs
     return {"gemm.mlp_fwd1": T * h * 2 + h * Fs * 2 + 2 * T * Fs * 2,
             "gemm.mlp_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,

@@ -704,6 +704,19 @@ __global__ void __launch_bounds__(256, 1) gemm_w4_pair_kernel(const GemmArgs p0,
     gemm_w4_body<BM, BN, A_KMAJ, B_KMAJ, EPI>(p1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
 }
 
+// Two independent products with different operand layouts or epilogues in
+// one launch: workgroups [0, n0) compute p0 and are dispatched first, the rest
+// p1 (n0 a multiple of 8, so each workgroup keeps its XCD within its product).
+// With p0 the product of longer tiles, p1's tiles fill the CUs that p0's
+// leave free and then the CUs its tiles release.
+template <int BM, int BN, bool AK0, bool BK0, int E0, bool AK1, bool BK1, int E1>
+__global__ void __launch_bounds__(256, 1) gemm_w4_duo_kernel(const GemmArgs p0, const GemmArgs p1, int n0) {
+  if ((int)blockIdx.x < n0)
+    gemm_w4_body<BM, BN, AK0, BK0, E0>(p0, (int)blockIdx.x, n0);
+  else
+    gemm_w4_body<BM, BN, AK1, BK1, E1>(p1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
+}
+
 // The MLP backward's two weight gradients (both operands M/N-contiguous) and
 // its input gradient (both K-contiguous), independent of each other, in one
 // launch: workgroups [0, n0) compute p0, [n0, n0 + n1) p1, the rest p2 (n0

@@ -326,6 +326,30 @@ int run_gemm_w4(const char* role, GemmArgs a, hipStream_t s, int group) {
   return launch(role, sym, gemm_w4_kernel<BM, BN, AK, BKM, EPI>, dim3((unsigned)grid), dim3(256), s, a);
 }
 
+// Two independent products in one launch of the four-wave kernel at BM x BN
+// (gemm_w4_duo_kernel): a0's tiles first, a0's tile count a multiple of 8.
+template <int BM, int BN, bool AK0, bool BK0, int E0, bool AK1, bool BK1, int E1>
+int run_gemm_w4_duo(const char* role, GemmArgs a0, int g0, GemmArgs a1, int g1, hipStream_t s) {
+  auto prep = [](GemmArgs& a, int group) {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    a.group_m = group;
+    a.splits = 1;
+    a.k_per_split = ((a.K + 63) / 64) * 64;
+    a.clk = nullptr;
+    return (int64_t)a.tiles_m * a.tiles_n;
+  };
+  const int64_t n0 = prep(a0, g0), n1 = prep(a1, g1);
+  if (n0 % 8 != 0) return fail(TPMLP_E_SHAPE, "%s: first product's tile count %lld is not a multiple of 8", role,
+                               (long long)n0);
+  char sym[96];
+  snprintf(sym, sizeof(sym), "gemm_w4_duo_kernel<%d,%d,%d,%d,%d,%d,%d,%d>", BM, BN, (int)AK0, (int)BK0, E0, (int)AK1,
+           (int)BK1, E1);
+  a0.clk = prof_clock_slot(role);
+  return launch(role, sym, gemm_w4_duo_kernel<BM, BN, AK0, BK0, E0, AK1, BK1, E1>, dim3((unsigned)(n0 + n1)),
+                dim3(256), s, a0, a1, (int)n0);
+}
+
 // Buffer offsets inside a tile are 32-bit: a tile spans at most 320 rows of
 // a K-contiguous operand (or 64 K-rows of an M/N-contiguous one).
 constexpr int64_t kMaxLd = (int64_t)1 << 22;
@@ -349,6 +373,37 @@ int square_group(int per_xcd, int tiles_m) {
     if (c < cost) cost = c, best = g;
   }
   return best;
+}
+
+// Raster group of a product's own launch at tile configuration cfg: the tiles
+// one XCD runs at once (CUs/8 x occupancy) span whole rows of tiles, so each
+// round of an XCD shares its A rows; weight gradients (both operands
+// activations, shared by no other XCD) and products of at most 8 tile rows
+// (where whole rows would make every XCD stream all of B) take a square block
+// of those tiles instead.
+int raster_group(bool wgrad, int64_t M, int64_t N, int cfg, int cus) {
+  const int bm = kCfgBf16[cfg].bm, bn = kCfgBf16[cfg].bn;
+  const int tiles_m = (int)((M + bm - 1) / bm), tiles_n = (int)((N + bn - 1) / bn);
+  if (wgrad || tiles_m <= 8) {
+    const int64_t slots = (int64_t)cus * kCfgBf16[cfg].occ, tiles = (int64_t)tiles_m * tiles_n;
+    return square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
+  }
+  return std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
+}
+
+// A weight gradient w (long K: the token count) and an independent product o
+// of the same backward pass in one launch of 256x256 tiles, w's first, when
+// w's tiles leave CUs idle (fewer than the CUs, a multiple of 8) and o's
+// tiles, run on the idle CUs and then on the ones o's own tiles release,
+// finish within one of w's tiles: the launch then takes about one w tile,
+// against w's launch plus o's launch apart.
+bool joins_under_wgrad(const GemmArgs& w, const GemmArgs& o, int cus) {
+  if (w.M <= 0 || w.N <= 0 || o.M <= 0 || o.N <= 0) return false;
+  const int64_t nw = ((w.M + 255) / 256) * ((w.N + 255) / 256), no = ((o.M + 255) / 256) * ((o.N + 255) / 256);
+  if (nw % 8 != 0 || nw >= cus) return false;
+  const int64_t kw = (w.K + 63) / 64, ko = (o.K + 63) / 64;
+  const int64_t free_cus = cus - nw;
+  return ((no + free_cus - 1) / free_cus) * ko <= kw;
 }
 
 // The two weight gradients of the MLP backward (A^T dZ and X^T dH) in one
@@ -440,11 +495,7 @@ int run_bwd_trio(const char* role, int dtype, GemmArgs a0, GemmArgs a1, GemmArgs
     };
     const int64_t m0 = prep256(a0, square_group(std::max(1, (int)(tiles(a0, 256) / 8)), (int)((a0.M + 255) / 256)));
     const int64_t m1 = prep256(a1, square_group(std::max(1, (int)(tiles(a1, 256) / 8)), (int)((a1.M + 255) / 256)));
-    // dX: whole tile rows per XCD, as its own launch would take them.
-    const int tm2 = (int)((a2.M + 255) / 256), tn2 = (int)((a2.N + 255) / 256);
-    const int g2 = tm2 <= 8 ? square_group(std::max(1, (int)std::min<int64_t>((int64_t)tm2 * tn2, cus) / 8), tm2)
-                            : std::max(1, std::min(tm2, (cus / 8) / tn2));
-    const int64_t m2 = prep256(a2, g2);
+    const int64_t m2 = prep256(a2, raster_group(false, a2.M, a2.N, 0, cus));   // as dX's own launch
     a0.clk = prof_clock_slot(role);
     *done = true;
     return launch(role, "gemm_w4_trio_kernel<256,256>", gemm_w4_trio_kernel<256, 256>, dim3((unsigned)(m0 + m1 + m2)),
@@ -481,19 +532,7 @@ int run_gemm(const char* role, int dtype, GemmArgs a, hipStream_t s) {
   TPMLP_TRY(device_cus(&cus));
   const int cfg = plan_cfg(dtype, a.M, a.N, EPI, cus);
   if (dtype == TPMLP_BF16) {
-    // Raster group: the tiles one XCD runs at once (CUs/8 x occupancy) span
-    // whole rows of tiles, so each round of an XCD shares its A rows.
-    const int bm = kCfgBf16[cfg].bm, bn = kCfgBf16[cfg].bn;
-    const int tiles_m = (a.M + bm - 1) / bm, tiles_n = (a.N + bn - 1) / bn;
-    // Weight gradients (both operands activations, shared by no other XCD)
-    // take a square block of the tiles one XCD runs at once instead.
-    int group = std::max(1, std::min(tiles_m, (cus / 8) * kCfgBf16[cfg].occ / tiles_n));
-    // So do products of at most 8 tile rows: whole rows there would make
-    // every XCD stream all of B.
-    if ((!AK && !BKM) || tiles_m <= 8) {
-      const int64_t slots = (int64_t)cus * kCfgBf16[cfg].occ, tiles = (int64_t)tiles_m * tiles_n;
-      group = square_group((int)std::max<int64_t>(1, std::min(tiles, slots) / 8), tiles_m);
-    }
+    const int group = raster_group(!AK && !BKM, a.M, a.N, cfg, cus);
     switch (cfg) {
       case 0: return run_gemm_w4<256, 256, AK, BKM, EPI>(role, a, s, group);
       case 3: return run_gemm_w4<256, 192, AK, BKM, EPI>(role, a, s, group);
@@ -1165,12 +1204,20 @@ int tp_swiglu_bwd(void* stream, int dtype, int64_t T, int64_t h, int64_t F, int 
   a.ldy = 2 * Fs;
   a.H = const_cast<void*>(GU_save);
   a.ldh = 2 * Fs;
-  TPMLP_TRY((run_gemm<true, true, kEpiSwiGLUBwd>("gemm.swiglu_dgrad_act", dtype, a, s)));
-  // dW_down_i = A^T dZ
-  a = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
-  a.C = dW_down_shard;
-  a.ldc = h;
-  TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.swiglu_wgrad2", dtype, a, s)));
+  // dW_down_i = A^T dZ (needs dZ only, like dA)
+  GemmArgs wd = gemm_args(A_save, Fs, dZ, h, Fs, h, T);
+  wd.C = dW_down_shard;
+  wd.ldc = h;
+  int cus = 256;
+  TPMLP_TRY(device_cus(&cus));
+  if (joins_under_wgrad(wd, a, cus)) {
+    TPMLP_TRY((run_gemm_w4_duo<256, 256, false, false, kEpiF32, true, true, kEpiSwiGLUBwd>(
+        "gemm.swiglu_wgrad2+gemm.swiglu_dgrad_act", wd, raster_group(true, wd.M, wd.N, 0, cus), a,
+        raster_group(false, a.M, a.N, 0, cus), s)));
+  } else {
+    TPMLP_TRY((run_gemm<true, true, kEpiSwiGLUBwd>("gemm.swiglu_dgrad_act", dtype, a, s)));
+    TPMLP_TRY((run_gemm<false, false, kEpiF32>("gemm.swiglu_wgrad2", dtype, wd, s)));
+  }
   // dW_gu = X^T dGU (packed)
   a = gemm_args(X, h, dGU, 2 * Fs, h, 2 * Fs, T);
   a.C = dW_gu_shard;

@@ -11,7 +11,7 @@ import synth
 
 ROLES = ["gemm.mlp_fwd1", "gemm.mlp_fwd2", "gemm.mlp_dgrad_act", "gemm.mlp_wgrad2", "gemm.mlp_wgrad1",
          "gemm.mlp_wgrad", "gemm.mlp_bwd_trio", "gemm.mlp_dgrad1", "gemm.swiglu_fwd1", "gemm.swiglu_fwd2", "gemm.swiglu_dgrad_act", "gemm.swiglu_wgrad2",
-         "gemm.swiglu_wgrad1", "gemm.swiglu_dgrad1", "partial_sum", "colsum", "layernorm_fwd", "layernorm_bwd",
+         "gemm.swiglu_wgrad1", "gemm.swiglu_dgrad1", "gemm.swiglu_wgrad2+gemm.swiglu_dgrad_act", "partial_sum", "colsum", "layernorm_fwd", "layernorm_bwd",
          "layernorm_param_grad", "sp_sum_dropout_residual", "sp_dropout_bwd", "gemm.attn_qkv", "attn_fwd",
          "gemm.attn_out", "gemm.attn_out_dgrad", "gemm.attn_out_wgrad", "attn_bwd_dot", "attn_bwd_dkdv",
          "attn_bwd_dq", "gemm.attn_qkv_wgrad", "gemm.attn_qkv_dgrad"]
@@ -27,7 +27,7 @@ def test_accounting_defined_for_every_role(name):
     for role in ROLES:
         f = bench.role_flops(wl, role)
         assert f >= 0.0
-        if role.startswith("gemm.") and role not in bench.JOINED_ROLES:   # joined launches repeat their parts
+        if role.startswith("gemm.") and role not in bench.JOINED_ROLES and "+" not in role:   # joined launches repeat their parts
             gemm_sum += f
         b = bench.algorithmic_bytes(wl, role)
         assert b is None or b > 0
@@ -55,3 +55,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_joined_roles_sum_their_parts():
+    wl = synth.WORKLOADS["qwen3_swiglu_bf16"]
+    j = "gemm.swiglu_wgrad2+gemm.swiglu_dgrad_act"
+    assert bench.role_flops(wl, j) == bench.role_flops(wl, "gemm.swiglu_wgrad2") + \
+        bench.role_flops(wl, "gemm.swiglu_dgrad_act")
+    assert bench.algorithmic_bytes(wl, j) == bench.algorithmic_bytes(wl, "gemm.swiglu_wgrad2") + \
+        bench.algorithmic_bytes(wl, "gemm.swiglu_dgrad_act")

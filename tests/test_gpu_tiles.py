@@ -195,13 +195,19 @@ def test_tp_mlp_bwd_trio_256x256_ragged():
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
-@pytest.mark.parametrize("T,h,F,tile", [(8000, 136, 2000, "256,256"), (8000, 136, 1496, "256,192"),
-                                         (1000, 136, 296, "128,128")])
-def test_swiglu_bwd_ragged(T, h, F, tile):
+@pytest.mark.parametrize("T,h,F,tile,dact", [
+    (8000, 136, 2000, "256,256", "gemm_w4_duo_kernel<256,256,0,0,0,1,1,4>"),
+    (8000, 136, 1720, "256,256", "gemm_w4_kernel<256,256,1,1,4>"),
+    (8000, 136, 1496, "256,192", "gemm_w4_kernel<256,192,1,1,4>"),
+    (1000, 136, 296, "128,128", "gemm_w4_kernel<128,128,1,1,4>")])
+def test_swiglu_bwd_ragged(T, h, F, tile, dact):
     """The gated MLP with h = 136: dA = dZ W_down^T with its gate/up epilogue runs on the four-wave
-    kernel at 256x256 (T = 8000, F/tp = 2000; the last tile column 208 wide), at 256x192 (F/tp =
-    1496, with the forward's joined gate/up product: the last columns 152 and 112 wide) and at
-    128x128 (T = 1000, F/tp = 296; the last columns 40 and 80 wide)."""
+    kernel at 256x256 (T = 8000, F/tp = 2000 and 1720; the last tile column 208 and 184 wide), at
+    256x192 (F/tp = 1496, with the forward's joined gate/up product: the last columns 152 and 112
+    wide) and at 128x128 (T = 1000, F/tp = 296; the last columns 40 and 80 wide).  At F/tp = 2000 the
+    weight gradient A^T dZ (8 tiles of 256x256 over K = 8000) leaves the chip nearly idle, and dA
+    runs in the same launch, after it; at 1720 its 7 tiles are not a multiple of 8, and dA runs
+    alone."""
     need_gpu()
     _say(f"swiglu T={T} h={h} F={F}")
     wl = synth.Workload("t", 36, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, dz_std=1.0, kind="swiglu")
@@ -218,7 +224,7 @@ def test_swiglu_bwd_ragged(T, h, F, tile):
         tl.tp_swiglu_bwd(X, W_gu, Wd, GU, A, dZ, 1, dX, dW_gu, dW_down)
 
     syms = _launched(run)
-    _has(syms, f"gemm_w4_kernel<{tile},1,1,4>")
+    _has(syms, dact)
     if tile != "256,256":
         _has(syms, f"gemm_w4_kernel<{tile},1,0,3>")
     o = sw.tp_swiglu_fwd_shard(f["X"], f["W_gate"], f["W_up"], f["W_down"], 1, 0)
