@@ -106,17 +106,16 @@ def canon(name: str) -> str:
 
 
 # GEMMs of one shard's step, in units of 2*T*h*(F/tp) flops: the plain MLP
-# has six equal ones (the two weight gradients either as two launches,
-# gemm.mlp_wgrad2 and gemm.mlp_wgrad1, or as one paired launch, gemm.mlp_wgrad,
-# which counts both, or joined by dX in gemm.mlp_bwd_trio, which counts all
-# three); in the gated MLP the joined gate/up layer is twice as
+# has six equal ones; in the gated MLP the joined gate/up layer is twice as
 # wide, so its forward product, its weight gradient and the input gradient
-# through it count twice.
+# through it count twice.  A launch that runs several products reports their
+# role names joined by '+' (e.g. gemm.mlp_wgrad2+gemm.mlp_wgrad1+gemm.mlp_dgrad1)
+# and counts as the sum of its parts.
 ROLE_UNITS = {
     "sp_mlp": {"gemm.mlp_fwd1": 1, "gemm.mlp_fwd2": 1, "gemm.mlp_dgrad_act": 1, "gemm.mlp_wgrad2": 1,
-               "gemm.mlp_wgrad1": 1, "gemm.mlp_wgrad": 2, "gemm.mlp_bwd_trio": 3, "gemm.mlp_dgrad1": 1},
+               "gemm.mlp_wgrad1": 1, "gemm.mlp_dgrad1": 1},
     "mlp": {"gemm.mlp_fwd1": 1, "gemm.mlp_fwd2": 1, "gemm.mlp_dgrad_act": 1, "gemm.mlp_wgrad2": 1,
-            "gemm.mlp_wgrad1": 1, "gemm.mlp_wgrad": 2, "gemm.mlp_bwd_trio": 3, "gemm.mlp_dgrad1": 1},
+            "gemm.mlp_wgrad1": 1, "gemm.mlp_dgrad1": 1},
     "swiglu": {"gemm.swiglu_fwd1": 2, "gemm.swiglu_fwd2": 1, "gemm.swiglu_dgrad_act": 1, "gemm.swiglu_wgrad2": 1,
                "gemm.swiglu_wgrad1": 2, "gemm.swiglu_dgrad1": 2},
 }
@@ -144,9 +143,6 @@ def proj_role_flops(wl, T=None):
 
 # Launches that run several of a step's products together (each part also has
 # a role of its own).
-JOINED_ROLES = {"gemm.mlp_wgrad", "gemm.mlp_bwd_trio"}
-
-
 def role_flops(wl, role):
     if "+" in role:      # products joined in one launch: the sum of their parts
         return sum(role_flops(wl, r) for r in role.split("+"))
@@ -164,7 +160,7 @@ def step_flops(wl, T=None):
     T = wl.T if T is None else T
     if wl.kind == "mlp" and wl.dz_std is None:      # forward only, every shard on this GPU
         return wl.tp * 2 * 2.0 * T * wl.h * wl.Fs
-    units = sum(u for k, u in ROLE_UNITS[wl.kind].items() if k not in JOINED_ROLES)   # their parts count once
+    units = sum(ROLE_UNITS[wl.kind].values())
     return units * 2.0 * T * wl.h * wl.Fs
 
 
@@ -180,10 +176,7 @@ def algorithmic_bytes(wl, role):
             "gemm.mlp_dgrad_act": T * h * 2 + Fs * h * 2 + T * Fs * 2 + T * Fs * 2,
             "gemm.mlp_wgrad2": T * Fs * 2 + T * h * 2 + Fs * h * 4,
             "gemm.mlp_wgrad1": T * h * 2 + T * Fs * 2 + h * Fs * 4,
-            "gemm.mlp_wgrad": (T * Fs * 2 + T * h * 2 + Fs * h * 4) + (T * h * 2 + T * Fs * 2 + h * Fs * 4),
             "gemm.mlp_dgrad1": T * Fs * 2 + h * Fs * 2 + T * h * 4,
-            "gemm.mlp_bwd_trio": ((T * Fs * 2 + T * h * 2 + Fs * h * 4) + (T * h * 2 + T * Fs * 2 + h * Fs * 4) +
-                                  (T * Fs * 2 + h * Fs * 2 + T * h * 4)),
             "gemm.swiglu_fwd1": T * h * 2 + h * 2 * Fs * 2 + T * Fs * 2 + T * 2 * Fs * 2,
             "gemm.swiglu_fwd2": T * Fs * 2 + Fs * h * 2 + T * h * 4,
             "gemm.swiglu_dgrad_act": T * h * 2 + Fs * h * 2 + T * 2 * Fs * 2 + T * 2 * Fs * 2,

@@ -433,7 +433,8 @@ const char* tpmlp_version(void);
 /* Per-kernel timing on the launch stream (a profiling aid for benchmarks).
  * tpmlp_profile_enable(filter): while enabled, every kernel the library
  * launches whose role name contains `filter` ("" = all, NULL = disable) is
- * bracketed by two hipEvents recorded on the launch stream.
+ * bracketed by two hipEvents recorded on the launch stream.  A launch that
+ * runs several products reports their role names joined by '+'.
  * tpmlp_profile_collect(buf, len): waits for the recorded events, writes the
  * launches in order as a JSON list [["role", "kernel_symbol", ms, ghz], ...]
  * to buf and clears the record.  ghz is the shader clock over workgroup 0's

@@ -753,10 +753,10 @@ int mlp_bwd_launch(hipStream_t s, int dtype, int64_t T, int64_t h, int64_t Fs, c
   a.C = dX_partial;
   a.ldc = h;
   bool joined = false;
-  TPMLP_TRY(run_bwd_trio("gemm.mlp_bwd_trio", dtype, w2, w1, a, s, &joined));
+  TPMLP_TRY(run_bwd_trio("gemm.mlp_wgrad2+gemm.mlp_wgrad1+gemm.mlp_dgrad1", dtype, w2, w1, a, s, &joined));
   if (joined) return TPMLP_OK;
   bool paired = false;
-  TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad", dtype, w2, w1, s, &paired));
+  TPMLP_TRY(run_wgrad_pair("gemm.mlp_wgrad2+gemm.mlp_wgrad1", dtype, w2, w1, s, &paired));
   if (!paired) {
     float* slices = reinterpret_cast<float*>(ws + L.split_off);
     TPMLP_TRY(run_wgrad_split("gemm.mlp_wgrad2", "wgrad_split_sum", dtype, w2, slices, s));

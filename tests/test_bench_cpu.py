@@ -10,7 +10,7 @@ import bench
 import synth
 
 ROLES = ["gemm.mlp_fwd1", "gemm.mlp_fwd2", "gemm.mlp_dgrad_act", "gemm.mlp_wgrad2", "gemm.mlp_wgrad1",
-         "gemm.mlp_wgrad", "gemm.mlp_bwd_trio", "gemm.mlp_dgrad1", "gemm.swiglu_fwd1", "gemm.swiglu_fwd2", "gemm.swiglu_dgrad_act", "gemm.swiglu_wgrad2",
+         "gemm.mlp_wgrad2+gemm.mlp_wgrad1", "gemm.mlp_wgrad2+gemm.mlp_wgrad1+gemm.mlp_dgrad1", "gemm.mlp_dgrad1", "gemm.swiglu_fwd1", "gemm.swiglu_fwd2", "gemm.swiglu_dgrad_act", "gemm.swiglu_wgrad2",
          "gemm.swiglu_wgrad1", "gemm.swiglu_dgrad1", "gemm.swiglu_wgrad2+gemm.swiglu_dgrad_act", "partial_sum", "colsum", "layernorm_fwd", "layernorm_bwd",
          "layernorm_param_grad", "sp_sum_dropout_residual", "sp_dropout_bwd", "gemm.attn_qkv", "attn_fwd",
          "gemm.attn_out", "gemm.attn_out_dgrad", "gemm.attn_out_wgrad", "attn_bwd_dot", "attn_bwd_dkdv",
@@ -27,7 +27,7 @@ def test_accounting_defined_for_every_role(name):
     for role in ROLES:
         f = bench.role_flops(wl, role)
         assert f >= 0.0
-        if role.startswith("gemm.") and role not in bench.JOINED_ROLES and "+" not in role:   # joined launches repeat their parts
+        if role.startswith("gemm.") and "+" not in role:   # joined launches repeat their parts
             gemm_sum += f
         b = bench.algorithmic_bytes(wl, role)
         assert b is None or b > 0
@@ -39,8 +39,8 @@ def test_mlp_step_is_six_equal_gemms():
     wl = synth.WORKLOADS["llama7b_bf16"]
     u = 2.0 * wl.T * wl.h * wl.Fs
     assert bench.step_flops(wl) == 6 * u
-    assert bench.role_flops(wl, "gemm.mlp_wgrad") == 2 * u   # the paired weight gradients
-    assert bench.role_flops(wl, "gemm.mlp_bwd_trio") == 3 * u   # joined by dX
+    assert bench.role_flops(wl, "gemm.mlp_wgrad2+gemm.mlp_wgrad1") == 2 * u   # the paired weight gradients
+    assert bench.role_flops(wl, "gemm.mlp_wgrad2+gemm.mlp_wgrad1+gemm.mlp_dgrad1") == 3 * u   # joined by dX
 
 
 def test_attention_block_counts():
