@@ -411,15 +411,32 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
   const int coff = 16 * (g4 & 1) + 8 * (g4 >> 1);
   if constexpr (EPI == kEpiF32) {
     float* __restrict__ C = p.C + (int64_t)ks * p.split_stride;
+    // Non-temporal stores of whole 128-byte lines: for blocks (2jj, 2jj+1)
+    // the lanes of rows 8-15 of a 16-lane row swap with those of rows 0-7
+    // (DPP row_ror:8), so one store covers rows 0-7 and one rows 8-15, each
+    // row's 32 columns from 8 lanes.
+    const bool lower = (lane & 15) < 8;
+    const int rsub = lane & 7;
+    const int csub = 4 * g4 + (lower ? 0 : 16);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       row_block(i);
-      const int row = mrow + 16 * i;
-      if (row >= M) continue;
+      const int rowA = m0 + wm * WTM + 16 * i + rsub, rowB = rowA + 8;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = ncol + 16 * j;
-        if (col < N) *reinterpret_cast<f32x4_w4_t*>(C + (int64_t)row * p.ldc + col) = acc[i][j];
+      for (int jj = 0; jj < FN / 2; ++jj) {
+        const int col = n0 + wn * WTN + 32 * jj + csub;
+        f32x4_w4_t a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[i][2 * jj][e], y = acc[i][2 * jj + 1][e];
+          const float r = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(lower ? y : x), 0x128, 0xf, 0xf, false));
+          a[e] = lower ? x : r;
+          b[e] = lower ? r : y;
+        }
+        if (col < N) {
+          if (rowA < M) __builtin_nontemporal_store(a, reinterpret_cast<f32x4_w4_t*>(C + (int64_t)rowA * p.ldc + col));
+          if (rowB < M) __builtin_nontemporal_store(b, reinterpret_cast<f32x4_w4_t*>(C + (int64_t)rowB * p.ldc + col));
+        }
       }
     }
   } else if constexpr (EPI == kEpiBiasAct) {
