@@ -453,42 +453,89 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
         bw[j] = u32x2_t{0u, 0u};
         if (bias && c < N) bw[j] = *reinterpret_cast<const u32x2_t*>(bias + c);
       }
+      // A and H of block pair jj in the store layout: 8 consecutive columns
+      // from 32 jj + coff (a permlane16_swap of the pair's packed values).
+      auto pair_values = [&](int i, int jj, u32x4_t& av, u32x4_t& hvv) {
+        uint32_t aw[2][2], hw[2][2];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        row_block(i);
-        const int row = mrow + 16 * i;
+        for (int q = 0; q < 2; ++q) {
+          const int j = 2 * jj + q;
+          const float hv[4] = {acc[i][j][0] + bf16lo(bw[j][0]), acc[i][j][1] + bf16hi(bw[j][0]),
+                               acc[i][j][2] + bf16lo(bw[j][1]), acc[i][j][3] + bf16hi(bw[j][1])};
+          if constexpr (kGelu) {
+            aw[q][0] = pack_bf16x2(gelu_tanh(hv[0]), gelu_tanh(hv[1]));
+            aw[q][1] = pack_bf16x2(gelu_tanh(hv[2]), gelu_tanh(hv[3]));
+          } else {
+            aw[q][0] = pack_bf16x2(hv[0], hv[1]);
+            aw[q][1] = pack_bf16x2(hv[2], hv[3]);
+          }
+          hw[q][0] = pack_bf16x2(hv[0], hv[1]);
+          hw[q][1] = pack_bf16x2(hv[2], hv[3]);
+        }
 #pragma unroll
-        for (int jj = 0; jj < FN / 2; ++jj) {
-          uint32_t aw[2][2], hw[2][2];
+        for (int w = 0; w < 2; ++w) {
+          const auto ra = __builtin_amdgcn_permlane16_swap(aw[0][w], aw[1][w], false, false);
+          aw[0][w] = ra[0];
+          aw[1][w] = ra[1];
+          const auto rh = __builtin_amdgcn_permlane16_swap(hw[0][w], hw[1][w], false, false);
+          hw[0][w] = rh[0];
+          hw[1][w] = rh[1];
+        }
+        av = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
+        hvv = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+      };
+      if constexpr ((FN / 2) % 2 == 0) {
+        // Two block pairs (64 columns, 128 bytes of a row) at a time: the
+        // lanes of rows 8-15 of each 16-lane row swap with those of rows 0-7
+        // (DPP row_ror:8), so each store covers 8 whole rows of 128 bytes.
+        // H, kept for the backward pass, leaves with non-temporal stores.
+        const bool lower = (lane & 15) < 8;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int j = 2 * jj + q;
-            const float hv[4] = {acc[i][j][0] + bf16lo(bw[j][0]), acc[i][j][1] + bf16hi(bw[j][0]),
-                                 acc[i][j][2] + bf16lo(bw[j][1]), acc[i][j][3] + bf16hi(bw[j][1])};
-            if constexpr (kGelu) {
-              aw[q][0] = pack_bf16x2(gelu_tanh(hv[0]), gelu_tanh(hv[1]));
-              aw[q][1] = pack_bf16x2(gelu_tanh(hv[2]), gelu_tanh(hv[3]));
-            } else {
-              aw[q][0] = pack_bf16x2(hv[0], hv[1]);
-              aw[q][1] = pack_bf16x2(hv[2], hv[3]);
+        for (int i = 0; i < FM; ++i) {
+          row_block(i);
+          const int rowA = m0 + wm * WTM + 16 * i + (lane & 7), rowB = rowA + 8;
+#pragma unroll
+          for (int jp = 0; jp < FN / 4; ++jp) {
+            u32x4_t a0, h0, a1, h1;
+            pair_values(i, 2 * jp, a0, h0);
+            pair_values(i, 2 * jp + 1, a1, h1);
+            u32x4_t aA, aB, hA, hB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t ra = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lower ? a1[e] : a0[e]), 0x128, 0xf, 0xf, false);
+              const uint32_t rh = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lower ? h1[e] : h0[e]), 0x128, 0xf, 0xf, false);
+              aA[e] = lower ? a0[e] : ra;
+              aB[e] = lower ? ra : a1[e];
+              hA[e] = lower ? h0[e] : rh;
+              hB[e] = lower ? rh : h1[e];
             }
-            hw[q][0] = pack_bf16x2(hv[0], hv[1]);
-            hw[q][1] = pack_bf16x2(hv[2], hv[3]);
+            const int cs = n0 + wn * WTN + 64 * jp + (lower ? 0 : 32) + coff;
+            if (cs < N) {
+              if (rowA < M) {
+                *reinterpret_cast<u32x4_t*>(Y + (int64_t)rowA * p.ldy + cs) = aA;
+                if (Hs) __builtin_nontemporal_store(hA, reinterpret_cast<u32x4_t*>(Hs + (int64_t)rowA * p.ldh + cs));
+              }
+              if (rowB < M) {
+                *reinterpret_cast<u32x4_t*>(Y + (int64_t)rowB * p.ldy + cs) = aB;
+                if (Hs) __builtin_nontemporal_store(hB, reinterpret_cast<u32x4_t*>(Hs + (int64_t)rowB * p.ldh + cs));
+              }
+            }
           }
+        }
+      } else {
 #pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const auto ra = __builtin_amdgcn_permlane16_swap(aw[0][w], aw[1][w], false, false);
-            aw[0][w] = ra[0];
-            aw[1][w] = ra[1];
-            const auto rh = __builtin_amdgcn_permlane16_swap(hw[0][w], hw[1][w], false, false);
-            hw[0][w] = rh[0];
-            hw[1][w] = rh[1];
-          }
-          const int cs = n0 + wn * WTN + 32 * jj + coff;
-          if (row < M && cs < N) {
-            *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
-            if (Hs)
-              *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+        for (int i = 0; i < FM; ++i) {
+          row_block(i);
+          const int row = mrow + 16 * i;
+#pragma unroll
+          for (int jj = 0; jj < FN / 2; ++jj) {
+            u32x4_t av, hv;
+            pair_values(i, jj, av, hv);
+            const int cs = n0 + wn * WTN + 32 * jj + coff;
+            if (row < M && cs < N) {
+              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = av;
+              if (Hs) *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) = hv;
+            }
           }
         }
       }
