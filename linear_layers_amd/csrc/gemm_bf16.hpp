@@ -520,20 +520,49 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int n
   static_assert(EPI == kEpiF32, "this kernel keeps the fp32 epilogue only");
   if constexpr (EPI == kEpiF32) {
     float* __restrict__ C = p.C + (int64_t)ks * p.split_stride;
+    // Through LDS to whole 128-byte lines, stored non-temporally: a store
+    // straight from the sums covers 32 rows x 32 bytes.  Each wave takes its
+    // tile 16 rows at a time into its own region of the (now free) stages,
+    // row-major with a 16-byte pad per row, and reads it back as runs of 64
+    // consecutive 16-byte chunks of those rows (a row is a whole number of
+    // lines: WTN * 4 bytes, a multiple of 128).
+    constexpr int RB = WTN * 4 + 16;   // bytes per staged row
+    static_assert((WTN * 4) % 128 == 0 && 16 * RB * (NW / 2) <= STAGE, "epilogue staging");
+    static_assert((16 * WTN / 4) % 64 == 0, "whole chunk runs per wave");
+    lds_char* const reg = (wave < NW / 2 ? stage(std::integral_constant<int, 0>{}) : stage(std::integral_constant<int, 1>{})) +
+                          (wave % (NW / 2)) * 16 * RB;
+    const int half = (lane & 31) >> 4;   // rows 0-15 or 16-31 of a 32-row block
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int row = mrow + 32 * i;
-      if (row >= M) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int hsel = 0; hsel < 2; ++hsel) {
+        if (half == hsel) {
+          const int r = lane & 15;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = ncol + 32 * j + 8 * g;
-          if (col < N)
-            *reinterpret_cast<f32x4_t*>(C + (int64_t)row * p.ldc + col) =
-                f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<__attribute__((address_space(3))) f32x4_t*>(reg + r * RB + (32 * j + 8 * g + 4 * (lane >> 5)) * 4) =
+                  f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        const int row0 = m0 + wm * WTM + 32 * i + 16 * hsel;
+        const int col0 = n0 + wn * WTN;
+#pragma unroll
+        for (int k = 0; k < 16 * WTN / 4 / 64; ++k) {
+          const int c = 64 * k + lane;          // chunk of the 16 rows x WTN/4 chunks
+          const int r = c / (WTN / 4), q = c % (WTN / 4);
+          const f32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(reg + r * RB + q * 16);
+          const int row = row0 + r, col = col0 + 4 * q;
+          if (row < M && col < N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(C + (int64_t)row * p.ldc + col));
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next rows overwrite the region
+        __builtin_amdgcn_wave_barrier();
+      }
     }
+    (void)mrow;
+    (void)ncol;
   }
 }
 
