@@ -222,7 +222,7 @@ struct FragLoop<NF, NF, S> {
 // One workgroup's tile: workgroup pid of the nwg that compute product p.
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI, int NS, int OCC, int BKT, int WGN, int WGM>
 __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& p, int pid, int nwg) {
-  constexpr int NW = WGM * WGN, NT = 64 * NW;  // WGM x WGN waves
+  constexpr int NW = WGM * WGN;  // WGM x WGN waves
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 * WGM == BM && FN * 32 * WGN == BN, "wave tiles of whole 32x32 blocks");
