@@ -31,6 +31,12 @@
 //     4 (l >> 4) .. 4 (l >> 4) + 3.
 //   * Two LDS stages of K steps of 64; the step schedule is described at
 //     gemm_w4_body.
+//   * Epilogues move the sums to a store layout with lane swaps
+//     (permlane16/32_swap, DPP row_ror:8).  fp32 outputs and the saved
+//     pre-activation H leave as whole 128-byte lines with non-temporal
+//     stores: nothing in the same pass reads them next, and stored that way
+//     they leave no dirty lines in L2 or the Infinity Cache for the next
+//     kernels to evict.
 #pragma once
 
 #include "common.hpp"
