@@ -186,6 +186,46 @@ __device__ __forceinline__ char* w4_lds() {
 //   substep 1: MFMAs of (k, 1); loads of step k + 2 into stage k; reads of
 //              (k + 1, 0)'s fragments from stage k + 1.
 // So a step's loads have a whole step (128 MFMAs) to land.
+// Stores the lane's 16-byte values v0, v1 of block pairs jj0 and jj0 + 1 of a
+// 16-row block (8 consecutive bf16 of row (lane & 15) from column
+// 32 jj + coff, the store layout of the epilogues) as whole 128-byte lines:
+// the lanes of rows 8-15 of each 16-lane row swap with those of rows 0-7 (DPP
+// row_ror:8), so one store covers rows 0-7 and one rows 8-15, each row's 64
+// columns from 8 lanes.  row0, col0: the block's first row and pair jj0's
+// first column (col0 a multiple of 64, so the lines are whole).
+template <bool NT>
+__device__ __forceinline__ void w4_store_pair_lines(bf16_t* base, int64_t ld, int row0, int col0, int M, int N,
+                                                    int lane, int coff, const u32x4_t& v0, const u32x4_t& v1) {
+  const bool lower = (lane & 15) < 8;
+  u32x4_t a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lower ? v1[e] : v0[e]), 0x128, 0xf, 0xf, false);
+    a[e] = lower ? v0[e] : r;
+    b[e] = lower ? r : v1[e];
+  }
+  const int rowA = row0 + (lane & 7), rowB = rowA + 8;
+  const int cs = col0 + (lower ? 0 : 32) + coff;
+  if (cs >= N) return;
+  if (rowA < M) {
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (int64_t)rowA * ld + cs);
+    if constexpr (NT) __builtin_nontemporal_store(a, d);
+    else *d = a;
+  }
+  if (rowB < M) {
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(base + (int64_t)rowB * ld + cs);
+    if constexpr (NT) __builtin_nontemporal_store(b, d);
+    else *d = b;
+  }
+}
+
+// The lane's 16-byte value of one block pair in the store layout, as a plain
+// store (the two halves of a line from neighbouring pairs meet in L2).
+__device__ __forceinline__ void w4_store_pair(bf16_t* base, int64_t ld, int row, int cs, int M, int N,
+                                              const u32x4_t& v) {
+  if (row < M && cs < N) *reinterpret_cast<u32x4_t*>(base + (int64_t)row * ld + cs) = v;
+}
+
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int EPI>
 __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg) {
   constexpr int WGM = 2, WGN = 2, NW = 4, NT = 256, BKT = 64;
@@ -490,58 +530,41 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
         av = u32x4_t{aw[0][0], aw[0][1], aw[1][0], aw[1][1]};
         hvv = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
       };
-      if constexpr ((FN / 2) % 2 == 0) {
-        // Two block pairs (64 columns, 128 bytes of a row) at a time: the
-        // lanes of rows 8-15 of each 16-lane row swap with those of rows 0-7
-        // (DPP row_ror:8), so each store covers 8 whole rows of 128 bytes.
-        // H, kept for the backward pass, leaves with non-temporal stores.
-        const bool lower = (lane & 15) < 8;
+      // A (read by the next product) as plain stores, H (kept for the
+      // backward pass) as non-temporal ones; both in whole lines where the
+      // wave's columns allow: pairs (0,1), (2,3) at 256x256 and 128x128; at
+      // 256x192 (three pairs, 96 columns a wave) pairs (0,1) of wave column 0
+      // and (1,2) of wave column 1, the pair between them (one line shared
+      // by the two waves) as plain half-line stores.
+      auto two = [&](int i, int jj0) {
+        u32x4_t a0, h0, a1, h1;
+        pair_values(i, jj0, a0, h0);
+        pair_values(i, jj0 + 1, a1, h1);
+        const int row0 = m0 + wm * WTM + 16 * i, col0 = n0 + wn * WTN + 32 * jj0;
+        w4_store_pair_lines<false>(Y, p.ldy, row0, col0, M, N, lane, coff, a0, a1);
+        if (Hs) w4_store_pair_lines<true>(Hs, p.ldh, row0, col0, M, N, lane, coff, h0, h1);
+      };
+      auto one = [&](int i, int jj) {
+        u32x4_t av, hv;
+        pair_values(i, jj, av, hv);
+        const int row = mrow + 16 * i, cs = n0 + wn * WTN + 32 * jj + coff;
+        w4_store_pair(Y, p.ldy, row, cs, M, N, av);
+        if (Hs) w4_store_pair(Hs, p.ldh, row, cs, M, N, hv);
+      };
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          row_block(i);
-          const int rowA = m0 + wm * WTM + 16 * i + (lane & 7), rowB = rowA + 8;
+      for (int i = 0; i < FM; ++i) {
+        row_block(i);
+        if constexpr ((FN / 2) % 2 == 0) {
 #pragma unroll
-          for (int jp = 0; jp < FN / 4; ++jp) {
-            u32x4_t a0, h0, a1, h1;
-            pair_values(i, 2 * jp, a0, h0);
-            pair_values(i, 2 * jp + 1, a1, h1);
-            u32x4_t aA, aB, hA, hB;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t ra = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lower ? a1[e] : a0[e]), 0x128, 0xf, 0xf, false);
-              const uint32_t rh = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lower ? h1[e] : h0[e]), 0x128, 0xf, 0xf, false);
-              aA[e] = lower ? a0[e] : ra;
-              aB[e] = lower ? ra : a1[e];
-              hA[e] = lower ? h0[e] : rh;
-              hB[e] = lower ? rh : h1[e];
-            }
-            const int cs = n0 + wn * WTN + 64 * jp + (lower ? 0 : 32) + coff;
-            if (cs < N) {
-              if (rowA < M) {
-                *reinterpret_cast<u32x4_t*>(Y + (int64_t)rowA * p.ldy + cs) = aA;
-                if (Hs) __builtin_nontemporal_store(hA, reinterpret_cast<u32x4_t*>(Hs + (int64_t)rowA * p.ldh + cs));
-              }
-              if (rowB < M) {
-                *reinterpret_cast<u32x4_t*>(Y + (int64_t)rowB * p.ldy + cs) = aB;
-                if (Hs) __builtin_nontemporal_store(hB, reinterpret_cast<u32x4_t*>(Hs + (int64_t)rowB * p.ldh + cs));
-              }
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          row_block(i);
-          const int row = mrow + 16 * i;
-#pragma unroll
-          for (int jj = 0; jj < FN / 2; ++jj) {
-            u32x4_t av, hv;
-            pair_values(i, jj, av, hv);
-            const int cs = n0 + wn * WTN + 32 * jj + coff;
-            if (row < M && cs < N) {
-              *reinterpret_cast<u32x4_t*>(Y + (int64_t)row * p.ldy + cs) = av;
-              if (Hs) *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) = hv;
-            }
+          for (int jp = 0; jp < FN / 4; ++jp) two(i, 2 * jp);
+        } else {
+          static_assert(FN / 2 == 3, "three block pairs a wave (256x192) when not even");
+          if (wn == 0) {
+            two(i, 0);
+            one(i, 2);
+          } else {
+            one(i, 0);
+            two(i, 1);
           }
         }
       }
@@ -647,49 +670,73 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs& p, int pid, int nwg
     // columns.
     bf16_t* __restrict__ Y = static_cast<bf16_t*>(p.Y);   // [M, N/2]
     bf16_t* __restrict__ Hs = static_cast<bf16_t*>(p.H);  // [M, N] packed, or null
+    // Block pair jj of row block i: stores silu(gate) * up (8 bytes a lane,
+    // plain: the next product reads it) and returns the packed gate/up
+    // values in the store layout (8 consecutive packed columns from
+    // 32 jj + coff).
+    auto pair_a = [&](int i, int jj) -> u32x4_t {
+      const int j0 = 2 * jj;
+      uint32_t hw[2][2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        hw[q][0] = pack_bf16x2(acc[i][j0 + q][0], acc[i][j0 + q][1]);
+        hw[q][1] = pack_bf16x2(acc[i][j0 + q][2], acc[i][j0 + q][3]);
+      }
+      float gv[4], uv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j0][e]),
+                                                        __float_as_uint(acc[i][j0 + 1][e]), false, false);
+        gv[e] = __uint_as_float(r[0]);
+        uv[e] = __uint_as_float(r[1]);
+      }
+      uint32_t aw[2];
+      {
+        float av[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = gv[e] * sigmoidf_fast(gv[e]) * uv[e];
+        aw[0] = pack_bf16x2(av[0], av[1]);
+        aw[1] = pack_bf16x2(av[2], av[3]);
+      }
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto rh = __builtin_amdgcn_permlane16_swap(hw[0][w], hw[1][w], false, false);
+        hw[0][w] = rh[0];
+        hw[1][w] = rh[1];
+      }
+      const int row = mrow + 16 * i;
+      // lanes 0-31: block 2jj, lanes 32-63: block 2jj+1; group parity picks r 0..3 or 4..7
+      const int pc = n0 + wn * WTN + 16 * (j0 + (g4 >> 1));   // packed column of the block, 16q
+      if (row < M && pc < N)
+        *reinterpret_cast<u32x2_t*>(Y + (int64_t)row * p.ldy + pc / 2 + 4 * (g4 & 1)) = u32x2_t{aw[0], aw[1]};
+      return u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+    };
+    // gate/up, kept for the backward pass, as whole lines with non-temporal
+    // stores where the wave's columns allow (as H in the bias+GeLU epilogue).
+    auto two = [&](int i, int jj0) {
+      const u32x4_t g0 = pair_a(i, jj0), g1 = pair_a(i, jj0 + 1);
+      if (Hs)
+        w4_store_pair_lines<true>(Hs, p.ldh, m0 + wm * WTM + 16 * i, n0 + wn * WTN + 32 * jj0, M, N, lane, coff, g0,
+                                  g1);
+    };
+    auto one = [&](int i, int jj) {
+      const u32x4_t g = pair_a(i, jj);
+      if (Hs) w4_store_pair(Hs, p.ldh, mrow + 16 * i, n0 + wn * WTN + 32 * jj + coff, M, N, g);
+    };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       row_block(i);
-      const int row = mrow + 16 * i;
+      if constexpr ((FN / 2) % 2 == 0) {
 #pragma unroll
-      for (int jj = 0; jj < FN / 2; ++jj) {
-        const int j0 = 2 * jj;
-        uint32_t hw[2][2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          hw[q][0] = pack_bf16x2(acc[i][j0 + q][0], acc[i][j0 + q][1]);
-          hw[q][1] = pack_bf16x2(acc[i][j0 + q][2], acc[i][j0 + q][3]);
-        }
-        float gv[4], uv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j0][e]),
-                                                          __float_as_uint(acc[i][j0 + 1][e]), false, false);
-          gv[e] = __uint_as_float(r[0]);
-          uv[e] = __uint_as_float(r[1]);
-        }
-        uint32_t aw[2];
-        {
-          float av[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) av[e] = gv[e] * sigmoidf_fast(gv[e]) * uv[e];
-          aw[0] = pack_bf16x2(av[0], av[1]);
-          aw[1] = pack_bf16x2(av[2], av[3]);
-        }
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const auto rh = __builtin_amdgcn_permlane16_swap(hw[0][w], hw[1][w], false, false);
-          hw[0][w] = rh[0];
-          hw[1][w] = rh[1];
-        }
-        if (row < M) {
-          // lanes 0-31: block 2jj, lanes 32-63: block 2jj+1; group parity picks r 0..3 or 4..7
-          const int pc = n0 + wn * WTN + 16 * (j0 + (g4 >> 1));   // packed column of the block, 16q
-          if (pc < N)
-            *reinterpret_cast<u32x2_t*>(Y + (int64_t)row * p.ldy + pc / 2 + 4 * (g4 & 1)) = u32x2_t{aw[0], aw[1]};
-          const int cs = n0 + wn * WTN + 32 * jj + coff;
-          if (Hs && cs < N)
-            *reinterpret_cast<u32x4_t*>(Hs + (int64_t)row * p.ldh + cs) = u32x4_t{hw[0][0], hw[0][1], hw[1][0], hw[1][1]};
+        for (int jp = 0; jp < FN / 4; ++jp) two(i, 2 * jp);
+      } else {
+        static_assert(FN / 2 == 3, "three block pairs a wave (256x192) when not even");
+        if (wn == 0) {
+          two(i, 0);
+          one(i, 2);
+        } else {
+          one(i, 0);
+          two(i, 1);
         }
       }
     }
