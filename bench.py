@@ -21,6 +21,10 @@ Profiling helpers (used with rocprofv3, see the profiles/ summaries):
                             the step's kernel roles and symbols in launch order
   --summarize-profile DIR   turn rocprofv3 output under DIR into the text
                             summaries and traffic table under profiles/
+Machine probes (libtpmlp_probe.so, no MLP work):
+  --probe                   per-CU load-path rate for the GEMM tiles' operand
+                            patterns and LDS fragment-read rates, the bounds
+                            the GEMM design is measured against
 """
 from __future__ import annotations
 
@@ -74,22 +78,25 @@ def parse():
                     help="also time the step's six products through torch.matmul (hipBLASLt) as a yardstick")
     ap.add_argument("--profile-pass", metavar="OUT_JSON", default=None)
     ap.add_argument("--summarize-profile", metavar="DIR", default=None)
+    ap.add_argument("--probe", action="store_true", help="run the machine probes and exit")
     return ap.parse_args()
 
 
 # Kernel sources that cannot affect a workload's kernels (they hold other
-# kernels only), left out of its fingerprint.
+# kernels only), left out of its fingerprint.  probes.hip builds a library of
+# its own and never affects any.
 _UNRELATED_SOURCES = {"mlp": {"attn.hpp", "sp.hpp", "swiglu.hpp", "epilogue.hpp"},
                       "swiglu": {"attn.hpp", "sp.hpp", "epilogue.hpp"},
                       "sp_mlp": {"attn.hpp", "swiglu.hpp", "epilogue.hpp"},
                       "proj": {"sp.hpp", "swiglu.hpp", "epilogue.hpp"}}
+_NEVER_IN_FINGERPRINT = {"probes.hip"}
 
 
 def kernel_fingerprint(kind: str) -> str:
     """Hash of the kernel sources a workload's kernels are built from: counters
     taken on other sources are stale."""
     h = hashlib.sha256()
-    skip = _UNRELATED_SOURCES.get(kind, set())
+    skip = _UNRELATED_SOURCES.get(kind, set()) | _NEVER_IN_FINGERPRINT
     for f in sorted(glob.glob(os.path.join(ROOT, "linear_layers_amd", "csrc", "*"))):
         if os.path.basename(f) in skip:
             continue
@@ -1090,8 +1097,58 @@ def summarize_profile(d):
     print(f"wrote profiles for {roles['workload']}")
 
 
+# (mode, pattern, label) of the load-path probe, run at two pairs of leading
+# dimensions: powers of two, and padded by 64 elements.
+PROBE_LOADS = [
+    (0, 0, "LDS DMA, A and B as in the GEMM tiles"),
+    (0, 1, "LDS DMA, A only (8 rows x 128 B a load)"),
+    (0, 3, "LDS DMA, A only, a load's rows 32 apart"),
+    (0, 2, "LDS DMA, B only (2 K-rows x 512 B a load)"),
+    (1, 0, "register loads, A and B"),
+    (1, 1, "register loads, A only"),
+    (1, 2, "register loads, B only"),
+    (2, 0, "register loads + ds_write_b128, A and B"),
+]
+PROBE_LDS = [(0, w, "ds_read_b128") for w in (4, 8, 16)] + [(1, w, "ds_read_b64_tr_b16") for w in (4, 8, 16)]
+
+
+def run_probes():
+    """Run libtpmlp_probe.so's probes on the current GPU: one text line per
+    case, then one JSON line with every figure."""
+    import ctypes
+    path = os.path.join(ROOT, "linear_layers_amd", "libtpmlp_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.tpmlp_probe_last_error.restype = ctypes.c_char_p
+    out = (ctypes.c_double * 4)()
+    res = {"load_path": [], "lds_read": []}
+    for lda, ldb in ((4096, 8192), (4160, 8256)):
+        print(f"load path, lda {lda}, ldb {ldb} (bf16 elements; 64 KB per CU per step, 64 steps)", flush=True)
+        for mode, pat, label in PROBE_LOADS:
+            rc = lib.tpmlp_probe_load_path(mode, pat, lda, ldb, 20, out)
+            if rc != 0:
+                raise SystemExit(f"load probe {mode}/{pat}: {lib.tpmlp_probe_last_error().decode()}")
+            us, ghz, gbs, bpc = out[0], out[1], out[2], out[3]
+            print(f"  {label:44s} {us:7.1f} us {gbs:7.0f} GB/s  clk {ghz:.2f} GHz  {bpc:5.1f} B/clk/CU", flush=True)
+            res["load_path"].append({"mode": mode, "pattern": pat, "lda": lda, "ldb": ldb, "label": label,
+                                     "us": round(us, 2), "sclk_ghz": round(ghz, 3), "gb_s": round(gbs, 1),
+                                     "bytes_per_clk_cu": round(bpc, 2)})
+    print("LDS reads (8 independent reads per wave, then a wait)", flush=True)
+    for tr, waves, label in PROBE_LDS:
+        rc = lib.tpmlp_probe_lds_read(tr, waves, 4096, out)
+        if rc != 0:
+            raise SystemExit(f"LDS probe {label}/{waves}: {lib.tpmlp_probe_last_error().decode()}")
+        print(f"  {label:20s} {waves:2d} waves: {out[1]:6.1f} B/clk/CU", flush=True)
+        res["lds_read"].append({"instruction": label, "waves": waves, "bytes_per_clk_cu": round(out[1], 1)})
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
+    if args.probe:
+        run_probes()
+        return
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
         return

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpmlp.so")
 SOURCES = [os.path.join(CSRC, "tpmlp.hip")]
+# The machine probes (bench.py --probe) build into a library of their own.
+PROBE_LIB = os.path.join(HERE, "libtpmlp_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probes.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,10 +35,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every HIP source into linear_layers_amd/libtpmlp.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
+def _compile(out: str, sources, verbose: bool, extra) -> None:
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +47,14 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile libtpmlp.so and the probe library libtpmlp_probe.so into
+    linear_layers_amd/; returns the path of libtpmlp.so."""
+    _compile(LIB, SOURCES, verbose, extra)
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose, extra)
     return LIB
 
 
