@@ -410,9 +410,17 @@ bool joins_under_wgrad(const GemmArgs& w, const GemmArgs& o, int cus) {
 // launch of the four-wave kernel when together they fill the chip once: at
 // 256x256 (one workgroup per CU) when their tiles cover 3/4 to all of the
 // CUs, else at 128x128 (up to two workgroups per CU) when theirs cover 3/4 of
-// the CUs to all of the workgroup slots.  The first product's tile count must
-// be a multiple of 8 (so each workgroup keeps its XCD within its product).
-// *done reports whether the pair ran; when it did not, nothing was launched.
+// the CUs to all of the workgroup slots.  Past one round, at 256x256 when
+// each would run as 256x256 tiles of its own (unsplit, the planner's choice)
+// over the same K and their part-filled last rounds together save a round
+// (GPT-3 shard: 1152 + 1152 tiles, 5 + 5 rounds apart, 9 together); each
+// keeps the raster of its own launch, and the second's tiles start on the
+// CUs the first's last round leaves free.  The first product's tile count
+// must be a multiple of 8 (so each workgroup keeps its XCD within its
+// product).  *done reports whether the pair ran; when it did not, nothing
+// was launched.
+int wgrad_splits(int dtype, int64_t M, int64_t N, int64_t K);
+
 int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStream_t s, bool* done) {
   *done = false;
   if (dtype != TPMLP_BF16 || a0.M <= 0 || a0.N <= 0 || a1.M <= 0 || a1.N <= 0) return TPMLP_OK;
@@ -450,6 +458,20 @@ int run_wgrad_pair(const char* role, int dtype, GemmArgs a0, GemmArgs a1, hipStr
     *done = true;
     return launch(role, "gemm_w4_pair_kernel<128,128,0,0,0>", gemm_w4_pair_kernel<128, 128, false, false, kEpiF32>,
                   dim3((unsigned)(n0 + n1)), dim3(256), s, b0, b1, (int)n0);
+  }
+  if (a0.K == a1.K && wgrad_splits(dtype, a0.M, a0.N, a0.K) == 1 && wgrad_splits(dtype, a1.M, a1.N, a1.K) == 1 &&
+      plan_cfg(dtype, a0.M, a0.N, kEpiF32, cus) == 0 && plan_cfg(dtype, a1.M, a1.N, kEpiF32, cus) == 0) {
+    b0 = a0, b1 = a1;
+    n0 = prep(b0, 256, 256), n1 = prep(b1, 256, 256);
+    b0.group_m = raster_group(true, b0.M, b0.N, 0, cus);
+    b1.group_m = raster_group(true, b1.M, b1.N, 0, cus);
+    auto rounds = [&](int64_t n) { return (n + cus - 1) / cus; };
+    if (n0 % 8 == 0 && n0 + n1 <= 0x7fffffff && rounds(n0 + n1) < rounds(n0) + rounds(n1)) {
+      b0.clk = prof_clock_slot(role);
+      *done = true;
+      return launch(role, "gemm_w4_pair_kernel<256,256,0,0,0>", gemm_w4_pair_kernel<256, 256, false, false, kEpiF32>,
+                    dim3((unsigned)(n0 + n1)), dim3(256), s, b0, b1, (int)n0);
+    }
   }
   return TPMLP_OK;
 }

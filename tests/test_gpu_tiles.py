@@ -195,6 +195,34 @@ def test_tp_mlp_bwd_trio_256x256_ragged():
         assert_close(to_f64(got), g[name], "bf16", name)
 
 
+def test_tp_mlp_bwd_wgrad_pair_several_rounds_ragged():
+    """The MLP backward with T = 200, h = 12200, F/tp = 6104: each weight gradient is 24 x 48 tiles of
+    256x256 (1152, five rounds of the 256 CUs with the last half full), so the two run in one launch of
+    the four-wave pair kernel (nine rounds), the second's tiles after the first's; ragged M and N in
+    both (12200 = 47 x 256 + 168, 6104 = 23 x 256 + 216) and K = 200 ending in a partial 64-deep
+    step.  dX then runs on its own launch."""
+    need_gpu()
+    T, h, F = 200, 12200, 6104
+    _say(f"mlp wgrad pair over several rounds T={T} h={h} F={F}")
+    wl = synth.Workload("t", 43, "bf16", T=T, h=h, F=F, tp=1, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
+    raw = synth.mlp_inputs(wl)
+    f = {k: synth.to_f64(v, "bf16") for k, v in raw.items()}
+    X, W1, W2, b1, dZ = (to_dev(raw[k], "bf16") for k in ("X", "W1", "W2", "b1", "dZ"))
+    A, H, Z = empty((T, F), "bf16"), empty((T, F), "bf16"), empty_f32((T, h))
+    dX, dW1, db1, dW2 = empty_f32((T, h)), empty_f32((h, F)), empty_f32((F,)), empty_f32((F, h))
+    tl.tp_mlp_fwd(X, W1, b1, W2, 1, A, Z, H_save=H)
+
+    def run():
+        tl.tp_mlp_bwd(X, W1, W2, H, A, dZ, 1, dX, dW1, dW2, db1_shard=db1)
+
+    syms = _launched(run)
+    _has(syms, "gemm_w4_pair_kernel<256,256,0,0,0>")
+    assert not any("trio" in k or "256,256,0,0,0>" in k and "pair" not in k for k in syms), syms
+    g = ref.tp_mlp_bwd_shard(f["X"], f["W1"], f["b1"], f["W2"], f["dZ"], 1, 0)
+    for name, got in (("dX", dX), ("dW1", dW1), ("db1", db1), ("dW2", dW2)):
+        assert_close(to_f64(got), g[name], "bf16", name)
+
+
 @pytest.mark.parametrize("T,h,F,tile,dact", [
     (8000, 136, 2000, "256,256", "gemm_w4_duo_kernel<256,256,0,0,0,1,1,4>"),
     (8000, 136, 1720, "256,256", "gemm_w4_kernel<256,256,1,1,4>"),
