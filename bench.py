@@ -193,6 +193,27 @@ def algorithmic_bytes(wl, role):
         else _proj_bytes(wl, role)
 
 
+def hbm_role_bytes(wl, role, colsum_bm=256):
+    """Algorithmic HBM bytes of one launch of a memory-bound role of the step:
+    the partial sum reads the tp partials of its rows and writes their sum
+    (rows [0, T/tp): this GPU's share, or all T rows in the forward-only
+    step); the db1 reduction reads one fp32 row of column sums per tile row of
+    the dH product (colsum_bm rows a tile) and writes db1.  None for others."""
+    T, h, Fs, tp = wl.T, wl.h, wl.Fs, wl.tp
+    if role == "partial_sum":
+        rows = T if (wl.kind == "mlp" and wl.dz_std is None) else T // tp
+        return (tp + 1) * rows * h * 4
+    if role == "colsum":
+        return (((T + colsum_bm - 1) // colsum_bm) * Fs + Fs) * 4
+    return None
+
+
+def tile_rows(sym):
+    """BM of a GEMM kernel symbol such as gemm_w4_kernel<128,128,1,1,2> (None if not one)."""
+    m = re.search(r"<(\d+),", sym or "")
+    return int(m.group(1)) if m else None
+
+
 def _proj_bytes(wl, role):
     T, h = wl.T, wl.h
     hs = wl.heads // wl.tp
@@ -226,20 +247,37 @@ def _time_sample(run, probe, T, target_s):
     return rows, reps, dt
 
 
+def _blas_info():
+    """(BLAS threads, 'library version') of numpy's BLAS as threadpoolctl sees it."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in libs] or [1])
+        blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in libs) or None
+        return threads, blas
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1, None
+
+
+def _host_ram_gb():
+    try:
+        with open("/proc/meminfo") as f:
+            kib = int(next(ln for ln in f if ln.startswith("MemTotal")).split()[1])
+        return round(kib / 2**20, 1)
+    except (OSError, StopIteration, ValueError):
+        return None
+
+
 def cpu_baseline(wl, raw, target_s: float):
     """Time the float64 oracle (fwd + bwd of shard 0) on a sample of rows."""
     import synth
     from oracle import ref
     from oracle import swiglu as sw
     from oracle import sp as osp
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    threads, blas = _blas_info()
     Fs = wl.Fs
     if wl.kind == "proj":
-        return _cpu_baseline_proj(wl, raw, target_s, threads)
+        return _cpu_baseline_proj(wl, raw, target_s, threads, blas)
     if wl.kind == "swiglu":
         W_gu = sw.pack_shard(synth.to_f64(raw["W_gate"], wl.dtype), synth.to_f64(raw["W_up"], wl.dtype), wl.tp, 0)
         Wd = synth.to_f64(raw["W_down"][:Fs], wl.dtype)
@@ -249,6 +287,7 @@ def cpu_baseline(wl, raw, target_s: float):
         b1 = synth.to_f64(raw["b1"][:Fs], wl.dtype) if "b1" in raw else None
 
     fwd_only = "dZ" not in raw
+    calls = []   # (forward seconds, backward seconds) of every run() call
 
     def run_fwd(rows):
         # every shard's forward, then the sum of the partials (the forward-only workload's step)
@@ -263,7 +302,9 @@ def cpu_baseline(wl, raw, target_s: float):
                 H = H + synth.to_f64(raw["b1"][i * Fs:(i + 1) * Fs], wl.dtype)[None, :]
             parts.append(ref.matmul(ref.gelu_tanh(H), W2i))
         ref.shard_partial_sum(parts)
-        return time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        calls.append((dt, 0.0))
+        return dt
 
     def run(rows):
         if fwd_only:
@@ -278,6 +319,7 @@ def cpu_baseline(wl, raw, target_s: float):
             G, U = sw.deinterleave(ref.matmul(X, W_gu))
             A = sw.silu(G) * U
             out = [ref.matmul(A, Wd)]
+            t_fwd = time.perf_counter()
             dA = ref.matmul(dZ, Wd.T)
             dGU = sw.interleave(dA * U * sw.silu_grad(G), dA * sw.silu(G))
             out += [ref.matmul(A.T, dZ), ref.matmul(X.T, dGU), ref.matmul(dGU, W_gu.T)]
@@ -285,6 +327,7 @@ def cpu_baseline(wl, raw, target_s: float):
             H = ref.matmul(X, W1) + (b1[None, :] if b1 is not None else 0.0)
             A = ref.gelu_tanh(H)
             out = [ref.matmul(A, W2)]
+            t_fwd = time.perf_counter()
             dA = ref.matmul(dZ, W2.T)
             dH = dA * ref.gelu_tanh_grad(H)
             out += [ref.matmul(A.T, dZ), ref.matmul(X.T, dH), ref.matmul(dH, W1.T)]
@@ -294,11 +337,16 @@ def cpu_baseline(wl, raw, target_s: float):
             out.append(osp.dropout_bwd(dZ, synth.SP_DROPOUT_P, wl.seed, 0))
             out.append(osp.layernorm_bwd(Xr, raw["ln_gamma"], out[3])["dX"])
         del out
-        return time.perf_counter() - t0
+        t1 = time.perf_counter()
+        calls.append((t_fwd - t0, t1 - t_fwd))
+        return t1 - t0
 
     rows, reps, dt = _time_sample(run, min(wl.T, 256), wl.T, target_s)
     flops = step_flops(wl) * rows / wl.T * reps
+    measured = calls[-reps:]   # the calls dt covers (the probe call comes first)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "fwd_seconds": round(sum(c[0] for c in measured), 6), "bwd_seconds": round(sum(c[1] for c in measured), 6),
+            "blas": blas, "host_ram_gb": _host_ram_gb(),
             "sample": (f"float64 numpy oracle, all {wl.tp} shards' forward and their partial sum" if fwd_only else
                        "float64 numpy oracle, shard 0 fwd+bwd") +
                       f" on the first {rows} of {wl.T} token rows (h={wl.h}, F/tp={Fs})" +
@@ -308,7 +356,7 @@ def cpu_baseline(wl, raw, target_s: float):
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
-def _cpu_baseline_proj(wl, raw, target_s, threads):
+def _cpu_baseline_proj(wl, raw, target_s, threads, blas=None):
     """The attention block oracle (shard 0 fwd+bwd) on a causal sequence made of
     the first rows tokens; the flops use the same count at that length."""
     import synth
@@ -330,6 +378,7 @@ def _cpu_baseline_proj(wl, raw, target_s, threads):
                       f"first {rows} of {wl.T} tokens (h={wl.h}, {wl.heads // wl.tp} heads)" +
                       (f", {reps} repetitions" if reps > 1 else "") + f"; {dt:.2f} s for "
                       f"{flops / 1e9:.1f} GFLOP",
+            "fwd_seconds": None, "bwd_seconds": None, "blas": blas, "host_ram_gb": _host_ram_gb(),
             "seconds": round(dt, 3), "host_cpus": os.cpu_count(),
             "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
@@ -785,6 +834,22 @@ def workload_text(wl):
             f"fp32 accumulate; fwd+bwd plus this GPU's 1/tp share of the output and dX partial sums")
 
 
+def smi_sclk_mhz():
+    """GPU 0's shader clock as rocm-smi reports it at this moment, in MHz
+    (None when rocm-smi is missing or prints no sclk line)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", r.stdout, re.I)
+    return int(m.group(1)) if m else None
+
+
 def run_bench(args):
     import torch
     import synth
@@ -810,6 +875,7 @@ def run_bench(args):
     gc.collect()
     gc.freeze()
     gc.disable()
+    smi_before = smi_sclk_mhz()   # before the warm-up, so that the query's idle time precedes it
 
     # Warm-up, with every kernel timed once to find the dominant one.
     tl.profile_enable("")
@@ -839,6 +905,7 @@ def run_bench(args):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    smi_after = smi_sclk_mhz()
     timed = tl.profile_collect()
     tl.profile_enable(None)
     ms_step = e0.elapsed_time(e1) / args.steps
@@ -924,11 +991,10 @@ def run_bench(args):
             entry["sclk_ghz"] = round(sum(clocks) / len(clocks), 3)
         if role.startswith("gemm") or role_flops(wl, role):
             entry["tflops"] = round(role_flops(wl, role) / (us * 1e-6) / 1e12, 1)
-        elif role == "partial_sum":
-            entry["gbs"] = round((tp + 1) * step.rows * h * 4 / (us * 1e-6) / 1e9, 1)
-        elif role == "colsum":
-            # the per-tile column sums of dH (one row per 256-row tile) in, db1 out
-            entry["gbs"] = round((((T + 255) // 256) * Fs + Fs) * 4 / (us * 1e-6) / 1e9, 1)
+        elif role in ("partial_sum", "colsum"):
+            bm = tile_rows(by_role.get("gemm.mlp_dgrad_act", (0, 0, "", []))[2]) or 256
+            nbytes = hbm_role_bytes(wl, role, bm)
+            entry["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         kernels[role] = entry
 
     out = {
@@ -951,6 +1017,9 @@ def run_bench(args):
                    "global_batch": T, "seq_len": None, "parallelism": f"tp{tp} shard simulated on 1 GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "step_ms": step_ms,
+        "sclk_rocm_smi_mhz": {"before_warmup": smi_before, "after_timed": smi_after,
+                              "note": "instantaneous readings outside the timed steps; the clock the dominant "
+                                      "kernel ran at is roofline.sclk_ghz (sampled in-kernel)"},
         "cold": cold,
         "roofline": roofline,
         "parts": parts,
@@ -1066,13 +1135,20 @@ def summarize_profile(d):
              f"(copy read {scaled['_calibration']['FETCH_SIZE']['counter_kib']:.0f} KiB)",
              f"  WRITE_SIZE factor {scaled['_calibration']['WRITE_SIZE']['factor']:.4f} "
              f"(copy wrote {scaled['_calibration']['WRITE_SIZE']['counter_kib']:.0f} KiB)", "",
-             f"{'role':22s} {'kernel':44s} {'fetch MB':>9s} {'write MB':>9s}"]
+             "alg MB: the algorithmic bytes of the launch (operands and outputs once each); "
+             "ratio: (fetch + write) / alg MB.", "",
+             f"{'role':22s} {'kernel':44s} {'fetch MB':>9s} {'write MB':>9s} {'alg MB':>9s} {'ratio':>6s}"]
+    import synth
+    wl = synth.WORKLOADS[roles["workload"]]
+    bm = tile_rows(scaled.get("gemm.mlp_dgrad_act", {}).get("kernel")) or 256
     for role, e in scaled.items():
         if role.startswith("_"):
             continue
         fb, wb = e["FETCH_SIZE"][1], e["WRITE_SIZE"][1]
-        launches[role] = {"kernel": e["kernel"], "fetch_bytes": fb, "write_bytes": wb}
-        lines.append(f"{role:22s} {e['kernel']:44s} {fb / 1e6:9.1f} {wb / 1e6:9.1f}")
+        alg = algorithmic_bytes(wl, role) if role.startswith("gemm") else hbm_role_bytes(wl, role, bm)
+        launches[role] = {"kernel": e["kernel"], "fetch_bytes": fb, "write_bytes": wb, "algorithmic_bytes": alg}
+        tail = f" {alg / 1e6:9.1f} {(fb + wb) / alg:6.2f}" if alg else f" {'-':>9s} {'-':>6s}"
+        lines.append(f"{role:22s} {e['kernel']:44s} {fb / 1e6:9.1f} {wb / 1e6:9.1f}" + tail)
     with open(os.path.join(PROFILES, f"{roles['workload']}_step_hbm_traffic.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(traffic_path(roles["workload"]), "w") as f:

@@ -64,3 +64,30 @@ def test_joined_roles_sum_their_parts():
         bench.role_flops(wl, "gemm.swiglu_dgrad_act")
     assert bench.algorithmic_bytes(wl, j) == bench.algorithmic_bytes(wl, "gemm.swiglu_wgrad2") + \
         bench.algorithmic_bytes(wl, "gemm.swiglu_dgrad_act")
+
+
+def test_cpu_baseline_reports_its_split_and_host():
+    """The oracle's CPU time on a small MLP shard: the forward and backward
+    seconds of the measured calls add up to the reported time, and the BLAS
+    library and host memory are named."""
+    wl = synth.Workload("t", 3, "bf16", T=64, h=64, F=256, tp=2, x_std=1.0, w_std=0.05, b_std=0.1, dz_std=1.0)
+    out = bench.cpu_baseline(wl, synth.mlp_inputs(wl), 0.3)
+    assert out["kind"] == "oracle" and out["value"] > 0
+    assert abs(out["fwd_seconds"] + out["bwd_seconds"] - out["seconds"]) <= 0.01 + 0.05 * out["seconds"]
+    assert out["fwd_seconds"] > 0 and out["bwd_seconds"] > 0
+    assert out["host_ram_gb"] is None or out["host_ram_gb"] > 0
+    assert "blas" in out
+
+
+def test_memory_bound_role_bytes():
+    """The partial sum of this GPU's T/tp rows reads tp partials and writes one
+    sum (all T rows in the forward-only step); the db1 reduction reads one row
+    of column sums per tile row of the dH product."""
+    wl = synth.WORKLOADS["llama7b_bf16"]
+    assert bench.hbm_role_bytes(wl, "partial_sum") == (8 + 1) * (8192 // 8) * 4096 * 4
+    tiny = synth.WORKLOADS["tiny_f32"]
+    assert bench.hbm_role_bytes(tiny, "partial_sum") == 3 * 128 * 256 * 4
+    g = synth.WORKLOADS["gpt2m_bf16"]
+    assert bench.hbm_role_bytes(g, "colsum", 128) == (4096 // 128 * 2048 + 2048) * 4
+    assert bench.hbm_role_bytes(g, "gemm.mlp_fwd1") is None
+    assert bench.tile_rows("gemm_w4_kernel<128,128,1,1,2>") == 128 and bench.tile_rows("partial_sum_kernel<4>") is None
