@@ -63,12 +63,23 @@ COLD_FLUSH_BYTES = 512 << 20   # written between steps by the cold-cache timing
 
 CALIB_BYTES = 256 << 20     # the plain copy used to scale the HBM byte counters
 
+# Default warm-up.  After the GPU has idled, the first tens of milliseconds of
+# steps run slower while its clocks ramp up: measured on the Llama-7B shard,
+# 50 steps timed after 10 warm-up steps took 0.676 ms each, after 50 to 400
+# warm-up steps 0.651-0.657 ms.  So by default the warm-up runs at least this
+# many steps and this long; `--warmup W` runs exactly W steps instead.
+WARMUP_MIN_STEPS = 100
+WARMUP_MIN_S = 0.15
+WARMUP_PROFILED = 10        # the last warm-up steps, timed per kernel to find the dominant one
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least %d steps and %.0f ms, until the clocks settle)"
+                    % (WARMUP_MIN_STEPS, WARMUP_MIN_S * 1e3))
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing")
     ap.add_argument("--workload", default="llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -877,9 +888,25 @@ def run_bench(args):
     gc.disable()
     smi_before = smi_sclk_mhz()   # before the warm-up, so that the query's idle time precedes it
 
-    # Warm-up, with every kernel timed once to find the dominant one.
+    # Warm-up: plain steps until the clocks settle, then the last few with
+    # every kernel timed to find the dominant one.
+    profiled = WARMUP_PROFILED if args.warmup is None else max(1, min(args.warmup, WARMUP_PROFILED))
+    plain = 0
+    t_w = time.perf_counter()
+    if args.warmup is None:
+        while plain < WARMUP_MIN_STEPS - profiled or time.perf_counter() - t_w < WARMUP_MIN_S:
+            step()
+            plain += 1
+            if plain % 10 == 0:
+                torch.cuda.synchronize()   # count GPU time, not launch time
+    else:
+        for _ in range(max(0, args.warmup - profiled)):
+            step()
+            plain += 1
+    torch.cuda.synchronize()
+    warmup_steps = plain + profiled
     tl.profile_enable("")
-    for _ in range(max(1, args.warmup)):
+    for _ in range(profiled):
         step()
     torch.cuda.synchronize()
     warm = tl.profile_collect()
@@ -1006,7 +1033,7 @@ def run_bench(args):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup_steps,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
