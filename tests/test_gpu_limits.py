@@ -61,3 +61,31 @@ def test_column_parallel_layer_at_the_largest_leading_dimension():
     assert_close(to_f64(dX), g["dX"], "bf16", "dX")
     assert_close(to_f64(dW), g["dW"], "bf16", "dW")
     assert_close(to_f64(db), g["db"], "bf16", "db")
+
+
+def test_outputs_past_two_to_the_31_elements():
+    """Z = X W (fp32) and Y = GeLU(X W + b) with H saved (bf16), X [33000, 64], W [64, 65536]: the
+    outputs hold 2.16e9 elements, so element indices pass 2^31 from row 32768 on, which is also where
+    the last, ragged row of 256-row tiles starts (232 rows).  The first rows, rows on both sides of
+    32768 and rows through the end of that tile row against the oracle, row by row."""
+    need_gpu()
+    T, K, N = 33000, 64, 65536
+    print(f"outputs past 2^31 elements: T={T} K={K} N={N}", flush=True)
+    Xr, Wr = synth.draw(62, 0, (T, K), 1.0, "bf16"), synth.draw(62, 1, (K, N), 0.05, "bf16")
+    br = synth.draw(62, 2, (N,), 0.1, "bf16")
+    X, W, b = to_dev(Xr, "bf16"), to_dev(Wr, "bf16"), to_dev(br, "bf16")
+    rows = np.r_[0:3, 32766:32771, T - 105:T - 102, T - 3:T]
+    fW, fb = synth.to_f64(Wr, "bf16"), synth.to_f64(br, "bf16")
+    fX = synth.to_f64(Xr[rows], "bf16")
+    Z = empty_f32((T, N))
+    tl.row_parallel_fwd(X, W, 1, Z)
+    sync()
+    assert_close(to_f64(Z[torch.from_numpy(rows).cuda()]), ref.row_parallel_fwd_shard(fX, fW), "bf16", "Z rows")
+    del Z
+    Y, H = empty((T, N), "bf16"), empty((T, N), "bf16")
+    tl.column_parallel_fwd(X, W, 1, Y, bias_shard=b, H_save=H)
+    sync()
+    Hr, Yr = ref.column_parallel_fwd(fX, fW, fb, 1, 0)
+    idx = torch.from_numpy(rows).cuda()
+    assert_close(to_f64(H[idx]), Hr, "bf16", "H rows")
+    assert_close(to_f64(Y[idx]), Yr, "bf16", "Y rows")
