@@ -25,6 +25,8 @@ Machine probes (libtpmlp_probe.so, no MLP work):
   --probe                   per-CU load-path rate for the GEMM tiles' operand
                             patterns and LDS fragment-read rates, the bounds
                             the GEMM design is measured against
+  --power                   board power (hwmon) against its cap while the
+                            workload's step runs back to back for 3 s
 """
 from __future__ import annotations
 
@@ -90,6 +92,8 @@ def parse():
     ap.add_argument("--profile-pass", metavar="OUT_JSON", default=None)
     ap.add_argument("--summarize-profile", metavar="DIR", default=None)
     ap.add_argument("--probe", action="store_true", help="run the machine probes and exit")
+    ap.add_argument("--power", action="store_true",
+                    help="sample the board power (hwmon) while the workload's step runs back to back, and exit")
     return ap.parse_args()
 
 
@@ -1247,10 +1251,78 @@ def run_probes():
     print(json.dumps(res))
 
 
+POWER_SECONDS = 3.0      # back-to-back steps timed by --power
+POWER_SAMPLE_S = 0.02
+
+
+def run_power(args):
+    """Board power while the workload's step runs back to back: the GPU's
+    hwmon power1_input (instantaneous, microwatts) and power1_cap, read from
+    sysfs by a host thread every 20 ms; the first 0.5 s is left out.  Prints
+    one text line and one JSON line."""
+    import threading
+    import torch
+    import synth
+    import linear_layers_amd as tl
+    mons = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    if not mons or not torch.cuda.is_available():
+        raise SystemExit("no GPU power sensor (hwmon power1_input) or no GPU visible")
+    hw = os.path.dirname(mons[0])
+
+    def read(name):
+        try:
+            with open(os.path.join(hw, name)) as f:
+                return int(f.read())
+        except (OSError, ValueError):
+            return None
+
+    wl = synth.WORKLOADS[args.workload]
+    _, step = make_step(wl, tl, torch)
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    idle = read("power1_input")
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            samples.append((time.perf_counter(), read("power1_input"), read("temp2_input")))
+            time.sleep(POWER_SAMPLE_S)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < POWER_SECONDS:
+        step()
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    gc.enable()
+    watts = sorted(p / 1e6 for t, p, _ in samples if t - t0 > 0.5 and p is not None)
+    temps = [c / 1e3 for t, _, c in samples if t - t0 > 0.5 and c is not None]
+    cap = read("power1_cap")
+    res = {"workload": wl.name, "steps": n, "ms_per_step": round(wall / n * 1e3, 4),
+           "power_cap_w": cap / 1e6 if cap else None, "idle_w": idle / 1e6 if idle else None,
+           "samples": len(watts), "median_w": watts[len(watts) // 2], "p10_w": watts[len(watts) // 10],
+           "p90_w": watts[9 * len(watts) // 10], "max_w": watts[-1],
+           "junction_c": [min(temps), max(temps)] if temps else None}
+    print(f"{wl.name}: {n} steps in {wall:.2f} s; power cap {res['power_cap_w']} W, idle {res['idle_w']} W; "
+          f"under load median {res['median_w']:.0f} W (p10 {res['p10_w']:.0f}, p90 {res['p90_w']:.0f}, "
+          f"max {res['max_w']:.0f}); junction {res['junction_c']} C", flush=True)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.probe:
         run_probes()
+        return
+    if args.power:
+        run_power(args)
         return
     if args.summarize_profile:
         summarize_profile(args.summarize_profile)
