@@ -54,7 +54,7 @@ constexpr int kAttnBQ = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kAttnBK = 64;   // keys per block
 
 // Causal work split along keys: query block b of 128 rows sees up to 2 (b + 1)
-// key blocks of 64; they are taken in chunks of kc key blocks (kc even: 32,
+// key blocks of 64; they are taken in chunks of kc key blocks (kc even: 26,
 // more where a block would otherwise have more than 8 chunks), one workgroup
 // per (block, chunk).  Chunk c exists for blocks b >= c * kc / 2.  Work items are numbered
 // chunk by chunk, the blocks of one chunk from the last down:

@@ -1385,12 +1385,13 @@ struct AttnFwdWs {
   size_t lse_off, total;
 };
 
-// Key blocks per chunk (at least): 32 (2048 keys) measured best for 4096
-// causal tokens, for the forward (80 + 8 us merge, against 87 + 13 at 16 and
-// 83 + 20 at 8) and for dQ (101 + 7.5 us sum, against 102 + 9 at 24 and
-// 107 + 11 at 16).
-constexpr int64_t kAttnFwdMinKc = 32;
-constexpr int64_t kAttnDqMinKc = 32;
+// Key blocks per chunk (at least): 26 (1664 keys) measured best for 4096
+// causal tokens and 10 heads on the current kernels, for the forward (62 + 9.5
+// us merge, against 72 + 8 at 32, 68.6 + 9.8 at 30, 65.3 + 9.4 at 28 and
+// 63 + 10 at 24) and for dQ (81 + 8.8 us sum, against 91 + 7.5 at 32 and
+// 81 + 9.5 at 24): the longest work item shortens more than the merge grows.
+constexpr int64_t kAttnFwdMinKc = 26;
+constexpr int64_t kAttnDqMinKc = 26;
 
 AttnFwdWs attn_fwd_ws(int64_t batch, int64_t seq, int64_t heads) {
   AttnFwdWs w{0, 0};

@@ -168,9 +168,11 @@ def test_attn_validation():
     assert f(None, 1, 8, 2, 128, 1, 0.1, P, 128, P, 256, P, 256, P, 256, None, None, 0) == E_SHAPE   # ldq < heads*128
     assert f(None, 1, 8, 1, 128, 1, 0.1, None, 128, P, 128, P, 128, P, 128, None, None, 0) == E_NULL
     assert f(None, 1, 8, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P + 8, 128, None, None, 0) == E_ALIGN
-    # causal, 4096 tokens: key chunks need the workspace (checked after the shapes)
+    # causal, 4096 tokens: key chunks need the workspace (checked after the shapes); up to 1664
+    # tokens (26 key blocks of 64, one chunk) every query block is whole and none is needed
     need = tl.attn_fwd_workspace_bytes(1, 4096, 1)
-    assert need >= 2 * 16 * 128 * 128 * 4 and tl.attn_fwd_workspace_bytes(1, 2048, 1) == 0
+    assert need >= 2 * 16 * 128 * 128 * 4
+    assert tl.attn_fwd_workspace_bytes(1, 1664, 1) == 0 and tl.attn_fwd_workspace_bytes(1, 1728, 1) > 0
     fw = [None, 1, 4096, 1, 128, 1, 0.1, P, 128, P, 128, P, 128, P, 128, None]
     assert f(*fw, None, 0) == E_NULL
     assert f(*fw, P, need - 1) == E_WS
@@ -199,8 +201,10 @@ def test_attn_block_validation():
     fw = [None, 1, 4096, 512, 4, 128, 2, 1, 0.1, P, P, P, P, P, P, P]
     assert f(*fw, None, 0) == E_NULL
     assert f(*fw, P, need - 1) == E_WS
-    # causal dQ partials: none up to 2048 tokens; at 32K tokens at most 8 key chunks per query block
-    assert tl.attn_bwd_workspace_bytes(1, 2048, 10) == 2 * 2048 * 10 * 4
+    # causal dQ partials: none up to 1664 tokens (one chunk of 26 key blocks); at 32K tokens at most
+    # 8 key chunks per query block
+    assert tl.attn_bwd_workspace_bytes(1, 1664, 10) == 2 * 1664 * 10 * 4
+    assert tl.attn_bwd_workspace_bytes(1, 1728, 10) > 2 * 1728 * 10 * 4
     assert tl.attn_bwd_workspace_bytes(1, 32768, 10) <= 2 * 32768 * 10 * 4 + 256 * 10 * 4.5 * 65536
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 3) == 0
     assert tl.lib.tp_attn_bwd_workspace_bytes(1, 8, 4, 128, 2) >= 8 * 256 * 2 * 4

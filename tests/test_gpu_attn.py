@@ -42,8 +42,8 @@ def _qkv(seed, T, heads, std=1.0):
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 300, 2, False), (3, 128, 1, True),
                                                     (1, 1000, 2, True),
-                                                    # causal query blocks past row 2048 split their keys into
-                                                    # chunks of 2048, merged by log-sum-exp (2 and 3 chunks,
+                                                    # causal query blocks past row 1664 split their keys into
+                                                    # chunks of 1664, merged by log-sum-exp (2 and 3 chunks,
                                                     # ragged last block)
                                                     (2, 1100, 1, True), (1, 2100, 2, True), (1, 2100, 1, False),
                                                     (1, 4200, 1, True)])
@@ -106,9 +106,9 @@ def test_attn_fwd_split_workspace():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("batch,seq,heads,chunk", [(2, 8400, 2, 2048), (1, 16500, 1, 2176)])
+@pytest.mark.parametrize("batch,seq,heads,chunk", [(2, 8400, 2, 1664), (1, 16500, 1, 2176)])
 def test_attn_fwd_long_sequence_sampled(batch, seq, heads, chunk):
-    """Long causal sequences (ragged): 8400 tokens take 5 key chunks of 2048; past 16384 tokens the chunks
+    """Long causal sequences (ragged): 8400 tokens take 6 key chunks of 1664; past 13312 tokens the chunks
     grow (34 key blocks of 64 at 16500, 8 chunks for the last query block).  Sampled rows of O and lse of
     every (sequence, head) against the oracle, on both sides of the chunk edges."""
     need_gpu()
@@ -185,8 +185,8 @@ def _bwd_case(batch, seq, heads, causal, seed, scale=None):
 @pytest.mark.parametrize("batch,seq,heads,causal", [(1, 1, 1, True), (2, 77, 3, True), (2, 77, 3, False),
                                                     (1, 300, 2, True), (1, 130, 1, False), (3, 128, 1, True),
                                                     (1, 1000, 2, True), (1, 1000, 1, False),
-                                                    # causal query blocks past row 2048 split their keys into
-                                                    # chunks of 2048 (2 and 3 chunks here, ragged last block)
+                                                    # causal query blocks past row 1664 split their keys into
+                                                    # chunks of 1664 (2 and 3 chunks here, ragged last block)
                                                     (2, 1100, 1, True), (1, 2100, 2, True), (1, 4200, 1, True)])
 def test_attn_bwd(batch, seq, heads, causal):
     need_gpu()
@@ -238,7 +238,7 @@ def test_attn_bwd_workload_two_heads():
 
 @pytest.mark.slow
 def test_attn_bwd_long_sequence_sampled():
-    """8400 tokens (ragged), 2 sequences, 2 heads, causal: 5 dQ key chunks of 2048 for the last query
+    """8400 tokens (ragged), 2 sequences, 2 heads, causal: 6 dQ key chunks of 1664 for the last query
     block.  Sampled rows of dQ, dK, dV of two (sequence, head) pairs against the oracle, rows on both sides
     of the chunk edges."""
     need_gpu()
@@ -247,7 +247,8 @@ def test_attn_bwd_long_sequence_sampled():
     qkv, dO, dqkv = _bwd_case(batch, seq, heads, True, seed=8400)
     w = heads * D
     f, fd, g = synth.to_f64(qkv, "bf16"), synth.to_f64(dO, "bf16"), to_f64(dqkv)
-    rows = np.array([0, 1, 127, 2047, 2048, 2049, 4095, 4096, 6143, 6144, 8191, 8192, 8270, 8271, 8399])
+    rows = np.array([0, 1, 127, 1663, 1664, 1665, 3327, 3328, 4991, 4992, 6655, 6656, 8191, 8192, 8270, 8271,
+                     8399])
     for b, hd in ((0, 0), (1, 1)):
         ref = oat.attn_bwd_rows(f[:, :w], f[:, w:2 * w], f[:, 2 * w:], fd, batch, seq, heads, D, True, D ** -0.5,
                                 b, hd, rows)
